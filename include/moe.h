@@ -1,0 +1,157 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse-MoE decode layer.
+ *
+ * The layer (per token t of a decode batch of T tokens, E experts, top_k = k):
+ *   logits[t, e] = sum_h W_r[e, h] * x[t, h]  (+ bias[e])
+ *   ids[t, 0..k)  = the k largest logits, ordered by (logit descending,
+ *                   expert index ascending); ties go to the lower index
+ *   w[t, j]       = softmax over all E logits, renormalised over the k chosen
+ *   routes r = t*k + j are grouped by expert with a stable counting sort
+ *   pass 1: for each unique expert e, each row of gate_up[e] is read once and
+ *           applied to every route of e:  g = gate_up[e][i]   . x[t]
+ *                                         u = gate_up[e][I+i] . x[t]
+ *                                         a[r, i] = silu(g) * u
+ *   pass 2: each row of down[e] is read once and applied to every route of e:
+ *           y[r, h] = down[e][h] . a[r]
+ *   combine: out[t, h] = sum_j w[t, j] * y[t*k + j, h]   (j ascending)
+ *
+ * Sources (page title, section):
+ *  - "MoE Performance Optimization Analysis" (markbaseengine): Root Cause
+ *    (router, top-expert selection, experts, combine per layer) and Option 1 /
+ *    GPU Router Design (router, selection and dispatch on the device, no host
+ *    read and no wait per layer).
+ *  - "perf(cpu-moe): dedup experts across the batch in pass 1" (FreeToken
+ *    PR #46), commit message and "What this adds": routes grouped by expert
+ *    with a counting sort over their ids; pass 1 split by (unique expert, row
+ *    block) with the expert's routes as the inner loop; pass 2 (down) per
+ *    route, or deduplicated the same way as the follow-up change does.
+ *  - "TEXT Generation Optimization Report" (markbaseengine), Phase 1: a whole
+ *    forward recorded as one submission with one wait.
+ *  The gating function (softmax, top-k, renormalise), SiLU(gate) * up, the
+ *  gate/up row split [0, I) / [I, 2I) and the lowest-index tie rule are the
+ *  workload's definition; the pages leave them open.
+ *
+ * Conventions for every entry point:
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *    library never allocates, frees or caches device memory; scratch comes
+ *    from the caller's workspace `ws` of `ws_bytes` bytes (see
+ *    moe_workspace_bytes).  Workspace contents need not be initialised and
+ *    are clobbered.
+ *  - Calls only enqueue work on `stream` (a hipStream_t; NULL = the null
+ *    stream) and return.  They never synchronise or read device memory back,
+ *    so they can be recorded into a HIP graph.
+ *  - Layout is row-major and contiguous.  Activations, logits, weights of the
+ *    combine and outputs are fp32; expert weights are fp32, bf16 or OCP fp8
+ *    E4M3 with fp32 scales per 128x128 block; the router is fp32 or bf16.
+ *  - The status covers host-side validation and launch errors only.  A
+ *    device fault shows up at the caller's next synchronisation.  Inputs must
+ *    be finite: NaN or Inf give an unspecified routing.
+ *  - T == 0 is a no-op that returns MOE_OK.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_ARG = 1,         /* NULL pointer, negative size, k < 1 or k > E ... */
+    MOE_ERR_SHAPE = 2,       /* size limits or divisibility (see below)       */
+    MOE_ERR_DTYPE = 3,       /* unknown dtype or combination                   */
+    MOE_ERR_WORKSPACE = 4,   /* ws NULL or smaller than required               */
+    MOE_ERR_HIP = 5,         /* a HIP launch reported an error                 */
+    MOE_ERR_UNSUPPORTED = 6, /* valid request this build does not implement    */
+    MOE_ERR_ALIGN = 7        /* a pointer is not 16-byte aligned               */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+
+/* One MoE layer.  Limits: 1 <= E <= 1024, 1 <= top_k <= min(E, 32);
+ * H, I >= 1 with H, I multiples of 4 (fp32), 8 (bf16) or 128 (fp8), and at
+ * most 512 16-byte chunks per weight row (H, I <= 2048 fp32, 4096 bf16,
+ * 8192 fp8).  Weight pointers must be 16-byte aligned. */
+typedef struct {
+    int32_t E, top_k, H, I;
+    int32_t router_dtype;     /* MOE_F32 or MOE_BF16                          */
+    int32_t expert_dtype;     /* MOE_F32, MOE_BF16 or MOE_FP8_E4M3            */
+    const void *w_router;     /* [E, H]                                       */
+    const void *w_gate_up;    /* [E, 2I, H]: rows [0, I) gate, [I, 2I) up     */
+    const void *w_down;       /* [E, H, I]                                    */
+    const float *s_gate_up;   /* fp8 only: [E, 2I/128, H/128] block scales    */
+    const float *s_down;      /* fp8 only: [E, H/128, I/128] block scales     */
+    const float *router_bias; /* [E] added to the logits, or NULL             */
+} moe_layer_t;
+
+/* flags */
+enum {
+    MOE_WALK_DEDUP = 0,        /* pass 1 and pass 2 once per unique expert     */
+    MOE_WALK_PER_ROUTE = 1,    /* every route reads its expert itself          */
+    MOE_WALK_DEDUP_PASS1 = 2,  /* pass 1 per unique expert, pass 2 per route   */
+    MOE_WALK_MASK = 0xF,
+    MOE_ACCUM_RESIDUAL = 1 << 4, /* out = x + MoE(...) (x = the layer input)   */
+    MOE_RMSNORM_IN = 1 << 6,     /* normalise x (eps 1e-6, gamma 1) first       */
+    MOE_NO_MFMA = 1 << 7         /* keep every segment on the GEMV path         */
+};
+
+/* Bytes of workspace needed for up to max_tokens tokens (max_tokens >= 0).
+ * Returns 0 if the layer description is invalid. */
+size_t moe_workspace_bytes(const moe_layer_t *layer, int32_t max_tokens);
+
+/* Router and selection.  Either x [T, H] (logits computed on the device from
+ * W_r and router_bias) or logits_in [T, E] (selection fed with given logits)
+ * must be non-NULL; logits_in wins if both are.  Writes topk_ids [T, k]
+ * (int32) and topk_w [T, k] (fp32) and, if non-NULL, logits_out [T, E].
+ * ws may be NULL when logits_in or logits_out is given; otherwise it must
+ * hold moe_workspace_bytes(layer, T) bytes. */
+moe_status moe_route(const moe_layer_t *layer, const float *x, const float *logits_in, int32_t T,
+                     float *logits_out, int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes,
+                     void *stream);
+
+/* Stable counting sort of the T*k routes (r = t*k + j) by expert id.
+ * counts [E]; offsets [E+1] exclusive prefix sum (offsets[E] = T*k);
+ * sorted_routes [T*k]: routes of expert 0, then 1, ..., each ascending;
+ * uniq [E]: experts with a nonzero count, ascending (first n_uniq entries);
+ * n_uniq [1].  An id outside [0, E) sets *n_uniq = -1 and leaves the other
+ * outputs unspecified (nothing is written out of bounds). */
+moe_status moe_sort(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int32_t *counts, int32_t *offsets,
+                    int32_t *sorted_routes, int32_t *uniq, int32_t *n_uniq, void *stream);
+
+/* Experts and combine for a given routing (the outputs of moe_route and
+ * moe_sort on the same ids).  x [T, H] is the expert input; out [T, H] is
+ * overwritten (flags MOE_ACCUM_RESIDUAL: out = x + combine).  The walk arm
+ * comes from flags & MOE_WALK_MASK; all arms give bitwise the same output
+ * when no segment takes the MFMA path.  out may alias x. */
+moe_status moe_expert_fwd(const moe_layer_t *layer, const float *x, int32_t T, const int32_t *topk_ids,
+                          const float *topk_w, const int32_t *counts, const int32_t *offsets,
+                          const int32_t *sorted_routes, const int32_t *uniq, const int32_t *n_uniq, float *out,
+                          uint32_t flags, void *ws, size_t ws_bytes, void *stream);
+
+/* The whole layer: [RMSNorm] -> router -> selection -> sort -> pass 1 ->
+ * pass 2 -> combine [-> + x], all on the device.  out may alias x.  After the
+ * call (once the stream reaches it) the first 16 bytes of ws hold int32
+ * {n_uniq, T*k, max routes of one expert, 0}. */
+moe_status moe_layer_fwd(const moe_layer_t *layer, const float *x, int32_t T, float *out, uint32_t flags,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/* Device addresses, inside a workspace that moe_layer_fwd used for T tokens,
+ * of the routing that call computed (valid once the stream has reached it,
+ * until the workspace is reused): topk_ids [T, k], topk_w [T, k],
+ * counts [E], offsets [E+1], sorted_routes [T*k], uniq [E], n_uniq [1].
+ * Any output pointer may be NULL.  For expert-usage telemetry and tests. */
+moe_status moe_layer_routing(const moe_layer_t *layer, int32_t T, void *ws, size_t ws_bytes, int32_t **topk_ids,
+                             float **topk_w, int32_t **counts, int32_t **offsets, int32_t **sorted_routes,
+                             int32_t **uniq, int32_t **n_uniq);
+
+/* Static text for a status code. */
+const char *moe_status_str(moe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,197 @@
+// C ABI of the gfx950 MoE decode library: host-side validation, workspace
+// carving and the launch sequence.  Nothing here allocates, synchronises or
+// reads device memory back; every call only enqueues work on the caller's
+// stream, so a stack of layers can be recorded into one HIP graph
+// ("TEXT Generation Optimization Report", Phase 1: one submission and one
+// wait per forward; "MoE Performance Optimization Analysis", Option 1: no
+// host read between router and experts).
+#include <stdint.h>
+
+#include "common.h"
+
+namespace moe {
+
+int num_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    if (dev >= 64) dev = 63;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+static moe_status check_layer(const moe_layer_t *L) {
+    if (!L) return MOE_ERR_ARG;
+    if (L->E < 1 || L->top_k < 1 || L->top_k > L->E || L->H < 1 || L->I < 1) return MOE_ERR_ARG;
+    if (L->E > kMaxE || L->top_k > kMaxK) return MOE_ERR_SHAPE;
+    if (L->router_dtype != MOE_F32 && L->router_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+    if (L->expert_dtype != MOE_F32 && L->expert_dtype != MOE_BF16 && L->expert_dtype != MOE_FP8_E4M3)
+        return MOE_ERR_DTYPE;
+    const int epc = elems_per_chunk(L->expert_dtype), repc = elems_per_chunk(L->router_dtype);
+    if (L->H % epc || L->I % epc || L->H % repc || L->H % 4 || L->I % 4) return MOE_ERR_SHAPE;
+    if (L->expert_dtype == MOE_FP8_E4M3 && (L->H % 128 || L->I % 128)) return MOE_ERR_SHAPE;
+    if (L->H / epc > kWave * kMaxChunksPerLane || L->I / epc > kWave * kMaxChunksPerLane ||
+        L->H / repc > kWave * kMaxChunksPerLane)
+        return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+static moe_status check_weights(const moe_layer_t *L, bool router, bool experts) {
+    if (router && !L->w_router) return MOE_ERR_ARG;
+    if (router && !aligned16(L->w_router)) return MOE_ERR_ALIGN;
+    if (experts) {
+        if (!L->w_gate_up || !L->w_down) return MOE_ERR_ARG;
+        if (!aligned16(L->w_gate_up) || !aligned16(L->w_down)) return MOE_ERR_ALIGN;
+        if (L->expert_dtype == MOE_FP8_E4M3 && (!L->s_gate_up || !L->s_down)) return MOE_ERR_ARG;
+    }
+    return MOE_OK;
+}
+
+static moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_layer_t *layer, int32_t max_tokens) {
+    if (check_layer(layer) != MOE_OK || max_tokens < 0) return 0;
+    return ws_layout(*layer, max_tokens).total;
+}
+
+moe_status moe_route(const moe_layer_t *layer, const float *x, const float *logits_in, int32_t T,
+                     float *logits_out, int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes,
+                     void *stream) {
+    moe_status s = check_layer(layer);
+    if (s != MOE_OK) return s;
+    if (T < 0 || !topk_ids || !topk_w || (!x && !logits_in)) return MOE_ERR_ARG;
+    if (T == 0) return MOE_OK;
+    hipStream_t st = (hipStream_t)stream;
+    const float *lg = logits_in;
+    if (!lg) {
+        if ((s = check_weights(layer, true, false)) != MOE_OK) return s;
+        if (!aligned16(x)) return MOE_ERR_ALIGN;
+        float *dst = logits_out;
+        if (!dst) {
+            const WsLayout wl = ws_layout(*layer, T);
+            if (!ws || ws_bytes < wl.total) return MOE_ERR_WORKSPACE;
+            dst = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.logits);
+        }
+        if ((s = hip_status(launch_router(*layer, x, dst, T, st))) != MOE_OK) return s;
+        lg = dst;
+    } else if (logits_out && logits_out != logits_in) {
+        if (hipMemcpyAsync(logits_out, logits_in, (size_t)T * layer->E * 4, hipMemcpyDeviceToDevice, st) !=
+            hipSuccess)
+            return MOE_ERR_HIP;
+    }
+    return hip_status(launch_select(lg, T, layer->E, layer->top_k, topk_ids, topk_w, st));
+}
+
+moe_status moe_sort(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int32_t *counts, int32_t *offsets,
+                    int32_t *sorted_routes, int32_t *uniq, int32_t *n_uniq, void *stream) {
+    if (T < 0 || k < 1 || E < 1 || k > E) return MOE_ERR_ARG;
+    if (E > kMaxE || k > kMaxK) return MOE_ERR_SHAPE;
+    if (!topk_ids || !counts || !offsets || !sorted_routes || !uniq || !n_uniq) return MOE_ERR_ARG;
+    if ((int64_t)T * k > INT32_MAX / 2) return MOE_ERR_SHAPE;
+    if (T == 0) return MOE_OK;
+    return hip_status(
+        launch_sort(topk_ids, T * k, E, counts, offsets, sorted_routes, uniq, n_uniq, nullptr, (hipStream_t)stream));
+}
+
+moe_status moe_expert_fwd(const moe_layer_t *layer, const float *x, int32_t T, const int32_t *topk_ids,
+                          const float *topk_w, const int32_t *counts, const int32_t *offsets,
+                          const int32_t *sorted_routes, const int32_t *uniq, const int32_t *n_uniq, float *out,
+                          uint32_t flags, void *ws, size_t ws_bytes, void *stream) {
+    moe_status s = check_layer(layer);
+    if (s != MOE_OK) return s;
+    if ((s = check_weights(layer, false, true)) != MOE_OK) return s;
+    if (T < 0 || !x || !topk_ids || !topk_w || !counts || !offsets || !sorted_routes || !uniq || !n_uniq || !out)
+        return MOE_ERR_ARG;
+    if ((flags & MOE_WALK_MASK) > MOE_WALK_DEDUP_PASS1) return MOE_ERR_ARG;
+    if (!aligned16(x) || !aligned16(out)) return MOE_ERR_ALIGN;
+    if (T == 0) return MOE_OK;
+    const WsLayout wl = ws_layout(*layer, T);
+    if (!ws || ws_bytes < wl.total) return MOE_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MOE_ERR_ALIGN;
+    char *b = static_cast<char *>(ws);
+    Routing rt{topk_ids, counts, offsets, sorted_routes, uniq, n_uniq, topk_w};
+    return hip_status(launch_experts(*layer, x, (flags & MOE_ACCUM_RESIDUAL) ? x : nullptr, T, rt,
+                                     reinterpret_cast<float *>(b + wl.act), reinterpret_cast<float *>(b + wl.y), out,
+                                     flags, (hipStream_t)stream));
+}
+
+moe_status moe_layer_fwd(const moe_layer_t *layer, const float *x, int32_t T, float *out, uint32_t flags, void *ws,
+                         size_t ws_bytes, void *stream) {
+    moe_status s = check_layer(layer);
+    if (s != MOE_OK) return s;
+    if ((s = check_weights(layer, true, true)) != MOE_OK) return s;
+    if (T < 0 || !x || !out) return MOE_ERR_ARG;
+    if ((flags & MOE_WALK_MASK) > MOE_WALK_DEDUP_PASS1) return MOE_ERR_ARG;
+    if (!aligned16(x) || !aligned16(out)) return MOE_ERR_ALIGN;
+    if (T == 0) return MOE_OK;
+    const WsLayout wl = ws_layout(*layer, T);
+    if (!ws || ws_bytes < wl.total) return MOE_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MOE_ERR_ALIGN;
+    hipStream_t st = (hipStream_t)stream;
+    char *b = static_cast<char *>(ws);
+    auto F = [&](size_t o) { return reinterpret_cast<float *>(b + o); };
+    auto I32 = [&](size_t o) { return reinterpret_cast<int32_t *>(b + o); };
+    const int R = T * layer->top_k;
+
+    const float *xin = x;
+    if (flags & MOE_RMSNORM_IN) {
+        if ((s = hip_status(launch_rmsnorm(x, F(wl.xn), T, layer->H, 1e-6f, st))) != MOE_OK) return s;
+        xin = F(wl.xn);
+    }
+    if ((s = hip_status(launch_router(*layer, xin, F(wl.logits), T, st))) != MOE_OK) return s;
+    if ((s = hip_status(launch_select(F(wl.logits), T, layer->E, layer->top_k, I32(wl.ids), F(wl.w), st))) != MOE_OK)
+        return s;
+    if ((s = hip_status(launch_sort(I32(wl.ids), R, layer->E, I32(wl.counts), I32(wl.offsets), I32(wl.sorted),
+                                    I32(wl.uniq), I32(wl.nuniq), I32(wl.stats), st))) != MOE_OK)
+        return s;
+    Routing rt{I32(wl.ids), I32(wl.counts), I32(wl.offsets), I32(wl.sorted), I32(wl.uniq), I32(wl.nuniq), F(wl.w)};
+    return hip_status(launch_experts(*layer, xin, (flags & MOE_ACCUM_RESIDUAL) ? x : nullptr, T, rt, F(wl.act),
+                                     F(wl.y), out, flags, st));
+}
+
+moe_status moe_layer_routing(const moe_layer_t *layer, int32_t T, void *ws, size_t ws_bytes, int32_t **topk_ids,
+                             float **topk_w, int32_t **counts, int32_t **offsets, int32_t **sorted_routes,
+                             int32_t **uniq, int32_t **n_uniq) {
+    moe_status s = check_layer(layer);
+    if (s != MOE_OK) return s;
+    if (T < 0 || !ws) return MOE_ERR_ARG;
+    const WsLayout wl = ws_layout(*layer, T);
+    if (ws_bytes < wl.total) return MOE_ERR_WORKSPACE;
+    char *b = static_cast<char *>(ws);
+    if (topk_ids) *topk_ids = reinterpret_cast<int32_t *>(b + wl.ids);
+    if (topk_w) *topk_w = reinterpret_cast<float *>(b + wl.w);
+    if (counts) *counts = reinterpret_cast<int32_t *>(b + wl.counts);
+    if (offsets) *offsets = reinterpret_cast<int32_t *>(b + wl.offsets);
+    if (sorted_routes) *sorted_routes = reinterpret_cast<int32_t *>(b + wl.sorted);
+    if (uniq) *uniq = reinterpret_cast<int32_t *>(b + wl.uniq);
+    if (n_uniq) *n_uniq = reinterpret_cast<int32_t *>(b + wl.nuniq);
+    return MOE_OK;
+}
+
+const char *moe_status_str(moe_status status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_ARG: return "invalid argument";
+        case MOE_ERR_SHAPE: return "unsupported or inconsistent shape";
+        case MOE_ERR_DTYPE: return "unsupported dtype";
+        case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+        case MOE_ERR_HIP: return "HIP launch error";
+        case MOE_ERR_UNSUPPORTED: return "not supported by this build";
+        case MOE_ERR_ALIGN: return "pointer not 16-byte aligned";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

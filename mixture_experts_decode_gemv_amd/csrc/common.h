@@ -1,0 +1,147 @@
+// Internal header of the gfx950 MoE decode library: device helpers shared by
+// the kernels, launcher declarations and the workspace layout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;  // 4 waves per workgroup everywhere
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 32;
+constexpr int kMaxChunksPerLane = 8;  // 16-byte chunks per lane per weight row
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Elements held by one 16-byte chunk of a weight row.
+template <int WDT> struct WT;
+template <> struct WT<MOE_F32> { static constexpr int kEpc = 4; static constexpr int kBytes = 4; };
+template <> struct WT<MOE_BF16> { static constexpr int kEpc = 8; static constexpr int kBytes = 2; };
+template <> struct WT<MOE_FP8_E4M3> { static constexpr int kEpc = 16; static constexpr int kBytes = 1; };
+
+__host__ __device__ constexpr int elems_per_chunk(int dtype) {
+    return dtype == MOE_F32 ? 4 : dtype == MOE_BF16 ? 8 : 16;
+}
+__host__ __device__ constexpr int bytes_per_elem(int dtype) {
+    return dtype == MOE_F32 ? 4 : dtype == MOE_BF16 ? 2 : 1;
+}
+
+// bf16 halves of a packed 32-bit word (element 0 in the low half).
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// OCP E4M3 byte -> (its value) * 2^-120, exactly: the 4 exponent and 3
+// mantissa bits go straight into the fp32 exponent and mantissa fields, so
+// exponent field e becomes 2^(e-127) (the code's 2^(e-7) times 2^-120) and
+// exponent field 0 lands on the fp32 subnormals m * 2^-129 (the code's
+// m * 2^-9 times 2^-120).  The 2^120 is folded into the block scale.  The
+// NaN code is never produced by the encoder and decodes as 480 * 2^-120.
+constexpr float kE4m3Unscale = 1.329227995784916e36f;  // 2^120
+
+__device__ __forceinline__ float e4m3_scaled_down(uint32_t c) {
+    return __uint_as_float(((c & 0x7Fu) << 20) | ((c & 0x80u) << 24));
+}
+
+// acc + sum_e w[e] * xs[e] over the elements of one 16-byte weight chunk,
+// in element order.
+template <int WDT>
+__device__ __forceinline__ float chunk_dot(const u32x4 w, const float *xs, float acc);
+
+template <>
+__device__ __forceinline__ float chunk_dot<MOE_F32>(const u32x4 w, const float *xs, float acc) {
+    acc = fmaf(__uint_as_float(w.x), xs[0], acc);
+    acc = fmaf(__uint_as_float(w.y), xs[1], acc);
+    acc = fmaf(__uint_as_float(w.z), xs[2], acc);
+    acc = fmaf(__uint_as_float(w.w), xs[3], acc);
+    return acc;
+}
+
+template <>
+__device__ __forceinline__ float chunk_dot<MOE_BF16>(const u32x4 w, const float *xs, float acc) {
+    acc = fmaf(bf16_lo(w.x), xs[0], acc);
+    acc = fmaf(bf16_hi(w.x), xs[1], acc);
+    acc = fmaf(bf16_lo(w.y), xs[2], acc);
+    acc = fmaf(bf16_hi(w.y), xs[3], acc);
+    acc = fmaf(bf16_lo(w.z), xs[4], acc);
+    acc = fmaf(bf16_hi(w.z), xs[5], acc);
+    acc = fmaf(bf16_lo(w.w), xs[6], acc);
+    acc = fmaf(bf16_hi(w.w), xs[7], acc);
+    return acc;
+}
+
+// fp8: the sum is (true value) * 2^-120; callers multiply by scale * 2^120.
+template <>
+__device__ __forceinline__ float chunk_dot<MOE_FP8_E4M3>(const u32x4 w, const float *xs, float acc) {
+    const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc = fmaf(e4m3_scaled_down(v[q] >> (8 * b)), xs[4 * q + b], acc);
+    return acc;
+}
+
+// Sum over the 64 lanes; every lane receives the same value (each butterfly
+// step adds the same two operands in both partner lanes).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// Streaming 16-byte weight load (weights are read once per step).
+__device__ __forceinline__ u32x4 load_weight_chunk(const u32x4 *p) { return __builtin_nontemporal_load(p); }
+
+// Rows held by one wave for a given number of chunks per lane.
+__host__ __device__ constexpr int rows_per_wave(int nc) { return nc <= 2 ? 8 : nc <= 4 ? 4 : 2; }
+
+// ---- workspace layout (all offsets 256-byte aligned) ----------------------
+struct WsLayout {
+    size_t stats, logits, ids, w, counts, offsets, sorted, uniq, nuniq, xn, act, y, total;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+inline WsLayout ws_layout(const moe_layer_t &L, int64_t T) {
+    WsLayout s;
+    const int64_t R = T * L.top_k;
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
+    s.stats = take(16);
+    s.logits = take((size_t)T * L.E * 4);
+    s.ids = take((size_t)R * 4);
+    s.w = take((size_t)R * 4);
+    s.counts = take((size_t)L.E * 4);
+    s.offsets = take((size_t)(L.E + 1) * 4);
+    s.sorted = take((size_t)R * 4);
+    s.uniq = take((size_t)L.E * 4);
+    s.nuniq = take(4);
+    s.xn = take((size_t)T * L.H * 4);
+    s.act = take((size_t)R * L.I * 4);
+    s.y = take((size_t)R * L.H * 4);
+    s.total = o;
+    return s;
+}
+
+// ---- launchers (return hipSuccess or the launch error) -----------------------
+int num_cus();
+
+hipError_t launch_rmsnorm(const float *x, float *xn, int T, int H, float eps, hipStream_t st);
+hipError_t launch_router(const moe_layer_t &L, const float *x, float *logits, int T, hipStream_t st);
+hipError_t launch_select(const float *logits, int T, int E, int k, int32_t *ids, float *w, hipStream_t st);
+hipError_t launch_sort(const int32_t *ids, int R, int E, int32_t *counts, int32_t *offsets, int32_t *sorted,
+                       int32_t *uniq, int32_t *n_uniq, int32_t *stats, hipStream_t st);
+
+struct Routing {
+    const int32_t *ids, *counts, *offsets, *sorted, *uniq, *n_uniq;
+    const float *w;
+};
+hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xres, int T, const Routing &rt,
+                          float *act, float *y, float *out, uint32_t flags, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,97 @@
+// Expert passes and combine: grouped GEMV over the unique experts.
+//
+// "perf(cpu-moe): dedup experts across the batch in pass 1" (FreeToken PR
+// #46), commit message: pass 1 is split by (unique expert, row block) with
+// the expert's routes as the inner loop, so each gate_up row is read from
+// memory once and reused for every token routed to that expert; pass 2 reads
+// down [H, I]; the follow-up change deduplicates pass 2 the same way.  Here:
+//
+//  * A segment is one expert with its routes: a unique expert and its slice
+//    of the sorted route list (grouped walk), or a single route (per-route
+//    walk).  Work items are (segment, row block); a persistent grid strides
+//    over the items, whose count depends on the device-side n_uniq.
+//  * A wave keeps its weight rows in registers as raw 16-byte chunks (lane l
+//    holds chunks l, l+64, ...), loaded once with streaming loads, and then
+//    walks the segment's routes: each (row, route) dot product is one lane
+//    partial in chunk order followed by one butterfly reduction.  The same
+//    (row, route) pair is computed the same way whatever segment it sits in,
+//    so every walk gives bitwise the same result.
+//  * Pass 1 keeps gate row i and up row I+i in the same wave and writes the
+//    activation a[r, i] = silu(g) * u directly; pass 2 writes y[r, h]; rows of
+//    both workspaces are indexed by route r = t*k + j.
+//  * Combine: out[t, h] = sum_j w[t, j] * y[t*k + j, h], j ascending
+//    ("MoE Performance Optimization Analysis", Root Cause, step 6, combine
+//    on the device), plus x[t, h] for the residual form.
+#include "experts_impl.h"
+
+namespace moe {
+
+// ---- combine ------------------------------------------------------------------
+// out may alias xres: each thread reads its residual before storing there.
+__global__ __launch_bounds__(kBlock) void combine_kernel(const float *__restrict__ y, const float *__restrict__ w,
+                                                         const float *xres, float *out, int k, int H) {
+    const int t = blockIdx.x;
+    const int h = (blockIdx.y * kBlock + threadIdx.x) * 4;
+    if (h >= H) return;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+        const float wj = w[(size_t)t * k + j];
+        const float4 v = *reinterpret_cast<const float4 *>(y + ((size_t)t * k + j) * H + h);
+        acc.x = fmaf(wj, v.x, acc.x);
+        acc.y = fmaf(wj, v.y, acc.y);
+        acc.z = fmaf(wj, v.z, acc.z);
+        acc.w = fmaf(wj, v.w, acc.w);
+    }
+    if (xres) {
+        const float4 r = *reinterpret_cast<const float4 *>(xres + (size_t)t * H + h);
+        acc.x += r.x; acc.y += r.y; acc.z += r.z; acc.w += r.w;
+    }
+    *reinterpret_cast<float4 *>(out + (size_t)t * H + h) = acc;
+}
+
+// ---- launchers -------------------------------------------------------------------
+static int persistent_grid(long long max_items) {
+    const long long cap = (long long)num_cus() * 8;
+    long long g = max_items < cap ? max_items : cap;
+    return (int)(g < 1 ? 1 : g);
+}
+
+hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xres, int T, const Routing &rt,
+                          float *act, float *y, float *out, uint32_t flags, hipStream_t st) {
+    const int R = T * L.top_k;
+    const int walk = (int)(flags & MOE_WALK_MASK);
+    const int epc = elems_per_chunk(L.expert_dtype);
+    const int max_uniq = R < L.E ? R : L.E;
+    SegArgs grouped{rt.ids, rt.counts, rt.offsets, rt.sorted, rt.uniq, rt.n_uniq, 1, R, L.E};
+    SegArgs per_route = grouped;
+    per_route.grouped = 0;
+
+    Pass1Args p1{L.w_gate_up, L.s_gate_up, x, act, L.H, L.I, L.top_k, walk == MOE_WALK_PER_ROUTE ? per_route : grouped};
+    const int nc1 = (L.H / epc + kWave - 1) / kWave;
+    const int pairs_item = 4 * (rows_per_wave(nc_instance(nc1)) / 2);
+    const long long items1 = (long long)(p1.sa.grouped ? max_uniq : R) * ((L.I + pairs_item - 1) / pairs_item);
+    hipError_t err;
+    switch (L.expert_dtype) {
+        case MOE_F32: err = launch_pass1<MOE_F32>(nc1, persistent_grid(items1), st, p1); break;
+        case MOE_BF16: err = launch_pass1<MOE_BF16>(nc1, persistent_grid(items1), st, p1); break;
+        default: err = launch_pass1<MOE_FP8_E4M3>(nc1, persistent_grid(items1), st, p1); break;
+    }
+    if (err != hipSuccess) return err;
+
+    Pass2Args p2{L.w_down, L.s_down, act, y, L.H, L.I, walk == MOE_WALK_DEDUP ? grouped : per_route};
+    const int nc2 = (L.I / epc + kWave - 1) / kWave;
+    const int rows_item = 4 * rows_per_wave(nc_instance(nc2));
+    const long long items2 = (long long)(p2.sa.grouped ? max_uniq : R) * ((L.H + rows_item - 1) / rows_item);
+    switch (L.expert_dtype) {
+        case MOE_F32: err = launch_pass2<MOE_F32>(nc2, persistent_grid(items2), st, p2); break;
+        case MOE_BF16: err = launch_pass2<MOE_BF16>(nc2, persistent_grid(items2), st, p2); break;
+        default: err = launch_pass2<MOE_FP8_E4M3>(nc2, persistent_grid(items2), st, p2); break;
+    }
+    if (err != hipSuccess) return err;
+
+    hipLaunchKernelGGL(combine_kernel, dim3(T, (L.H / 4 + kBlock - 1) / kBlock), dim3(kBlock), 0, st, y, rt.w, xres,
+                       out, L.top_k, L.H);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,98 @@
+"""The C-ABI library loads, exports what include/moe.h declares, and
+validates arguments on the host (no GPU work is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_decode_gemv_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding_names():
+    assert sorted(moe.EXPORTS) == _declared()
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(moe.LIB_PATH)
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def _layer(**kw):
+    d = dict(E=8, top_k=2, H=64, I=32, router_dtype=moe.MOE_F32, expert_dtype=moe.MOE_F32,
+             w_router=0x1000, w_gate_up=0x2000, w_down=0x3000, s_gate_up=None, s_down=None, router_bias=None)
+    d.update(kw)
+    return moe.moe_layer_t(*[d[f] for f, _ in moe.moe_layer_t._fields_])
+
+
+def test_workspace_bytes():
+    n = moe.moe_workspace_bytes(_layer(), 4)
+    assert n > 4 * 2 * (64 + 32) * 4
+    assert moe.moe_workspace_bytes(_layer(), 0) > 0
+    assert moe.moe_workspace_bytes(_layer(top_k=9), 4) == 0
+    assert moe.moe_workspace_bytes(_layer(), -1) == 0
+    assert moe.moe_workspace_bytes(_layer(), 64) > moe.moe_workspace_bytes(_layer(), 4)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(top_k=0), 1), (dict(top_k=9), 1), (dict(E=2000, top_k=2), 2), (dict(top_k=33, E=64), 2),
+    (dict(H=66), 2), (dict(expert_dtype=7), 3), (dict(router_dtype=moe.MOE_FP8_E4M3), 3),
+    (dict(expert_dtype=moe.MOE_FP8_E4M3, H=64), 2), (dict(expert_dtype=moe.MOE_BF16, I=36), 2),
+    (dict(expert_dtype=moe.MOE_BF16, H=8192, router_dtype=moe.MOE_BF16), 2),
+])
+def test_layer_validation(kw, status):
+    L = _layer(**kw)
+    st = moe.lib().moe_layer_fwd(ctypes.byref(L), 0x4000, 4, 0x5000, 0, 0x6000, 1 << 30, None)
+    assert st == status
+
+
+def test_argument_errors_return_before_any_launch():
+    L = _layer()
+    lib = moe.lib()
+    # NULL x / out
+    assert lib.moe_layer_fwd(ctypes.byref(L), None, 4, 0x5000, 0, 0x6000, 1 << 30, None) == 1
+    # workspace too small
+    assert lib.moe_layer_fwd(ctypes.byref(L), 0x4000, 4, 0x5000, 0, 0x6000, 16, None) == 4
+    # misaligned activations
+    assert lib.moe_layer_fwd(ctypes.byref(L), 0x4004, 4, 0x5000, 0, 0x6000, 1 << 30, None) == 7
+    # misaligned weights
+    assert lib.moe_layer_fwd(ctypes.byref(_layer(w_gate_up=0x2008)), 0x4000, 4, 0x5000, 0, 0x6000, 1 << 30,
+                             None) == 7
+    # unknown walk
+    assert lib.moe_layer_fwd(ctypes.byref(L), 0x4000, 4, 0x5000, 5, 0x6000, 1 << 30, None) == 1
+    # T == 0 is a no-op
+    assert lib.moe_layer_fwd(ctypes.byref(L), 0x4000, 0, 0x5000, 0, 0x6000, 1 << 30, None) == 0
+    # route needs x or logits
+    assert lib.moe_route(ctypes.byref(L), None, None, 4, None, 0x100, 0x200, None, 0, None) == 1
+    # sort argument checks
+    assert lib.moe_sort(0x100, 4, 3, 2, 0x1, 0x2, 0x3, 0x4, 0x5, None) == 1
+    assert lib.moe_sort(0x100, 4, 2, 2000, 0x1, 0x2, 0x3, 0x4, 0x5, None) == 2
+    assert lib.moe_sort(None, 4, 2, 8, 0x1, 0x2, 0x3, 0x4, 0x5, None) == 1
+    assert lib.moe_sort(0x100, 0, 2, 8, 0x1, 0x2, 0x3, 0x4, 0x5, None) == 0
+    # fp8 without scales
+    L8 = _layer(expert_dtype=moe.MOE_FP8_E4M3, H=128, I=128)
+    assert lib.moe_layer_fwd(ctypes.byref(L8), 0x4000, 4, 0x5000, 0, 0x6000, 1 << 30, None) == 1
+
+
+def test_status_strings():
+    for st in range(8):
+        assert moe.moe_status_str(st) and moe.moe_status_str(st) != "unknown status"
+    assert moe.moe_status_str(99) == "unknown status"
+
+
+def test_routing_accessor_points_into_the_workspace():
+    L = _layer()
+    n = moe.moe_workspace_bytes(L, 4)
+    r = moe.moe_layer_routing(L, 4, 0x10000, n)
+    for v in r.values():
+        assert 0x10000 <= v < 0x10000 + n
+    with pytest.raises(moe.MoeError):
+        moe.moe_layer_routing(L, 4, 0x10000, 8)
