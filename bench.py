@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""MoE decode layer benchmark on one MI355X.
+
+A step is one whole MoE layer forward (router GEMV, top-k selection, counting
+sort, pass 1, pass 2, combine) over one decode batch, all through
+``moe_layer_fwd``.  The default workload is the uniform-routing batch sweep
+layer: E=256 experts, top_k=8, H=2048, I=768, bf16 experts (9 MiB each).
+Steps rotate over several resident copies of the layer (distinct seeded
+weights) and several seeded activation draws, so consecutive steps never
+re-read the same expert bytes from the 256 MiB Infinity Cache; the steps are
+recorded once into a HIP graph and replayed.
+
+Reported: layer steps/s at the headline batch size, and for every batch size
+of the sweep the achieved HBM GB/s on unique-expert bytes
+(n_uniq * 3 * H * I * bytes per weight, n_uniq read back from each step's
+statistics), the roofline of the expert phase, and the CPU oracle timed on
+a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--bs", type=int, default=64, help="headline batch size")
+    ap.add_argument("--sweep", default="1,4,8,16,32,64", help="batch sizes reported besides the headline")
+    ap.add_argument("--layers", type=int, default=4, help="resident layer copies rotated over")
+    ap.add_argument("--draws", type=int, default=16, help="activation draws rotated over")
+    ap.add_argument("--walk", default="dedup", choices=["dedup", "per_route", "dedup_pass1"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the layer is built and timed on a single MI355X; "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixture_experts_decode_gemv_amd as moe
+    import workload as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream(dev)
+    spec = wl.SWEEP
+    walk = {"dedup": moe.MOE_WALK_DEDUP, "per_route": moe.MOE_WALK_PER_ROUTE,
+            "dedup_pass1": moe.MOE_WALK_DEDUP_PASS1}[args.walk]
+    bpw = 2  # bf16
+    expert_bytes = 3 * spec.H * spec.I * bpw
+
+    t0 = time.time()
+    layers = []
+    host0 = None
+    for l in range(args.layers):
+        w = wl.make_layer(spec, layer=l)
+        layers.append(moe.DeviceLayer(w, device=dev))
+        if l == 0:
+            host0 = w
+        del w
+    print("[bench] %d layers generated and resident (%.1f s)" % (args.layers, time.time() - t0), file=sys.stderr,
+          flush=True)
+
+    sizes = sorted(set([args.bs] + [int(s) for s in args.sweep.split(",") if s]))
+    maxT = max(sizes)
+    ws = layers[0].workspace(maxT)
+    out = torch.empty((maxT, spec.H), dtype=torch.float32, device=dev)
+    results = {}
+
+    for T in sizes:
+        xs = [torch.from_numpy(wl.make_x(T, spec.H, draw=d)).to(dev) for d in range(args.draws)]
+        G = max(args.layers, args.draws)
+        plan = [(s % args.layers, s % args.draws) for s in range(G)]
+
+        def step(i, with_stats=False):
+            li, di = plan[i % G]
+            moe.moe_layer_fwd(layers[li].struct, xs[di], T, out, walk, ws, ws.numel(), stream)
+
+        # unique experts of every planned step (read back outside the timed region)
+        uniq = []
+        with torch.cuda.stream(stream):
+            for i in range(G):
+                step(i)
+                stream.synchronize()
+                uniq.append(int(ws[:4].view(torch.int32).item()))
+        mean_u = float(np.mean(uniq))
+
+        graph = None
+        if not args.no_graph:
+            with torch.cuda.stream(stream):
+                for i in range(3 * G):
+                    step(i)
+            stream.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                for i in range(G):
+                    step(i)
+            stream.synchronize()
+
+        reps = max(1, (args.steps + G - 1) // G)
+        nsteps = reps * G
+        wreps = max(1, (args.warmup + G - 1) // G)
+        with torch.cuda.stream(stream):
+            for _ in range(wreps):
+                if graph is not None:
+                    graph.replay()
+                else:
+                    for i in range(G):
+                        step(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(reps):
+                if graph is not None:
+                    graph.replay()
+                else:
+                    for i in range(G):
+                        step(i)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / nsteps
+        gbs = mean_u * expert_bytes / (ms * 1e-3) / 1e9
+        results[T] = dict(bs=T, ms_per_step=ms, steps_per_s=1e3 / ms, unique_experts=mean_u,
+                          reuse=T * spec.top_k / mean_u, unique_expert_MiB=mean_u * expert_bytes / 2 ** 20,
+                          hbm_GBps=gbs, hbm_frac=gbs / HBM_PEAK_GBS, timed_steps=nsteps)
+        print("[bench] bs=%d  %.1f us/step  %.0f steps/s  U=%.1f  %.0f GB/s (%.1f%% of 8 TB/s)"
+              % (T, ms * 1e3, 1e3 / ms, mean_u, gbs, 100 * gbs / HBM_PEAK_GBS), file=sys.stderr, flush=True)
+        del graph, xs
+
+    # ---- expert phase of the headline batch, timed on its own ----------------
+    T = args.bs
+    xs = [torch.from_numpy(wl.make_x(T, spec.H, draw=d)).to(dev) for d in range(args.draws)]
+    routed = []
+    for li in range(args.layers):
+        wsl = layers[li].workspace(T)
+        with torch.cuda.stream(stream):
+            moe.moe_layer_fwd(layers[li].struct, xs[li % args.draws], T, out, walk, wsl, wsl.numel(), stream)
+        stream.synchronize()
+        r = moe.moe_layer_routing(layers[li].struct, T, wsl, wsl.numel())
+        routed.append((li, li % args.draws, wsl, r, int(wsl[:4].view(torch.int32).item())))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup + args.steps):
+            li, di, wsl, r, u = routed[i % len(routed)]
+            if i >= args.warmup:
+                ev[i - args.warmup][0].record(stream)
+            moe.moe_expert_fwd(layers[li].struct, xs[di], T, r["topk_ids"], r["topk_w"], r["counts"],
+                               r["offsets"], r["sorted_routes"], r["uniq"], r["n_uniq"], out, walk, wsl,
+                               wsl.numel(), stream)
+            if i >= args.warmup:
+                ev[i - args.warmup][1].record(stream)
+    torch.cuda.synchronize()
+    exp_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    exp_bytes = float(np.mean([routed[(i + args.warmup) % len(routed)][4] for i in range(args.steps)])) * expert_bytes
+    exp_gbs = exp_bytes / (exp_ms * 1e-3) / 1e9
+
+    # ---- CPU oracle on a bounded sample ------------------------------------------
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+
+        olayer = oracle.Layer(host0)
+        nthreads = max(1, min(os.cpu_count() or 1, 16))
+        done, t_start = 0, time.time()
+        while True:
+            oracle.moe_layer(olayer, wl.make_x(T, spec.H, draw=done), nthreads=nthreads)
+            done += 1
+            if time.time() - t_start >= args.cpu_seconds:
+                break
+        el = time.time() - t_start
+        cpu = dict(value=done / el, unit="steps/s", cores=nthreads, kind="oracle",
+                   sample="%d whole layer steps at bs=%d (E=256, k=8, H=2048, I=768, bf16), fp64 accumulation, "
+                          "%.1f s" % (done, T, el))
+
+    head = results[args.bs]
+    line = {
+        "metric": "MoE layer steps/s at bs=%d (uniform routing, E=256, top_k=8, H=2048, I=768, bf16); "
+                  "achieved HBM GB/s on unique-expert bytes" % args.bs,
+        "value": head["steps_per_s"],
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": head["timed_steps"],
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0, 1/sqrt(fan_in)) weights, N(0,1) activations)",
+        "config": {"workload": "single MoE layer, uniform routing, E=256 top_k=8 H=2048 I=768 bf16 experts, "
+                               "batch sweep", "bs": args.bs, "walk": args.walk, "resident_layers": args.layers,
+                   "draws": args.draws, "graph": not args.no_graph, "parallelism": "none (1 GPU)"},
+        "hbm_GBps_unique_expert_bytes": head["hbm_GBps"],
+        "sweep": [results[t] for t in sizes],
+        "roofline": {"bound": "hbm", "kernel": "expert phase (moe_expert_fwd: pass 1, pass 2, combine)",
+                     "achieved": exp_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": exp_gbs / HBM_PEAK_GBS,
+                     "traffic": None, "avg_launch_ms": exp_ms, "bytes_per_launch": exp_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -2,6 +2,7 @@
 // the kernels, launcher declarations and the workspace layout.
 #pragma once
 
+#include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,16 +35,19 @@ __host__ __device__ constexpr int bytes_per_elem(int dtype) {
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
-// OCP E4M3 byte -> (its value) * 2^-120, exactly: the 4 exponent and 3
-// mantissa bits go straight into the fp32 exponent and mantissa fields, so
-// exponent field e becomes 2^(e-127) (the code's 2^(e-7) times 2^-120) and
-// exponent field 0 lands on the fp32 subnormals m * 2^-129 (the code's
-// m * 2^-9 times 2^-120).  The 2^120 is folded into the block scale.  The
-// NaN code is never produced by the encoder and decodes as 480 * 2^-120.
-constexpr float kE4m3Unscale = 1.329227995784916e36f;  // 2^120
+// OCP E4M3 byte -> (its value) * 2^-8, exactly.  The sign, 4 exponent and 3
+// mantissa bits are placed in an fp16 (bias 15, 10 mantissa bits) as
+// S.0EEEE.MMM0000000: a normal code (1 + m/8) * 2^(e-7) becomes
+// (1 + m/8) * 2^(e-15) and a subnormal code m * 2^-9 becomes the fp16
+// subnormal m * 2^-17, both the code's value times 2^-8; the fp16 -> fp32
+// conversion is exact.  The 2^8 is folded into the block scale, so products
+// never approach the fp32 subnormal range.  The NaN code is never produced
+// by the encoder and decodes as 480 * 2^-8.
+constexpr float kE4m3Unscale = 256.0f;  // 2^8
 
 __device__ __forceinline__ float e4m3_scaled_down(uint32_t c) {
-    return __uint_as_float(((c & 0x7Fu) << 20) | ((c & 0x80u) << 24));
+    const unsigned short h = (unsigned short)(((c & 0x7Fu) << 7) | ((c & 0x80u) << 8));
+    return __half2float(__ushort_as_half(h));
 }
 
 // acc + sum_e w[e] * xs[e] over the elements of one 16-byte weight chunk,
@@ -73,7 +77,7 @@ __device__ __forceinline__ float chunk_dot<MOE_BF16>(const u32x4 w, const float 
     return acc;
 }
 
-// fp8: the sum is (true value) * 2^-120; callers multiply by scale * 2^120.
+// fp8: the sum is (true value) * 2^-8; callers multiply by scale * 2^8.
 template <>
 __device__ __forceinline__ float chunk_dot<MOE_FP8_E4M3>(const u32x4 w, const float *xs, float acc) {
     const uint32_t v[4] = {w.x, w.y, w.z, w.w};
