@@ -46,7 +46,23 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a device-to-device copy of this many MiB, 3 times (reference for HBM counters)")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    """A plain device-to-device copy of known size, for scaling the HBM
+    traffic counters (FETCH_SIZE / WRITE_SIZE) of the other kernels."""
+    import torch
+
+    n = mib * 2 ** 20 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "repeats": 3}), flush=True)
 
 
 def main():
@@ -55,6 +71,10 @@ def main():
         print("bench.py measures one GPU only: the layer is built and timed on a single MI355X; "
               "--gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
+        return
 
     import torch
 

@@ -35,8 +35,10 @@
  *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
  *    library never allocates, frees or caches device memory; scratch comes
  *    from the caller's workspace `ws` of `ws_bytes` bytes (see
- *    moe_workspace_bytes).  Workspace contents need not be initialised and
- *    are clobbered.
+ *    moe_workspace_bytes).  A new workspace is prepared once with
+ *    moe_workspace_init; after that every call leaves its synchronisation
+ *    words zero again, and the rest of the workspace is scratch.  Calls that
+ *    share a workspace must be ordered on one stream.
  *  - Calls only enqueue work on `stream` (a hipStream_t; NULL = the null
  *    stream) and return.  They never synchronise or read device memory back,
  *    so they can be recorded into a HIP graph.
@@ -102,12 +104,19 @@ enum {
  * Returns 0 if the layer description is invalid. */
 size_t moe_workspace_bytes(const moe_layer_t *layer, int32_t max_tokens);
 
+/* Zero the synchronisation words at the front of a workspace sized for up to
+ * max_tokens tokens (one small fill kernel on `stream`; no memset, so it can
+ * be recorded in a graph).  Call once after allocating ws, before the first
+ * call that uses it. */
+moe_status moe_workspace_init(const moe_layer_t *layer, int32_t max_tokens, void *ws, size_t ws_bytes,
+                              void *stream);
+
 /* Router and selection.  Either x [T, H] (logits computed on the device from
  * W_r and router_bias) or logits_in [T, E] (selection fed with given logits)
  * must be non-NULL; logits_in wins if both are.  Writes topk_ids [T, k]
  * (int32) and topk_w [T, k] (fp32) and, if non-NULL, logits_out [T, E].
- * ws may be NULL when logits_in or logits_out is given; otherwise it must
- * hold moe_workspace_bytes(layer, T) bytes. */
+ * With x, ws (moe_workspace_bytes(layer, T) bytes, initialised) is required;
+ * with logits_in it may be NULL. */
 moe_status moe_route(const moe_layer_t *layer, const float *x, const float *logits_in, int32_t T,
                      float *logits_out, int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes,
                      void *stream);

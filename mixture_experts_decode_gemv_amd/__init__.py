@@ -27,8 +27,8 @@ MOE_NO_MFMA = 1 << 7
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE", 4: "MOE_ERR_WORKSPACE",
           5: "MOE_ERR_HIP", 6: "MOE_ERR_UNSUPPORTED", 7: "MOE_ERR_ALIGN"}
 
-EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_sort", "moe_expert_fwd", "moe_layer_fwd", "moe_layer_routing",
-           "moe_status_str")
+EXPORTS = ("moe_workspace_bytes", "moe_workspace_init", "moe_route", "moe_sort", "moe_expert_fwd", "moe_layer_fwd",
+           "moe_layer_routing", "moe_status_str")
 
 
 class MoeError(RuntimeError):
@@ -58,6 +58,8 @@ def lib():
         P = ctypes.POINTER(moe_layer_t)
         L.moe_workspace_bytes.restype = sz
         L.moe_workspace_bytes.argtypes = [P, i32]
+        L.moe_workspace_init.restype = ctypes.c_int
+        L.moe_workspace_init.argtypes = [P, i32, vp, sz, vp]
         L.moe_route.restype = ctypes.c_int
         L.moe_route.argtypes = [P, vp, vp, i32, vp, vp, vp, vp, sz, vp]
         L.moe_sort.restype = ctypes.c_int
@@ -109,6 +111,11 @@ def moe_status_str(status: int) -> str:
 
 def moe_workspace_bytes(layer: moe_layer_t, max_tokens: int) -> int:
     return int(lib().moe_workspace_bytes(ctypes.byref(layer), int(max_tokens)))
+
+
+def moe_workspace_init(layer, max_tokens, ws, ws_bytes, stream=None):
+    _check("moe_workspace_init", lib().moe_workspace_init(ctypes.byref(layer), int(max_tokens), _p(ws),
+                                                          int(ws_bytes), _s(stream)))
 
 
 def moe_route(layer, x, logits_in, T, logits_out, topk_ids, topk_w, ws=None, ws_bytes=0, stream=None):
@@ -193,10 +200,15 @@ class DeviceLayer:
         other.struct = other._struct(other.tensors["router_bias"])
         return other
 
-    def workspace(self, max_tokens: int):
+    def workspace(self, max_tokens: int, stream=None):
+        """A workspace for up to max_tokens tokens, initialised on `stream`
+        (torch's current stream if None)."""
         import torch
 
         n = moe_workspace_bytes(self.struct, max_tokens)
         if n == 0:
             raise MoeError("moe_workspace_bytes", 1)
-        return torch.empty(n, dtype=torch.uint8, device=self.tensors["w_router"].device)
+        dev = self.tensors["w_router"].device
+        ws = torch.empty(n, dtype=torch.uint8, device=dev)
+        moe_workspace_init(self.struct, max_tokens, ws, n, stream if stream is not None else torch.cuda.current_stream(dev))
+        return ws

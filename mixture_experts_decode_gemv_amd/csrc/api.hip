@@ -66,6 +66,18 @@ size_t moe_workspace_bytes(const moe_layer_t *layer, int32_t max_tokens) {
     return ws_layout(*layer, max_tokens).total;
 }
 
+moe_status moe_workspace_init(const moe_layer_t *layer, int32_t max_tokens, void *ws, size_t ws_bytes,
+                              void *stream) {
+    moe_status s = check_layer(layer);
+    if (s != MOE_OK) return s;
+    if (max_tokens < 0 || !ws) return MOE_ERR_ARG;
+    const WsLayout wl = ws_layout(*layer, max_tokens);
+    if (ws_bytes < wl.total) return MOE_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MOE_ERR_ALIGN;
+    // stats and arrival counters sit at the front of the workspace
+    return hip_status(launch_zero(static_cast<unsigned *>(ws), (int)(wl.logits / 4), (hipStream_t)stream));
+}
+
 moe_status moe_route(const moe_layer_t *layer, const float *x, const float *logits_in, int32_t T,
                      float *logits_out, int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes,
                      void *stream) {
@@ -74,24 +86,23 @@ moe_status moe_route(const moe_layer_t *layer, const float *x, const float *logi
     if (T < 0 || !topk_ids || !topk_w || (!x && !logits_in)) return MOE_ERR_ARG;
     if (T == 0) return MOE_OK;
     hipStream_t st = (hipStream_t)stream;
-    const float *lg = logits_in;
-    if (!lg) {
-        if ((s = check_weights(layer, true, false)) != MOE_OK) return s;
-        if (!aligned16(x)) return MOE_ERR_ALIGN;
-        float *dst = logits_out;
-        if (!dst) {
-            const WsLayout wl = ws_layout(*layer, T);
-            if (!ws || ws_bytes < wl.total) return MOE_ERR_WORKSPACE;
-            dst = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.logits);
-        }
-        if ((s = hip_status(launch_router(*layer, x, dst, T, st))) != MOE_OK) return s;
-        lg = dst;
-    } else if (logits_out && logits_out != logits_in) {
-        if (hipMemcpyAsync(logits_out, logits_in, (size_t)T * layer->E * 4, hipMemcpyDeviceToDevice, st) !=
-            hipSuccess)
+    if (logits_in) {
+        if (logits_out && logits_out != logits_in &&
+            hipMemcpyAsync(logits_out, logits_in, (size_t)T * layer->E * 4, hipMemcpyDeviceToDevice, st) !=
+                hipSuccess)
             return MOE_ERR_HIP;
+        return hip_status(launch_route(*layer, nullptr, logits_in, T, nullptr, nullptr, topk_ids, topk_w, nullptr,
+                                       nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, false, st));
     }
-    return hip_status(launch_select(lg, T, layer->E, layer->top_k, topk_ids, topk_w, st));
+    if ((s = check_weights(layer, true, false)) != MOE_OK) return s;
+    if (!aligned16(x)) return MOE_ERR_ALIGN;
+    const WsLayout wl = ws_layout(*layer, T);
+    if (!ws || ws_bytes < wl.total) return MOE_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MOE_ERR_ALIGN;
+    char *b = static_cast<char *>(ws);
+    float *dst = logits_out ? logits_out : reinterpret_cast<float *>(b + wl.logits);
+    return hip_status(launch_route(*layer, x, nullptr, T, nullptr, dst, topk_ids, topk_w, nullptr, nullptr, nullptr,
+                                   nullptr, nullptr, nullptr, reinterpret_cast<unsigned *>(b + wl.arrive), false, st));
 }
 
 moe_status moe_sort(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int32_t *counts, int32_t *offsets,
@@ -101,8 +112,8 @@ moe_status moe_sort(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, in
     if (!topk_ids || !counts || !offsets || !sorted_routes || !uniq || !n_uniq) return MOE_ERR_ARG;
     if ((int64_t)T * k > INT32_MAX / 2) return MOE_ERR_SHAPE;
     if (T == 0) return MOE_OK;
-    return hip_status(
-        launch_sort(topk_ids, T * k, E, counts, offsets, sorted_routes, uniq, n_uniq, nullptr, (hipStream_t)stream));
+    return hip_status(launch_sort(topk_ids, T * k, E, counts, offsets, sorted_routes, uniq, n_uniq,
+                                  (hipStream_t)stream));
 }
 
 moe_status moe_expert_fwd(const moe_layer_t *layer, const float *x, int32_t T, const int32_t *topk_ids,
@@ -145,17 +156,14 @@ moe_status moe_layer_fwd(const moe_layer_t *layer, const float *x, int32_t T, fl
     auto I32 = [&](size_t o) { return reinterpret_cast<int32_t *>(b + o); };
     const int R = T * layer->top_k;
 
-    const float *xin = x;
-    if (flags & MOE_RMSNORM_IN) {
-        if ((s = hip_status(launch_rmsnorm(x, F(wl.xn), T, layer->H, 1e-6f, st))) != MOE_OK) return s;
-        xin = F(wl.xn);
-    }
-    if ((s = hip_status(launch_router(*layer, xin, F(wl.logits), T, st))) != MOE_OK) return s;
-    if ((s = hip_status(launch_select(F(wl.logits), T, layer->E, layer->top_k, I32(wl.ids), F(wl.w), st))) != MOE_OK)
+    const bool norm = (flags & MOE_RMSNORM_IN) != 0;
+    const float *xin = norm ? F(wl.xn) : x;
+    if ((s = hip_status(launch_route(*layer, x, nullptr, T, norm ? F(wl.xn) : nullptr, F(wl.logits), I32(wl.ids),
+                                     F(wl.w), I32(wl.counts), I32(wl.offsets), I32(wl.sorted), I32(wl.uniq),
+                                     I32(wl.nuniq), I32(wl.stats), reinterpret_cast<unsigned *>(b + wl.arrive), norm,
+                                     st))) != MOE_OK)
         return s;
-    if ((s = hip_status(launch_sort(I32(wl.ids), R, layer->E, I32(wl.counts), I32(wl.offsets), I32(wl.sorted),
-                                    I32(wl.uniq), I32(wl.nuniq), I32(wl.stats), st))) != MOE_OK)
-        return s;
+    (void)R;
     Routing rt{I32(wl.ids), I32(wl.counts), I32(wl.offsets), I32(wl.sorted), I32(wl.uniq), I32(wl.nuniq), F(wl.w)};
     return hip_status(launch_experts(*layer, xin, (flags & MOE_ACCUM_RESIDUAL) ? x : nullptr, T, rt, F(wl.act),
                                      F(wl.y), out, flags, st));

@@ -96,6 +96,67 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+
+// Reduce-scatter of NS slots of NW lane partials over the G lanes of a row:
+// level s (mask G/2 >> s) halves the live slots, each lane keeping the half
+// its lane bit selects and adding its partner's copy of that half; after
+// log2(NS) levels a lane holds slot (l % G) >> (log2 G - log2 NS), and a
+// butterfly over the remaining masks completes that slot's sum in every lane
+// of its group.  The order of the additions depends only on lane positions.
+template <int NS, int NW, int G>
+__device__ __forceinline__ void reduce_slots(float (&p)[NS][NW], int lane) {
+    constexpr int LOG = ilog2(NS);
+    static_assert((1 << LOG) == NS, "slots must be a power of two");
+    static_assert(NS <= G, "more slots than lanes");
+#pragma unroll
+    for (int s = 0; s < LOG; ++s) {
+        const int mask = (G / 2) >> s;
+        const int half = NS >> (s + 1);
+        const bool upper = (lane & mask) != 0;
+#pragma unroll
+        for (int i = 0; i < half; ++i)
+#pragma unroll
+            for (int v = 0; v < NW; ++v) {
+                const float keep = upper ? p[half + i][v] : p[i][v];
+                const float give = upper ? p[i][v] : p[half + i][v];
+                p[i][v] = keep + __shfl_xor(give, mask, kWave);
+            }
+    }
+#pragma unroll
+    for (int mask = (G / 2) >> LOG; mask >= 1; mask >>= 1)
+#pragma unroll
+        for (int v = 0; v < NW; ++v) p[0][v] += __shfl_xor(p[0][v], mask, kWave);
+}
+
+// Slot held by this lane after reduce_slots, and whether it writes it.
+template <int NS, int G>
+__device__ __forceinline__ int reduced_slot(int lane) { return (lane & (G - 1)) >> (ilog2(G) - ilog2(NS)); }
+template <int NS, int G>
+__device__ __forceinline__ bool slot_leader(int lane) { return (lane & ((G / NS) - 1)) == 0; }
+
+// ---- data shared between workgroups of one launch ---------------------------
+// The XCDs have separate L2 caches.  Rows written by one workgroup and read by
+// another in the same launch are stored and loaded with device-scope atomic
+// accesses, which are coherent across the L2s; a producer wave runs
+// wait_vm_stores() before the workgroup barrier that precedes its counter
+// update, and a consumer loads only after it has seen the counter.  This
+// avoids device-scope fences, which write back or invalidate a whole L2.
+
+// s_waitcnt vmcnt(0) (gfx9 encoding: vmcnt bits [3:0] and [15:14] = 0, expcnt
+// [6:4] = 7 and lgkmcnt [11:8] = 15 unconstrained).  The workgroup barrier
+// alone does not wait for stores.
+__device__ __forceinline__ void wait_vm_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <typename V>
+__device__ __forceinline__ void store_shared(V *p, V v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename V>
+__device__ __forceinline__ V load_shared(const V *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // Streaming 16-byte weight load (weights are read once per step).
@@ -105,8 +166,12 @@ __device__ __forceinline__ u32x4 load_weight_chunk(const u32x4 *p) { return __bu
 __host__ __device__ constexpr int rows_per_wave(int nc) { return nc <= 2 ? 8 : nc <= 4 ? 4 : 2; }
 
 // ---- workspace layout (all offsets 256-byte aligned) ----------------------
+// stats and the routing kernel's arrival counters come first, at offsets that
+// do not depend on the token count, so moe_workspace_init can zero them once.
+int route_arrive_words(int T);
+
 struct WsLayout {
-    size_t stats, logits, ids, w, counts, offsets, sorted, uniq, nuniq, xn, act, y, total;
+    size_t stats, arrive, logits, ids, w, counts, offsets, sorted, uniq, nuniq, xn, act, y, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -117,6 +182,7 @@ inline WsLayout ws_layout(const moe_layer_t &L, int64_t T) {
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
     s.stats = take(16);
+    s.arrive = take((size_t)route_arrive_words((int)T) * 4);
     s.logits = take((size_t)T * L.E * 4);
     s.ids = take((size_t)R * 4);
     s.w = take((size_t)R * 4);
@@ -135,11 +201,15 @@ inline WsLayout ws_layout(const moe_layer_t &L, int64_t T) {
 // ---- launchers (return hipSuccess or the launch error) -----------------------
 int num_cus();
 
-hipError_t launch_rmsnorm(const float *x, float *xn, int T, int H, float eps, hipStream_t st);
-hipError_t launch_router(const moe_layer_t &L, const float *x, float *logits, int T, hipStream_t st);
-hipError_t launch_select(const float *logits, int T, int E, int k, int32_t *ids, float *w, hipStream_t st);
+// Routing: router GEMV (unless logits_in), selection and, if counts is not
+// null, the sort; xn non-null with rmsnorm writes the normalised rows.
+hipError_t launch_route(const moe_layer_t &L, const float *x, const float *logits_in, int T, float *xn,
+                        float *logits, int32_t *ids, float *w, int32_t *counts, int32_t *offsets, int32_t *sorted,
+                        int32_t *uniq, int32_t *n_uniq, int32_t *stats, unsigned *arrive, bool rmsnorm,
+                        hipStream_t st);
 hipError_t launch_sort(const int32_t *ids, int R, int E, int32_t *counts, int32_t *offsets, int32_t *sorted,
-                       int32_t *uniq, int32_t *n_uniq, int32_t *stats, hipStream_t st);
+                       int32_t *uniq, int32_t *n_uniq, hipStream_t st);
+hipError_t launch_zero(unsigned *p, int n, hipStream_t st);
 
 struct Routing {
     const int32_t *ids, *counts, *offsets, *sorted, *uniq, *n_uniq;

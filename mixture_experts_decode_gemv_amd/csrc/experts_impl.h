@@ -1,5 +1,15 @@
-// Templates of the GEMV expert passes, instantiated once per weight dtype in
-// experts_<dtype>.hip.  See experts.hip for what the passes compute.
+// Templates of the grouped-GEMV expert passes, instantiated once per weight
+// dtype in experts_<dtype>.hip.  See experts.hip for what the passes compute.
+//
+// Layout of a wave's work: a wave holds NS "slots" of weight rows in
+// registers as raw 16-byte chunks.  G lanes share one row (G = 64 or 32), so
+// a slot covers 64/G rows at once; lane l works on row half = l / G of the
+// slot and on chunks (l % G) + G*c, c < NC.  The weights are loaded once per
+// work item with streaming loads; then every route of the segment is applied
+// to them: one lane partial per slot (chunks in order), then a reduce-scatter
+// across the G lanes of each row (see reduce_slots).  The arithmetic of one
+// (row, route) pair depends only on lane positions, never on the segment, so
+// every walk gives bitwise the same result.
 #pragma once
 
 #include "common.h"
@@ -34,33 +44,46 @@ __device__ __forceinline__ int segment_route(const SegArgs &sa, int first, int i
     return sa.grouped ? sa.sorted[first + i] : first + i;
 }
 
-__device__ __forceinline__ int segment_count(const SegArgs &sa) { return sa.grouped ? *sa.n_uniq : sa.R; }
+__device__ __forceinline__ int segment_count(const SegArgs &sa) {
+    const int n = sa.grouped ? *sa.n_uniq : sa.R;
+    return n > 0 ? n : 0;
+}
 
-// Loads chunk c of rows rows[r] (byte pointers), zero where invalid.
-template <int NC, int NR>
-__device__ __forceinline__ void load_rows(u32x4 (&w)[NR][NC], const char *const (&rows)[NR], const bool (&ok)[NR],
+// Loads chunk c of slot rows rows[s] (byte pointers of this lane's row), zero
+// where invalid.
+template <int NC, int NS, int G>
+__device__ __forceinline__ void load_rows(u32x4 (&w)[NS][NC], const char *const (&rows)[NS], const bool (&ok)[NS],
                                           int nq, int lane) {
+    const int sub = lane & (G - 1);
 #pragma unroll
-    for (int r = 0; r < NR; ++r)
+    for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            const int q = lane + kWave * c;
-            w[r][c] = (ok[r] && q < nq) ? load_weight_chunk(reinterpret_cast<const u32x4 *>(rows[r]) + q)
+            const int q = sub + G * c;
+            w[s][c] = (ok[s] && q < nq) ? load_weight_chunk(reinterpret_cast<const u32x4 *>(rows[s]) + q)
                                         : u32x4{0u, 0u, 0u, 0u};
         }
 }
 
-// acc[r] = lane partial of rows r . xv (chunk order), fp8 chunks scaled by
-// their block scale.
-template <int WDT, int NC, int NR>
-__device__ __forceinline__ void dot_rows(const u32x4 (&w)[NR][NC], const float (&sc)[NR][NC],
-                                         const float *__restrict__ xv, int nq, int lane, float (&acc)[NR]) {
+// acc[s] = this lane's partial of slot s . xv, chunks in order; fp8 chunks
+// are scaled by their block scale.  The weights stay packed in registers
+// across the route loop: the empty asm makes them opaque on every call, so
+// the compiler cannot hoist their decode out of the loop (which would double
+// their register footprint and halve the waves in flight).
+template <int WDT, int NC, int NS, int G>
+__device__ __forceinline__ void dot_rows(u32x4 (&w)[NS][NC], const float (&sc)[NS][NC],
+                                         const float *__restrict__ xv, int nq, int lane, float (&acc)[NS]) {
     constexpr int EPC = WT<WDT>::kEpc;
+    const int sub = lane & (G - 1);
 #pragma unroll
-    for (int r = 0; r < NR; ++r) acc[r] = 0.f;
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) asm volatile("" : "+v"(w[s][c]));
+#pragma unroll
+    for (int s = 0; s < NS; ++s) acc[s] = 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        const int q = lane + kWave * c;
+        const int q = sub + G * c;
         if (q < nq) {
             float xs[EPC];
             const float4 *xp = reinterpret_cast<const float4 *>(xv + q * EPC);
@@ -70,15 +93,20 @@ __device__ __forceinline__ void dot_rows(const u32x4 (&w)[NR][NC], const float (
                 xs[4 * v] = f.x; xs[4 * v + 1] = f.y; xs[4 * v + 2] = f.z; xs[4 * v + 3] = f.w;
             }
 #pragma unroll
-            for (int r = 0; r < NR; ++r) {
-                if (WDT == MOE_FP8_E4M3) acc[r] = fmaf(sc[r][c], chunk_dot<WDT>(w[r][c], xs, 0.f), acc[r]);
-                else acc[r] = chunk_dot<WDT>(w[r][c], xs, acc[r]);
+            for (int s = 0; s < NS; ++s) {
+                if (WDT == MOE_FP8_E4M3) acc[s] = fmaf(sc[s][c], chunk_dot<WDT>(w[s][c], xs, 0.f), acc[s]);
+                else acc[s] = chunk_dot<WDT>(w[s][c], xs, acc[s]);
             }
         }
     }
 }
 
-// ---- pass 1: gate_up rows, activation ------------------------------------
+// Slots per wave for NC chunks per lane: about 64 VGPRs of weights.
+__host__ __device__ constexpr int slots_for(int nc) { return nc <= 2 ? 8 : nc <= 4 ? 4 : 2; }
+
+// ---- pass 1: gate/up row pairs and the activation ------------------------
+// G = 64; slots 2p and 2p+1 hold gate row i0+p and up row I+i0+p, so one
+// reduce_slots leaves a pair's two sums in the same lane group.
 struct Pass1Args {
     const void *gate_up;
     const float *s_gate_up;
@@ -90,34 +118,39 @@ struct Pass1Args {
 
 template <int WDT, int NC>
 __global__ __launch_bounds__(kBlock) void pass1_kernel(Pass1Args a) {
-    constexpr int P = rows_per_wave(NC) / 2;  // gate/up pairs per wave
-    constexpr int NR = 2 * P;
+    constexpr int G = kWave;
+    constexpr int NS = slots_for(NC);
+    constexpr int P = NS / 2;  // gate/up pairs per wave
     constexpr int EPC = WT<WDT>::kEpc;
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int gwave = blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
+    const int nwaves = gridDim.x * (kBlock / kWave);
     const int H = a.H, I = a.I, nq = H / EPC;
-    const int pairs_per_item = 4 * P;
-    const int items_per_seg = (I + pairs_per_item - 1) / pairs_per_item;
+    const int items_per_seg = (I + P - 1) / P;
     const int n_items = segment_count(a.sa) * items_per_seg;
     const size_t row_bytes = (size_t)H * WT<WDT>::kBytes;
 
-    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-        const int s = item / items_per_seg, blk = item % items_per_seg;
-        int e, first, n;
-        segment(a.sa, s, e, first, n);
-        const int i0 = blk * pairs_per_item + wave * P;
-        const char *rows[NR];
-        bool ok[NR];
-        float sc[NR][NC];
+    // The segment of the next item is fetched while the current one is
+    // processed, so its index loads are off the critical path.
+    int e_nx = 0, first_nx = 0, n_nx = 0;
+    if (gwave < n_items) segment(a.sa, gwave / items_per_seg, e_nx, first_nx, n_nx);
+    for (int item = gwave; item < n_items; item += nwaves) {
+        const int blk = item % items_per_seg;
+        const int e = e_nx, first = first_nx, n = n_nx;
+        const int i0 = blk * P;
+        const char *rows[NS];
+        bool ok[NS];
+        float sc[NS][NC];
+        const char *base = static_cast<const char *>(a.gate_up) + (size_t)e * 2 * I * row_bytes;
 #pragma unroll
         for (int p = 0; p < P; ++p) {
             const int i = i0 + p;
-            ok[p] = ok[P + p] = i < I;
-            const char *base = static_cast<const char *>(a.gate_up) + (size_t)e * 2 * I * row_bytes;
-            rows[p] = base + (size_t)i * row_bytes;
-            rows[P + p] = base + (size_t)(I + i) * row_bytes;
+            ok[2 * p] = ok[2 * p + 1] = i < I && n > 0;
+            rows[2 * p] = base + (size_t)i * row_bytes;
+            rows[2 * p + 1] = base + (size_t)(I + i) * row_bytes;
         }
 #pragma unroll
-        for (int r = 0; r < NR; ++r)
+        for (int r = 0; r < NS; ++r)
 #pragma unroll
             for (int c = 0; c < NC; ++c) sc[r][c] = 1.f;
         if (WDT == MOE_FP8_E4M3) {
@@ -127,30 +160,33 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(Pass1Args a) {
                 const int i = min(i0 + p, I - 1);
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
-                    const int hb = min((lane + kWave * c) * EPC / 128, nbh - 1);
-                    sc[p][c] = a.s_gate_up[((size_t)e * (2 * I / 128) + i / 128) * nbh + hb] * kE4m3Unscale;
-                    sc[P + p][c] = a.s_gate_up[((size_t)e * (2 * I / 128) + (I + i) / 128) * nbh + hb] * kE4m3Unscale;
+                    const int hb = min((lane + G * c) * EPC / 128, nbh - 1);
+                    sc[2 * p][c] = a.s_gate_up[((size_t)e * (2 * I / 128) + i / 128) * nbh + hb] * kE4m3Unscale;
+                    sc[2 * p + 1][c] =
+                        a.s_gate_up[((size_t)e * (2 * I / 128) + (I + i) / 128) * nbh + hb] * kE4m3Unscale;
                 }
             }
         }
-        u32x4 w[NR][NC];
-        load_rows<NC, NR>(w, rows, ok, nq, lane);
+        u32x4 w[NS][NC];
+        load_rows<NC, NS, G>(w, rows, ok, nq, lane);
+        // the segment's routes, one per lane (first 64), loaded beside the weights
+        const int rl = lane < n ? segment_route(a.sa, first, lane) : 0;
+        if (item + nwaves < n_items) segment(a.sa, (item + nwaves) / items_per_seg, e_nx, first_nx, n_nx);
         for (int m = 0; m < n; ++m) {
-            const int r = segment_route(a.sa, first, m);
-            const int t = r / a.k;
-            float acc[NR];
-            dot_rows<WDT, NC, NR>(w, sc, a.x + (size_t)t * H, nq, lane, acc);
+            const int r = m < kWave ? __shfl(rl, m, kWave) : segment_route(a.sa, first, m);
+            float acc[NS];
+            dot_rows<WDT, NC, NS, G>(w, sc, a.x + (size_t)(r / a.k) * H, nq, lane, acc);
+            float gu[P][2];
 #pragma unroll
-            for (int p = 0; p < P; ++p) {
-                const float g = wave_sum(acc[p]);
-                const float u = wave_sum(acc[P + p]);
-                if (lane == p && ok[p]) a.act[(size_t)r * I + i0 + p] = silu(g) * u;
-            }
+            for (int p = 0; p < P; ++p) { gu[p][0] = acc[2 * p]; gu[p][1] = acc[2 * p + 1]; }
+            reduce_slots<P, 2, G>(gu, lane);
+            const int p = reduced_slot<P, G>(lane);
+            if (slot_leader<P, G>(lane) && i0 + p < I) a.act[(size_t)r * I + i0 + p] = silu(gu[0][0]) * gu[0][1];
         }
     }
 }
 
-// ---- pass 2: down rows ---------------------------------------------------
+// ---- pass 2: down rows -------------------------------------------------------
 struct Pass2Args {
     const void *down;
     const float *s_down;
@@ -160,63 +196,76 @@ struct Pass2Args {
     SegArgs sa;
 };
 
-template <int WDT, int NC>
+template <int WDT, int NC, int G>
 __global__ __launch_bounds__(kBlock) void pass2_kernel(Pass2Args a) {
-    constexpr int NR = rows_per_wave(NC);
+    constexpr int NS = slots_for(NC);
+    constexpr int RPS = kWave / G;  // rows per slot
+    constexpr int NR = NS * RPS;    // rows per wave
     constexpr int EPC = WT<WDT>::kEpc;
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1), half = lane / G;
+    const int gwave = blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
+    const int nwaves = gridDim.x * (kBlock / kWave);
     const int H = a.H, I = a.I, nq = I / EPC;
-    const int rows_per_item = 4 * NR;
-    const int items_per_seg = (H + rows_per_item - 1) / rows_per_item;
+    const int items_per_seg = (H + NR - 1) / NR;
     const int n_items = segment_count(a.sa) * items_per_seg;
     const size_t row_bytes = (size_t)I * WT<WDT>::kBytes;
 
-    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-        const int s = item / items_per_seg, blk = item % items_per_seg;
-        int e, first, n;
-        segment(a.sa, s, e, first, n);
-        const int h0 = blk * rows_per_item + wave * NR;
-        const char *rows[NR];
-        bool ok[NR];
-        float sc[NR][NC];
+    int e_nx = 0, first_nx = 0, n_nx = 0;
+    if (gwave < n_items) segment(a.sa, gwave / items_per_seg, e_nx, first_nx, n_nx);
+    for (int item = gwave; item < n_items; item += nwaves) {
+        const int blk = item % items_per_seg;
+        const int e = e_nx, first = first_nx, n = n_nx;
+        const int h0 = blk * NR;
+        // slot j, half hf: row h0 + j * RPS + hf
+        const char *rows[NS];
+        bool ok[NS];
+        float sc[NS][NC];
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            ok[r] = h0 + r < H;
-            rows[r] = static_cast<const char *>(a.down) + ((size_t)e * H + h0 + r) * row_bytes;
+        for (int j = 0; j < NS; ++j) {
+            const int h = h0 + j * RPS + half;
+            ok[j] = h < H && n > 0;
+            rows[j] = static_cast<const char *>(a.down) + ((size_t)e * H + min(h, H - 1)) * row_bytes;
 #pragma unroll
-            for (int c = 0; c < NC; ++c) sc[r][c] = 1.f;
+            for (int c = 0; c < NC; ++c) sc[j][c] = 1.f;
         }
         if (WDT == MOE_FP8_E4M3) {
             const int nbi = I / 128;
 #pragma unroll
-            for (int r = 0; r < NR; ++r) {
-                const int h = min(h0 + r, H - 1);
+            for (int j = 0; j < NS; ++j) {
+                const int h = min(h0 + j * RPS + half, H - 1);
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
-                    const int ib = min((lane + kWave * c) * EPC / 128, nbi - 1);
-                    sc[r][c] = a.s_down[((size_t)e * (H / 128) + h / 128) * nbi + ib] * kE4m3Unscale;
+                    const int ib = min(((lane & (G - 1)) + G * c) * EPC / 128, nbi - 1);
+                    sc[j][c] = a.s_down[((size_t)e * (H / 128) + h / 128) * nbi + ib] * kE4m3Unscale;
                 }
             }
         }
-        u32x4 w[NR][NC];
-        load_rows<NC, NR>(w, rows, ok, nq, lane);
+        u32x4 w[NS][NC];
+        load_rows<NC, NS, G>(w, rows, ok, nq, lane);
+        const int rl = lane < n ? segment_route(a.sa, first, lane) : 0;
+        if (item + nwaves < n_items) segment(a.sa, (item + nwaves) / items_per_seg, e_nx, first_nx, n_nx);
         for (int m = 0; m < n; ++m) {
-            const int r = segment_route(a.sa, first, m);
-            float acc[NR];
-            dot_rows<WDT, NC, NR>(w, sc, a.act + (size_t)r * I, nq, lane, acc);
+            const int r = m < kWave ? __shfl(rl, m, kWave) : segment_route(a.sa, first, m);
+            float acc[NS];
+            dot_rows<WDT, NC, NS, G>(w, sc, a.act + (size_t)r * I, nq, lane, acc);
+            float v[NS][1];
 #pragma unroll
-            for (int rr = 0; rr < NR; ++rr) {
-                const float v = wave_sum(acc[rr]);
-                if (lane == rr && ok[rr]) a.y[(size_t)r * H + h0 + rr] = v;
-            }
+            for (int j = 0; j < NS; ++j) v[j][0] = acc[j];
+            reduce_slots<NS, 1, G>(v, lane);
+            const int j = reduced_slot<NS, G>(lane);
+            const int h = h0 + j * RPS + half;
+            if (slot_leader<NS, G>(lane) && h < H) a.y[(size_t)r * H + h] = v[0][0];
         }
     }
 }
 
-
 // Chunks per lane are instantiated for 1, 2, 3, 4 and 8; other counts run on
 // the next larger instance (chunks past the row end are masked).
 __host__ __device__ constexpr int nc_instance(int nc) { return nc <= 4 ? nc : 8; }
+
+// Lanes per down row: 32 when a row's 16-byte chunks are a multiple of 32 but
+// not of 64 (e.g. 768 bf16), so no lane idles; otherwise 64.
+inline int pass2_lanes(int nq) { return (nq % 64 != 0 && nq % 32 == 0) ? 32 : 64; }
 
 template <int WDT>
 hipError_t launch_pass1(int nc, int grid, hipStream_t st, const Pass1Args &a) {
@@ -232,15 +281,28 @@ hipError_t launch_pass1(int nc, int grid, hipStream_t st, const Pass1Args &a) {
 }
 
 template <int WDT>
-hipError_t launch_pass2(int nc, int grid, hipStream_t st, const Pass2Args &a) {
-    switch (nc_instance(nc)) {
-        case 1: hipLaunchKernelGGL((pass2_kernel<WDT, 1>), dim3(grid), dim3(kBlock), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((pass2_kernel<WDT, 2>), dim3(grid), dim3(kBlock), 0, st, a); break;
-        case 3: hipLaunchKernelGGL((pass2_kernel<WDT, 3>), dim3(grid), dim3(kBlock), 0, st, a); break;
-        case 4: hipLaunchKernelGGL((pass2_kernel<WDT, 4>), dim3(grid), dim3(kBlock), 0, st, a); break;
-        case 8: hipLaunchKernelGGL((pass2_kernel<WDT, 8>), dim3(grid), dim3(kBlock), 0, st, a); break;
-        default: return hipErrorInvalidValue;
+hipError_t launch_pass2(int nc, int lanes, int grid, hipStream_t st, const Pass2Args &a) {
+#define MOE_P2(N, L) hipLaunchKernelGGL((pass2_kernel<WDT, N, L>), dim3(grid), dim3(kBlock), 0, st, a)
+    if (lanes == 32) {
+        switch (nc_instance(nc)) {
+            case 1: MOE_P2(1, 32); break;
+            case 2: MOE_P2(2, 32); break;
+            case 3: MOE_P2(3, 32); break;
+            case 4: MOE_P2(4, 32); break;
+            case 8: MOE_P2(8, 32); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (nc_instance(nc)) {
+            case 1: MOE_P2(1, 64); break;
+            case 2: MOE_P2(2, 64); break;
+            case 3: MOE_P2(3, 64); break;
+            case 4: MOE_P2(4, 64); break;
+            case 8: MOE_P2(8, 64); break;
+            default: return hipErrorInvalidValue;
+        }
     }
+#undef MOE_P2
     return hipGetLastError();
 }
 
@@ -248,8 +310,8 @@ hipError_t launch_pass2(int nc, int grid, hipStream_t st, const Pass2Args &a) {
 extern template hipError_t launch_pass1<MOE_F32>(int, int, hipStream_t, const Pass1Args &);
 extern template hipError_t launch_pass1<MOE_BF16>(int, int, hipStream_t, const Pass1Args &);
 extern template hipError_t launch_pass1<MOE_FP8_E4M3>(int, int, hipStream_t, const Pass1Args &);
-extern template hipError_t launch_pass2<MOE_F32>(int, int, hipStream_t, const Pass2Args &);
-extern template hipError_t launch_pass2<MOE_BF16>(int, int, hipStream_t, const Pass2Args &);
-extern template hipError_t launch_pass2<MOE_FP8_E4M3>(int, int, hipStream_t, const Pass2Args &);
+extern template hipError_t launch_pass2<MOE_F32>(int, int, int, hipStream_t, const Pass2Args &);
+extern template hipError_t launch_pass2<MOE_BF16>(int, int, int, hipStream_t, const Pass2Args &);
+extern template hipError_t launch_pass2<MOE_FP8_E4M3>(int, int, int, hipStream_t, const Pass2Args &);
 
 }  // namespace moe

@@ -1,109 +1,174 @@
-// Router GEMV, RMSNorm prologue and top-k selection on the device.
+// Routing of one MoE layer in one launch: [RMSNorm] -> router GEMV ->
+// top-k selection -> counting sort, with no host read anywhere.
 //
-// "MoE Performance Optimization Analysis" (markbaseengine), Option 1 and GPU
-// Router Design: router scores, expert selection and the expert dispatch all
-// stay on the device so no host read or wait sits between the router and the
-// experts.  Selection: the k largest logits by (logit descending, expert
-// index ascending); weights are a softmax over all E logits renormalised over
-// the k chosen, which equals a softmax over the chosen logits alone.
-#include "common.h"
+// "MoE Performance Optimization Analysis" (markbaseengine), Root Cause and
+// Option 1: the per-layer host read of the router scores and the host-side
+// top-2 are the cost; the fix is a device router with device selection and
+// dispatch.  "TEXT Generation Optimization Report", Phase 2: fewer, fused
+// dispatches.  Here the router, the selection and the sort are one kernel:
+//
+//  * Workgroup (eb, tb) computes the logits of 16 experts (4 per wave, rows
+//    held in registers) for a tile of up to 8 tokens staged in LDS
+//    (normalised there first for the RMSNorm form; workgroup eb = 0 also
+//    writes the normalised rows for the expert passes).
+//  * The last workgroup to finish a token tile (per-tile arrival counter)
+//    selects the top k for those tokens, one wave per token.
+//  * The last tile to be selected (arrival counter over tiles) runs the
+//    counting sort in that workgroup.
+// Nothing waits: a workgroup that is not last simply exits.  The arrival
+// counters are reset by the workgroup that consumed them, so they are zero
+// again when the launch ends (a fresh workspace is zeroed once by
+// moe_workspace_init).
+#include "route_impl.h"
 
 namespace moe {
 
-// ---- RMSNorm: xn[t] = x[t] / sqrt(mean(x[t]^2) + eps) (gamma = 1) ---------
-__global__ __launch_bounds__(kBlock) void rmsnorm_kernel(const float *__restrict__ x, float *__restrict__ xn,
-                                                         int H, float eps) {
-    __shared__ float part[kBlock / kWave];
-    const int t = blockIdx.x, tid = threadIdx.x;
-    const float4 *xr = reinterpret_cast<const float4 *>(x + (size_t)t * H);
-    float ss = 0.f;
-    for (int q = tid; q < H / 4; q += kBlock) {
-        float4 v = xr[q];
-        ss = fmaf(v.x, v.x, ss);
-        ss = fmaf(v.y, v.y, ss);
-        ss = fmaf(v.z, v.z, ss);
-        ss = fmaf(v.w, v.w, ss);
-    }
-    ss = wave_sum(ss);
-    if ((tid & (kWave - 1)) == 0) part[tid / kWave] = ss;
-    __syncthreads();
-    const float tot = (part[0] + part[1]) + (part[2] + part[3]);
-    const float r = 1.0f / sqrtf(tot / (float)H + eps);
-    float4 *o = reinterpret_cast<float4 *>(xn + (size_t)t * H);
-    for (int q = tid; q < H / 4; q += kBlock) {
-        float4 v = xr[q];
-        o[q] = make_float4(v.x * r, v.y * r, v.z * r, v.w * r);
-    }
+constexpr int kRouteRows = 4;                      // router rows per wave
+constexpr int kRouteExperts = 4 * kRouteRows;      // experts per workgroup
+constexpr int kRouteTileFloats = 14336;            // token tile: 56 KiB of LDS
+
+__host__ __device__ constexpr int route_tile_tokens(int H) {
+    return H >= kRouteTileFloats ? 1 : (kRouteTileFloats / H < 8 ? kRouteTileFloats / H : 8);
 }
 
-hipError_t launch_rmsnorm(const float *x, float *xn, int T, int H, float eps, hipStream_t st) {
-    hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(kBlock), 0, st, x, xn, H, eps);
-    return hipGetLastError();
-}
-
-// ---- router GEMV --------------------------------------------------------------
-// Workgroup = 16 experts x up to 8 tokens.  Each wave keeps 4 router rows in
-// registers (lane l holds 16-byte chunks l, l+64, ...) and dots them with the
-// token rows read through the cache; one butterfly reduction per (row, token).
-constexpr int kRouterRows = 4;
-constexpr int kRouterTok = 8;
+struct RouteArgs {
+    const void *wr;          // router weights [E, H] (null: logits_in given)
+    const float *bias;       // [E] or null
+    const float *x;          // [T, H]
+    const float *logits_in;  // [T, E] or null
+    float *xn;               // normalised rows [T, H] (RMSNorm form) or null
+    float *logits;           // [T, E] out (when computed)
+    int32_t *ids;            // [T, k]
+    float *w;                // [T, k]
+    int32_t *counts, *offsets, *sorted, *uniq, *n_uniq, *stats;  // counts null: no sort
+    unsigned *arrive;        // [n_tblk + 1] arrival counters, zero on entry and exit
+    int T, E, H, k, n_eblk, n_tblk, tile;
+    int rmsnorm;
+    float eps;
+};
 
 template <int RDT, int NC>
-__global__ __launch_bounds__(kBlock) void router_kernel(const void *__restrict__ wr, const float *__restrict__ bias,
-                                                        const float *__restrict__ x, float *__restrict__ logits,
-                                                        int T, int E, int H) {
+__global__ __launch_bounds__(kBlock) void route_kernel(RouteArgs a) {
+    extern __shared__ float4 dyn_lds[];
+    float *tile = reinterpret_cast<float *>(dyn_lds);
+    __shared__ int s_last;
     constexpr int EPC = WT<RDT>::kEpc;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const int e0 = blockIdx.x * (4 * kRouterRows) + wave * kRouterRows;
-    const int t0 = blockIdx.y * kRouterTok, t1 = min(T, t0 + kRouterTok);
-    const int nq = H / EPC;
-    const size_t row_bytes = (size_t)H * WT<RDT>::kBytes;
-    u32x4 w[kRouterRows][NC];
-#pragma unroll
-    for (int r = 0; r < kRouterRows; ++r)
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const int q = lane + kWave * c;
-            if (e0 + r < E && q < nq)
-                w[r][c] = load_weight_chunk(
-                    reinterpret_cast<const u32x4 *>(static_cast<const char *>(wr) + (size_t)(e0 + r) * row_bytes) + q);
-            else
-                w[r][c] = u32x4{0u, 0u, 0u, 0u};
-        }
-    for (int t = t0; t < t1; ++t) {
-        const float *xv = x + (size_t)t * H;
-        float acc[kRouterRows];
-#pragma unroll
-        for (int r = 0; r < kRouterRows; ++r) acc[r] = 0.f;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const int q = lane + kWave * c;
-            if (q < nq) {
-                float xs[EPC];
-                const float4 *xp = reinterpret_cast<const float4 *>(xv + q * EPC);
-#pragma unroll
-                for (int v = 0; v < EPC / 4; ++v) {
-                    float4 f = xp[v];
-                    xs[4 * v] = f.x; xs[4 * v + 1] = f.y; xs[4 * v + 2] = f.z; xs[4 * v + 3] = f.w;
+    const int eb = blockIdx.x % a.n_eblk, tb = blockIdx.x / a.n_eblk;
+    const int t0 = tb * a.tile, t1 = min(a.T, t0 + a.tile);
+    const int H = a.H, E = a.E;
+
+    if (!a.logits_in) {
+        // token tile -> LDS
+        const int h4 = H / 4;
+        for (int idx = threadIdx.x; idx < (t1 - t0) * h4; idx += kBlock)
+            reinterpret_cast<float4 *>(tile)[idx] = reinterpret_cast<const float4 *>(a.x + (size_t)t0 * H)[idx];
+        __syncthreads();
+        if (a.rmsnorm) {
+            for (int t = wave; t < t1 - t0; t += kBlock / kWave) {
+                float4 *row = reinterpret_cast<float4 *>(tile + (size_t)t * H);
+                float ss = 0.f;
+                for (int q = lane; q < h4; q += kWave) {
+                    const float4 v = row[q];
+                    ss = fmaf(v.x, v.x, ss);
+                    ss = fmaf(v.y, v.y, ss);
+                    ss = fmaf(v.z, v.z, ss);
+                    ss = fmaf(v.w, v.w, ss);
                 }
+                ss = wave_sum(ss);
+                const float rs = 1.0f / sqrtf(ss / (float)H + a.eps);
+                for (int q = lane; q < h4; q += kWave) {
+                    float4 v = row[q];
+                    v.x *= rs; v.y *= rs; v.z *= rs; v.w *= rs;
+                    row[q] = v;
+                    if (eb == 0) reinterpret_cast<float4 *>(a.xn + (size_t)(t0 + t) * H)[q] = v;
+                }
+            }
+            __syncthreads();
+        }
+        // router rows e0 .. e0+3 of this wave
+        const int e0 = eb * kRouteExperts + wave * kRouteRows;
+        const int nq = H / EPC;
+        const size_t row_bytes = (size_t)H * WT<RDT>::kBytes;
+        u32x4 wr[kRouteRows][NC];
 #pragma unroll
-                for (int r = 0; r < kRouterRows; ++r) acc[r] = chunk_dot<RDT>(w[r][c], xs, acc[r]);
+        for (int r = 0; r < kRouteRows; ++r)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const int q = lane + kWave * c;
+                wr[r][c] = (e0 + r < E && q < nq)
+                               ? load_weight_chunk(reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.wr) +
+                                                                                    (size_t)(e0 + r) * row_bytes) + q)
+                               : u32x4{0u, 0u, 0u, 0u};
+            }
+        for (int t = 0; t < t1 - t0; ++t) {
+            const float *xv = tile + (size_t)t * H;
+            // keep the rows packed across the token loop (see dot_rows)
+#pragma unroll
+            for (int r = 0; r < kRouteRows; ++r)
+#pragma unroll
+                for (int c = 0; c < NC; ++c) asm volatile("" : "+v"(wr[r][c]));
+            float acc[kRouteRows][1];
+#pragma unroll
+            for (int r = 0; r < kRouteRows; ++r) acc[r][0] = 0.f;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const int q = lane + kWave * c;
+                if (q < nq) {
+                    float xs[EPC];
+                    const float4 *xp = reinterpret_cast<const float4 *>(xv + q * EPC);
+#pragma unroll
+                    for (int v = 0; v < EPC / 4; ++v) {
+                        const float4 f = xp[v];
+                        xs[4 * v] = f.x; xs[4 * v + 1] = f.y; xs[4 * v + 2] = f.z; xs[4 * v + 3] = f.w;
+                    }
+#pragma unroll
+                    for (int r = 0; r < kRouteRows; ++r) acc[r][0] = chunk_dot<RDT>(wr[r][c], xs, acc[r][0]);
+                }
+            }
+            reduce_slots<kRouteRows, 1, kWave>(acc, lane);
+            const int r = reduced_slot<kRouteRows, kWave>(lane);
+            if (slot_leader<kRouteRows, kWave>(lane) && e0 + r < E) {
+                const float v = a.bias ? acc[0][0] + a.bias[e0 + r] : acc[0][0];
+                store_shared(a.logits + (size_t)(t0 + t) * E + e0 + r, v);
             }
         }
-#pragma unroll
-        for (int r = 0; r < kRouterRows; ++r) {
-            const float s = wave_sum(acc[r]);
-            if (lane == r && e0 + r < E) logits[(size_t)t * E + e0 + r] = bias ? s + bias[e0 + r] : s;
+        wait_vm_stores();
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            s_last = atomicAdd(a.arrive + tb, 1u) + 1u == (unsigned)a.n_eblk;
+            if (s_last) store_shared(a.arrive + tb, 0u);
         }
+        __syncthreads();
+        if (!s_last) return;
     }
+
+    // selection for the tile's tokens, one wave per token
+    const float *lg = a.logits_in ? a.logits_in : a.logits;
+    for (int t = t0 + wave; t < t1; t += kBlock / kWave) {
+        if (a.logits_in)
+            select_token<false>(lg + (size_t)t * E, E, a.k, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, lane);
+        else
+            select_token<true>(lg + (size_t)t * E, E, a.k, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, lane);
+    }
+    if (!a.counts) return;
+    wait_vm_stores();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        s_last = atomicAdd(a.arrive + a.n_tblk, 1u) + 1u == (unsigned)a.n_tblk;
+        if (s_last) store_shared(a.arrive + a.n_tblk, 0u);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    sort_block<true>(a.ids, a.T * a.k, E, a.counts, a.offsets, a.sorted, a.uniq, a.n_uniq, a.stats,
+                     reinterpret_cast<int *>(dyn_lds));
 }
 
 template <int RDT>
-static hipError_t router_dispatch(int nc, dim3 g, hipStream_t st, const void *wr, const float *bias,
-                                  const float *x, float *logits, int T, int E, int H) {
+static hipError_t route_dispatch(int nc, dim3 g, size_t lds, hipStream_t st, const RouteArgs &a) {
     switch (nc) {
 #define MOE_RC(N) \
-    case N: hipLaunchKernelGGL((router_kernel<RDT, N>), g, dim3(kBlock), 0, st, wr, bias, x, logits, T, E, H); break;
+    case N: hipLaunchKernelGGL((route_kernel<RDT, N>), g, dim3(kBlock), lds, st, a); break;
         MOE_RC(1) MOE_RC(2) MOE_RC(3) MOE_RC(4) MOE_RC(5) MOE_RC(6) MOE_RC(7) MOE_RC(8)
 #undef MOE_RC
         default: return hipErrorInvalidValue;
@@ -111,71 +176,58 @@ static hipError_t router_dispatch(int nc, dim3 g, hipStream_t st, const void *wr
     return hipGetLastError();
 }
 
-hipError_t launch_router(const moe_layer_t &L, const float *x, float *logits, int T, hipStream_t st) {
+int route_arrive_words(int T) { return T + 1; }
+
+hipError_t launch_route(const moe_layer_t &L, const float *x, const float *logits_in, int T, float *xn,
+                        float *logits, int32_t *ids, float *w, int32_t *counts, int32_t *offsets, int32_t *sorted,
+                        int32_t *uniq, int32_t *n_uniq, int32_t *stats, unsigned *arrive, bool rmsnorm,
+                        hipStream_t st) {
+    RouteArgs a;
+    a.wr = L.w_router;
+    a.bias = L.router_bias;
+    a.x = x;
+    a.logits_in = logits_in;
+    a.xn = xn;
+    a.logits = logits;
+    a.ids = ids;
+    a.w = w;
+    a.counts = counts;
+    a.offsets = offsets;
+    a.sorted = sorted;
+    a.uniq = uniq;
+    a.n_uniq = n_uniq;
+    a.stats = stats;
+    a.arrive = arrive;
+    a.T = T;
+    a.E = L.E;
+    a.H = L.H;
+    a.k = L.top_k;
+    a.rmsnorm = rmsnorm ? 1 : 0;
+    a.eps = 1e-6f;
+    a.tile = logits_in ? (kBlock / kWave) : route_tile_tokens(L.H);
+    a.n_eblk = logits_in ? 1 : (L.E + kRouteExperts - 1) / kRouteExperts;
+    a.n_tblk = (T + a.tile - 1) / a.tile;
+    size_t lds = (size_t)sort_lds_ints(L.E) * 4;
+    if (!logits_in) {
+        const size_t tb = (size_t)a.tile * L.H * 4;
+        lds = tb > lds ? tb : lds;
+    }
     const int epc = elems_per_chunk(L.router_dtype);
-    const int nc = (L.H / epc + kWave - 1) / kWave;
-    dim3 g((L.E + 4 * kRouterRows - 1) / (4 * kRouterRows), (T + kRouterTok - 1) / kRouterTok);
-    if (L.router_dtype == MOE_BF16)
-        return router_dispatch<MOE_BF16>(nc, g, st, L.w_router, L.router_bias, x, logits, T, L.E, L.H);
-    return router_dispatch<MOE_F32>(nc, g, st, L.w_router, L.router_bias, x, logits, T, L.E, L.H);
+    const int nc = logits_in ? 1 : (L.H / epc + kWave - 1) / kWave;
+    const dim3 g(a.n_eblk * a.n_tblk);
+    if (L.router_dtype == MOE_BF16) return route_dispatch<MOE_BF16>(nc, g, lds, st, a);
+    return route_dispatch<MOE_F32>(nc, g, lds, st, a);
 }
 
-// ---- top-k selection: one wave per token ------------------------------------
-// Lane l holds logits e = l + 64c.  Round j: each lane offers its best
-// unchosen (value, index); a butterfly keeps the larger value, the lower
-// index on ties, so every lane agrees on the winner.  Lane j remembers the
-// winner of round j and finally writes slot j.
-constexpr int kSelPerLane = kMaxE / kWave;
-
-__global__ __launch_bounds__(kBlock) void select_kernel(const float *__restrict__ logits, int T, int E, int k,
-                                                        int32_t *__restrict__ ids, float *__restrict__ w) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int t = blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
-    if (t >= T) return;
-    const float *l = logits + (size_t)t * E;
-    float v[kSelPerLane];
-    uint32_t taken = 0;
-#pragma unroll
-    for (int c = 0; c < kSelPerLane; ++c) {
-        const int e = lane + kWave * c;
-        v[c] = e < E ? l[e] : 0.f;
-    }
-    float top = 0.f, sum = 0.f, mine = 0.f;
-    int mine_id = 0;
-    for (int j = 0; j < k; ++j) {
-        float bv = 0.f;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int c = 0; c < kSelPerLane; ++c) {
-            const int e = lane + kWave * c;
-            if (e < E && !((taken >> c) & 1u) && (bi == 0x7fffffff || v[c] > bv)) {
-                bv = v[c];
-                bi = e;
-            }
-        }
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-            const float ov = __shfl_xor(bv, m, kWave);
-            const int oi = __shfl_xor(bi, m, kWave);
-            const bool better = oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi));
-            if (better) { bv = ov; bi = oi; }
-        }
-        if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
-        if (j == 0) top = bv;
-        const float p = expf(bv - top);
-        sum += p;
-        if (lane == j) { mine = p; mine_id = bi; }
-    }
-    if (lane < k) {
-        ids[(size_t)t * k + lane] = mine_id;
-        w[(size_t)t * k + lane] = mine / sum;
-    }
+// ---- fill kernel (workspace initialisation) ----------------------------------
+__global__ __launch_bounds__(kBlock) void fill_zero_kernel(unsigned *p, int n) {
+    for (int i = blockIdx.x * kBlock + threadIdx.x; i < n; i += gridDim.x * kBlock) p[i] = 0u;
 }
 
-hipError_t launch_select(const float *logits, int T, int E, int k, int32_t *ids, float *w, hipStream_t st) {
-    const int per_block = kBlock / kWave;
-    hipLaunchKernelGGL(select_kernel, dim3((T + per_block - 1) / per_block), dim3(kBlock), 0, st, logits, T, E, k,
-                       ids, w);
+hipError_t launch_zero(unsigned *p, int n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((n + kBlock - 1) / kBlock < 64 ? (n + kBlock - 1) / kBlock : 64),
+                       dim3(kBlock), 0, st, p, n);
     return hipGetLastError();
 }
 

@@ -34,7 +34,9 @@ class _Shell:
 
     def workspace(self, T):
         n = moe.moe_workspace_bytes(self.struct, T)
-        return torch.empty(n, dtype=torch.uint8, device=dev())
+        ws = torch.empty(n, dtype=torch.uint8, device=dev())
+        moe.moe_workspace_init(self.struct, T, ws, n, torch.cuda.current_stream())
+        return ws
 
 
 # ------------------------------------------------------------------ selection --
