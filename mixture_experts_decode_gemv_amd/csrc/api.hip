@@ -92,7 +92,7 @@ moe_status moe_route(const moe_layer_t *layer, const float *x, const float *logi
                 hipSuccess)
             return MOE_ERR_HIP;
         return hip_status(launch_route(*layer, nullptr, logits_in, T, nullptr, nullptr, topk_ids, topk_w, nullptr,
-                                       nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, false, st));
+                                       nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, false, nullptr, 0, st));
     }
     if ((s = check_weights(layer, true, false)) != MOE_OK) return s;
     if (!aligned16(x)) return MOE_ERR_ALIGN;
@@ -102,7 +102,8 @@ moe_status moe_route(const moe_layer_t *layer, const float *x, const float *logi
     char *b = static_cast<char *>(ws);
     float *dst = logits_out ? logits_out : reinterpret_cast<float *>(b + wl.logits);
     return hip_status(launch_route(*layer, x, nullptr, T, nullptr, dst, topk_ids, topk_w, nullptr, nullptr, nullptr,
-                                   nullptr, nullptr, nullptr, reinterpret_cast<unsigned *>(b + wl.arrive), false, st));
+                                   nullptr, nullptr, nullptr, reinterpret_cast<unsigned *>(b + wl.arrive), false,
+                                   nullptr, 0, st));
 }
 
 moe_status moe_sort(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int32_t *counts, int32_t *offsets,
@@ -161,7 +162,7 @@ moe_status moe_layer_fwd(const moe_layer_t *layer, const float *x, int32_t T, fl
     if ((s = hip_status(launch_route(*layer, x, nullptr, T, norm ? F(wl.xn) : nullptr, F(wl.logits), I32(wl.ids),
                                      F(wl.w), I32(wl.counts), I32(wl.offsets), I32(wl.sorted), I32(wl.uniq),
                                      I32(wl.nuniq), I32(wl.stats), reinterpret_cast<unsigned *>(b + wl.arrive), norm,
-                                     st))) != MOE_OK)
+                                     nullptr, 0, st))) != MOE_OK)
         return s;
     (void)R;
     Routing rt{I32(wl.ids), I32(wl.counts), I32(wl.offsets), I32(wl.sorted), I32(wl.uniq), I32(wl.nuniq), F(wl.w)};

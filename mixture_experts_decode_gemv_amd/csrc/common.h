@@ -206,7 +206,7 @@ int num_cus();
 hipError_t launch_route(const moe_layer_t &L, const float *x, const float *logits_in, int T, float *xn,
                         float *logits, int32_t *ids, float *w, int32_t *counts, int32_t *offsets, int32_t *sorted,
                         int32_t *uniq, int32_t *n_uniq, int32_t *stats, unsigned *arrive, bool rmsnorm,
-                        hipStream_t st);
+                        unsigned *zero, int n_zero, hipStream_t st);
 hipError_t launch_sort(const int32_t *ids, int R, int E, int32_t *counts, int32_t *offsets, int32_t *sorted,
                        int32_t *uniq, int32_t *n_uniq, hipStream_t st);
 hipError_t launch_zero(unsigned *p, int n, hipStream_t st);

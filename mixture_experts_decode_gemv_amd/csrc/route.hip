@@ -8,7 +8,7 @@
 // dispatches.  Here the router, the selection and the sort are one kernel:
 //
 //  * Workgroup (eb, tb) computes the logits of 16 experts (4 per wave, rows
-//    held in registers) for a tile of up to 8 tokens staged in LDS
+//    held in registers) for a tile of up to 8 tokens (32 KiB) staged in LDS
 //    (normalised there first for the RMSNorm form; workgroup eb = 0 also
 //    writes the normalised rows for the expert passes).
 //  * The last workgroup to finish a token tile (per-tile arrival counter)
@@ -25,7 +25,7 @@ namespace moe {
 
 constexpr int kRouteRows = 4;                      // router rows per wave
 constexpr int kRouteExperts = 4 * kRouteRows;      // experts per workgroup
-constexpr int kRouteTileFloats = 14336;            // token tile: 56 KiB of LDS
+constexpr int kRouteTileFloats = 8192;             // token tile: 32 KiB of LDS
 
 __host__ __device__ constexpr int route_tile_tokens(int H) {
     return H >= kRouteTileFloats ? 1 : (kRouteTileFloats / H < 8 ? kRouteTileFloats / H : 8);
@@ -42,6 +42,8 @@ struct RouteArgs {
     float *w;                // [T, k]
     int32_t *counts, *offsets, *sorted, *uniq, *n_uniq, *stats;  // counts null: no sort
     unsigned *arrive;        // [n_tblk + 1] arrival counters, zero on entry and exit
+    unsigned *zero;          // counters of the kernels that follow, zeroed by the sort
+    int n_zero;
     int T, E, H, k, n_eblk, n_tblk, tile;
     int rmsnorm;
     float eps;
@@ -59,10 +61,40 @@ __global__ __launch_bounds__(kBlock) void route_kernel(RouteArgs a) {
     const int H = a.H, E = a.E;
 
     if (!a.logits_in) {
-        // token tile -> LDS
+        // router rows e0 .. e0+3 of this wave, issued first (they do not
+        // depend on the tokens)
+        const int e0 = eb * kRouteExperts + wave * kRouteRows;
+        const int nq = H / EPC;
+        const size_t row_bytes = (size_t)H * WT<RDT>::kBytes;
+        u32x4 wr[kRouteRows][NC];
+#pragma unroll
+        for (int r = 0; r < kRouteRows; ++r)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const int q = lane + kWave * c;
+                wr[r][c] = (e0 + r < E && q < nq)
+                               ? load_weight_chunk(reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.wr) +
+                                                                                    (size_t)(e0 + r) * row_bytes) + q)
+                               : u32x4{0u, 0u, 0u, 0u};
+            }
+        // token tile -> LDS, 8 loads in flight per thread
         const int h4 = H / 4;
-        for (int idx = threadIdx.x; idx < (t1 - t0) * h4; idx += kBlock)
-            reinterpret_cast<float4 *>(tile)[idx] = reinterpret_cast<const float4 *>(a.x + (size_t)t0 * H)[idx];
+        {
+            const int n4 = (t1 - t0) * h4;
+            const float4 *src = reinterpret_cast<const float4 *>(a.x + (size_t)t0 * H);
+            float4 *dst = reinterpret_cast<float4 *>(tile);
+            for (int base = 0; base < n4; base += 8 * kBlock) {
+                float4 v[8];
+                // unconditional loads (index clamped) keep v in registers
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] = src[min(base + u * kBlock + (int)threadIdx.x, n4 - 1)];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int idx = base + u * kBlock + threadIdx.x;
+                    if (idx < n4) dst[idx] = v[u];
+                }
+            }
+        }
         __syncthreads();
         if (a.rmsnorm) {
             for (int t = wave; t < t1 - t0; t += kBlock / kWave) {
@@ -86,51 +118,46 @@ __global__ __launch_bounds__(kBlock) void route_kernel(RouteArgs a) {
             }
             __syncthreads();
         }
-        // router rows e0 .. e0+3 of this wave
-        const int e0 = eb * kRouteExperts + wave * kRouteRows;
-        const int nq = H / EPC;
-        const size_t row_bytes = (size_t)H * WT<RDT>::kBytes;
-        u32x4 wr[kRouteRows][NC];
-#pragma unroll
-        for (int r = 0; r < kRouteRows; ++r)
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const int q = lane + kWave * c;
-                wr[r][c] = (e0 + r < E && q < nq)
-                               ? load_weight_chunk(reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.wr) +
-                                                                                    (size_t)(e0 + r) * row_bytes) + q)
-                               : u32x4{0u, 0u, 0u, 0u};
-            }
-        for (int t = 0; t < t1 - t0; ++t) {
-            const float *xv = tile + (size_t)t * H;
-            // keep the rows packed across the token loop (see dot_rows)
+        // two tokens per pass (independent chains); each token reduced on its
+        // own, so a logit never depends on its position in the tile
+        const int nt = t1 - t0;
+        for (int t = 0; t < nt; t += 2) {
+            const bool two = t + 1 < nt;
 #pragma unroll
             for (int r = 0; r < kRouteRows; ++r)
 #pragma unroll
                 for (int c = 0; c < NC; ++c) asm volatile("" : "+v"(wr[r][c]));
-            float acc[kRouteRows][1];
+            float acc0[kRouteRows][1], acc1[kRouteRows][1];
 #pragma unroll
-            for (int r = 0; r < kRouteRows; ++r) acc[r][0] = 0.f;
+            for (int r = 0; r < kRouteRows; ++r) { acc0[r][0] = 0.f; acc1[r][0] = 0.f; }
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 const int q = lane + kWave * c;
                 if (q < nq) {
-                    float xs[EPC];
-                    const float4 *xp = reinterpret_cast<const float4 *>(xv + q * EPC);
+                    float xs0[EPC], xs1[EPC];
+                    const float4 *xp0 = reinterpret_cast<const float4 *>(tile + (size_t)t * H + q * EPC);
+                    const float4 *xp1 = reinterpret_cast<const float4 *>(tile + (size_t)(two ? t + 1 : t) * H + q * EPC);
 #pragma unroll
                     for (int v = 0; v < EPC / 4; ++v) {
-                        const float4 f = xp[v];
-                        xs[4 * v] = f.x; xs[4 * v + 1] = f.y; xs[4 * v + 2] = f.z; xs[4 * v + 3] = f.w;
+                        const float4 f0 = xp0[v], f1 = xp1[v];
+                        xs0[4 * v] = f0.x; xs0[4 * v + 1] = f0.y; xs0[4 * v + 2] = f0.z; xs0[4 * v + 3] = f0.w;
+                        xs1[4 * v] = f1.x; xs1[4 * v + 1] = f1.y; xs1[4 * v + 2] = f1.z; xs1[4 * v + 3] = f1.w;
                     }
 #pragma unroll
-                    for (int r = 0; r < kRouteRows; ++r) acc[r][0] = chunk_dot<RDT>(wr[r][c], xs, acc[r][0]);
+                    for (int r = 0; r < kRouteRows; ++r) {
+                        acc0[r][0] = chunk_dot<RDT>(wr[r][c], xs0, acc0[r][0]);
+                        acc1[r][0] = chunk_dot<RDT>(wr[r][c], xs1, acc1[r][0]);
+                    }
                 }
             }
-            reduce_slots<kRouteRows, 1, kWave>(acc, lane);
+            reduce_slots<kRouteRows, 1, kWave>(acc0, lane);
+            reduce_slots<kRouteRows, 1, kWave>(acc1, lane);
             const int r = reduced_slot<kRouteRows, kWave>(lane);
             if (slot_leader<kRouteRows, kWave>(lane) && e0 + r < E) {
-                const float v = a.bias ? acc[0][0] + a.bias[e0 + r] : acc[0][0];
-                store_shared(a.logits + (size_t)(t0 + t) * E + e0 + r, v);
+                const float bias = a.bias ? a.bias[e0 + r] : 0.f;
+                store_shared(a.logits + (size_t)(t0 + t) * E + e0 + r, a.bias ? acc0[0][0] + bias : acc0[0][0]);
+                if (two)
+                    store_shared(a.logits + (size_t)(t0 + t + 1) * E + e0 + r, a.bias ? acc1[0][0] + bias : acc1[0][0]);
             }
         }
         wait_vm_stores();
@@ -152,6 +179,14 @@ __global__ __launch_bounds__(kBlock) void route_kernel(RouteArgs a) {
             select_token<true>(lg + (size_t)t * E, E, a.k, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, lane);
     }
     if (!a.counts) return;
+    if (a.n_tblk == 1) {
+        // one tile: this workgroup selected every token, no second arrival
+        wait_vm_stores();
+        __syncthreads();
+        sort_block<true>(a.ids, a.T * a.k, E, a.counts, a.offsets, a.sorted, a.uniq, a.n_uniq, a.stats,
+                          reinterpret_cast<int *>(dyn_lds), a.zero, a.n_zero);
+        return;
+    }
     wait_vm_stores();
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -161,7 +196,7 @@ __global__ __launch_bounds__(kBlock) void route_kernel(RouteArgs a) {
     __syncthreads();
     if (!s_last) return;
     sort_block<true>(a.ids, a.T * a.k, E, a.counts, a.offsets, a.sorted, a.uniq, a.n_uniq, a.stats,
-                     reinterpret_cast<int *>(dyn_lds));
+                     reinterpret_cast<int *>(dyn_lds), a.zero, a.n_zero);
 }
 
 template <int RDT>
@@ -181,8 +216,10 @@ int route_arrive_words(int T) { return T + 1; }
 hipError_t launch_route(const moe_layer_t &L, const float *x, const float *logits_in, int T, float *xn,
                         float *logits, int32_t *ids, float *w, int32_t *counts, int32_t *offsets, int32_t *sorted,
                         int32_t *uniq, int32_t *n_uniq, int32_t *stats, unsigned *arrive, bool rmsnorm,
-                        hipStream_t st) {
+                        unsigned *zero, int n_zero, hipStream_t st) {
     RouteArgs a;
+    a.zero = zero;
+    a.n_zero = n_zero;
     a.wr = L.w_router;
     a.bias = L.router_bias;
     a.x = x;

@@ -53,81 +53,124 @@ __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
 }
 
-// This lane's best untaken (key, index) over its logits e = lane + 64c;
-// key 0 means none.  Strictly greater wins, so the lowest c (lowest index)
-// keeps a tie.
-__device__ __forceinline__ void lane_best(const uint32_t (&key)[kSelPerLane], uint32_t taken, int nc, int E, int lane,
-                                          uint32_t &kb, uint32_t &ib) {
-    kb = 0u;
-    ib = 0xFFFFFFFFu;
-#pragma unroll
-    for (int c = 0; c < kSelPerLane; ++c) {
-        if (c < nc && lane + kWave * c < E && !((taken >> c) & 1u) && key[c] > kb) {
-            kb = key[c];
-            ib = (uint32_t)(lane + kWave * c);
-        }
-    }
+// Wave-wide float sum by the same DPP pattern (fixed order, so the result is
+// deterministic); every lane receives lane 63's total.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    auto add = [](float a, int b) { return a + __int_as_float(b); };
+    v = add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, false));
+    v = add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, false));
+    v = add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, false));
+    v = add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, false));
+    v = add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+    v = add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
 }
 
 // One wave selects for one token.  l: the token's E logits (COHERENT: written
 // by other workgroups of this launch).  Writes ids[0..k) and w[0..k) with
-// device-scope stores.
-template <bool COHERENT>
-__device__ void select_token(const float *l, int E, int k, int32_t *ids, float *w, int lane) {
-    uint32_t key[kSelPerLane];
+// device-scope stores.  Each lane sorts its own keys once (descending key,
+// ascending index); a round then takes the wave maximum of the lanes' heads,
+// finds its lane by ballot, and only on an exact tie between lanes runs a
+// second reduction for the lowest index; the winning lane advances its head.
+template <bool COHERENT, int NCS>
+__device__ void select_token_n(const float *l, int E, int k, int32_t *ids, float *w, int lane) {
+    uint32_t key[NCS];
+    uint32_t idx[NCS];
     const int nc = (E + kWave - 1) / kWave;
 #pragma unroll
-    for (int c = 0; c < kSelPerLane; ++c) {
+    for (int c = 0; c < NCS; ++c) {
         const int e = lane + kWave * c;
+        const bool valid = c < nc && e < E;
         float v = 0.f;
-        if (c < nc && e < E) v = COHERENT ? load_shared(l + e) : l[e];
-        key[c] = logit_key(v);
+        if (valid) v = COHERENT ? load_shared(l + e) : l[e];
+        key[c] = valid ? logit_key(v) : 0u;  // 0: no expert
+        idx[c] = (uint32_t)e;
     }
-    uint32_t taken = 0u, kb, ib;
-    lane_best(key, taken, nc, E, lane, kb, ib);
-    uint32_t my_key = 0u, my_idx = 0u, top = 0u;
-    for (int j = 0; j < k; ++j) {
-        const uint32_t m = wave_reduce_u32<true>(kb);
-        const uint32_t idx = wave_reduce_u32<false>(kb == m ? ib : 0xFFFFFFFFu);
-        if (j == 0) top = m;
-        if (lane == j) { my_key = m; my_idx = idx; }
-        if ((int)(idx & (kWave - 1)) == lane) {
-            taken |= 1u << (idx / kWave);
-            lane_best(key, taken, nc, E, lane, kb, ib);
+    // per-lane insertion sort, descending key (stable: equal keys keep the
+    // ascending index order they were generated in)
+#pragma unroll
+    for (int i = 1; i < NCS; ++i) {
+#pragma unroll
+        for (int j = i; j > 0; --j) {
+            if (key[j] > key[j - 1]) {
+                const uint32_t tk = key[j]; key[j] = key[j - 1]; key[j - 1] = tk;
+                const uint32_t ti = idx[j]; idx[j] = idx[j - 1]; idx[j - 1] = ti;
+            }
         }
     }
+    int head = 0;
+    uint32_t my_key = 0u, my_idx = 0u, top = 0u;
+    for (int j = 0; j < k; ++j) {
+        uint32_t hk = 0u, hi = 0xFFFFFFFFu;
+#pragma unroll
+        for (int c = 0; c < NCS; ++c)
+            if (c == head) { hk = key[c]; hi = idx[c]; }
+        const uint32_t m = wave_reduce_u32<true>(hk);
+        const unsigned long long holders = __ballot(hk == m);
+        uint32_t win;
+        if (__popcll(holders) == 1) win = (uint32_t)__shfl((int)hi, __ffsll((long long)holders) - 1, kWave);
+        else win = wave_reduce_u32<false>(hk == m ? hi : 0xFFFFFFFFu);
+        if (j == 0) top = m;
+        if (lane == j) { my_key = m; my_idx = win; }
+        if (hi == win) ++head;
+    }
     const float p = lane < k ? expf(key_logit(my_key) - key_logit(top)) : 0.f;
-    const float sum = wave_sum(p);
+    const float sum = wave_sum_dpp(p);
     if (lane < k) {
         store_shared(ids + lane, (int32_t)my_idx);
         store_shared(w + lane, p / sum);
     }
 }
 
+// Logits per lane instantiated for 1, 2, 4, 8 and 16 (E <= 1024).
+template <bool COHERENT>
+__device__ void select_token(const float *l, int E, int k, int32_t *ids, float *w, int lane) {
+    const int nc = (E + kWave - 1) / kWave;
+    if (nc <= 1) select_token_n<COHERENT, 1>(l, E, k, ids, w, lane);
+    else if (nc <= 2) select_token_n<COHERENT, 2>(l, E, k, ids, w, lane);
+    else if (nc <= 4) select_token_n<COHERENT, 4>(l, E, k, ids, w, lane);
+    else if (nc <= 8) select_token_n<COHERENT, 8>(l, E, k, ids, w, lane);
+    else select_token_n<COHERENT, 16>(l, E, k, ids, w, lane);
+}
+
 // LDS ints needed by sort_block for E experts.
 __host__ __device__ constexpr int sort_lds_ints(int E) { return 11 * E; }
 
 // One workgroup sorts R routes.  ids COHERENT: written by other workgroups
-// of this launch.  lds: sort_lds_ints(E) ints.
+// of this launch.  lds: sort_lds_ints(E) ints.  Each thread loads its routes
+// r = tid + 256 w once (up to 16 windows held in registers).  Also zeroes
+// n_zero words at zero (counters of the kernels that follow).
 template <bool COHERENT>
 __device__ void sort_block(const int32_t *ids, int R, int E, int32_t *counts, int32_t *offsets, int32_t *sorted,
-                           int32_t *uniq, int32_t *n_uniq, int32_t *stats, int *lds) {
-    __shared__ int s_tmp[kBlock / kWave];
+                           int32_t *uniq, int32_t *n_uniq, int32_t *stats, int *lds, unsigned *zero, int n_zero) {
+    constexpr int kWin = 16;
     __shared__ int s_bad, s_max;
+    __shared__ int s_wc[kBlock / kWave], s_wu[kBlock / kWave];
     int *s_cnt = lds, *s_off = lds + E, *s_run = lds + 2 * E;
     unsigned *s_bits = reinterpret_cast<unsigned *>(lds + 3 * E);  // [E][8]
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int nwin = (R + kBlock - 1) / kBlock;
 
+    int v[kWin];
+#pragma unroll
+    for (int w = 0; w < kWin; ++w) {
+        const int r = tid + kBlock * w;
+        v[w] = (w < nwin && r < R) ? (COHERENT ? load_shared(ids + r) : ids[r]) : -1;
+    }
+    for (int i = tid; i < n_zero; i += kBlock) zero[i] = 0u;
     for (int e = tid; e < E; e += kBlock) {
         s_cnt[e] = 0;
         s_run[e] = 0;
     }
     if (tid == 0) { s_bad = 0; s_max = 0; }
     __syncthreads();
-    for (int r = tid; r < R; r += kBlock) {
-        const int v = COHERENT ? load_shared(ids + r) : ids[r];
-        if (v < 0 || v >= E) s_bad = 1;
-        else atomicAdd(&s_cnt[v], 1);
+    for (int w = 0; w < nwin; ++w) {
+        const int r = tid + kBlock * w;
+        const int vv = w < kWin ? v[w] : (r < R ? (COHERENT ? load_shared(ids + r) : ids[r]) : -1);
+        if (r < R) {
+            if (vv < 0 || vv >= E) s_bad = 1;
+            else atomicAdd(&s_cnt[vv], 1);
+        }
     }
     __syncthreads();
     if (s_bad) {
@@ -152,7 +195,6 @@ __device__ void sort_block(const int32_t *ids, int R, int E, int32_t *counts, in
         const int oc = __shfl_up(cinc, d, kWave), ou = __shfl_up(uinc, d, kWave);
         if (lane >= d) { cinc += oc; uinc += ou; }
     }
-    __shared__ int s_wc[kBlock / kWave], s_wu[kBlock / kWave];
     if (lane == kWave - 1) { s_wc[wave] = cinc; s_wu[wave] = uinc; }
     atomicMax(&s_max, cmax);
     __syncthreads();
@@ -161,7 +203,6 @@ __device__ void sort_block(const int32_t *ids, int R, int E, int32_t *counts, in
         if (wv < wave) { cpre += s_wc[wv]; upre += s_wu[wv]; }
         utot += s_wu[wv];
     }
-    (void)s_tmp;
     for (int e = lo; e < hi; ++e) {
         const int c = s_cnt[e];
         s_off[e] = cpre;
@@ -175,30 +216,35 @@ __device__ void sort_block(const int32_t *ids, int R, int E, int32_t *counts, in
         *n_uniq = utot;
         if (stats) { stats[0] = utot; stats[1] = R; stats[2] = s_max; stats[3] = 0; }
     }
-    __syncthreads();
     // stable scatter, 256 routes per window
-    for (int base = 0; base < R; base += kBlock) {
+    for (int w = 0; w < nwin; ++w) {
         for (int i = tid; i < E * 8; i += kBlock) s_bits[i] = 0u;
         __syncthreads();
-        const int r = base + tid;
-        const int v = r < R ? (COHERENT ? load_shared(ids + r) : ids[r]) : -1;
-        const int word = tid >> 5, bit = tid & 31;
-        if (v >= 0) atomicOr(&s_bits[v * 8 + word], 1u << bit);
-        __syncthreads();
-        if (v >= 0) {
-            int rank = s_run[v];
-            for (int wd = 0; wd < word; ++wd) rank += __popc(s_bits[v * 8 + wd]);
-            rank += __popc(s_bits[v * 8 + word] & ((1u << bit) - 1u));
-            sorted[s_off[v] + rank] = r;
-        }
-        __syncthreads();
-        for (int e = tid; e < E; e += kBlock) {
-            int add = 0;
+        const int r = tid + kBlock * w;
+        int vv = -1;
 #pragma unroll
-            for (int wd = 0; wd < 8; ++wd) add += __popc(s_bits[e * 8 + wd]);
-            s_run[e] += add;
+        for (int u = 0; u < kWin; ++u)
+            if (u == w) vv = v[u];
+        if (w >= kWin && r < R) vv = COHERENT ? load_shared(ids + r) : ids[r];
+        const int word = tid >> 5, bit = tid & 31;
+        if (vv >= 0) atomicOr(&s_bits[vv * 8 + word], 1u << bit);
+        __syncthreads();
+        if (vv >= 0) {
+            int rank = s_run[vv];
+            for (int wd = 0; wd < word; ++wd) rank += __popc(s_bits[vv * 8 + wd]);
+            rank += __popc(s_bits[vv * 8 + word] & ((1u << bit) - 1u));
+            sorted[s_off[vv] + rank] = r;
         }
         __syncthreads();
+        if (w + 1 < nwin) {
+            for (int e = tid; e < E; e += kBlock) {
+                int add = 0;
+#pragma unroll
+                for (int wd = 0; wd < 8; ++wd) add += __popc(s_bits[e * 8 + wd]);
+                s_run[e] += add;
+            }
+            __syncthreads();
+        }
     }
 }
 
