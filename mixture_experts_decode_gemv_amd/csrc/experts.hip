@@ -22,6 +22,10 @@
 //  * Combine: out[t, h] = sum_j w[t, j] * y[t*k + j, h], j ascending
 //    ("MoE Performance Optimization Analysis", Root Cause, step 6, combine
 //    on the device), plus x[t, h] for the residual form.
+#include <limits.h>
+
+#include <algorithm>
+
 #include "experts_impl.h"
 
 namespace moe {
@@ -57,18 +61,42 @@ static int persistent_grid(long long max_items_waves) {
     return (int)(g < 1 ? 1 : g);
 }
 
+// Segments with at least kMfmaMinRoutes routes go to the MFMA kernels when the
+// weights are bf16 or fp8 with H and I multiples of 128, unless the caller
+// asked for the GEMV path only.  A segment cannot hold more routes than there
+// are tokens, so below kMfmaMinRoutes tokens no MFMA kernel is launched.
+static bool mfma_eligible(const moe_layer_t &L, int T, uint32_t flags) {
+    return (L.expert_dtype == MOE_BF16 || L.expert_dtype == MOE_FP8_E4M3) && L.H % 128 == 0 && L.I % 128 == 0 &&
+           !(flags & MOE_NO_MFMA) && T >= kMfmaMinRoutes && (int)(flags & MOE_WALK_MASK) != MOE_WALK_PER_ROUTE;
+}
+
+static hipError_t launch_mfma_pass(const moe_layer_t &L, int pass, int T, const MfmaArgs &a, hipStream_t st) {
+    // items <= row blocks x (segments that can reach the threshold + extra token blocks)
+    const long long R = (long long)T * L.top_k;
+    const long long segs = std::min<long long>(L.E, R / kMfmaMinRoutes);
+    const long long n_rb = pass == 1 ? L.I / 64 : L.H / 128;
+    const long long items = n_rb * (segs + R / kMfmaTokens);
+    const long long cap = (long long)num_cus() * 2;
+    const int grid = (int)std::max<long long>(1, std::min(items, cap));
+    return L.expert_dtype == MOE_BF16 ? launch_mfma<MOE_BF16>(pass, grid, st, a)
+                                      : launch_mfma<MOE_FP8_E4M3>(pass, grid, st, a);
+}
+
 hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xres, int T, const Routing &rt,
                           float *act, float *y, float *out, uint32_t flags, hipStream_t st) {
     const int R = T * L.top_k;
     const int walk = (int)(flags & MOE_WALK_MASK);
     const int epc = elems_per_chunk(L.expert_dtype);
     const int max_uniq = R < L.E ? R : L.E;
-    SegArgs grouped{rt.ids, rt.counts, rt.offsets, rt.sorted, rt.uniq, rt.n_uniq, 1, R, L.E};
+    const bool mfma = mfma_eligible(L, T, flags);
+    SegArgs grouped{rt.ids, rt.counts, rt.offsets, rt.sorted, rt.uniq, rt.n_uniq, 1, R, L.E, INT_MAX};
     SegArgs per_route = grouped;
     per_route.grouped = 0;
+    SegArgs split = grouped;  // the GEMV share of a pass that also has MFMA segments
+    if (mfma) split.gemv_below = kMfmaMinRoutes;
 
     // pass 1: one wave item = P gate/up pairs of one segment
-    Pass1Args p1{L.w_gate_up, L.s_gate_up, x, act, L.H, L.I, L.top_k, walk == MOE_WALK_PER_ROUTE ? per_route : grouped};
+    Pass1Args p1{L.w_gate_up, L.s_gate_up, x, act, L.H, L.I, L.top_k, walk == MOE_WALK_PER_ROUTE ? per_route : split};
     const int nq1 = L.H / epc;
     const int nc1 = nc_instance((nq1 + kWave - 1) / kWave);
     const int pairs = slots_for(nc1) / 2;
@@ -80,9 +108,14 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
         default: err = launch_pass1<MOE_FP8_E4M3>(nc1, persistent_grid(items1), st, p1); break;
     }
     if (err != hipSuccess) return err;
+    if (mfma) {
+        MfmaArgs m1{L.w_gate_up, L.s_gate_up, x, act, L.H, L.I, L.top_k, kMfmaMinRoutes, grouped};
+        if ((err = launch_mfma_pass(L, 1, T, m1, st)) != hipSuccess) return err;
+    }
 
     // pass 2: one wave item = slots x (64 / lanes) down rows of one segment
-    Pass2Args p2{L.w_down, L.s_down, act, y, L.H, L.I, walk == MOE_WALK_DEDUP ? grouped : per_route};
+    const bool mfma2 = mfma && walk == MOE_WALK_DEDUP;
+    Pass2Args p2{L.w_down, L.s_down, act, y, L.H, L.I, walk == MOE_WALK_DEDUP ? (mfma2 ? split : grouped) : per_route};
     const int nq2 = L.I / epc;
     const int lanes = pass2_lanes(nq2);
     const int nc2 = nc_instance((nq2 + lanes - 1) / lanes);
@@ -94,6 +127,10 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
         default: err = launch_pass2<MOE_FP8_E4M3>(nc2, lanes, persistent_grid(items2), st, p2); break;
     }
     if (err != hipSuccess) return err;
+    if (mfma2) {
+        MfmaArgs m2{L.w_down, L.s_down, act, y, L.H, L.I, L.top_k, kMfmaMinRoutes, grouped};
+        if ((err = launch_mfma_pass(L, 2, T, m2, st)) != hipSuccess) return err;
+    }
 
     hipLaunchKernelGGL(combine_kernel, dim3(T, (L.H / 4 + kBlock - 1) / kBlock), dim3(kBlock), 0, st, y, rt.w, xres,
                        out, L.top_k, L.H);

@@ -21,6 +21,7 @@ struct SegArgs {
     int grouped;  // 1: segment = unique expert, 0: segment = one route
     int R;        // routes
     int E;        // experts (ids outside [0, E) make an empty segment)
+    int gemv_below;  // segments with this many routes or more are left to the MFMA kernels
 };
 
 // Expert, first sorted slot and route count of segment s.
@@ -38,6 +39,7 @@ __device__ __forceinline__ void segment(const SegArgs &sa, int s, int &e, int &f
         e = 0;
         n = 0;
     }
+    if (n >= sa.gemv_below) n = 0;
 }
 
 __device__ __forceinline__ int segment_route(const SegArgs &sa, int first, int i) {
@@ -305,6 +307,27 @@ hipError_t launch_pass2(int nc, int lanes, int grid, hipStream_t st, const Pass2
 #undef MOE_P2
     return hipGetLastError();
 }
+
+// ---- MFMA segments ------------------------------------------------------------
+// Segments with at least kMfmaMinRoutes routes run on the matrix cores (see
+// experts_mfma.hip), in token blocks of kMfmaTokens routes.
+constexpr int kMfmaMinRoutes = 16;
+constexpr int kMfmaTokens = 128;
+
+struct MfmaArgs {
+    const void *w;        // pass 1: gate_up [E, 2I, H]; pass 2: down [E, H, I]
+    const float *scales;  // fp8 block scales of w, else null
+    const float *src;     // pass 1: x [T, H]; pass 2: act [R, I]
+    float *dst;           // pass 1: act [R, I]; pass 2: y [R, H]
+    int H, I, k;
+    int min_n;            // segments with at least min_n routes
+    SegArgs sa;           // grouped segments
+};
+
+template <int WDT>
+hipError_t launch_mfma(int pass, int grid, hipStream_t st, const MfmaArgs &a);
+extern template hipError_t launch_mfma<MOE_BF16>(int, int, hipStream_t, const MfmaArgs &);
+extern template hipError_t launch_mfma<MOE_FP8_E4M3>(int, int, hipStream_t, const MfmaArgs &);
 
 // Defined in experts_<dtype>.hip.
 extern template hipError_t launch_pass1<MOE_F32>(int, int, hipStream_t, const Pass1Args &);

@@ -175,3 +175,36 @@ def check_layer_against_oracle(layer, olayer, x, flags=0, tol=1e-4, rmsnorm_in=F
 def make_device_layer(spec: wl.LayerSpec, bias=None, layer_idx=0):
     w = wl.make_layer(spec, layer=layer_idx)
     return w, moe.DeviceLayer(w, bias, device=dev()), oracle.Layer(w, bias)
+
+
+def oracle_weights_for(oracle_logits, ids):
+    """Combine weights of the given expert ids: softmax of the oracle's logits
+    over those experts."""
+    lg = np.take_along_axis(oracle_logits, ids.astype(np.int64), axis=1)
+    w = np.exp(lg - lg.max(axis=1, keepdims=True))
+    return w / w.sum(axis=1, keepdims=True)
+
+
+def check_layer_sampled(layer, olayer, x, sample, flags=0, tol=2e-2):
+    """moe_layer_fwd at a size the oracle cannot finish whole: routing of
+    every token against the oracle (ids bit-exact except near-ties, the sort
+    bit-exact on the GPU's ids), outputs on the sampled tokens only.
+    Returns (max rel err on the sample, GPU result dict)."""
+    s = layer.spec
+    g = gpu_layer_fwd(layer, x, flags, full=True)
+    logits = oracle.router_logits(olayer, x)
+    ids_ref, _ = oracle.select(logits, s.top_k)
+    amb = ambiguous_tokens(logits, s.top_k)
+    same = (g["ids"] == ids_ref).all(1)
+    assert (same | amb).all(), "selection differs on tokens with a clear gap: %s" % np.where(~(same | amb))[0]
+    r = oracle.sort(g["ids"], s.E)
+    for key in ("counts", "offsets", "sorted_routes", "uniq"):
+        assert np.array_equal(g[key], r[key]), key
+    sample = np.asarray(sample)
+    ids_s = g["ids"][sample]
+    ref = oracle.expert_fwd(olayer, x[sample], ids_s, oracle_weights_for(logits[sample], ids_s))
+    got = g["out"][sample]
+    assert np.isfinite(g["out"]).all()
+    err = max_rel(got, ref)
+    assert err <= tol, "max rel err %g > %g on the sampled tokens" % (err, tol)
+    return err, g

@@ -1,0 +1,203 @@
+"""Parity of the MFMA segment path (experts that hold >= 16 routes) with the
+CPU oracle, through the C ABI.
+
+The MFMA path rounds both operands of each product to bf16 and accumulates
+in fp32: the activations x (pass 1) and a (pass 2), and, for fp8 weights, the
+decoded code times its block scale.  Its bar is the 2e-2 max relative error
+(max abs error over max |ref|) stated for bf16 weights with fp32
+accumulation.  Segments below the threshold stay on the GEMV path, whose
+results must not change bit for bit when other segments of the same call
+take the MFMA path.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+import mixture_experts_decode_gemv_amd as moe  # noqa: E402
+import oracle  # noqa: E402
+import workload as wl  # noqa: E402
+
+from gpu_util import (check_layer_sampled, dev, gpu_expert_fwd, make_device_layer, max_rel,  # noqa: E402
+                      note, oracle_weights_for)
+
+NORTH_STAR_TOL = 2e-2
+MFMA_MIN = 16  # routes per expert from which a segment runs on MFMA
+
+# H = I = 384: 3 K-stages of 128 in both passes (an odd count), 6 pass-1 row
+# blocks of 64 gate/up pairs, 3 pass-2 row blocks of 128 down rows
+MIXED = wl.LayerSpec(E=8, top_k=2, H=384, I=384)
+MIXED_FP8 = wl.LayerSpec(E=8, top_k=2, H=384, I=256, expert_dtype=wl.FP8)
+
+
+def _oracle_routing(olayer, x):
+    logits = oracle.router_logits(olayer, x)
+    ids, _ = oracle.select(logits, olayer.k)
+    return ids, oracle_weights_for(logits, ids)
+
+
+def _routing(kind, olayer, x):
+    T = x.shape[0]
+    if kind == "router":
+        return _oracle_routing(olayer, x)
+    rng = np.random.default_rng(T)
+    rw = rng.uniform(0.1, 1.0, size=(T, 2))
+    rw /= rw.sum(1, keepdims=True)
+    if kind == "collide":  # every token on experts 0 and 1: T routes each
+        return np.tile(np.array([[0, 1]], np.int32), (T, 1)), rw
+    # "edge": 16 tokens on {0, 1} (exactly the threshold), the rest on {2, 3}
+    ids = np.tile(np.array([[2, 3]], np.int32), (T, 1))
+    ids[:MFMA_MIN] = [0, 1]
+    return ids, rw
+
+
+@pytest.mark.parametrize("spec", [MIXED, MIXED_FP8], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("T,kind", [(16, "collide"), (31, "edge"), (45, "router"), (300, "router"),
+                                    (300, "collide")])
+def test_mfma_expert_fwd(spec, T, kind):
+    note("mfma expert_fwd %s T=%d %s" % (wl.DTYPE_NAMES[spec.expert_dtype], T, kind))
+    w, layer, olayer = make_device_layer(spec)
+    x = wl.make_x(T, spec.H, draw=T)
+    ids, rw = _routing(kind, olayer, x)
+    counts = np.bincount(ids.ravel(), minlength=spec.E)
+    big = counts >= MFMA_MIN
+    ref = oracle.expert_fwd(olayer, x, ids, rw)
+    got = gpu_expert_fwd(layer, x, ids, rw)
+    gemv = gpu_expert_fwd(layer, x, ids, rw, flags=moe.MOE_NO_MFMA)
+    err = max_rel(got, ref)
+    note("  max rel err %.3g (GEMV path %.3g), %d of %d experts on MFMA" %
+         (err, max_rel(gemv, ref), big.sum(), (counts > 0).sum()))
+    assert err <= NORTH_STAR_TOL
+    assert max_rel(gemv, ref) <= 1e-4
+    assert big.any()
+    assert not np.array_equal(got, gemv), "no segment took the MFMA path"
+    small_only = ~big[ids].any(axis=1)
+    assert np.array_equal(got[small_only], gemv[small_only])
+    # MFMA pass 1 feeding the per-route GEMV pass 2
+    p1 = gpu_expert_fwd(layer, x, ids, rw, flags=moe.MOE_WALK_DEDUP_PASS1)
+    assert max_rel(p1, ref) <= NORTH_STAR_TOL
+    assert np.array_equal(p1[small_only], gemv[small_only])
+    # the per-route walk never takes the MFMA path
+    pr = gpu_expert_fwd(layer, x, ids, rw, flags=moe.MOE_WALK_PER_ROUTE)
+    assert np.array_equal(pr, gemv)
+
+
+def test_mfma_deterministic_and_token_permutation():
+    note("mfma determinism and token permutation")
+    w, layer, olayer = make_device_layer(MIXED)
+    T = 300
+    x = wl.make_x(T, MIXED.H, draw=5)
+    ids, rw = _oracle_routing(olayer, x)
+    a = gpu_expert_fwd(layer, x, ids, rw)
+    b = gpu_expert_fwd(layer, x, ids, rw)
+    assert np.array_equal(a, b)
+    perm = np.random.default_rng(1).permutation(T)
+    c = gpu_expert_fwd(layer, x[perm], ids[perm], rw[perm])
+    ref = oracle.expert_fwd(olayer, x, ids, rw)
+    assert max_rel(c[np.argsort(perm)], ref) <= NORTH_STAR_TOL
+
+
+def _fp8_codes_layer():
+    """Two fp8 experts, H = I = 128, whose gate rows carry every E4M3 code
+    once (expert e, gate row i: code 128*e + i in column 0, zeros elsewhere;
+    the two NaN codes replaced by 0); up rows are 1.0, down is the identity,
+    scales 1 except the gate blocks (0.5).  For a one-hot x = e_0 the output
+    is out[h] = silu(0.5 * value(code 128e + h))."""
+    E, H, I = 2, 128, 128
+    one = wl.e4m3_encode(1.0)
+    gu = np.zeros((E, 2 * I, H), np.uint8)
+    for e in range(E):
+        for i in range(I):
+            c = 128 * e + i
+            gu[e, i, 0] = c if c not in (0x7F, 0xFF) else 0
+        gu[e, I:, :] = one
+    dn = np.zeros((E, H, I), np.uint8)
+    for e in range(E):
+        dn[e, np.arange(H), np.arange(I)] = one
+    s_gu = np.ones((E, 2, 1), np.float32)
+    s_gu[:, 0, 0] = 0.5
+    s_dn = np.ones((E, 1, 1), np.float32)
+    spec = wl.LayerSpec(E=E, top_k=1, H=H, I=I, expert_dtype=wl.FP8, router_dtype=wl.BF16)
+    return dict(spec=spec, w_router=np.zeros((E, H), np.uint16), w_gate_up=gu, w_down=dn, s_gate_up=s_gu,
+                s_down=s_dn)
+
+
+def test_mfma_fp8_every_code():
+    """Every E4M3 code through the MFMA decode: code * 0.5 is exact in bf16,
+    so the only rounding is that of the activation to bf16 before the down
+    projection (at most 2^-8 relative)."""
+    note("mfma fp8 all codes")
+    w = _fp8_codes_layer()
+    layer = moe.DeviceLayer(w, device=dev())
+    olayer = oracle.Layer(w)
+    T = 2 * MFMA_MIN
+    x = np.zeros((T, 128), np.float32)
+    x[:, 0] = 1.0
+    ids = np.repeat(np.array([[0], [1]], np.int32), MFMA_MIN, axis=0)
+    got = gpu_expert_fwd(layer, x, ids, np.ones((T, 1)))
+    ref = oracle.expert_fwd(olayer, x, ids, np.ones((T, 1)))
+    assert np.allclose(got, ref, rtol=2.0 ** -8 * 1.01, atol=1e-30)
+    gemv = gpu_expert_fwd(layer, x, ids, np.ones((T, 1)), flags=moe.MOE_NO_MFMA)
+    assert not np.array_equal(got, gemv)
+
+
+# ---------------------------------------------------------------------------
+# The large-batch regime at its full size: E=256, top_k=8, H=4096, I=1536,
+# Zipf(1.1)-skewed routing, bf16 and fp8 e4m3 with 128x128 block scales.
+# Every token's routing is checked; outputs on sampled tokens.
+
+def _sample(g, T, n_random=6):
+    """Random tokens plus the last route of the hottest expert (the ragged
+    end of its last token block) and a route of the coldest MFMA expert."""
+    rng = np.random.default_rng(T)
+    pick = set(rng.choice(T, size=min(n_random, T), replace=False).tolist())
+    counts, offsets, srt = g["counts"], g["offsets"], g["sorted_routes"]
+    k = g["ids"].shape[1]
+    hot = int(np.argmax(counts))
+    pick.add(int(srt[offsets[hot + 1] - 1]) // k)
+    mf = np.where(counts >= MFMA_MIN)[0]
+    if len(mf):
+        cold = int(mf[np.argmin(counts[mf])])
+        pick.add(int(srt[offsets[cold]]) // k)
+    return np.array(sorted(pick))
+
+
+def _large(spec):
+    bias = wl.zipf_bias(spec.E)
+    return make_device_layer(spec, bias)
+
+
+@pytest.fixture(scope="module")
+def large_bf16():
+    note("generating the E=256 H=4096 I=1536 bf16 layer")
+    yield _large(wl.LARGE)
+
+
+@pytest.fixture(scope="module")
+def large_fp8():
+    note("generating the E=256 H=4096 I=1536 fp8 layer")
+    yield _large(wl.LARGE_FP8)
+
+
+def _run_large(fixture, T):
+    w, layer, olayer = fixture
+    x = wl.make_x(T, layer.spec.H, draw=500 + T)
+    g0 = check_layer_sampled(layer, olayer, x, [0])[1]
+    sample = _sample(g0, T)
+    err, g = check_layer_sampled(layer, olayer, x, sample)
+    c = g["counts"]
+    note("  T=%d: %d unique, max count %d, %d experts on MFMA, sampled %d tokens, max rel err %.3g" %
+         (T, g["n_uniq"], c.max(), (c >= MFMA_MIN).sum(), len(sample), err))
+    assert (c >= MFMA_MIN).any()
+
+
+@pytest.mark.parametrize("T", [128, 512])
+def test_large_bf16_sampled(large_bf16, T):
+    note("large bf16 T=%d" % T)
+    _run_large(large_bf16, T)
+
+
+@pytest.mark.parametrize("T", [128, 512])
+def test_large_fp8_sampled(large_fp8, T):
+    note("large fp8 T=%d" % T)
+    _run_large(large_fp8, T)
