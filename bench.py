@@ -31,6 +31,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFS = 2500.0  # dense bf16
 
 
 def parse():
@@ -46,9 +47,11 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--workload", default="sweep", choices=["sweep", "stack"],
+    ap.add_argument("--workload", default="sweep", choices=["sweep", "stack", "large"],
                     help="sweep: one layer, uniform routing, batch sweep (headline); "
-                         "stack: 30-layer stack, one HIP graph vs a host-sync arm")
+                         "stack: 30-layer stack, one HIP graph vs a host-sync arm; "
+                         "large: E=256 H=4096 I=1536 Zipf layer at bs 128/256/512 with MFMA segments")
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp8"], help="expert weights (large workload)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a device-to-device copy of this many MiB, 3 times (reference for HBM counters)")
     return ap.parse_args()
@@ -68,6 +71,98 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n * 4, "repeats": 3}), flush=True)
 
 
+def stage_events(torch, n):
+    """n sets of MOE_N_STAGES + 1 timing events, each recorded once so that
+    its HIP handle exists."""
+    import mixture_experts_decode_gemv_amd as moe
+
+    sets = []
+    for _ in range(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(moe.MOE_N_STAGES + 1)]
+        for e in evs:
+            e.record()
+        sets.append(evs)
+    torch.cuda.synchronize()
+    return sets
+
+
+def time_layer(torch, moe, layers, xs, T, walk, steps, warmup, graph=True, stage_steps=None):
+    """Replay len(plan) layer steps (layer l, draw d) in a HIP graph; then the
+    same steps eagerly through moe_layer_fwd_events for per-stage times.
+    Returns a dict with ms/step, per-draw routing statistics and stage times."""
+    dev = xs[0].device
+    stream = torch.cuda.Stream(dev)
+    spec = layers[0].spec
+    G = max(len(layers), len(xs))
+    plan = [(s % len(layers), s % len(xs)) for s in range(G)]
+    ws = layers[0].workspace(T, stream)
+    out = torch.empty((T, spec.H), dtype=torch.float32, device=dev)
+
+    def step(i):
+        li, di = plan[i % G]
+        moe.moe_layer_fwd(layers[li].struct, xs[di], T, out, walk, ws, ws.numel(), stream)
+
+    # routing statistics of every planned step (read back outside the timed region)
+    uniq, counts = [], []
+    with torch.cuda.stream(stream):
+        for i in range(G):
+            step(i)
+            stream.synchronize()
+            uniq.append(int(ws[:4].view(torch.int32).item()))
+            off = moe.moe_layer_routing(layers[plan[i][0]].struct, T, ws, ws.numel())["counts"] - ws.data_ptr()
+            counts.append(ws[off:off + 4 * spec.E].view(torch.int32).cpu().numpy())
+    g = None
+    if graph:
+        with torch.cuda.stream(stream):
+            for i in range(3 * G):
+                step(i)
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(G):
+                step(i)
+        stream.synchronize()
+    reps = max(1, (steps + G - 1) // G)
+    wreps = max(1, (warmup + G - 1) // G)
+
+    def run(n):
+        for _ in range(n):
+            if g is not None:
+                g.replay()
+            else:
+                for i in range(G):
+                    step(i)
+
+    with torch.cuda.stream(stream):
+        run(wreps)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        run(reps)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * G)
+
+    # per-stage times: the same steps, eager, with events between the stages
+    ns = stage_steps or G
+    sets = stage_events(torch, ns)
+    with torch.cuda.stream(stream):
+        for i in range(G):
+            step(i)
+        for i in range(ns):
+            li, di = plan[i % G]
+            moe.moe_layer_fwd_events(layers[li].struct, xs[di], T, out, walk, ws, ws.numel(), stream,
+                                     [e.cuda_event for e in sets[i]])
+    torch.cuda.synchronize()
+    st = np.array([[sets[i][j].elapsed_time(sets[i][j + 1]) for j in range(moe.MOE_N_STAGES)] for i in range(ns)])
+    stage_ms = dict(zip(moe.STAGES, st.mean(axis=0).tolist()))
+    del g
+    # stage_steps: index into uniq/counts of each event-timed step
+    return dict(ms=ms, timed_steps=reps * G, uniq=uniq, counts=counts, plan=plan, stage_ms=stage_ms,
+                stage_steps=[i % G for i in range(ns)])
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -81,6 +176,9 @@ def main():
     if args.workload == "stack":
         bench_stack(args)
         return
+    if args.workload == "large":
+        bench_large(args)
+        return
 
     import torch
 
@@ -89,12 +187,12 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    stream = torch.cuda.Stream(dev)
     spec = wl.SWEEP
     walk = {"dedup": moe.MOE_WALK_DEDUP, "per_route": moe.MOE_WALK_PER_ROUTE,
             "dedup_pass1": moe.MOE_WALK_DEDUP_PASS1}[args.walk]
     bpw = 2  # bf16
     expert_bytes = 3 * spec.H * spec.I * bpw
+    gate_up_bytes = 2 * spec.H * spec.I * bpw
 
     t0 = time.time()
     layers = []
@@ -109,99 +207,32 @@ def main():
           flush=True)
 
     sizes = sorted(set([args.bs] + [int(s) for s in args.sweep.split(",") if s]))
-    maxT = max(sizes)
-    ws = layers[0].workspace(maxT)
-    out = torch.empty((maxT, spec.H), dtype=torch.float32, device=dev)
-    results = {}
-
+    results, head_run = {}, None
     for T in sizes:
         xs = [torch.from_numpy(wl.make_x(T, spec.H, draw=d)).to(dev) for d in range(args.draws)]
-        G = max(args.layers, args.draws)
-        plan = [(s % args.layers, s % args.draws) for s in range(G)]
-
-        def step(i, with_stats=False):
-            li, di = plan[i % G]
-            moe.moe_layer_fwd(layers[li].struct, xs[di], T, out, walk, ws, ws.numel(), stream)
-
-        # unique experts of every planned step (read back outside the timed region)
-        uniq = []
-        with torch.cuda.stream(stream):
-            for i in range(G):
-                step(i)
-                stream.synchronize()
-                uniq.append(int(ws[:4].view(torch.int32).item()))
-        mean_u = float(np.mean(uniq))
-
-        graph = None
-        if not args.no_graph:
-            with torch.cuda.stream(stream):
-                for i in range(3 * G):
-                    step(i)
-            stream.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph, stream=stream):
-                for i in range(G):
-                    step(i)
-            stream.synchronize()
-
-        reps = max(1, (args.steps + G - 1) // G)
-        nsteps = reps * G
-        wreps = max(1, (args.warmup + G - 1) // G)
-        with torch.cuda.stream(stream):
-            for _ in range(wreps):
-                if graph is not None:
-                    graph.replay()
-                else:
-                    for i in range(G):
-                        step(i)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            e0.record(stream)
-            for _ in range(reps):
-                if graph is not None:
-                    graph.replay()
-                else:
-                    for i in range(G):
-                        step(i)
-            e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / nsteps
+        run = time_layer(torch, moe, layers, xs, T, walk, args.steps, args.warmup, graph=not args.no_graph)
+        ms = run["ms"]
+        mean_u = float(np.mean(run["uniq"]))
         gbs = mean_u * expert_bytes / (ms * 1e-3) / 1e9
         results[T] = dict(bs=T, ms_per_step=ms, steps_per_s=1e3 / ms, unique_experts=mean_u,
                           reuse=T * spec.top_k / mean_u, unique_expert_MiB=mean_u * expert_bytes / 2 ** 20,
-                          hbm_GBps=gbs, hbm_frac=gbs / HBM_PEAK_GBS, timed_steps=nsteps)
-        print("[bench] bs=%d  %.1f us/step  %.0f steps/s  U=%.1f  %.0f GB/s (%.1f%% of 8 TB/s)"
-              % (T, ms * 1e3, 1e3 / ms, mean_u, gbs, 100 * gbs / HBM_PEAK_GBS), file=sys.stderr, flush=True)
-        del graph, xs
+                          hbm_GBps=gbs, hbm_frac=gbs / HBM_PEAK_GBS, timed_steps=run["timed_steps"],
+                          stage_us={k: v * 1e3 for k, v in run["stage_ms"].items()})
+        if T == args.bs:
+            head_run = run
+        print("[bench] bs=%d  %.1f us/step  %.0f steps/s  U=%.1f  %.0f GB/s (%.1f%% of 8 TB/s)  stages(us) %s"
+              % (T, ms * 1e3, 1e3 / ms, mean_u, gbs, 100 * gbs / HBM_PEAK_GBS,
+                 " ".join("%s=%.1f" % (k, v * 1e3) for k, v in run["stage_ms"].items())),
+              file=sys.stderr, flush=True)
+        del xs
 
-    # ---- expert phase of the headline batch, timed on its own ----------------
+    # roofline of the dominant kernel at the headline batch: pass 1 (grouped
+    # GEMV), algorithmic bytes = gate_up bytes of the unique experts
     T = args.bs
-    xs = [torch.from_numpy(wl.make_x(T, spec.H, draw=d)).to(dev) for d in range(args.draws)]
-    routed = []
-    for li in range(args.layers):
-        wsl = layers[li].workspace(T)
-        with torch.cuda.stream(stream):
-            moe.moe_layer_fwd(layers[li].struct, xs[li % args.draws], T, out, walk, wsl, wsl.numel(), stream)
-        stream.synchronize()
-        r = moe.moe_layer_routing(layers[li].struct, T, wsl, wsl.numel())
-        routed.append((li, li % args.draws, wsl, r, int(wsl[:4].view(torch.int32).item())))
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    with torch.cuda.stream(stream):
-        for i in range(args.warmup + args.steps):
-            li, di, wsl, r, u = routed[i % len(routed)]
-            if i >= args.warmup:
-                ev[i - args.warmup][0].record(stream)
-            moe.moe_expert_fwd(layers[li].struct, xs[di], T, r["topk_ids"], r["topk_w"], r["counts"],
-                               r["offsets"], r["sorted_routes"], r["uniq"], r["n_uniq"], out, walk, wsl,
-                               wsl.numel(), stream)
-            if i >= args.warmup:
-                ev[i - args.warmup][1].record(stream)
-    torch.cuda.synchronize()
-    exp_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    exp_bytes = float(np.mean([routed[(i + args.warmup) % len(routed)][4] for i in range(args.steps)])) * expert_bytes
-    exp_gbs = exp_bytes / (exp_ms * 1e-3) / 1e9
+    u_evt = float(np.mean([head_run["uniq"][i] for i in head_run["stage_steps"]]))
+    p1_ms = head_run["stage_ms"]["pass1_gemv"]
+    p1_bytes = u_evt * gate_up_bytes
+    p1_gbs = p1_bytes / (p1_ms * 1e-3) / 1e9
 
     # ---- CPU oracle on a bounded sample ------------------------------------------
     cpu = None
@@ -241,12 +272,121 @@ def main():
                    "draws": args.draws, "graph": not args.no_graph, "parallelism": "none (1 GPU)"},
         "hbm_GBps_unique_expert_bytes": head["hbm_GBps"],
         "sweep": [results[t] for t in sizes],
-        "roofline": {"bound": "hbm", "kernel": "expert phase (moe_expert_fwd: pass 1, pass 2, combine)",
-                     "achieved": exp_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": exp_gbs / HBM_PEAK_GBS,
-                     "traffic": None, "avg_launch_ms": exp_ms, "bytes_per_launch": exp_bytes},
+        "roofline": {"bound": "hbm", "kernel": "pass1_kernel (grouped GEMV, gate_up rows x routes)",
+                     "achieved": p1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": p1_gbs / HBM_PEAK_GBS,
+                     "traffic": None, "avg_launch_us": p1_ms * 1e3, "bytes_per_launch": p1_bytes,
+                     "bytes_rule": "unique experts x 2I x H x 2 B (gate_up, bf16)"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def bench_large(args):
+    """Large-batch regime: one layer E=256, top_k=8, H=4096, I=1536 with
+    Zipf(1.1)-skewed routing, bs 128/256/512, bf16 or fp8 e4m3 experts with
+    128x128 block scales.  Experts holding >= 16 routes run on MFMA."""
+    import torch
+
+    import mixture_experts_decode_gemv_amd as moe
+    import workload as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = wl.LARGE_FP8 if args.dtype == "fp8" else wl.LARGE
+    fp8 = spec.expert_dtype == wl.FP8
+    bpw = 1 if fp8 else 2
+    H, I = spec.H, spec.I
+    scale_bytes = (2 * I * H + H * I) // (128 * 128) * 4 if fp8 else 0
+    expert_bytes = 3 * H * I * bpw + scale_bytes
+    bias = wl.zipf_bias(spec.E)
+    t0 = time.time()
+    host = wl.make_layer(spec)
+    layer = moe.DeviceLayer(host, bias, device=dev)
+    print("[bench] large %s layer resident (%.1f s)" % (args.dtype, time.time() - t0), file=sys.stderr, flush=True)
+    sizes = [int(s) for s in args.sweep.split(",")] if args.sweep != "1,4,8,16,32,64" else list(wl.LARGE_BS)
+    bs_head = args.bs if args.bs in sizes else max(sizes)
+    rows = {}
+    for T in sizes:
+        xs = [torch.from_numpy(wl.make_x(T, H, draw=d)).to(dev) for d in range(args.draws)]
+        run = time_layer(torch, moe, [layer], xs, T, moe.MOE_WALK_DEDUP, args.steps, args.warmup,
+                         graph=not args.no_graph)
+        ms = run["ms"]
+        st = run["stage_ms"]
+        ev_idx = run["stage_steps"]
+        u = float(np.mean(run["uniq"]))
+        u_ev = float(np.mean([run["uniq"][i] for i in ev_idx]))
+        cs = [run["counts"][i] for i in ev_idx]
+        big = [c[c >= 16] for c in cs]
+        n_big = float(np.mean([len(b) for b in big]))
+        routes_big = float(np.mean([b.sum() for b in big]))
+        tiles_big = float(np.mean([(np.ceil(b / 16) * 16).sum() for b in big]))
+        flops_useful = 2 * routes_big * 3 * H * I
+        flops_issued = 2 * tiles_big * 3 * H * I
+        mfma_ms = st["pass1_mfma"] + st["pass2_mfma"]
+        mfma_tf = flops_useful / (mfma_ms * 1e-3) / 1e12 if mfma_ms > 0 else 0.0
+        p1m_bytes = n_big * 2 * I * H * bpw
+        p1m_gbs = p1m_bytes / (st["pass1_mfma"] * 1e-3) / 1e9 if st["pass1_mfma"] > 0 else 0.0
+        gbs = u * expert_bytes / (ms * 1e-3) / 1e9
+        rows[T] = dict(bs=T, ms_per_step=ms, steps_per_s=1e3 / ms, unique_experts=u, mfma_experts=n_big,
+                       mfma_route_frac=routes_big / (T * spec.top_k), hbm_GBps=gbs, hbm_frac=gbs / HBM_PEAK_GBS,
+                       stage_us={k: v * 1e3 for k, v in st.items()},
+                       mfma_TFLOPs_useful=mfma_tf, mfma_frac_of_peak=mfma_tf / MFMA_PEAK_TFS,
+                       mfma_issued_over_useful=flops_issued / max(flops_useful, 1.0),
+                       pass1_mfma_GBps=p1m_gbs, timed_steps=run["timed_steps"], unique_ev=u_ev)
+        print("[bench] large %s bs=%d  %.1f us/step  U=%.1f (MFMA %.1f, %.0f%% of routes)  %.0f GB/s (%.1f%%)  "
+              "MFMA %.0f TF/s useful  stages(us) %s" %
+              (args.dtype, T, ms * 1e3, u, n_big, 100 * routes_big / (T * spec.top_k), gbs,
+               100 * gbs / HBM_PEAK_GBS, mfma_tf, " ".join("%s=%.1f" % (k, v * 1e3) for k, v in st.items())),
+              file=sys.stderr, flush=True)
+        del xs
+    head = rows[bs_head]
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+
+        olayer = oracle.Layer(host, bias)
+        nthreads = max(1, min(os.cpu_count() or 1, 16))
+        x = wl.make_x(bs_head, H, draw=0)
+        done, t_start = 0, time.time()
+        while done < bs_head:
+            n = min(4, bs_head - done)
+            oracle.moe_layer(olayer, x[done:done + n], nthreads=nthreads)
+            done += n
+            if time.time() - t_start >= args.cpu_seconds:
+                break
+        el = time.time() - t_start
+        cpu = dict(value=(done / bs_head) / el, unit="steps/s", cores=nthreads, kind="oracle",
+                   sample="%d of the %d tokens of one bs=%d step (whole layer per token, fp64), %.1f s, scaled "
+                          "to a step" % (done, bs_head, bs_head, el))
+    st = head["stage_us"]
+    dom = max(st, key=st.get)
+    line = {
+        "metric": "MoE layer steps/s at bs=%d (Zipf(1.1) routing, E=256, top_k=8, H=4096, I=1536, %s); "
+                  "achieved HBM GB/s on unique-expert bytes; MFMA TFLOP/s" % (bs_head, spec_name(args.dtype)),
+        "value": head["steps_per_s"], "unit": "steps/s", "n_gpus": 1, "steps": head["timed_steps"],
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if not fp8 else "fp8_e4m3 weights, bf16 MFMA operands",
+        "data": "synthetic (seeded)",
+        "config": {"workload": "large-batch single MoE layer, Zipf(1.1) routing, E=256 top_k=8 H=4096 I=1536 "
+                               "%s experts, MFMA for experts with >= 16 routes" % spec_name(args.dtype),
+                   "bs": bs_head, "draws": args.draws, "graph": not args.no_graph},
+        "hbm_GBps_unique_expert_bytes": head["hbm_GBps"],
+        "sweep": [rows[t] for t in sizes],
+        "roofline": {"bound": "hbm", "kernel": "mfma_kernel pass 1" if dom == "pass1_mfma" else dom,
+                     "achieved": head["pass1_mfma_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": head["pass1_mfma_GBps"] / HBM_PEAK_GBS, "traffic": None,
+                     "avg_launch_us": st["pass1_mfma"],
+                     "bytes_rule": "MFMA experts x 2I x H x bytes per weight (gate_up)",
+                     "dominant_stage": dom},
+        "mfma": {"achieved": head["mfma_TFLOPs_useful"], "peak": MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                 "frac": head["mfma_frac_of_peak"], "rule": "2 x MFMA routes x 3HI over pass 1 + pass 2 MFMA time"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def spec_name(dtype):
+    return "fp8 e4m3 (128x128 block scales)" if dtype == "fp8" else "bf16"
 
 
 def host_topk(logits, k):

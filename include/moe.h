@@ -147,6 +147,20 @@ moe_status moe_expert_fwd(const moe_layer_t *layer, const float *x, int32_t T, c
 moe_status moe_layer_fwd(const moe_layer_t *layer, const float *x, int32_t T, float *out, uint32_t flags,
                          void *ws, size_t ws_bytes, void *stream);
 
+/* moe_layer_fwd with per-stage timing: events[s] (hipEvent_t, created by
+ * the caller with timing enabled) is recorded on `stream` before stage s and
+ * events[MOE_N_STAGES] after the last, for the stages
+ *   0 routing (RMSNorm, router, selection, sort), 1 pass 1 GEMV segments,
+ *   2 pass 1 MFMA segments, 3 pass 2 GEMV segments, 4 pass 2 MFMA segments,
+ *   5 combine.
+ * A stage that does not run for this call takes no time between its two
+ * events.  events == NULL behaves as moe_layer_fwd; a NULL entry is
+ * MOE_ERR_ARG.  For kernel timing in benchmarks; the extra event records
+ * make it unsuited to graph capture. */
+enum { MOE_N_STAGES = 6 };
+moe_status moe_layer_fwd_events(const moe_layer_t *layer, const float *x, int32_t T, float *out, uint32_t flags,
+                                void *ws, size_t ws_bytes, void *stream, void *const *events);
+
 /* Device addresses, inside a workspace that moe_layer_fwd used for T tokens,
  * of the routing that call computed (valid once the stream has reached it,
  * until the workspace is reused): topk_ids [T, k], topk_w [T, k],

@@ -7,7 +7,7 @@ missing or fails to load, importing the functions raises.
 
 Entry points (same names as ``include/moe.h``): ``moe_workspace_bytes``,
 ``moe_route``, ``moe_sort``, ``moe_expert_fwd``, ``moe_layer_fwd``,
-``moe_status_str``.  Tensor arguments may be torch tensors (their
+``moe_layer_fwd_events``, ``moe_layer_routing``, ``moe_status_str``.  Tensor arguments may be torch tensors (their
 ``data_ptr()`` is passed), raw integer device addresses or None (NULL).
 """
 from __future__ import annotations
@@ -28,7 +28,10 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE",
           5: "MOE_ERR_HIP", 6: "MOE_ERR_UNSUPPORTED", 7: "MOE_ERR_ALIGN"}
 
 EXPORTS = ("moe_workspace_bytes", "moe_workspace_init", "moe_route", "moe_sort", "moe_expert_fwd", "moe_layer_fwd",
-           "moe_layer_routing", "moe_status_str")
+           "moe_layer_fwd_events", "moe_layer_routing", "moe_status_str")
+
+MOE_N_STAGES = 6
+STAGES = ("routing", "pass1_gemv", "pass1_mfma", "pass2_gemv", "pass2_mfma", "combine")
 
 
 class MoeError(RuntimeError):
@@ -68,6 +71,8 @@ def lib():
         L.moe_expert_fwd.argtypes = [P, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, u32, vp, sz, vp]
         L.moe_layer_fwd.restype = ctypes.c_int
         L.moe_layer_fwd.argtypes = [P, vp, i32, vp, u32, vp, sz, vp]
+        L.moe_layer_fwd_events.restype = ctypes.c_int
+        L.moe_layer_fwd_events.argtypes = [P, vp, i32, vp, u32, vp, sz, vp, ctypes.POINTER(ctypes.c_void_p)]
         pp = ctypes.POINTER(ctypes.c_void_p)
         L.moe_layer_routing.restype = ctypes.c_int
         L.moe_layer_routing.argtypes = [P, i32, vp, sz, pp, pp, pp, pp, pp, pp, pp]
@@ -139,6 +144,17 @@ def moe_expert_fwd(layer, x, T, topk_ids, topk_w, counts, offsets, sorted_routes
 def moe_layer_fwd(layer, x, T, out, flags=0, ws=None, ws_bytes=0, stream=None):
     _check("moe_layer_fwd", lib().moe_layer_fwd(ctypes.byref(layer), _p(x), int(T), _p(out), int(flags), _p(ws),
                                                 int(ws_bytes), _s(stream)))
+
+
+def moe_layer_fwd_events(layer, x, T, out, flags=0, ws=None, ws_bytes=0, stream=None, events=None):
+    """``events``: MOE_N_STAGES + 1 raw hipEvent_t handles (ints), or None."""
+    arr = None
+    if events is not None:
+        if len(events) != MOE_N_STAGES + 1:
+            raise ValueError("moe_layer_fwd_events needs %d events" % (MOE_N_STAGES + 1))
+        arr = (ctypes.c_void_p * len(events))(*[int(e) for e in events])
+    _check("moe_layer_fwd_events", lib().moe_layer_fwd_events(ctypes.byref(layer), _p(x), int(T), _p(out),
+                                                              int(flags), _p(ws), int(ws_bytes), _s(stream), arr))
 
 
 ROUTING_FIELDS = ("topk_ids", "topk_w", "counts", "offsets", "sorted_routes", "uniq", "n_uniq")

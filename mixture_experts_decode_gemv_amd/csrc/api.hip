@@ -139,8 +139,8 @@ moe_status moe_expert_fwd(const moe_layer_t *layer, const float *x, int32_t T, c
                                      flags, (hipStream_t)stream));
 }
 
-moe_status moe_layer_fwd(const moe_layer_t *layer, const float *x, int32_t T, float *out, uint32_t flags, void *ws,
-                         size_t ws_bytes, void *stream) {
+static moe_status layer_fwd(const moe_layer_t *layer, const float *x, int32_t T, float *out, uint32_t flags,
+                            void *ws, size_t ws_bytes, void *stream, const hipEvent_t *ev) {
     moe_status s = check_layer(layer);
     if (s != MOE_OK) return s;
     if ((s = check_weights(layer, true, true)) != MOE_OK) return s;
@@ -155,19 +155,32 @@ moe_status moe_layer_fwd(const moe_layer_t *layer, const float *x, int32_t T, fl
     char *b = static_cast<char *>(ws);
     auto F = [&](size_t o) { return reinterpret_cast<float *>(b + o); };
     auto I32 = [&](size_t o) { return reinterpret_cast<int32_t *>(b + o); };
-    const int R = T * layer->top_k;
 
     const bool norm = (flags & MOE_RMSNORM_IN) != 0;
     const float *xin = norm ? F(wl.xn) : x;
+    if (ev && (s = hip_status(hipEventRecord(ev[0], st))) != MOE_OK) return s;
     if ((s = hip_status(launch_route(*layer, x, nullptr, T, norm ? F(wl.xn) : nullptr, F(wl.logits), I32(wl.ids),
                                      F(wl.w), I32(wl.counts), I32(wl.offsets), I32(wl.sorted), I32(wl.uniq),
                                      I32(wl.nuniq), I32(wl.stats), reinterpret_cast<unsigned *>(b + wl.arrive), norm,
                                      nullptr, 0, st))) != MOE_OK)
         return s;
-    (void)R;
+    if (ev && (s = hip_status(hipEventRecord(ev[1], st))) != MOE_OK) return s;
     Routing rt{I32(wl.ids), I32(wl.counts), I32(wl.offsets), I32(wl.sorted), I32(wl.uniq), I32(wl.nuniq), F(wl.w)};
     return hip_status(launch_experts(*layer, xin, (flags & MOE_ACCUM_RESIDUAL) ? x : nullptr, T, rt, F(wl.act),
-                                     F(wl.y), out, flags, st));
+                                     F(wl.y), out, flags, st, ev ? ev + 2 : nullptr));
+}
+
+moe_status moe_layer_fwd(const moe_layer_t *layer, const float *x, int32_t T, float *out, uint32_t flags, void *ws,
+                         size_t ws_bytes, void *stream) {
+    return layer_fwd(layer, x, T, out, flags, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_layer_fwd_events(const moe_layer_t *layer, const float *x, int32_t T, float *out, uint32_t flags,
+                                void *ws, size_t ws_bytes, void *stream, void *const *events) {
+    if (events)
+        for (int i = 0; i <= MOE_N_STAGES; ++i)
+            if (!events[i]) return MOE_ERR_ARG;
+    return layer_fwd(layer, x, T, out, flags, ws, ws_bytes, stream, reinterpret_cast<const hipEvent_t *>(events));
 }
 
 moe_status moe_layer_routing(const moe_layer_t *layer, int32_t T, void *ws, size_t ws_bytes, int32_t **topk_ids,

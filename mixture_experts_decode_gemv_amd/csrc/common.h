@@ -215,7 +215,11 @@ struct Routing {
     const int32_t *ids, *counts, *offsets, *sorted, *uniq, *n_uniq;
     const float *w;
 };
+// ev (optional): events recorded after pass 1 GEMV, pass 1 MFMA, pass 2 GEMV,
+// pass 2 MFMA and the combine (ev[0..4]); a stage that does not run records
+// its event right after the previous one.
 hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xres, int T, const Routing &rt,
-                          float *act, float *y, float *out, uint32_t flags, hipStream_t st);
+                          float *act, float *y, float *out, uint32_t flags, hipStream_t st,
+                          const hipEvent_t *ev = nullptr);
 
 }  // namespace moe

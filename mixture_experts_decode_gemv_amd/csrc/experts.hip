@@ -83,7 +83,8 @@ static hipError_t launch_mfma_pass(const moe_layer_t &L, int pass, int T, const 
 }
 
 hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xres, int T, const Routing &rt,
-                          float *act, float *y, float *out, uint32_t flags, hipStream_t st) {
+                          float *act, float *y, float *out, uint32_t flags, hipStream_t st, const hipEvent_t *ev) {
+    auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], st) : hipSuccess; };
     const int R = T * L.top_k;
     const int walk = (int)(flags & MOE_WALK_MASK);
     const int epc = elems_per_chunk(L.expert_dtype);
@@ -107,11 +108,12 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
         case MOE_BF16: err = launch_pass1<MOE_BF16>(nc1, persistent_grid(items1), st, p1); break;
         default: err = launch_pass1<MOE_FP8_E4M3>(nc1, persistent_grid(items1), st, p1); break;
     }
-    if (err != hipSuccess) return err;
+    if (err != hipSuccess || (err = mark(0)) != hipSuccess) return err;
     if (mfma) {
         MfmaArgs m1{L.w_gate_up, L.s_gate_up, x, act, L.H, L.I, L.top_k, kMfmaMinRoutes, grouped};
         if ((err = launch_mfma_pass(L, 1, T, m1, st)) != hipSuccess) return err;
     }
+    if ((err = mark(1)) != hipSuccess) return err;
 
     // pass 2: one wave item = slots x (64 / lanes) down rows of one segment
     const bool mfma2 = mfma && walk == MOE_WALK_DEDUP;
@@ -126,15 +128,17 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
         case MOE_BF16: err = launch_pass2<MOE_BF16>(nc2, lanes, persistent_grid(items2), st, p2); break;
         default: err = launch_pass2<MOE_FP8_E4M3>(nc2, lanes, persistent_grid(items2), st, p2); break;
     }
-    if (err != hipSuccess) return err;
+    if (err != hipSuccess || (err = mark(2)) != hipSuccess) return err;
     if (mfma2) {
         MfmaArgs m2{L.w_down, L.s_down, act, y, L.H, L.I, L.top_k, kMfmaMinRoutes, grouped};
         if ((err = launch_mfma_pass(L, 2, T, m2, st)) != hipSuccess) return err;
     }
+    if ((err = mark(3)) != hipSuccess) return err;
 
     hipLaunchKernelGGL(combine_kernel, dim3(T, (L.H / 4 + kBlock - 1) / kBlock), dim3(kBlock), 0, st, y, rt.w, xres,
                        out, L.top_k, L.H);
-    return hipGetLastError();
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    return mark(4);
 }
 
 }  // namespace moe
