@@ -47,8 +47,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--workload", default="sweep", choices=["sweep", "stack", "large"],
+    ap.add_argument("--no-mfma", action="store_true", help="keep every segment on the GEMV kernels")
+    ap.add_argument("--workload", default="sweep", choices=["sweep", "skewed", "stack", "large"],
                     help="sweep: one layer, uniform routing, batch sweep (headline); "
+                         "skewed: E=256 top_k=6 Zipf(1.1) routing, bs 1/8/32/64; "
                          "stack: 30-layer stack, one HIP graph vs a host-sync arm; "
                          "large: E=256 H=4096 I=1536 Zipf layer at bs 128/256/512 with MFMA segments")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp8"], help="expert weights (large workload)")
@@ -187,9 +189,13 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    spec = wl.SWEEP
+    skewed = args.workload == "skewed"
+    spec = wl.SKEWED if skewed else wl.SWEEP
+    bias = wl.zipf_bias(spec.E) if skewed else None
     walk = {"dedup": moe.MOE_WALK_DEDUP, "per_route": moe.MOE_WALK_PER_ROUTE,
             "dedup_pass1": moe.MOE_WALK_DEDUP_PASS1}[args.walk]
+    if args.no_mfma:
+        walk |= moe.MOE_NO_MFMA
     bpw = 2  # bf16
     expert_bytes = 3 * spec.H * spec.I * bpw
     gate_up_bytes = 2 * spec.H * spec.I * bpw
@@ -199,14 +205,17 @@ def main():
     host0 = None
     for l in range(args.layers):
         w = wl.make_layer(spec, layer=l)
-        layers.append(moe.DeviceLayer(w, device=dev))
+        layers.append(moe.DeviceLayer(w, bias, device=dev))
         if l == 0:
             host0 = w
         del w
     print("[bench] %d layers generated and resident (%.1f s)" % (args.layers, time.time() - t0), file=sys.stderr,
           flush=True)
 
-    sizes = sorted(set([args.bs] + [int(s) for s in args.sweep.split(",") if s]))
+    sweep = args.sweep
+    if skewed and sweep == "1,4,8,16,32,64":
+        sweep = ",".join(str(t) for t in wl.SKEWED_BS)
+    sizes = sorted(set([args.bs] + [int(s) for s in sweep.split(",") if s]))
     results, head_run = {}, None
     for T in sizes:
         xs = [torch.from_numpy(wl.make_x(T, spec.H, draw=d)).to(dev) for d in range(args.draws)]
@@ -229,9 +238,13 @@ def main():
     # roofline of the dominant kernel at the headline batch: pass 1 (grouped
     # GEMV), algorithmic bytes = gate_up bytes of the unique experts
     T = args.bs
-    u_evt = float(np.mean([head_run["uniq"][i] for i in head_run["stage_steps"]]))
+    # experts that the GEMV kernel streams: those below the MFMA threshold
+    # (all of them when the MFMA path is off or T < 16)
+    mfma_on = not args.no_mfma and T >= 16 and args.walk != "per_route"
+    u_gemv = [int((c > 0).sum() - ((c >= 16).sum() if mfma_on else 0)) for c in
+              (head_run["counts"][i] for i in head_run["stage_steps"])]
     p1_ms = head_run["stage_ms"]["pass1_gemv"]
-    p1_bytes = u_evt * gate_up_bytes
+    p1_bytes = float(np.mean(u_gemv)) * gate_up_bytes
     p1_gbs = p1_bytes / (p1_ms * 1e-3) / 1e9
 
     # ---- CPU oracle on a bounded sample ------------------------------------------
@@ -239,7 +252,7 @@ def main():
     if not args.no_cpu:
         import oracle
 
-        olayer = oracle.Layer(host0)
+        olayer = oracle.Layer(host0, bias)
         nthreads = max(1, min(os.cpu_count() or 1, 16))
         done, t_start = 0, time.time()
         while True:
@@ -249,13 +262,14 @@ def main():
                 break
         el = time.time() - t_start
         cpu = dict(value=done / el, unit="steps/s", cores=nthreads, kind="oracle",
-                   sample="%d whole layer steps at bs=%d (E=256, k=8, H=2048, I=768, bf16), fp64 accumulation, "
-                          "%.1f s" % (done, T, el))
+                   sample="%d whole layer steps at bs=%d (E=256, k=%d, H=2048, I=768, bf16%s), fp64 "
+                          "accumulation, %.1f s" % (done, T, spec.top_k, ", Zipf bias" if skewed else "", el))
 
     head = results[args.bs]
     line = {
-        "metric": "MoE layer steps/s at bs=%d (uniform routing, E=256, top_k=8, H=2048, I=768, bf16); "
-                  "achieved HBM GB/s on unique-expert bytes" % args.bs,
+        "metric": "MoE layer steps/s at bs=%d (%s routing, E=256, top_k=%d, H=2048, I=768, bf16); "
+                  "achieved HBM GB/s on unique-expert bytes" % (args.bs, "Zipf(1.1)" if skewed else "uniform",
+                                                              spec.top_k),
         "value": head["steps_per_s"],
         "unit": "steps/s",
         "n_gpus": 1,
@@ -267,15 +281,16 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0, 1/sqrt(fan_in)) weights, N(0,1) activations)",
-        "config": {"workload": "single MoE layer, uniform routing, E=256 top_k=8 H=2048 I=768 bf16 experts, "
-                               "batch sweep", "bs": args.bs, "walk": args.walk, "resident_layers": args.layers,
+        "config": {"workload": "single MoE layer, %s routing, E=256 top_k=%d H=2048 I=768 bf16 experts, batch "
+                               "sweep" % ("Zipf(1.1)" if skewed else "uniform", spec.top_k), "bs": args.bs,
+                   "walk": args.walk, "mfma": not args.no_mfma, "resident_layers": args.layers,
                    "draws": args.draws, "graph": not args.no_graph, "parallelism": "none (1 GPU)"},
         "hbm_GBps_unique_expert_bytes": head["hbm_GBps"],
         "sweep": [results[t] for t in sizes],
         "roofline": {"bound": "hbm", "kernel": "pass1_kernel (grouped GEMV, gate_up rows x routes)",
                      "achieved": p1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": p1_gbs / HBM_PEAK_GBS,
                      "traffic": None, "avg_launch_us": p1_ms * 1e3, "bytes_per_launch": p1_bytes,
-                     "bytes_rule": "unique experts x 2I x H x 2 B (gate_up, bf16)"},
+                     "bytes_rule": "unique experts on the GEMV path x 2I x H x 2 B (gate_up, bf16)"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

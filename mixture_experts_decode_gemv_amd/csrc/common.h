@@ -31,6 +31,13 @@ __host__ __device__ constexpr int bytes_per_elem(int dtype) {
     return dtype == MOE_F32 ? 4 : dtype == MOE_BF16 ? 2 : 1;
 }
 
+// Two fp32 -> packed bf16 pair (element 0 in the low half), round to nearest even.
+__device__ __forceinline__ uint32_t bf16_pair_rne(float lo, float hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 // bf16 halves of a packed 32-bit word (element 0 in the low half).
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
@@ -171,7 +178,7 @@ __host__ __device__ constexpr int rows_per_wave(int nc) { return nc <= 2 ? 8 : n
 int route_arrive_words(int T);
 
 struct WsLayout {
-    size_t stats, arrive, logits, ids, w, counts, offsets, sorted, uniq, nuniq, xn, act, y, total;
+    size_t stats, arrive, logits, ids, w, counts, offsets, sorted, uniq, nuniq, xn, xb, act, y, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -192,6 +199,7 @@ inline WsLayout ws_layout(const moe_layer_t &L, int64_t T) {
     s.uniq = take((size_t)L.E * 4);
     s.nuniq = take(4);
     s.xn = take((size_t)T * L.H * 4);
+    s.xb = take((size_t)T * L.H * 2);
     s.act = take((size_t)R * L.I * 4);
     s.y = take((size_t)R * L.H * 4);
     s.total = o;
@@ -218,8 +226,9 @@ struct Routing {
 // ev (optional): events recorded after pass 1 GEMV, pass 1 MFMA, pass 2 GEMV,
 // pass 2 MFMA and the combine (ev[0..4]); a stage that does not run records
 // its event right after the previous one.
+// xb: scratch for a bf16 copy of x [T, H] (used when segments take the MFMA path).
 hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xres, int T, const Routing &rt,
-                          float *act, float *y, float *out, uint32_t flags, hipStream_t st,
+                          void *xb, float *act, float *y, float *out, uint32_t flags, hipStream_t st,
                           const hipEvent_t *ev = nullptr);
 
 }  // namespace moe

@@ -83,7 +83,8 @@ static hipError_t launch_mfma_pass(const moe_layer_t &L, int pass, int T, const 
 }
 
 hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xres, int T, const Routing &rt,
-                          float *act, float *y, float *out, uint32_t flags, hipStream_t st, const hipEvent_t *ev) {
+                          void *xb, float *act, float *y, float *out, uint32_t flags, hipStream_t st,
+                          const hipEvent_t *ev) {
     auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], st) : hipSuccess; };
     const int R = T * L.top_k;
     const int walk = (int)(flags & MOE_WALK_MASK);
@@ -97,7 +98,8 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
     if (mfma) split.gemv_below = kMfmaMinRoutes;
 
     // pass 1: one wave item = P gate/up pairs of one segment
-    Pass1Args p1{L.w_gate_up, L.s_gate_up, x, act, L.H, L.I, L.top_k, walk == MOE_WALK_PER_ROUTE ? per_route : split};
+    Pass1Args p1{L.w_gate_up, L.s_gate_up, x, act, L.H, L.I, L.top_k, walk == MOE_WALK_PER_ROUTE ? per_route : split,
+                 mfma ? static_cast<uint32_t *>(xb) : nullptr};
     const int nq1 = L.H / epc;
     const int nc1 = nc_instance((nq1 + kWave - 1) / kWave);
     const int pairs = slots_for(nc1) / 2;
@@ -109,14 +111,14 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
         default: err = launch_pass1<MOE_FP8_E4M3>(nc1, persistent_grid(items1), st, p1); break;
     }
     if (err != hipSuccess || (err = mark(0)) != hipSuccess) return err;
+    const bool mfma2 = mfma && walk == MOE_WALK_DEDUP;
     if (mfma) {
-        MfmaArgs m1{L.w_gate_up, L.s_gate_up, x, act, L.H, L.I, L.top_k, kMfmaMinRoutes, grouped};
+        MfmaArgs m1{L.w_gate_up, L.s_gate_up, xb, act, L.H, L.I, L.top_k, kMfmaMinRoutes, mfma2 ? 1 : 0, grouped};
         if ((err = launch_mfma_pass(L, 1, T, m1, st)) != hipSuccess) return err;
     }
     if ((err = mark(1)) != hipSuccess) return err;
 
     // pass 2: one wave item = slots x (64 / lanes) down rows of one segment
-    const bool mfma2 = mfma && walk == MOE_WALK_DEDUP;
     Pass2Args p2{L.w_down, L.s_down, act, y, L.H, L.I, walk == MOE_WALK_DEDUP ? (mfma2 ? split : grouped) : per_route};
     const int nq2 = L.I / epc;
     const int lanes = pass2_lanes(nq2);
@@ -130,7 +132,7 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
     }
     if (err != hipSuccess || (err = mark(2)) != hipSuccess) return err;
     if (mfma2) {
-        MfmaArgs m2{L.w_down, L.s_down, act, y, L.H, L.I, L.top_k, kMfmaMinRoutes, grouped};
+        MfmaArgs m2{L.w_down, L.s_down, act, y, L.H, L.I, L.top_k, kMfmaMinRoutes, 0, grouped};
         if ((err = launch_mfma_pass(L, 2, T, m2, st)) != hipSuccess) return err;
     }
     if ((err = mark(3)) != hipSuccess) return err;

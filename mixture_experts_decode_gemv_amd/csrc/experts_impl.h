@@ -116,6 +116,7 @@ struct Pass1Args {
     float *act;
     int H, I, k;
     SegArgs sa;
+    uint32_t *xb;  // if set: bf16 copy of x [T, H] for the MFMA segments, written first
 };
 
 template <int WDT, int NC>
@@ -131,6 +132,14 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(Pass1Args a) {
     const int items_per_seg = (I + P - 1) / P;
     const int n_items = segment_count(a.sa) * items_per_seg;
     const size_t row_bytes = (size_t)H * WT<WDT>::kBytes;
+
+    if (a.xb) {  // the MFMA pass 1, launched after this kernel, reads x as bf16
+        const int npairs = a.sa.R / a.k * H / 2;
+        for (int i = blockIdx.x * kBlock + threadIdx.x; i < npairs; i += gridDim.x * kBlock) {
+            const float2 v = reinterpret_cast<const float2 *>(a.x)[i];
+            a.xb[i] = bf16_pair_rne(v.x, v.y);
+        }
+    }
 
     // The segment of the next item is fetched while the current one is
     // processed, so its index loads are off the critical path.
@@ -312,15 +321,16 @@ hipError_t launch_pass2(int nc, int lanes, int grid, hipStream_t st, const Pass2
 // Segments with at least kMfmaMinRoutes routes run on the matrix cores (see
 // experts_mfma.hip), in token blocks of kMfmaTokens routes.
 constexpr int kMfmaMinRoutes = 16;
-constexpr int kMfmaTokens = 128;
+constexpr int kMfmaTokens = 64;
 
 struct MfmaArgs {
     const void *w;        // pass 1: gate_up [E, 2I, H]; pass 2: down [E, H, I]
     const float *scales;  // fp8 block scales of w, else null
-    const float *src;     // pass 1: x [T, H]; pass 2: act [R, I]
+    const void *src;      // bf16 rows: pass 1 x [T, H]; pass 2 a[r] in the first half of fp32 row r of act
     float *dst;           // pass 1: act [R, I]; pass 2: y [R, H]
     int H, I, k;
     int min_n;            // segments with at least min_n routes
+    int act_bf16;         // pass 1: write a[r] as bf16 (for the MFMA pass 2) instead of fp32
     SegArgs sa;           // grouped segments
 };
 
