@@ -54,10 +54,9 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const float *__restrict
 }
 
 // ---- launchers -------------------------------------------------------------------
-static int persistent_grid(long long max_items_waves) {
+static int persistent_grid(long long max_items) {
     const long long cap = (long long)num_cus() * 8;
-    long long g = (max_items_waves + (kBlock / kWave) - 1) / (kBlock / kWave);
-    g = g < cap ? g : cap;
+    long long g = max_items < cap ? max_items : cap;
     return (int)(g < 1 ? 1 : g);
 }
 
@@ -99,10 +98,10 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
 
     // pass 1: one wave item = P gate/up pairs of one segment
     Pass1Args p1{L.w_gate_up, L.s_gate_up, x, act, L.H, L.I, L.top_k, walk == MOE_WALK_PER_ROUTE ? per_route : split,
-                 mfma ? static_cast<uint32_t *>(xb) : nullptr};
+                 mfma ? static_cast<uint32_t *>(xb) : nullptr, lds_batch_rows(L.H)};
     const int nq1 = L.H / epc;
     const int nc1 = nc_instance((nq1 + kWave - 1) / kWave);
-    const int pairs = slots_for(nc1) / 2;
+    const int pairs = slots_for(nc1) / 2 * (kBlock / kWave);  // per workgroup item
     const long long items1 = (long long)(p1.sa.grouped ? max_uniq : R) * ((L.I + pairs - 1) / pairs);
     hipError_t err;
     switch (L.expert_dtype) {
@@ -119,11 +118,12 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
     if ((err = mark(1)) != hipSuccess) return err;
 
     // pass 2: one wave item = slots x (64 / lanes) down rows of one segment
-    Pass2Args p2{L.w_down, L.s_down, act, y, L.H, L.I, walk == MOE_WALK_DEDUP ? (mfma2 ? split : grouped) : per_route};
+    Pass2Args p2{L.w_down, L.s_down, act, y, L.H, L.I, walk == MOE_WALK_DEDUP ? (mfma2 ? split : grouped) : per_route,
+                 lds_batch_rows(L.I)};
     const int nq2 = L.I / epc;
     const int lanes = pass2_lanes(nq2);
     const int nc2 = nc_instance((nq2 + lanes - 1) / lanes);
-    const int rows2 = slots_for(nc2) * (kWave / lanes);
+    const int rows2 = slots_for(nc2) * (kWave / lanes) * (kBlock / kWave);  // per workgroup item
     const long long items2 = (long long)(p2.sa.grouped ? max_uniq : R) * ((L.H + rows2 - 1) / rows2);
     switch (L.expert_dtype) {
         case MOE_F32: err = launch_pass2<MOE_F32>(nc2, lanes, persistent_grid(items2), st, p2); break;

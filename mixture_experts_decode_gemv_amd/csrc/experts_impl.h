@@ -24,14 +24,28 @@ struct SegArgs {
     int gemv_below;  // segments with this many routes or more are left to the MFMA kernels
 };
 
-// Expert, first sorted slot and route count of segment s.
+// A wave-uniform int32 read through the scalar cache (s_load_dword), waited
+// for on the LDS/scalar counter: it never waits behind the wave's
+// outstanding vector loads, as a vector load would (those complete in
+// order).  The routing arrays were written by an earlier launch.
+__device__ __forceinline__ int load_uniform(const int32_t *p) {
+    int v;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+    return v;
+}
+
+// Expert, first sorted slot and route count of segment s (s uniform).
 __device__ __forceinline__ void segment(const SegArgs &sa, int s, int &e, int &first, int &n) {
+    first = 0;
+    n = 0;
     if (sa.grouped) {
-        e = sa.uniq[s];
-        first = sa.offsets[e];
-        n = sa.counts[e];
+        e = load_uniform(sa.uniq + s);
+        if (e >= 0 && e < sa.E) {
+            first = load_uniform(sa.offsets + e);
+            n = load_uniform(sa.counts + e);
+        }
     } else {
-        e = sa.ids[s];
+        e = load_uniform(sa.ids + s);
         first = s;
         n = 1;
     }
@@ -44,6 +58,11 @@ __device__ __forceinline__ void segment(const SegArgs &sa, int s, int &e, int &f
 
 __device__ __forceinline__ int segment_route(const SegArgs &sa, int first, int i) {
     return sa.grouped ? sa.sorted[first + i] : first + i;
+}
+
+// The same for a wave-uniform i, through the scalar cache.
+__device__ __forceinline__ int segment_route_uniform(const SegArgs &sa, int first, int i) {
+    return sa.grouped ? load_uniform(sa.sorted + first + i) : first + i;
 }
 
 __device__ __forceinline__ int segment_count(const SegArgs &sa) {
@@ -67,14 +86,46 @@ __device__ __forceinline__ void load_rows(u32x4 (&w)[NS][NC], const char *const 
         }
 }
 
-// acc[s] = this lane's partial of slot s . xv, chunks in order; fp8 chunks
-// are scaled by their block scale.  The weights stay packed in registers
-// across the route loop: the empty asm makes them opaque on every call, so
-// the compiler cannot hoist their decode out of the loop (which would double
-// their register footprint and halve the waves in flight).
+// ---- activation rows in LDS ---------------------------------------------------
+// The four waves of a workgroup work on the same segment, so the activation
+// rows of its routes (x[t] in pass 1, a[r] in pass 2, fp32, K elements) are
+// staged once into LDS with direct global->LDS loads and read by every wave;
+// with the rows fetched by each wave itself, several routes per segment
+// carry more x than weight traffic through the CU's vector memory path and
+// the weight stream slows down.
+
+// Issue the loads of rows m = 0..mb-1 (global rows src(m) of q4 float4s)
+// into LDS rows of q4 float4s at xl; the caller waits (vmcnt(0)) and syncs.
+template <typename RowOf>
+__device__ __forceinline__ void stage_rows_lds(float4 *xl, int mb, int q4, RowOf row_of) {
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+    for (int m = 0; m < mb; ++m) {
+        const float4 *src = row_of(m);  // m is uniform: route lookups may shuffle
+        for (int u0 = wv * kWave; u0 < q4; u0 += kBlock)
+            if (u0 + lane < q4)
+                __builtin_amdgcn_global_load_lds(static_cast<const void *>(src + u0 + lane),
+                                                 (__attribute__((address_space(3))) void *)(xl + m * q4 + u0), 16, 0,
+                                                 0);
+    }
+}
+
+// Workgroup barrier after this wave's LDS reads have completed; unlike
+// __syncthreads it does not wait for outstanding global loads (the weights).
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Wait for this wave's loads (weights and staged rows), then for the
+// workgroup: the staged rows of every wave are in LDS after it.
+__device__ __forceinline__ void wait_loads_and_sync() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// acc[s] = this lane's partial of slot s . x, chunks in order, with x read
+// from an LDS row; fp8 chunks are scaled by their
+// block scale.  The weights stay packed in registers across the route loop:
+// the empty asm makes them opaque on every call, so the compiler cannot
+// hoist their decode out of the loop (which would double their register
+// footprint and halve the waves in flight).
 template <int WDT, int NC, int NS, int G>
-__device__ __forceinline__ void dot_rows(u32x4 (&w)[NS][NC], const float (&sc)[NS][NC],
-                                         const float *__restrict__ xv, int nq, int lane, float (&acc)[NS]) {
+__device__ __forceinline__ void dot_rows(u32x4 (&w)[NS][NC], const float (&sc)[NS][NC], const float4 *xl, int nq,
+                                         int lane, float (&acc)[NS]) {
     constexpr int EPC = WT<WDT>::kEpc;
     const int sub = lane & (G - 1);
 #pragma unroll
@@ -88,10 +139,9 @@ __device__ __forceinline__ void dot_rows(u32x4 (&w)[NS][NC], const float (&sc)[N
         const int q = sub + G * c;
         if (q < nq) {
             float xs[EPC];
-            const float4 *xp = reinterpret_cast<const float4 *>(xv + q * EPC);
 #pragma unroll
             for (int v = 0; v < EPC / 4; ++v) {
-                const float4 f = xp[v];
+                const float4 f = xl[q * (EPC / 4) + v];
                 xs[4 * v] = f.x; xs[4 * v + 1] = f.y; xs[4 * v + 2] = f.z; xs[4 * v + 3] = f.w;
             }
 #pragma unroll
@@ -103,12 +153,20 @@ __device__ __forceinline__ void dot_rows(u32x4 (&w)[NS][NC], const float (&sc)[N
     }
 }
 
-// Slots per wave for NC chunks per lane: about 64 VGPRs of weights.
-__host__ __device__ constexpr int slots_for(int nc) { return nc <= 2 ? 8 : nc <= 4 ? 4 : 2; }
+// Slots per wave for NC chunks per lane: 32 to 64 VGPRs of weights.
+__host__ __device__ constexpr int slots_for(int nc) { return nc <= 2 ? 8 : 4; }
+
+// Routes staged per LDS batch for rows of K floats: 32 KiB of LDS per
+// workgroup, at most 16 rows.
+inline int lds_batch_rows(int K) {
+    const int nb = (32 * 1024) / (K * 4);
+    return nb < 1 ? 1 : nb > 16 ? 16 : nb;
+}
 
 // ---- pass 1: gate/up row pairs and the activation ------------------------
 // G = 64; slots 2p and 2p+1 hold gate row i0+p and up row I+i0+p, so one
-// reduce_slots leaves a pair's two sums in the same lane group.
+// reduce_slots leaves a pair's two sums in the same lane group.  A
+// workgroup item is one segment and 4 * P consecutive pairs (P per wave).
 struct Pass1Args {
     const void *gate_up;
     const float *s_gate_up;
@@ -117,38 +175,43 @@ struct Pass1Args {
     int H, I, k;
     SegArgs sa;
     uint32_t *xb;  // if set: bf16 copy of x [T, H] for the MFMA segments, written first
+    int nb;        // routes per LDS batch
 };
 
 template <int WDT, int NC>
 __global__ __launch_bounds__(kBlock) void pass1_kernel(Pass1Args a) {
+    extern __shared__ float4 xl[];  // nb rows of H floats
     constexpr int G = kWave;
     constexpr int NS = slots_for(NC);
     constexpr int P = NS / 2;  // gate/up pairs per wave
     constexpr int EPC = WT<WDT>::kEpc;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int gwave = blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
-    const int nwaves = gridDim.x * (kBlock / kWave);
+    constexpr int WPB = kBlock / kWave;
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
     const int H = a.H, I = a.I, nq = H / EPC;
-    const int items_per_seg = (I + P - 1) / P;
+    const int items_per_seg = (I + P * WPB - 1) / (P * WPB);
     const int n_items = segment_count(a.sa) * items_per_seg;
     const size_t row_bytes = (size_t)H * WT<WDT>::kBytes;
 
     if (a.xb) {  // the MFMA pass 1, launched after this kernel, reads x as bf16
         const int npairs = a.sa.R / a.k * H / 2;
+        // stored as float-typed words: no store of this kernel may alias the
+        // int32 routing arrays, whose wave-uniform loads can then be scalar
+        float *xb = reinterpret_cast<float *>(a.xb);
         for (int i = blockIdx.x * kBlock + threadIdx.x; i < npairs; i += gridDim.x * kBlock) {
             const float2 v = reinterpret_cast<const float2 *>(a.x)[i];
-            a.xb[i] = bf16_pair_rne(v.x, v.y);
+            xb[i] = __uint_as_float(bf16_pair_rne(v.x, v.y));
         }
     }
 
-    // The segment of the next item is fetched while the current one is
-    // processed, so its index loads are off the critical path.
+    // Items are strided over the workgroups, so at any time the grid streams
+    // one narrow window of the weights.  The segment of the next item is
+    // fetched while the current one is processed.
     int e_nx = 0, first_nx = 0, n_nx = 0;
-    if (gwave < n_items) segment(a.sa, gwave / items_per_seg, e_nx, first_nx, n_nx);
-    for (int item = gwave; item < n_items; item += nwaves) {
+    if (blockIdx.x < n_items) segment(a.sa, blockIdx.x / items_per_seg, e_nx, first_nx, n_nx);
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
         const int blk = item % items_per_seg;
         const int e = e_nx, first = first_nx, n = n_nx;
-        const int i0 = blk * P;
+        const int i0 = (blk * WPB + wv) * P;
         const char *rows[NS];
         bool ok[NS];
         float sc[NS][NC];
@@ -180,24 +243,39 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(Pass1Args a) {
         }
         u32x4 w[NS][NC];
         load_rows<NC, NS, G>(w, rows, ok, nq, lane);
-        // the segment's routes, one per lane (first 64), loaded beside the weights
-        const int rl = lane < n ? segment_route(a.sa, first, lane) : 0;
-        if (item + nwaves < n_items) segment(a.sa, (item + nwaves) / items_per_seg, e_nx, first_nx, n_nx);
-        for (int m = 0; m < n; ++m) {
-            const int r = m < kWave ? __shfl(rl, m, kWave) : segment_route(a.sa, first, m);
-            float acc[NS];
-            dot_rows<WDT, NC, NS, G>(w, sc, a.x + (size_t)(r / a.k) * H, nq, lane, acc);
-            float gu[P][2];
+        if (item + gridDim.x < n_items) segment(a.sa, (item + gridDim.x) / items_per_seg, e_nx, first_nx, n_nx);
+        // one batch of routes: rows into LDS, then every route of the batch
+        // against the wave's rows.  The first batch (the whole segment when
+        // it fits) is peeled off the loop so the compiler's wait counts stay
+        // exact and the staging does not wait for the weights.
+        auto batch = [&](int m0, int mb) {
+            lds_sync();  // every wave is done reading the rows in LDS
+            // route ids are wave-uniform (scalar loads): the staging does not
+            // wait behind the weight loads
+            stage_rows_lds(xl, mb, H / 4, [&](int m) {
+                const int r = segment_route_uniform(a.sa, first, m0 + m);
+                return reinterpret_cast<const float4 *>(a.x + (size_t)(r / a.k) * H);
+            });
+            wait_loads_and_sync();
+            for (int m = 0; m < mb; ++m) {
+                const int r = segment_route_uniform(a.sa, first, m0 + m);
+                float acc[NS];
+                dot_rows<WDT, NC, NS, G>(w, sc, xl + (size_t)m * (H / 4), nq, lane, acc);
+                float gu[P][2];
 #pragma unroll
-            for (int p = 0; p < P; ++p) { gu[p][0] = acc[2 * p]; gu[p][1] = acc[2 * p + 1]; }
-            reduce_slots<P, 2, G>(gu, lane);
-            const int p = reduced_slot<P, G>(lane);
-            if (slot_leader<P, G>(lane) && i0 + p < I) a.act[(size_t)r * I + i0 + p] = silu(gu[0][0]) * gu[0][1];
-        }
+                for (int p = 0; p < P; ++p) { gu[p][0] = acc[2 * p]; gu[p][1] = acc[2 * p + 1]; }
+                reduce_slots<P, 2, G>(gu, lane);
+                const int p = reduced_slot<P, G>(lane);
+                if (slot_leader<P, G>(lane) && i0 + p < I) a.act[(size_t)r * I + i0 + p] = silu(gu[0][0]) * gu[0][1];
+            }
+        };
+        if (n > 0) batch(0, min(a.nb, n));
+        for (int m0 = a.nb; m0 < n; m0 += a.nb) batch(m0, min(a.nb, n - m0));
     }
 }
 
 // ---- pass 2: down rows -------------------------------------------------------
+// A workgroup item is one segment and 4 * NR consecutive down rows.
 struct Pass2Args {
     const void *down;
     const float *s_down;
@@ -205,28 +283,29 @@ struct Pass2Args {
     float *y;
     int H, I;
     SegArgs sa;
+    int nb;  // routes per LDS batch
 };
 
 template <int WDT, int NC, int G>
 __global__ __launch_bounds__(kBlock) void pass2_kernel(Pass2Args a) {
+    extern __shared__ float4 xl[];  // nb rows of I floats
     constexpr int NS = slots_for(NC);
     constexpr int RPS = kWave / G;  // rows per slot
     constexpr int NR = NS * RPS;    // rows per wave
     constexpr int EPC = WT<WDT>::kEpc;
-    const int lane = threadIdx.x & (kWave - 1), half = lane / G;
-    const int gwave = blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
-    const int nwaves = gridDim.x * (kBlock / kWave);
+    constexpr int WPB = kBlock / kWave;
+    const int lane = threadIdx.x & (kWave - 1), half = lane / G, wv = threadIdx.x / kWave;
     const int H = a.H, I = a.I, nq = I / EPC;
-    const int items_per_seg = (H + NR - 1) / NR;
+    const int items_per_seg = (H + NR * WPB - 1) / (NR * WPB);
     const int n_items = segment_count(a.sa) * items_per_seg;
     const size_t row_bytes = (size_t)I * WT<WDT>::kBytes;
 
     int e_nx = 0, first_nx = 0, n_nx = 0;
-    if (gwave < n_items) segment(a.sa, gwave / items_per_seg, e_nx, first_nx, n_nx);
-    for (int item = gwave; item < n_items; item += nwaves) {
+    if (blockIdx.x < n_items) segment(a.sa, blockIdx.x / items_per_seg, e_nx, first_nx, n_nx);
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
         const int blk = item % items_per_seg;
         const int e = e_nx, first = first_nx, n = n_nx;
-        const int h0 = blk * NR;
+        const int h0 = (blk * WPB + wv) * NR;
         // slot j, half hf: row h0 + j * RPS + hf
         const char *rows[NS];
         bool ok[NS];
@@ -253,20 +332,29 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Pass2Args a) {
         }
         u32x4 w[NS][NC];
         load_rows<NC, NS, G>(w, rows, ok, nq, lane);
-        const int rl = lane < n ? segment_route(a.sa, first, lane) : 0;
-        if (item + nwaves < n_items) segment(a.sa, (item + nwaves) / items_per_seg, e_nx, first_nx, n_nx);
-        for (int m = 0; m < n; ++m) {
-            const int r = m < kWave ? __shfl(rl, m, kWave) : segment_route(a.sa, first, m);
-            float acc[NS];
-            dot_rows<WDT, NC, NS, G>(w, sc, a.act + (size_t)r * I, nq, lane, acc);
-            float v[NS][1];
+        if (item + gridDim.x < n_items) segment(a.sa, (item + gridDim.x) / items_per_seg, e_nx, first_nx, n_nx);
+        auto batch = [&](int m0, int mb) {
+            lds_sync();  // every wave is done reading the rows in LDS
+            stage_rows_lds(xl, mb, I / 4, [&](int m) {
+                const int r = segment_route_uniform(a.sa, first, m0 + m);
+                return reinterpret_cast<const float4 *>(a.act + (size_t)r * I);
+            });
+            wait_loads_and_sync();
+            for (int m = 0; m < mb; ++m) {
+                const int r = segment_route_uniform(a.sa, first, m0 + m);
+                float acc[NS];
+                dot_rows<WDT, NC, NS, G>(w, sc, xl + (size_t)m * (I / 4), nq, lane, acc);
+                float v[NS][1];
 #pragma unroll
-            for (int j = 0; j < NS; ++j) v[j][0] = acc[j];
-            reduce_slots<NS, 1, G>(v, lane);
-            const int j = reduced_slot<NS, G>(lane);
-            const int h = h0 + j * RPS + half;
-            if (slot_leader<NS, G>(lane) && h < H) a.y[(size_t)r * H + h] = v[0][0];
-        }
+                for (int j = 0; j < NS; ++j) v[j][0] = acc[j];
+                reduce_slots<NS, 1, G>(v, lane);
+                const int j = reduced_slot<NS, G>(lane);
+                const int h = h0 + j * RPS + half;
+                if (slot_leader<NS, G>(lane) && h < H) a.y[(size_t)r * H + h] = v[0][0];
+            }
+        };
+        if (n > 0) batch(0, min(a.nb, n));
+        for (int m0 = a.nb; m0 < n; m0 += a.nb) batch(m0, min(a.nb, n - m0));
     }
 }
 
@@ -280,20 +368,24 @@ inline int pass2_lanes(int nq) { return (nq % 64 != 0 && nq % 32 == 0) ? 32 : 64
 
 template <int WDT>
 hipError_t launch_pass1(int nc, int grid, hipStream_t st, const Pass1Args &a) {
+    const size_t lds = (size_t)a.nb * a.H * 4;
+#define MOE_P1(N) hipLaunchKernelGGL((pass1_kernel<WDT, N>), dim3(grid), dim3(kBlock), lds, st, a)
     switch (nc_instance(nc)) {
-        case 1: hipLaunchKernelGGL((pass1_kernel<WDT, 1>), dim3(grid), dim3(kBlock), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((pass1_kernel<WDT, 2>), dim3(grid), dim3(kBlock), 0, st, a); break;
-        case 3: hipLaunchKernelGGL((pass1_kernel<WDT, 3>), dim3(grid), dim3(kBlock), 0, st, a); break;
-        case 4: hipLaunchKernelGGL((pass1_kernel<WDT, 4>), dim3(grid), dim3(kBlock), 0, st, a); break;
-        case 8: hipLaunchKernelGGL((pass1_kernel<WDT, 8>), dim3(grid), dim3(kBlock), 0, st, a); break;
+        case 1: MOE_P1(1); break;
+        case 2: MOE_P1(2); break;
+        case 3: MOE_P1(3); break;
+        case 4: MOE_P1(4); break;
+        case 8: MOE_P1(8); break;
         default: return hipErrorInvalidValue;
     }
+#undef MOE_P1
     return hipGetLastError();
 }
 
 template <int WDT>
 hipError_t launch_pass2(int nc, int lanes, int grid, hipStream_t st, const Pass2Args &a) {
-#define MOE_P2(N, L) hipLaunchKernelGGL((pass2_kernel<WDT, N, L>), dim3(grid), dim3(kBlock), 0, st, a)
+    const size_t lds = (size_t)a.nb * a.I * 4;
+#define MOE_P2(N, L) hipLaunchKernelGGL((pass2_kernel<WDT, N, L>), dim3(grid), dim3(kBlock), lds, st, a)
     if (lanes == 32) {
         switch (nc_instance(nc)) {
             case 1: MOE_P2(1, 32); break;
