@@ -31,6 +31,26 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+
+# HBM traffic of pass1_kernel per launch at the headline configuration
+# (uniform routing, bs=64), from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+# scaled by a 1 GiB copy calibration: profiles/pass_kernels_uniform_bs64_hbm_counters.md.
+# Reported only while the kernel source is the one that was measured.
+PASS1_TRAFFIC_BS64 = {"read_bytes": 1.3999e9, "write_bytes": 1.835e6, "source": "3559e2db0f1734b5"}
+
+
+def pass1_source_fingerprint():
+    """Hash of the pass-1 GEMV kernel source: the grouped-GEMV section of
+    experts_impl.h (segments through pass 1) and the chunk dot products of
+    common.h."""
+    import hashlib
+
+    d = os.path.join(ROOT, "mixture_experts_decode_gemv_amd", "csrc")
+    impl = open(os.path.join(d, "experts_impl.h")).read()
+    common = open(os.path.join(d, "common.h")).read()
+    a = impl[impl.index("struct SegArgs"):impl.index("// ---- pass 2: down rows")]
+    b = common[common.index("// acc + sum_e w[e]"):common.index("// Sum over the 64 lanes")]
+    return hashlib.sha256((a + b).encode()).hexdigest()[:16]
 MFMA_PEAK_TFS = 2500.0  # dense bf16
 
 
@@ -247,6 +267,13 @@ def main():
     p1_bytes = float(np.mean(u_gemv)) * gate_up_bytes
     p1_gbs = p1_bytes / (p1_ms * 1e-3) / 1e9
 
+    # measured HBM bytes per pass-1 launch (headline configuration only, and
+    # only for the kernel source the counters were taken on)
+    traffic = None
+    if (not skewed and args.bs == 64 and args.walk == "dedup" and not args.no_mfma
+            and pass1_source_fingerprint() == PASS1_TRAFFIC_BS64["source"]):
+        traffic = PASS1_TRAFFIC_BS64["read_bytes"] + PASS1_TRAFFIC_BS64["write_bytes"]
+
     # ---- CPU oracle on a bounded sample ------------------------------------------
     cpu = None
     if not args.no_cpu:
@@ -289,7 +316,7 @@ def main():
         "sweep": [results[t] for t in sizes],
         "roofline": {"bound": "hbm", "kernel": "pass1_kernel (grouped GEMV, gate_up rows x routes)",
                      "achieved": p1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": p1_gbs / HBM_PEAK_GBS,
-                     "traffic": None, "avg_launch_us": p1_ms * 1e3, "bytes_per_launch": p1_bytes,
+                     "traffic": traffic, "avg_launch_us": p1_ms * 1e3, "bytes_per_launch": p1_bytes,
                      "bytes_rule": "unique experts on the GEMV path x 2I x H x 2 B (gate_up, bf16)"},
         "cpu_baseline": cpu,
     }

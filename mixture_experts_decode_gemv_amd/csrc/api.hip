@@ -133,7 +133,7 @@ moe_status moe_expert_fwd(const moe_layer_t *layer, const float *x, int32_t T, c
     if (!ws || ws_bytes < wl.total) return MOE_ERR_WORKSPACE;
     if (!aligned16(ws)) return MOE_ERR_ALIGN;
     char *b = static_cast<char *>(ws);
-    Routing rt{topk_ids, counts, offsets, sorted_routes, uniq, n_uniq, topk_w};
+    Routing rt{topk_ids, counts, offsets, sorted_routes, uniq, n_uniq, topk_w, nullptr};
     return hip_status(launch_experts(*layer, x, (flags & MOE_ACCUM_RESIDUAL) ? x : nullptr, T, rt, b + wl.xb,
                                      reinterpret_cast<float *>(b + wl.act), reinterpret_cast<float *>(b + wl.y), out,
                                      flags, (hipStream_t)stream));
@@ -165,7 +165,8 @@ static moe_status layer_fwd(const moe_layer_t *layer, const float *x, int32_t T,
                                      nullptr, 0, st))) != MOE_OK)
         return s;
     if (ev && (s = hip_status(hipEventRecord(ev[1], st))) != MOE_OK) return s;
-    Routing rt{I32(wl.ids), I32(wl.counts), I32(wl.offsets), I32(wl.sorted), I32(wl.uniq), I32(wl.nuniq), F(wl.w)};
+    Routing rt{I32(wl.ids),  I32(wl.counts), I32(wl.offsets), I32(wl.sorted),
+               I32(wl.uniq), I32(wl.nuniq),  F(wl.w),         I32(wl.stats) + 2};
     return hip_status(launch_experts(*layer, xin, (flags & MOE_ACCUM_RESIDUAL) ? x : nullptr, T, rt, b + wl.xb, F(wl.act),
                                      F(wl.y), out, flags, st, ev ? ev + 2 : nullptr));
 }

@@ -222,6 +222,7 @@ hipError_t launch_zero(unsigned *p, int n, hipStream_t st);
 struct Routing {
     const int32_t *ids, *counts, *offsets, *sorted, *uniq, *n_uniq;
     const float *w;
+    const int32_t *max_count;  // largest count of one expert (from the sort), or null
 };
 // ev (optional): events recorded after pass 1 GEMV, pass 1 MFMA, pass 2 GEMV,
 // pass 2 MFMA and the combine (ev[0..4]); a stage that does not run records

@@ -112,7 +112,8 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
     if (err != hipSuccess || (err = mark(0)) != hipSuccess) return err;
     const bool mfma2 = mfma && walk == MOE_WALK_DEDUP;
     if (mfma) {
-        MfmaArgs m1{L.w_gate_up, L.s_gate_up, xb, act, L.H, L.I, L.top_k, kMfmaMinRoutes, mfma2 ? 1 : 0, grouped};
+        MfmaArgs m1{L.w_gate_up, L.s_gate_up, xb, act, L.H, L.I, L.top_k, kMfmaMinRoutes, mfma2 ? 1 : 0, grouped,
+                    rt.max_count};
         if ((err = launch_mfma_pass(L, 1, T, m1, st)) != hipSuccess) return err;
     }
     if ((err = mark(1)) != hipSuccess) return err;
@@ -132,7 +133,7 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
     }
     if (err != hipSuccess || (err = mark(2)) != hipSuccess) return err;
     if (mfma2) {
-        MfmaArgs m2{L.w_down, L.s_down, act, y, L.H, L.I, L.top_k, kMfmaMinRoutes, 0, grouped};
+        MfmaArgs m2{L.w_down, L.s_down, act, y, L.H, L.I, L.top_k, kMfmaMinRoutes, 0, grouped, rt.max_count};
         if ((err = launch_mfma_pass(L, 2, T, m2, st)) != hipSuccess) return err;
     }
     if ((err = mark(3)) != hipSuccess) return err;

@@ -424,6 +424,7 @@ struct MfmaArgs {
     int min_n;            // segments with at least min_n routes
     int act_bf16;         // pass 1: write a[r] as bf16 (for the MFMA pass 2) instead of fp32
     SegArgs sa;           // grouped segments
+    const int32_t *max_count;  // if set: largest segment; below min_n the launch has no work
 };
 
 template <int WDT>

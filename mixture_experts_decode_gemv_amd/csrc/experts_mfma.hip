@@ -138,6 +138,9 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
     __shared__ int wsum[kBlock / kWave];
     __shared__ int rts[kTB];
 
+    // no expert reaches the threshold (known from the sort's statistics):
+    // nothing to do, without building the item table
+    if (a.max_count && load_uniform(a.max_count) < a.min_n) return;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
     const int K = PASS == 1 ? a.H : a.I;
     const int nst = K / kKS;
