@@ -402,6 +402,17 @@ def bench_large(args):
                           "to a step" % (done, bs_head, bs_head, el))
     st = head["stage_us"]
     dom = max(st, key=st.get)
+    # algorithmic bytes of each stage at the headline batch: weights of the
+    # experts it streams (GEMV: below 16 routes, MFMA: 16 or more)
+    n_gemv = head["unique_ev"] - head["mfma_experts"]
+    per_expert = {"pass1": 2 * I * H * bpw + (2 * I * H // (128 * 128) * 4 if fp8 else 0),
+                  "pass2": H * I * bpw + (H * I // (128 * 128) * 4 if fp8 else 0)}
+    stage_bytes = {"pass1_gemv": n_gemv * per_expert["pass1"], "pass1_mfma": head["mfma_experts"] * per_expert["pass1"],
+                   "pass2_gemv": n_gemv * per_expert["pass2"], "pass2_mfma": head["mfma_experts"] * per_expert["pass2"],
+                   "routing": spec.E * H * 2, "combine": 0}
+    dom_gbs = stage_bytes[dom] / (st[dom] * 1e-6) / 1e9 if st[dom] > 0 else 0.0
+    kernel_of = {"pass1_gemv": "pass1_kernel", "pass1_mfma": "mfma_kernel (pass 1)", "pass2_gemv": "pass2_kernel",
+                 "pass2_mfma": "mfma_kernel (pass 2)", "routing": "route_kernel", "combine": "combine_kernel"}
     line = {
         "metric": "MoE layer steps/s at bs=%d (Zipf(1.1) routing, E=256, top_k=8, H=4096, I=1536, %s); "
                   "achieved HBM GB/s on unique-expert bytes; MFMA TFLOP/s" % (bs_head, spec_name(args.dtype)),
@@ -414,12 +425,10 @@ def bench_large(args):
                    "bs": bs_head, "draws": args.draws, "graph": not args.no_graph},
         "hbm_GBps_unique_expert_bytes": head["hbm_GBps"],
         "sweep": [rows[t] for t in sizes],
-        "roofline": {"bound": "hbm", "kernel": "mfma_kernel pass 1" if dom == "pass1_mfma" else dom,
-                     "achieved": head["pass1_mfma_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": head["pass1_mfma_GBps"] / HBM_PEAK_GBS, "traffic": None,
-                     "avg_launch_us": st["pass1_mfma"],
-                     "bytes_rule": "MFMA experts x 2I x H x bytes per weight (gate_up)",
-                     "dominant_stage": dom},
+        "roofline": {"bound": "hbm", "kernel": kernel_of[dom], "stage": dom, "achieved": dom_gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dom_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "avg_launch_us": st[dom], "bytes_per_launch": stage_bytes[dom],
+                     "bytes_rule": "experts the stage streams x their weight bytes (GEMV: < 16 routes, MFMA: >= 16)"},
         "mfma": {"achieved": head["mfma_TFLOPs_useful"], "peak": MFMA_PEAK_TFS, "unit": "TFLOP/s",
                  "frac": head["mfma_frac_of_peak"], "rule": "2 x MFMA routes x 3HI over pass 1 + pass 2 MFMA time"},
         "cpu_baseline": cpu,

@@ -42,20 +42,11 @@ __device__ __forceinline__ uint32_t bf16_pair_rne(float lo, float hi) {
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
-// OCP E4M3 byte -> (its value) * 2^-8, exactly.  The sign, 4 exponent and 3
-// mantissa bits are placed in an fp16 (bias 15, 10 mantissa bits) as
-// S.0EEEE.MMM0000000: a normal code (1 + m/8) * 2^(e-7) becomes
-// (1 + m/8) * 2^(e-15) and a subnormal code m * 2^-9 becomes the fp16
-// subnormal m * 2^-17, both the code's value times 2^-8; the fp16 -> fp32
-// conversion is exact.  The 2^8 is folded into the block scale, so products
-// never approach the fp32 subnormal range.  The NaN code is never produced
-// by the encoder and decodes as 480 * 2^-8.
-constexpr float kE4m3Unscale = 256.0f;  // 2^8
-
-__device__ __forceinline__ float e4m3_scaled_down(uint32_t c) {
-    const unsigned short h = (unsigned short)(((c & 0x7Fu) << 7) | ((c & 0x80u) << 8));
-    return __half2float(__ushort_as_half(h));
-}
+// OCP E4M3 codes are converted by the hardware (v_cvt_pk_f32_fp8 reads the
+// OCP format on gfx950): two codes of a 16-bit half of a word to two exact
+// fp32 values, subnormals included (the NaN code is never produced by the
+// encoder).  Products with activations of ordinary magnitude stay far from
+// the fp32 subnormal range (the smallest code is 2^-9).
 
 // acc + sum_e w[e] * xs[e] over the elements of one 16-byte weight chunk,
 // in element order.
@@ -84,14 +75,19 @@ __device__ __forceinline__ float chunk_dot<MOE_BF16>(const u32x4 w, const float 
     return acc;
 }
 
-// fp8: the sum is (true value) * 2^-8; callers multiply by scale * 2^8.
+// fp8: the sum of code values times x; callers multiply by the block scale.
 template <>
 __device__ __forceinline__ float chunk_dot<MOE_FP8_E4M3>(const u32x4 w, const float *xs, float acc) {
     const uint32_t v[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc = fmaf(e4m3_scaled_down(v[q] >> (8 * b)), xs[4 * q + b], acc);
+    for (int q = 0; q < 4; ++q) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[q], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[q], true);
+        acc = fmaf(lo[0], xs[4 * q], acc);
+        acc = fmaf(lo[1], xs[4 * q + 1], acc);
+        acc = fmaf(hi[0], xs[4 * q + 2], acc);
+        acc = fmaf(hi[1], xs[4 * q + 3], acc);
+    }
     return acc;
 }
 

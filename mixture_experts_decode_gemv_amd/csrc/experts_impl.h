@@ -235,9 +235,9 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(Pass1Args a) {
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
                     const int hb = min((lane + G * c) * EPC / 128, nbh - 1);
-                    sc[2 * p][c] = a.s_gate_up[((size_t)e * (2 * I / 128) + i / 128) * nbh + hb] * kE4m3Unscale;
+                    sc[2 * p][c] = a.s_gate_up[((size_t)e * (2 * I / 128) + i / 128) * nbh + hb];
                     sc[2 * p + 1][c] =
-                        a.s_gate_up[((size_t)e * (2 * I / 128) + (I + i) / 128) * nbh + hb] * kE4m3Unscale;
+                        a.s_gate_up[((size_t)e * (2 * I / 128) + (I + i) / 128) * nbh + hb];
                 }
             }
         }
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Pass2Args a) {
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
                     const int ib = min(((lane & (G - 1)) + G * c) * EPC / 128, nbi - 1);
-                    sc[j][c] = a.s_down[((size_t)e * (H / 128) + h / 128) * nbi + ib] * kE4m3Unscale;
+                    sc[j][c] = a.s_down[((size_t)e * (H / 128) + h / 128) * nbi + ib];
                 }
             }
         }
