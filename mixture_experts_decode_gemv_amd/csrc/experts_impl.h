@@ -30,7 +30,7 @@ struct SegArgs {
 // order).  The routing arrays were written by an earlier launch.
 __device__ __forceinline__ int load_uniform(const int32_t *p) {
     int v;
-    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=&s"(v) : "s"(p) : "memory");
     return v;
 }
 

@@ -308,3 +308,20 @@ def test_out_may_alias_x():
     moe.moe_layer_fwd(layer.struct, xd, 4, xd, moe.MOE_ACCUM_RESIDUAL, ws, ws.numel(), torch.cuda.current_stream())
     torch.cuda.synchronize()
     assert np.array_equal(xd.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("flags", [0, moe.MOE_ACCUM_RESIDUAL])
+def test_token_output_independent_of_batch_bitwise(sweep_layer, flags):
+    """A token's expert rows and its combine do not depend on the rest of the
+    batch (segment sizes, grid sizes, persistent-loop strides), so the first
+    tokens of a 16-token batch come out bitwise as the same tokens alone."""
+    note("batch independence, flags=%d" % flags)
+    w, layer, olayer = sweep_layer
+    x = wl.make_x(16, wl.SWEEP.H, draw=11)
+    f = flags | moe.MOE_NO_MFMA
+    full = gpu_layer_fwd(layer, x, f)
+    for T in (1, 5, 15):
+        part = gpu_layer_fwd(layer, x[:T], f)
+        assert np.array_equal(part, full[:T]), T
+    again = gpu_layer_fwd(layer, x[:5], f)
+    assert np.array_equal(again, full[:5])
