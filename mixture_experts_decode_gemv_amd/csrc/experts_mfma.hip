@@ -53,8 +53,9 @@ constexpr int kTT = kTB / 16;                        // 16-token MFMA tiles per 
 constexpr int kKS = 128;                             // K per stage
 constexpr int kRowLds = kKS * 2 + 16;                // padded bf16 activation row (bytes)
 constexpr int kBufLds = kTB * kRowLds;               // one stage of activations
-constexpr int kThrPerRow = kBlock / kTB;             // threads staging one activation row
-constexpr int kXChunks = kKS * 2 / 16 / kThrPerRow;  // 16-byte chunks per thread per stage
+constexpr int kChunksPerRow = kKS * 2 / 16;           // 16-byte chunks of a staged row (16)
+constexpr int kRowsPerPass = kBlock / kChunksPerRow;  // rows staged per pass of the workgroup (16)
+constexpr int kXChunks = kTB / kRowsPerPass;          // rows (one chunk each) per thread per stage
 constexpr int kXcds = 8;
 // wave-private weight tile of one stage: 32 rows (two 16-row MFMA tiles)
 constexpr int kWRow = kKS * 2 + 16;  // bf16 row segment + pad (bytes); fp8 uses kKS + 16
@@ -202,26 +203,30 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
             sp0 = a.scales + ((size_t)e * (w_rows / 128) + r0 / 128) * kb;
             sp1 = a.scales + ((size_t)e * (w_rows / 128) + r1 / 128) * kb;
         }
-        // activation row this thread stages: token tid / kThrPerRow, chunks
-        // (tid % kThrPerRow) + kThrPerRow * j of the stage's 256 bytes
-        const int xtok = tid / kThrPerRow, xq = tid % kThrPerRow;
-        const bool xok = xtok < nv;
-        // rows past the block's routes load token 0's row (their LDS rows only
-        // feed output columns that are never stored), so every lane issues
-        // the same loads and the wait counts stay exact
-        const int xr = rts[xok ? xtok : 0];
-        const char *xsrc = static_cast<const char *>(a.src) + xq * 16 +
-                           (size_t)(PASS == 1 ? xr / a.k : xr) * src_stride;
-        unsigned char *xdst = xs + xtok * kRowLds + xq * 16;
+        // activation rows this thread stages: chunk tid % 16 of tokens
+        // tid / 16 + 16 j (16 lanes fill one 256-byte row segment: contiguous
+        // global reads and conflict-free LDS writes).  Rows past the block's
+        // routes load token 0's row (their LDS rows only feed output columns
+        // that are never stored), so every lane issues the same loads and the
+        // wait counts stay exact.
+        const int xq = tid % kChunksPerRow, xt0 = tid / kChunksPerRow;
+        const char *xsrc[kXChunks];
+#pragma unroll
+        for (int j = 0; j < kXChunks; ++j) {
+            const int tok = xt0 + kRowsPerPass * j;
+            const int xr = rts[tok < nv ? tok : 0];
+            xsrc[j] = static_cast<const char *>(a.src) + xq * 16 + (size_t)(PASS == 1 ? xr / a.k : xr) * src_stride;
+        }
+        unsigned char *xdst = xs + xt0 * kRowLds + xq * 16;
 
         auto load_x = [&](int ks, u32x4(&X)[kXChunks]) {
 #pragma unroll
-            for (int j = 0; j < kXChunks; ++j)
-                X[j] = *reinterpret_cast<const u32x4 *>(xsrc + ks * kKS * 2 + j * kThrPerRow * 16);
+            for (int j = 0; j < kXChunks; ++j) X[j] = *reinterpret_cast<const u32x4 *>(xsrc[j] + ks * kKS * 2);
         };
         auto store_x = [&](int buf, const u32x4(&X)[kXChunks]) {
 #pragma unroll
-            for (int j = 0; j < kXChunks; ++j) *reinterpret_cast<u32x4 *>(xdst + buf * kBufLds + j * kThrPerRow * 16) = X[j];
+            for (int j = 0; j < kXChunks; ++j)
+                *reinterpret_cast<u32x4 *>(xdst + buf * kBufLds + kRowsPerPass * j * kRowLds) = X[j];
         };
         auto load_w = [&](int ks, u32x4(&W)[2 * NWL], float(&S)[2]) {
             const size_t off = (size_t)ks * kKS * WT<WDT>::kBytes;
