@@ -65,18 +65,29 @@ static int persistent_grid(long long max_items) {
 // asked for the GEMV path only.  A segment cannot hold more routes than there
 // are tokens, so below kMfmaMinRoutes tokens no MFMA kernel is launched.
 static bool mfma_eligible(const moe_layer_t &L, int T, uint32_t flags) {
+    // the narrow kernels address activation rows with 32-bit byte offsets
+    const bool offsets32 = (unsigned long long)T * L.H * 2 < (1ull << 32) &&
+                           (unsigned long long)T * L.top_k * L.I * 4 < (1ull << 32);
     return (L.expert_dtype == MOE_BF16 || L.expert_dtype == MOE_FP8_E4M3) && L.H % 128 == 0 && L.I % 128 == 0 &&
-           !(flags & MOE_NO_MFMA) && T >= kMfmaMinRoutes && (int)(flags & MOE_WALK_MASK) != MOE_WALK_PER_ROUTE;
+           !(flags & MOE_NO_MFMA) && T >= kMfmaMinRoutes && (int)(flags & MOE_WALK_MASK) != MOE_WALK_PER_ROUTE &&
+           offsets32;
 }
 
+// Small batches have few hot experts: narrow items (32 weight rows) spread
+// them over the chip.  Large batches have many items anyway, and wide items
+// (128 weight rows) read each staged activation row for 4x more weights.
 static hipError_t launch_mfma_pass(const moe_layer_t &L, int pass, int T, const MfmaArgs &a, hipStream_t st) {
+    const bool wide = T >= kMfmaWideTokens;
     // items <= row blocks x (segments that can reach the threshold + extra token blocks)
     const long long R = (long long)T * L.top_k;
     const long long segs = std::min<long long>(L.E, R / kMfmaMinRoutes);
-    const long long n_rb = pass == 1 ? L.I / 64 : L.H / 128;
+    const long long n_rb = pass == 1 ? L.I / (wide ? 64 : 16) : L.H / (wide ? 128 : 32);
     const long long items = n_rb * (segs + R / kMfmaTokens);
     const long long cap = (long long)num_cus() * 2;
     const int grid = (int)std::max<long long>(1, std::min(items, cap));
+    if (wide)
+        return L.expert_dtype == MOE_BF16 ? launch_mfma_wide<MOE_BF16>(pass, grid, st, a)
+                                          : launch_mfma_wide<MOE_FP8_E4M3>(pass, grid, st, a);
     return L.expert_dtype == MOE_BF16 ? launch_mfma<MOE_BF16>(pass, grid, st, a)
                                       : launch_mfma<MOE_FP8_E4M3>(pass, grid, st, a);
 }

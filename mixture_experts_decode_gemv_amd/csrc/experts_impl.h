@@ -411,7 +411,8 @@ hipError_t launch_pass2(int nc, int lanes, int grid, hipStream_t st, const Pass2
 
 // ---- MFMA segments ------------------------------------------------------------
 // Segments with at least kMfmaMinRoutes routes run on the matrix cores (see
-// experts_mfma.hip), in token blocks of kMfmaTokens routes.
+// experts_mfma.hip and experts_mfma_wide.hip), in token blocks of
+// kMfmaTokens routes.
 constexpr int kMfmaMinRoutes = 16;
 constexpr int kMfmaTokens = 64;
 
@@ -427,10 +428,18 @@ struct MfmaArgs {
     const int32_t *max_count;  // if set: largest segment; below min_n the launch has no work
 };
 
+// Narrow tiles (experts_mfma.hip): 32 weight rows per item, the 4 waves
+// split K.  Wide tiles (experts_mfma_wide.hip): 128 weight rows per item,
+// for batches of at least kMfmaWideTokens tokens.
+constexpr int kMfmaWideTokens = 128;
 template <int WDT>
 hipError_t launch_mfma(int pass, int grid, hipStream_t st, const MfmaArgs &a);
 extern template hipError_t launch_mfma<MOE_BF16>(int, int, hipStream_t, const MfmaArgs &);
 extern template hipError_t launch_mfma<MOE_FP8_E4M3>(int, int, hipStream_t, const MfmaArgs &);
+template <int WDT>
+hipError_t launch_mfma_wide(int pass, int grid, hipStream_t st, const MfmaArgs &a);
+extern template hipError_t launch_mfma_wide<MOE_BF16>(int, int, hipStream_t, const MfmaArgs &);
+extern template hipError_t launch_mfma_wide<MOE_FP8_E4M3>(int, int, hipStream_t, const MfmaArgs &);
 
 // Defined in experts_<dtype>.hip.
 extern template hipError_t launch_pass1<MOE_F32>(int, int, hipStream_t, const Pass1Args &);

@@ -9,27 +9,29 @@
 // cpu-moe): dedup experts across the batch in pass 1", commit message: the
 // expert's routes are the inner loop over each weight row block).
 //
-// Work item = (segment, row block, token block of up to kMfmaTokens routes).
-// A workgroup of 4 waves owns 64 gate/up row pairs (pass 1) or 128 down rows
-// (pass 2); each wave holds two 16-row weight tiles:
-//   pass 1: gate rows i0..i0+15 and up rows I+i0..I+i0+15, so the MFMA
-//           outputs of a pair sit in the same lane and register and
+// Work item = (segment, row block of 32 weight rows, token block of up to
+// kMfmaTokens routes).  The 32 rows are two 16-row MFMA tiles:
+//   pass 1: gate rows i0..i0+15 and up rows I+i0..I+i0+15, so the outputs of
+//           a gate/up pair sit in the same lane and register and
 //           a[r, i] = silu(g) * u is formed in registers;
 //   pass 2: down rows h0..h0+31.
-// K runs in stages of 128.  The weights of a stage are loaded from HBM into
-// registers with each load instruction covering whole 256-byte (bf16) or
-// 128-byte (fp8) row segments of 4 or 8 rows: loads that give each lane 16
-// bytes of a different row, as the MFMA operand layout (lane l: row l % 16)
-// would, reach only about half the HBM bandwidth on gfx950.  The loads run
-// through a ring of three stages (stage s+2 is issued while stage s is
-// computed); each stage is written to a wave-private LDS tile and read back
-// in the operand layout.  The activation rows of the token block are bf16 in
-// memory (a copy of x made by the GEMV pass-1 kernel, and a[r] as written by
-// the pass-1 epilogue); each stage of them is loaded two stages ahead into
-// registers and written into a padded LDS tile shared by the 4 waves.  The k
-// order inside an MFMA operand only has to agree between the two operands,
-// so fp8 rows are loaded as 16 consecutive codes per lane and used for two
-// k-steps.
+// Small items keep every CU busy even when only a few experts are hot.
+//
+// K runs in stages of 128.  Each stage of the weight tile and of the bf16
+// activation rows of the token block is copied from memory straight into LDS
+// (global_load_lds_dwordx4: no register staging, so the depth of the
+// pipeline is set by LDS, not by VGPRs), through a ring of three stages with
+// stage s+2 in flight while stage s is computed.  A lane's 16-byte chunk is
+// stored at chunk position (chunk ^ row) of its LDS row: the copies stay
+// coalesced (a row's 16 chunks are still read by 16 adjacent lanes) and the
+// operand reads (16 rows, same chunk) hit 16 different bank groups.
+//
+// The four waves split every stage by k: wave w runs the MFMA k-step
+// 32w..32w+31 of each stage for both tiles and all token tiles, so all four
+// share one copy of the weights and of the activations.  At the end the four
+// partial sums are added through LDS in the fixed order w = 0, 1, 2, 3, so
+// the result of a (row, route) pair depends on nothing but its own operands:
+// not on the segment's size, the token block or the position in it.
 //
 // Items are numbered (segment, row block, token block) with the token block
 // fastest and dealt out in contiguous ranges per XCD (workgroup b runs on
@@ -48,18 +50,27 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 namespace {
 
-constexpr int kTB = kMfmaTokens;                     // routes per token block
-constexpr int kTT = kTB / 16;                        // 16-token MFMA tiles per block
-constexpr int kKS = 128;                             // K per stage
-constexpr int kRowLds = kKS * 2 + 16;                // padded bf16 activation row (bytes)
-constexpr int kBufLds = kTB * kRowLds;               // one stage of activations
-constexpr int kChunksPerRow = kKS * 2 / 16;           // 16-byte chunks of a staged row (16)
-constexpr int kRowsPerPass = kBlock / kChunksPerRow;  // rows staged per pass of the workgroup (16)
-constexpr int kXChunks = kTB / kRowsPerPass;          // rows (one chunk each) per thread per stage
+constexpr int kTB = kMfmaTokens;      // routes per token block (32 or 64)
+constexpr int kTT = kTB / 16;         // 16-token MFMA tiles per block
+constexpr int kKS = 128;              // K per stage
+constexpr int kWaves = kBlock / kWave;
+constexpr int kRing = 3;              // LDS stages
+constexpr int kXRowB = kKS * 2;       // bytes of a staged activation row (bf16)
+constexpr int kXBytes = kTB * kXRowB;  // activations of one stage (16 KiB)
 constexpr int kXcds = 8;
-// wave-private weight tile of one stage: 32 rows (two 16-row MFMA tiles)
-constexpr int kWRow = kKS * 2 + 16;  // bf16 row segment + pad (bytes); fp8 uses kKS + 16
-constexpr int kWTile = 32 * kWRow;
+static_assert(kTT <= kWaves, "one token tile per wave in the epilogue");
+
+template <int WDT>
+struct Stage {
+    static constexpr bool kFp8 = WDT == MOE_FP8_E4M3;
+    static constexpr int kRowB = kKS * (kFp8 ? 1 : 2);       // bytes of a weight row per stage
+    static constexpr int kChunks = kRowB / 16;                // 16-byte chunks per weight row
+    static constexpr int kWBytes = 32 * kRowB;                // weights of one stage
+    static constexpr int kWLoads = kWBytes / 1024 / kWaves;   // weight copies per wave per stage
+    static constexpr int kXLoads = kXBytes / 1024 / kWaves;   // activation copies per wave per stage
+    static constexpr int kLoads = kWLoads + kXLoads;          // copies per wave per stage
+    static constexpr int kBytes = kWBytes + kXBytes;
+};
 
 __device__ __forceinline__ f32x4_t mfma16(const u32x4 &a, const u32x4 &b, const f32x4_t &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
@@ -76,53 +87,109 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16(unsigned w0, unsigned w1, float 
                  bf16_pair_rne(c[0] * s, c[1] * s), bf16_pair_rne(d[0] * s, d[1] * s)};
 }
 
-// Workgroup barrier that waits for this wave's LDS traffic only: the global
-// loads of later stages stay in flight across it.
+// Copy of 16 bytes per lane from base + off (base wave-uniform, off this
+// lane's byte offset) into LDS at dst + 16 * lane (dst wave-uniform; M0
+// carries it and is restored afterwards).  Issued from asm: the compiler,
+// which tracks the LDS writes of its own copies, would wait for every copy in
+// flight (vmcnt(0)) before the next LDS read and so drain the ring at each
+// stage; the waits here are explicit (wait_copies_and_sync).  Its own waits
+// stay correct: copies issued after one of its loads only make a vmcnt wait
+// for that load stricter.
+__device__ __forceinline__ void copy_to_lds(const void *base, unsigned off, const unsigned char *dst) {
+    const unsigned l = __builtin_amdgcn_readfirstlane(
+        (unsigned)(size_t)(const __attribute__((address_space(3))) unsigned char *)dst);
+    unsigned saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off), "s"(base), "s"(l)
+        : "memory");
+}
+
+// A wave-uniform pointer (kept in scalar registers).
+template <typename P>
+__device__ __forceinline__ P *uniform_ptr(P *p) {
+    const unsigned long long v = (unsigned long long)p;
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+    return reinterpret_cast<P *>(((unsigned long long)hi << 32) | lo);
+}
+
+// Wait until at most N of this wave's global loads are outstanding and all
+// of its LDS operations are done, then meet the other waves.  The copies
+// complete in issue order, so N = the copies issued after the stage that is
+// needed.
+template <int N>
+__device__ __forceinline__ void wait_copies_and_sync() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier that waits for this wave's LDS traffic only.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Exclusive prefix over the unique segments of the items each one yields
-// (segments below min_n yield none); returns the total.  pre has nu + 1
-// entries.
-__device__ int build_item_table(const MfmaArgs &a, int nu, int n_rb, int *pre, int *wsum) {
-    const int tid = threadIdx.x;
+// Item and route tables over the experts, from the counts alone: pre[e] =
+// items of the experts below e (an expert with n >= min_n routes yields
+// n_rb x token blocks items, others none), pre[E] = total; off[e] = routes
+// of the experts below e, which is where the sorted routes of e start (the
+// counting sort lays the segments out in expert order).  Returns the total.
+__device__ int build_tables(const MfmaArgs &a, int n_rb, int *pre, int *off, int *wsum) {
+    const int tid = threadIdx.x, E = a.sa.E;
     constexpr int kPer = (kMaxE + kBlock - 1) / kBlock;
-    int c[kPer], loc = 0;
+    const int per = (E + kBlock - 1) / kBlock;  // experts per thread, contiguous
+    int it[kPer], ct[kPer], li = 0, lc = 0;
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
-        const int s = tid * kPer + q;
-        int items = 0;
-        if (s < nu) {
-            const int e = a.sa.uniq[s];
-            if (e >= 0 && e < a.sa.E) {
-                const int n = a.sa.counts[e];
-                if (n >= a.min_n) items = n_rb * ((n + kTB - 1) / kTB);
-            }
-        }
-        c[q] = items;
-        loc += items;
+        const int e = tid * per + q;
+        const int n = (q < per && e < E) ? a.sa.counts[e] : 0;
+        ct[q] = n;
+        it[q] = n >= a.min_n ? n_rb * ((n + kTB - 1) / kTB) : 0;
+        li += it[q];
+        lc += n;
     }
-    int v = loc;  // inclusive scan over the wave
+    int vi = li, vc = lc;  // inclusive scans over the wave
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
-        const int o = __shfl_up(v, d, kWave);
-        if ((tid & (kWave - 1)) >= d) v += o;
+        const int oi = __shfl_up(vi, d, kWave), oc = __shfl_up(vc, d, kWave);
+        if ((tid & (kWave - 1)) >= d) {
+            vi += oi;
+            vc += oc;
+        }
     }
-    if ((tid & (kWave - 1)) == kWave - 1) wsum[tid / kWave] = v;
+    if ((tid & (kWave - 1)) == kWave - 1) {
+        wsum[tid / kWave] = vi;
+        wsum[kWaves + tid / kWave] = vc;
+    }
     __syncthreads();
-    int base = 0, total = 0;
+    int bi = 0, bc = 0, total = 0, routes = 0;
 #pragma unroll
-    for (int w = 0; w < kBlock / kWave; ++w) {
-        base += w < tid / kWave ? wsum[w] : 0;
+    for (int w = 0; w < kWaves; ++w) {
+        if (w < tid / kWave) {
+            bi += wsum[w];
+            bc += wsum[kWaves + w];
+        }
         total += wsum[w];
+        routes += wsum[kWaves + w];
     }
-    int ex = base + v - loc;
+    int xi = bi + vi - li, xc = bc + vc - lc;
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
-        const int s = tid * kPer + q;
-        if (s < nu) pre[s] = ex;
-        ex += c[q];
+        const int e = tid * per + q;
+        if (q < per && e < E) {
+            pre[e] = xi;
+            off[e] = xc;
+        }
+        xi += it[q];
+        xc += ct[q];
     }
-    if (tid == 0) pre[nu] = total;
+    if (tid == 0) {
+        pre[E] = total;
+        off[E] = routes;
+    }
     __syncthreads();
     return total;
 }
@@ -131,203 +198,206 @@ __device__ int build_item_table(const MfmaArgs &a, int nu, int n_rb, int *pre, i
 
 template <int WDT, int PASS>
 __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
-    constexpr bool kFp8 = WDT == MOE_FP8_E4M3;
-    constexpr int NWL = kFp8 ? 2 : 4;  // 16-byte weight loads per tile per stage
-    __shared__ __align__(16) unsigned char xs[2 * kBufLds];
-    __shared__ __align__(16) unsigned char wls[kBlock / kWave][kWTile];
-    __shared__ int pre[kMaxE + 1];
-    __shared__ int wsum[kBlock / kWave];
-    __shared__ int rts[kTB];
+    using S = Stage<WDT>;
+    constexpr bool kFp8 = S::kFp8;
+    static_assert(kRing == 3, "the prologue below fills two stages");
+    __shared__ __align__(1024) unsigned char ring[kRing * S::kBytes];
+    __shared__ int wsum[2 * kWaves];
+    extern __shared__ int tables[];  // pre [E + 1], off [E + 1]
+    static_assert(kWaves * 2 * kTT * kWave * 16 <= kRing * S::kBytes, "partial sums fit in the ring");
 
-    // no expert reaches the threshold (known from the sort's statistics):
-    // nothing to do, without building the item table
+    // no expert reaches the threshold (known from the sort's statistics), or
+    // the routing was rejected: nothing to do
     if (a.max_count && load_uniform(a.max_count) < a.min_n) return;
+    if (segment_count(a.sa) == 0) return;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+    const int E = a.sa.E;
+    int *pre = tables, *off = tables + E + 1;
     const int K = PASS == 1 ? a.H : a.I;
     const int nst = K / kKS;
-    const int n_rb = PASS == 1 ? a.I / 64 : a.H / 128;
+    const int n_rb = PASS == 1 ? a.I / 16 : a.H / 32;
     const int w_rows = PASS == 1 ? 2 * a.I : a.H;
-    const size_t row_bytes = (size_t)K * WT<WDT>::kBytes;
+    const unsigned row_bytes = (unsigned)K * WT<WDT>::kBytes;
     // bf16 activation rows: pass 1 reads xb [T, H]; pass 2 reads a[r] from the
     // first half of the fp32 activation row r (4I bytes apart)
-    const size_t src_stride = PASS == 1 ? (size_t)a.H * 2 : (size_t)a.I * 4;
-    const int nu = min(segment_count(a.sa), a.sa.E);
-    const int total = build_item_table(a, nu, n_rb, pre, wsum);
+    const unsigned src_stride = PASS == 1 ? (unsigned)a.H * 2 : (unsigned)a.I * 4;
+    const int total = build_tables(a, n_rb, pre, off, wsum);
     // contiguous item ranges per XCD (the grid is a multiple of kXcds)
     const int per_xcd = (total + kXcds - 1) / kXcds;
     const int slots = per_xcd * kXcds;
+    const int m = lane & 15, g = lane >> 4;
 
     for (int it = blockIdx.x; it < slots; it += gridDim.x) {
         const int item = (it % kXcds) * per_xcd + it / kXcds;
         if (item >= total) continue;  // uniform over the workgroup
-        int lo = 0, hi = nu;          // pre[lo] <= item < pre[hi]
+        int lo = 0, hi = E;           // pre[lo] <= item < pre[hi]
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
             if (pre[mid] <= item) lo = mid;
             else hi = mid;
         }
-        const int local = item - pre[lo];
-        const int e = a.sa.uniq[lo];
-        const int first = a.sa.offsets[e], n = a.sa.counts[e];
+        const int e = __builtin_amdgcn_readfirstlane(lo);
+        const int local = item - pre[e];
+        const int first = off[e], n = off[e + 1] - first;
         const int ntb = (n + kTB - 1) / kTB;
         const int rb = local / ntb, tb = local - rb * ntb;
         const int nv = min(kTB, n - tb * kTB);
         const int ntt = (nv + 15) >> 4;
+        const int32_t *routes = a.sa.sorted + first + tb * kTB;
 
-        __syncthreads();  // the previous item is done with rts and the LDS tiles
-        if (tid < kTB) rts[tid] = tid < nv ? a.sa.sorted[first + tb * kTB + tid] : 0;
-        __syncthreads();
+        lds_barrier();  // the previous item is done with the ring
 
-        // the wave's two weight tiles: rows r0.. (tile 0) and r1.. (tile 1)
-        const int r0 = PASS == 1 ? rb * 64 + 16 * wv : rb * 128 + 32 * wv;
+        // weight rows of the item: row rho < 16 of tile 0, rho >= 16 of tile 1.
+        // This lane's weight copy c covers rows (64 / kChunks) apart; its chunk
+        // is the one that lands at its LDS position (position ^ row).
+        const int r0 = PASS == 1 ? rb * 16 : rb * 32;
         const int r1 = PASS == 1 ? a.I + r0 : r0 + 16;
-        const char *wbase = static_cast<const char *>(a.w) + (size_t)e * w_rows * row_bytes;
-        // load c covers rows RPL*(c % (16/RPL)) + lane / (64/RPL) of tile c / (16/RPL):
-        // bf16 4 rows x 256 B (16 lanes per row), fp8 8 rows x 128 B (8 lanes per row)
-        constexpr int LPR = kFp8 ? 8 : 16;     // lanes per row segment
-        constexpr int RPL = kWave / LPR;       // rows per load
-        constexpr int WROW = kFp8 ? kKS + 16 : kWRow;
-        const char *wsrc[NWL * 2];
-        int wdst[NWL * 2];
+        const char *wbase = uniform_ptr(static_cast<const char *>(a.w) + (size_t)e * w_rows * row_bytes);
+        unsigned woff[S::kWLoads];
 #pragma unroll
-        for (int c = 0; c < 2 * NWL; ++c) {
-            const int t = c / (16 / RPL);
-            const int rho = RPL * (c % (16 / RPL)) + lane / LPR;
-            wsrc[c] = wbase + (size_t)((t ? r1 : r0) + rho) * row_bytes + (lane % LPR) * 16;
-            wdst[c] = (t * 16 + rho) * WROW + (lane % LPR) * 16;
+        for (int c = 0; c < S::kWLoads; ++c) {
+            const int rho = (wv * S::kWLoads + c) * (kWave / S::kChunks) + lane / S::kChunks;
+            const int pos = lane % S::kChunks;
+            const int chunk = pos ^ (rho & (S::kChunks - 1));
+            woff[c] = (unsigned)(rho < 16 ? r0 + rho : r1 + rho - 16) * row_bytes + chunk * 16;
         }
-        unsigned char *wl = wls[wv];
-        const float *sp0 = nullptr, *sp1 = nullptr;
+        auto issue_w = [&](int ks, int sl) {
+            const unsigned char *wd = ring + sl * S::kBytes;
+#pragma unroll
+            for (int c = 0; c < S::kWLoads; ++c)
+                copy_to_lds(wbase + (size_t)ks * S::kRowB, woff[c], wd + (wv * S::kWLoads + c) * 1024);
+        };
+
+        // activation copy j covers tokens 4 apart; only the waves whose token
+        // tile holds routes copy.  Rows past the block's routes load the first
+        // route's row (their LDS rows only feed outputs that are never stored).
+        const bool xw = wv * kTB / (16 * kWaves) < ntt;
+        const char *xbase = uniform_ptr(static_cast<const char *>(a.src));
+        unsigned xoff[S::kXLoads];
+#pragma unroll
+        for (int j = 0; j < S::kXLoads; ++j) {
+            const int tau = (wv * S::kXLoads + j) * 4 + (lane >> 4);
+            const int r = routes[tau < nv ? tau : 0];
+            const int chunk = (lane & 15) ^ (tau & 15);
+            xoff[j] = (unsigned)(PASS == 1 ? r / a.k : r) * src_stride + chunk * 16;
+        }
+        auto issue_x = [&](int ks, int sl) {
+            const unsigned char *xd = ring + sl * S::kBytes + S::kWBytes;
+            if (xw)
+#pragma unroll
+                for (int j = 0; j < S::kXLoads; ++j)
+                    copy_to_lds(xbase + (size_t)ks * kXRowB, xoff[j], xd + (wv * S::kXLoads + j) * 1024);
+        };
+        // stages 0 and 1 in flight.  (Copying the weights ahead of the route
+        // reads would gain nothing: loads complete in issue order, so the wait
+        // for the route ids would wait for those copies as well.)
+        issue_w(0, 0);
+        issue_x(0, 0);
+        if (nst > 1) {
+            issue_w(1, 1);
+            issue_x(1, 1);
+        }
+
+        // fp8 block scales of the two tiles, stage ks in lane ks (K <= 64 * 128)
+        float sc0 = 1.f, sc1 = 1.f;
         if (kFp8) {
             const int kb = K / 128;
-            sp0 = a.scales + ((size_t)e * (w_rows / 128) + r0 / 128) * kb;
-            sp1 = a.scales + ((size_t)e * (w_rows / 128) + r1 / 128) * kb;
-        }
-        // activation rows this thread stages: chunk tid % 16 of tokens
-        // tid / 16 + 16 j (16 lanes fill one 256-byte row segment: contiguous
-        // global reads and conflict-free LDS writes).  Rows past the block's
-        // routes load token 0's row (their LDS rows only feed output columns
-        // that are never stored), so every lane issues the same loads and the
-        // wait counts stay exact.
-        const int xq = tid % kChunksPerRow, xt0 = tid / kChunksPerRow;
-        const char *xsrc[kXChunks];
-#pragma unroll
-        for (int j = 0; j < kXChunks; ++j) {
-            const int tok = xt0 + kRowsPerPass * j;
-            const int xr = rts[tok < nv ? tok : 0];
-            xsrc[j] = static_cast<const char *>(a.src) + xq * 16 + (size_t)(PASS == 1 ? xr / a.k : xr) * src_stride;
-        }
-        unsigned char *xdst = xs + xt0 * kRowLds + xq * 16;
-
-        auto load_x = [&](int ks, u32x4(&X)[kXChunks]) {
-#pragma unroll
-            for (int j = 0; j < kXChunks; ++j) X[j] = *reinterpret_cast<const u32x4 *>(xsrc[j] + ks * kKS * 2);
-        };
-        auto store_x = [&](int buf, const u32x4(&X)[kXChunks]) {
-#pragma unroll
-            for (int j = 0; j < kXChunks; ++j)
-                *reinterpret_cast<u32x4 *>(xdst + buf * kBufLds + kRowsPerPass * j * kRowLds) = X[j];
-        };
-        auto load_w = [&](int ks, u32x4(&W)[2 * NWL], float(&S)[2]) {
-            const size_t off = (size_t)ks * kKS * WT<WDT>::kBytes;
-#pragma unroll
-            for (int c = 0; c < 2 * NWL; ++c) W[c] = load_weight_chunk(reinterpret_cast<const u32x4 *>(wsrc[c] + off));
-            if (kFp8) {
-                S[0] = sp0[ks];
-                S[1] = sp1[ks];
+            const float *sp0 = a.scales + ((size_t)e * (w_rows / 128) + r0 / 128) * kb;
+            const float *sp1 = a.scales + ((size_t)e * (w_rows / 128) + r1 / 128) * kb;
+            if (lane < kb) {
+                sc0 = sp0[lane];
+                sc1 = sp1[lane];
             }
-        };
+        }
 
         f32x4_t acc0[kTT], acc1[kTT];
 #pragma unroll
         for (int tt = 0; tt < kTT; ++tt) acc0[tt] = acc1[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        // the stage's weights into the wave's LDS tile, then the MFMAs reading
-        // both operands from LDS (A: lane (m, g) row m, k-group g of the step)
-        auto compute = [&](int buf, const u32x4(&W)[2 * NWL], const float(&S)[2]) {
+        // k-step wv of stage ks from slot sl: A lane (m, g) holds row m of a
+        // tile at k 32 wv + 8 g .. +7, B lane (m, g) token m of a token tile.
+        // Every operand of the stage is read before the copies of a later
+        // stage are issued and before the first MFMA, so the LDS latency is
+        // paid once per stage; tiles past ntt read rows that feed no output.
+        const int aoff = kFp8 ? (((2 * wv + (g >> 1)) ^ (m & 7)) << 4) + ((g & 1) << 3) : ((4 * wv + g) ^ m) << 4;
+        const int boff = m * kXRowB + (((4 * wv + g) ^ m) << 4);
+        int sl = 0;
+        for (int ks = 0; ks < nst; ++ks) {
+            // copies issued after the stage that is needed: stage ks + 1's
+            if (ks + 1 >= nst) wait_copies_and_sync<0>();
+            else if (xw) wait_copies_and_sync<S::kLoads>();
+            else wait_copies_and_sync<S::kWLoads>();
+
+            const unsigned char *wd = ring + sl * S::kBytes;
+            const unsigned char *xd = wd + S::kWBytes;
+            u32x4 a0, a1, b[kTT];
+            uint2 c0, c1;
+            if (kFp8) {
+                c0 = *reinterpret_cast<const uint2 *>(wd + m * S::kRowB + aoff);
+                c1 = *reinterpret_cast<const uint2 *>(wd + (16 + m) * S::kRowB + aoff);
+            } else {
+                a0 = *reinterpret_cast<const u32x4 *>(wd + m * S::kRowB + aoff);
+                a1 = *reinterpret_cast<const u32x4 *>(wd + (16 + m) * S::kRowB + aoff);
+            }
 #pragma unroll
-            for (int c = 0; c < 2 * NWL; ++c) *reinterpret_cast<u32x4 *>(wl + wdst[c]) = W[c];
-            const unsigned char *xb = xs + buf * kBufLds + (lane & 15) * kRowLds;
-            const int g = lane >> 4;
-            const unsigned char *wa0 = wl + (lane & 15) * WROW;
-            const unsigned char *wa1 = wl + (16 + (lane & 15)) * WROW;
+            for (int tt = 0; tt < kTT; ++tt) b[tt] = *reinterpret_cast<const u32x4 *>(xd + tt * 16 * kXRowB + boff);
+
+            if (ks + kRing - 1 < nst) {
+                const int ns = sl == 0 ? kRing - 1 : sl - 1;
+                issue_w(ks + kRing - 1, ns);
+                issue_x(ks + kRing - 1, ns);
+            }
+            if (kFp8) {
+                a0 = e4m3x8_to_bf16(c0.x, c0.y, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc0), ks)));
+                a1 = e4m3x8_to_bf16(c1.x, c1.y, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc1), ks)));
+            }
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int koff = 32 * s + 8 * g;  // k of this lane's 8 elements within the stage
-                u32x4 a0, a1;
-                if (kFp8) {
-                    const uint2 c0 = *reinterpret_cast<const uint2 *>(wa0 + koff);
-                    const uint2 c1 = *reinterpret_cast<const uint2 *>(wa1 + koff);
-                    a0 = e4m3x8_to_bf16(c0.x, c0.y, S[0]);
-                    a1 = e4m3x8_to_bf16(c1.x, c1.y, S[1]);
-                } else {
-                    a0 = *reinterpret_cast<const u32x4 *>(wa0 + koff * 2);
-                    a1 = *reinterpret_cast<const u32x4 *>(wa1 + koff * 2);
-                }
-#pragma unroll
-                for (int tt = 0; tt < kTT; ++tt) {
-                    if (tt < ntt) {
-                        const u32x4 b = *reinterpret_cast<const u32x4 *>(xb + tt * 16 * kRowLds + koff * 2);
-                        acc0[tt] = mfma16(a0, b, acc0[tt]);
-                        acc1[tt] = mfma16(a1, b, acc1[tt]);
-                    }
+            for (int tt = 0; tt < kTT; ++tt) {
+                if (tt < ntt) {
+                    acc0[tt] = mfma16(a0, b[tt], acc0[tt]);
+                    acc1[tt] = mfma16(a1, b[tt], acc1[tt]);
                 }
             }
-        };
-
-        // ring of three stages: W/X/S index ks % 3
-        u32x4 W0[2 * NWL], W1[2 * NWL], W2[2 * NWL];
-        u32x4 X0[kXChunks], X1[kXChunks], X2[kXChunks];
-        float S0[2] = {1.f, 1.f}, S1[2] = {1.f, 1.f}, S2[2] = {1.f, 1.f};
-        // Every stage issues the same loads (stage indices past the end are
-        // clamped to the last stage) and the loop runs a multiple of 3 stages,
-        // so the compiler's wait counts see the same load sequence on every
-        // path and only wait for the stage being consumed.
-        load_x(0, X0);
-        load_w(0, W0, S0);
-        load_x(min(1, nst - 1), X1);
-        load_w(min(1, nst - 1), W1, S1);
-        store_x(0, X0);
-        // one stage: issue stage ks+2, compute stage ks, stage ks+1 into LDS
-        auto stage = [&](int ks, const u32x4(&Wc)[2 * NWL], const float(&Sc)[2], const u32x4(&Xn)[kXChunks],
-                         u32x4(&Wn2)[2 * NWL], float(&Sn2)[2], u32x4(&Xn2)[kXChunks]) {
-            const int kl = min(ks + 2, nst - 1);
-            load_x(kl, Xn2);
-            load_w(kl, Wn2, Sn2);
-            lds_barrier();
-            if (ks < nst) compute(ks & 1, Wc, Sc);
-            if (ks + 1 < nst) store_x((ks + 1) & 1, Xn);
-        };
-        for (int ks = 0; ks < nst; ks += 3) {
-            stage(ks, W0, S0, X1, W2, S2, X2);
-            stage(ks + 1, W1, S1, X2, W0, S0, X0);
-            stage(ks + 2, W2, S2, X0, W1, S1, X1);
+            sl = sl == kRing - 1 ? 0 : sl + 1;
         }
 
-        // epilogue: lane holds rows 4*(lane/16)+v of both tiles for token lane%16
+        // partial sums of the four waves, added in wave order
+        lds_barrier();  // every wave is done reading the ring
+        f32x4_t *red = reinterpret_cast<f32x4_t *>(ring);
 #pragma unroll
         for (int tt = 0; tt < kTT; ++tt) {
-            const int tok = tt * 16 + (lane & 15);
-            if (tt < ntt && tok < nv) {
-                const int r = rts[tok];
-                const int row = r0 + 4 * (lane >> 4);
-                if (PASS == 1) {
-                    float o[4];
+            if (tt < ntt) {
+                red[((wv * 2 + 0) * kTT + tt) * kWave + lane] = acc0[tt];
+                red[((wv * 2 + 1) * kTT + tt) * kWave + lane] = acc1[tt];
+            }
+        }
+        lds_barrier();
+        const int tt = wv;  // this wave's token tile in the epilogue (waves < kTT)
+        const int tok = tt * 16 + m;
+        if (tt < ntt && tok < nv) {
+            f32x4_t s0 = red[((0 * 2 + 0) * kTT + tt) * kWave + lane];
+            f32x4_t s1 = red[((0 * 2 + 1) * kTT + tt) * kWave + lane];
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) o[v] = silu(acc0[tt][v]) * acc1[tt][v];
-                    if (a.act_bf16) {  // bf16 into the first half of the fp32 row r
-                        *reinterpret_cast<uint2 *>(reinterpret_cast<char *>(a.dst) + (size_t)r * a.I * 4 + row * 2) =
-                            make_uint2(bf16_pair_rne(o[0], o[1]), bf16_pair_rne(o[2], o[3]));
-                    } else {
-                        *reinterpret_cast<float4 *>(a.dst + (size_t)r * a.I + row) =
-                            make_float4(o[0], o[1], o[2], o[3]);
-                    }
+            for (int w = 1; w < kWaves; ++w) {
+                s0 += red[((w * 2 + 0) * kTT + tt) * kWave + lane];
+                s1 += red[((w * 2 + 1) * kTT + tt) * kWave + lane];
+            }
+            const int r = routes[tok];
+            const int row = r0 + 4 * g;  // lane holds rows 4g .. 4g+3 of both tiles for token m
+            if (PASS == 1) {
+                float o[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) o[v] = silu(s0[v]) * s1[v];
+                if (a.act_bf16) {  // bf16 into the first half of the fp32 row r
+                    *reinterpret_cast<uint2 *>(reinterpret_cast<char *>(a.dst) + (size_t)r * a.I * 4 + row * 2) =
+                        make_uint2(bf16_pair_rne(o[0], o[1]), bf16_pair_rne(o[2], o[3]));
                 } else {
-                    *reinterpret_cast<float4 *>(a.dst + (size_t)r * a.H + row) =
-                        make_float4(acc0[tt][0], acc0[tt][1], acc0[tt][2], acc0[tt][3]);
-                    *reinterpret_cast<float4 *>(a.dst + (size_t)r * a.H + row + 16) =
-                        make_float4(acc1[tt][0], acc1[tt][1], acc1[tt][2], acc1[tt][3]);
+                    *reinterpret_cast<float4 *>(a.dst + (size_t)r * a.I + row) = make_float4(o[0], o[1], o[2], o[3]);
                 }
+            } else {
+                *reinterpret_cast<float4 *>(a.dst + (size_t)r * a.H + row) = make_float4(s0[0], s0[1], s0[2], s0[3]);
+                *reinterpret_cast<float4 *>(a.dst + (size_t)r * a.H + row + 16) =
+                    make_float4(s1[0], s1[1], s1[2], s1[3]);
             }
         }
     }
@@ -336,8 +406,9 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
 template <int WDT>
 hipError_t launch_mfma(int pass, int grid, hipStream_t st, const MfmaArgs &a) {
     grid = (grid + kXcds - 1) / kXcds * kXcds;
-    if (pass == 1) hipLaunchKernelGGL((mfma_kernel<WDT, 1>), dim3(grid), dim3(kBlock), 0, st, a);
-    else hipLaunchKernelGGL((mfma_kernel<WDT, 2>), dim3(grid), dim3(kBlock), 0, st, a);
+    const size_t lds = (size_t)2 * (a.sa.E + 1) * sizeof(int);
+    if (pass == 1) hipLaunchKernelGGL((mfma_kernel<WDT, 1>), dim3(grid), dim3(kBlock), lds, st, a);
+    else hipLaunchKernelGGL((mfma_kernel<WDT, 2>), dim3(grid), dim3(kBlock), lds, st, a);
     return hipGetLastError();
 }
 

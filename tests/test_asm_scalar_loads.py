@@ -34,7 +34,8 @@ def asm_blocks(text):
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
-@pytest.mark.parametrize("src", ["experts_bf16.hip", "experts_fp8.hip", "experts_f32.hip", "experts_mfma.hip"])
+@pytest.mark.parametrize("src", ["experts_bf16.hip", "experts_fp8.hip", "experts_f32.hip", "experts_mfma.hip",
+                                 "experts_mfma_wide.hip"])
 def test_scalar_load_blocks_do_not_alias(tmp_path, src):
     out = tmp_path / (src + ".s")
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
@@ -51,5 +52,5 @@ def test_scalar_load_blocks_do_not_alias(tmp_path, src):
         addrs = [{int(m.group(2)), int(m.group(3))} for m in loads]
         clash = [(a, b) for a in range(len(loads)) for b in range(len(loads)) if outs[a] in addrs[b]]
         assert not clash, "%s: load destination is another load's address: %s\n%s" % (src, clash, "\n".join(blk))
-    if src != "experts_mfma.hip":
+    if not src.startswith("experts_mfma"):
         assert n > 0

@@ -82,10 +82,10 @@ def test_mfma_expert_fwd(spec, T, kind):
     assert np.array_equal(pr, gemv)
 
 
-def test_mfma_deterministic_and_token_permutation():
-    note("mfma determinism and token permutation")
+@pytest.mark.parametrize("T", [64, 300], ids=["narrow", "wide"])
+def test_mfma_deterministic_and_token_permutation(T):
+    note("mfma determinism and token permutation, T=%d" % T)
     w, layer, olayer = make_device_layer(MIXED)
-    T = 300
     x = wl.make_x(T, MIXED.H, draw=5)
     ids, rw = _oracle_routing(olayer, x)
     a = gpu_expert_fwd(layer, x, ids, rw)
@@ -122,18 +122,18 @@ def _fp8_codes_layer():
                 s_down=s_dn)
 
 
-def test_mfma_fp8_every_code():
+@pytest.mark.parametrize("T", [2 * MFMA_MIN, 256], ids=["narrow", "wide"])
+def test_mfma_fp8_every_code(T):
     """Every E4M3 code through the MFMA decode: code * 0.5 is exact in bf16,
     so the only rounding is that of the activation to bf16 before the down
     projection (at most 2^-8 relative)."""
-    note("mfma fp8 all codes")
+    note("mfma fp8 all codes, T=%d" % T)
     w = _fp8_codes_layer()
     layer = moe.DeviceLayer(w, device=dev())
     olayer = oracle.Layer(w)
-    T = 2 * MFMA_MIN
     x = np.zeros((T, 128), np.float32)
     x[:, 0] = 1.0
-    ids = np.repeat(np.array([[0], [1]], np.int32), MFMA_MIN, axis=0)
+    ids = np.repeat(np.array([[0], [1]], np.int32), T // 2, axis=0)
     got = gpu_expert_fwd(layer, x, ids, np.ones((T, 1)))
     ref = oracle.expert_fwd(olayer, x, ids, np.ones((T, 1)))
     assert np.allclose(got, ref, rtol=2.0 ** -8 * 1.01, atol=1e-30)
