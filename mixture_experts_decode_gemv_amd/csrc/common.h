@@ -121,8 +121,14 @@ __device__ __forceinline__ void reduce_slots(float (&p)[NS][NW], int lane) {
         for (int i = 0; i < half; ++i)
 #pragma unroll
             for (int v = 0; v < NW; ++v) {
-                const float keep = upper ? p[half + i][v] : p[i][v];
-                const float give = upper ? p[i][v] : p[half + i][v];
+                // the empty asm makes lo and hi plain values: otherwise the
+                // selects below fold into a select of array addresses, which
+                // puts p in scratch memory (and its loads wait for every
+                // outstanding global load)
+                float lo = p[i][v], hi = p[half + i][v];
+                asm("" : "+v"(lo), "+v"(hi));
+                const float keep = upper ? hi : lo;
+                const float give = upper ? lo : hi;
                 p[i][v] = keep + __shfl_xor(give, mask, kWave);
             }
     }

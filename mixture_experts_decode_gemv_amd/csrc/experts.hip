@@ -25,10 +25,61 @@
 #include <limits.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "experts_impl.h"
 
 namespace moe {
+
+// ---- bf16 copy of the activations (MFMA pass 1 operand) ----------------------
+// Stored as float-typed words: no store of this kernel may alias the int32
+// routing arrays.
+__global__ __launch_bounds__(kBlock) void to_bf16_kernel(const float2 *__restrict__ x, float *__restrict__ xb,
+                                                         int npairs) {
+    for (int i = blockIdx.x * kBlock + threadIdx.x; i < npairs; i += gridDim.x * kBlock) {
+        const float2 v = x[i];
+        xb[i] = __uint_as_float(bf16_pair_rne(v.x, v.y));
+    }
+}
+
+// ---- second stream for the MFMA segments -------------------------------------
+// The GEMV segments and the MFMA segments of a pass read disjoint experts and
+// write disjoint routes, so for large batches the MFMA kernels run on a
+// second stream, forked from the caller's stream after routing and joined
+// before the combine; both halves then share the HBM bandwidth instead of
+// taking turns.  One stream and
+// two events per device, created on the first call made outside a graph
+// capture (until then the passes run in order on the caller's stream).  Calls
+// on one device share them: concurrent callers are serialised on the side
+// stream, which is still correct.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+
+static SideStream *side_stream(hipStream_t st) {
+    static std::mutex mu;
+    static SideStream sides[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    SideStream &sd = sides[dev];
+    if (sd.s) return &sd;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+    if (hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) != hipSuccess) {
+        sd.s = nullptr;
+        return nullptr;
+    }
+    if (hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) != hipSuccess) {
+        if (sd.fork) hipEventDestroy(sd.fork);
+        hipStreamDestroy(sd.s);
+        sd = SideStream{};
+        return nullptr;
+    }
+    return &sd;
+}
 
 // ---- combine ------------------------------------------------------------------
 // out may alias xres: each thread reads its residual before storing there.
@@ -95,64 +146,108 @@ static hipError_t launch_mfma_pass(const moe_layer_t &L, int pass, int T, const 
 hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xres, int T, const Routing &rt,
                           void *xb, float *act, float *y, float *out, uint32_t flags, hipStream_t st,
                           const hipEvent_t *ev) {
-    auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], st) : hipSuccess; };
     const int R = T * L.top_k;
     const int walk = (int)(flags & MOE_WALK_MASK);
     const int epc = elems_per_chunk(L.expert_dtype);
     const int max_uniq = R < L.E ? R : L.E;
     const bool mfma = mfma_eligible(L, T, flags);
+    const bool mfma2 = mfma && walk == MOE_WALK_DEDUP;
     SegArgs grouped{rt.ids, rt.counts, rt.offsets, rt.sorted, rt.uniq, rt.n_uniq, 1, R, L.E, INT_MAX};
     SegArgs per_route = grouped;
     per_route.grouped = 0;
     SegArgs split = grouped;  // the GEMV share of a pass that also has MFMA segments
     if (mfma) split.gemv_below = kMfmaMinRoutes;
 
-    // pass 1: one wave item = P gate/up pairs of one segment
-    Pass1Args p1{L.w_gate_up, L.s_gate_up, x, act, L.H, L.I, L.top_k, walk == MOE_WALK_PER_ROUTE ? per_route : split,
-                 mfma ? static_cast<uint32_t *>(xb) : nullptr, lds_batch_rows(L.H)};
-    const int nq1 = L.H / epc;
-    const int nc1 = nc_instance((nq1 + kWave - 1) / kWave);
-    const int pairs = slots_for(nc1) / 2 * (kBlock / kWave);  // per workgroup item
-    const long long items1 = (long long)(p1.sa.grouped ? max_uniq : R) * ((L.I + pairs - 1) / pairs);
-    hipError_t err;
-    switch (L.expert_dtype) {
-        case MOE_F32: err = launch_pass1<MOE_F32>(nc1, persistent_grid(items1), st, p1); break;
-        case MOE_BF16: err = launch_pass1<MOE_BF16>(nc1, persistent_grid(items1), st, p1); break;
-        default: err = launch_pass1<MOE_FP8_E4M3>(nc1, persistent_grid(items1), st, p1); break;
-    }
-    if (err != hipSuccess || (err = mark(0)) != hipSuccess) return err;
-    const bool mfma2 = mfma && walk == MOE_WALK_DEDUP;
-    if (mfma) {
+    // pass 1 on the GEMV kernel: one wave item = P gate/up pairs of one segment
+    auto gemv1 = [&](hipStream_t s) {
+        Pass1Args p1{L.w_gate_up, L.s_gate_up, x, act, L.H, L.I, L.top_k,
+                     walk == MOE_WALK_PER_ROUTE ? per_route : split, lds_batch_rows(L.H)};
+        const int nq1 = L.H / epc;
+        const int nc1 = nc_instance((nq1 + kWave - 1) / kWave);
+        const int pairs = slots_for(nc1) / 2 * (kBlock / kWave);  // per workgroup item
+        const long long items1 = (long long)(p1.sa.grouped ? max_uniq : R) * ((L.I + pairs - 1) / pairs);
+        switch (L.expert_dtype) {
+            case MOE_F32: return launch_pass1<MOE_F32>(nc1, persistent_grid(items1), s, p1);
+            case MOE_BF16: return launch_pass1<MOE_BF16>(nc1, persistent_grid(items1), s, p1);
+            default: return launch_pass1<MOE_FP8_E4M3>(nc1, persistent_grid(items1), s, p1);
+        }
+    };
+    // pass 1 of the MFMA segments, on a bf16 copy of x
+    auto mfma_1 = [&](hipStream_t s) {
+        const int npairs = T * L.H / 2;
+        const int g = std::max(1, std::min((npairs + kBlock - 1) / kBlock, num_cus() * 4));
+        hipLaunchKernelGGL(to_bf16_kernel, dim3(g), dim3(kBlock), 0, s, reinterpret_cast<const float2 *>(x),
+                           static_cast<float *>(xb), npairs);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
         MfmaArgs m1{L.w_gate_up, L.s_gate_up, xb, act, L.H, L.I, L.top_k, kMfmaMinRoutes, mfma2 ? 1 : 0, grouped,
                     rt.max_count};
-        if ((err = launch_mfma_pass(L, 1, T, m1, st)) != hipSuccess) return err;
-    }
-    if ((err = mark(1)) != hipSuccess) return err;
-
-    // pass 2: one wave item = slots x (64 / lanes) down rows of one segment
-    Pass2Args p2{L.w_down, L.s_down, act, y, L.H, L.I, walk == MOE_WALK_DEDUP ? (mfma2 ? split : grouped) : per_route,
-                 lds_batch_rows(L.I)};
-    const int nq2 = L.I / epc;
-    const int lanes = pass2_lanes(nq2);
-    const int nc2 = nc_instance((nq2 + lanes - 1) / lanes);
-    const int rows2 = slots_for(nc2) * (kWave / lanes) * (kBlock / kWave);  // per workgroup item
-    const long long items2 = (long long)(p2.sa.grouped ? max_uniq : R) * ((L.H + rows2 - 1) / rows2);
-    switch (L.expert_dtype) {
-        case MOE_F32: err = launch_pass2<MOE_F32>(nc2, lanes, persistent_grid(items2), st, p2); break;
-        case MOE_BF16: err = launch_pass2<MOE_BF16>(nc2, lanes, persistent_grid(items2), st, p2); break;
-        default: err = launch_pass2<MOE_FP8_E4M3>(nc2, lanes, persistent_grid(items2), st, p2); break;
-    }
-    if (err != hipSuccess || (err = mark(2)) != hipSuccess) return err;
-    if (mfma2) {
+        return launch_mfma_pass(L, 1, T, m1, s);
+    };
+    // pass 2 on the GEMV kernel: one wave item = slots x (64 / lanes) down rows of one segment
+    auto gemv2 = [&](hipStream_t s) {
+        Pass2Args p2{L.w_down, L.s_down, act, y, L.H, L.I,
+                     walk == MOE_WALK_DEDUP ? (mfma2 ? split : grouped) : per_route, lds_batch_rows(L.I)};
+        const int nq2 = L.I / epc;
+        const int lanes = pass2_lanes(nq2);
+        const int nc2 = nc_instance((nq2 + lanes - 1) / lanes);
+        const int rows2 = slots_for(nc2) * (kWave / lanes) * (kBlock / kWave);  // per workgroup item
+        const long long items2 = (long long)(p2.sa.grouped ? max_uniq : R) * ((L.H + rows2 - 1) / rows2);
+        switch (L.expert_dtype) {
+            case MOE_F32: return launch_pass2<MOE_F32>(nc2, lanes, persistent_grid(items2), s, p2);
+            case MOE_BF16: return launch_pass2<MOE_BF16>(nc2, lanes, persistent_grid(items2), s, p2);
+            default: return launch_pass2<MOE_FP8_E4M3>(nc2, lanes, persistent_grid(items2), s, p2);
+        }
+    };
+    auto mfma_2 = [&](hipStream_t s) {
         MfmaArgs m2{L.w_down, L.s_down, act, y, L.H, L.I, L.top_k, kMfmaMinRoutes, 0, grouped, rt.max_count};
-        if ((err = launch_mfma_pass(L, 2, T, m2, st)) != hipSuccess) return err;
-    }
-    if ((err = mark(3)) != hipSuccess) return err;
+        return launch_mfma_pass(L, 2, T, m2, s);
+    };
+    auto combine = [&]() {
+        hipLaunchKernelGGL(combine_kernel, dim3(T, (L.H / 4 + kBlock - 1) / kBlock), dim3(kBlock), 0, st, y, rt.w,
+                           xres, out, L.top_k, L.H);
+        return hipGetLastError();
+    };
+    hipError_t err;
+#define MOE_TRY(expr) \
+    if ((err = (expr)) != hipSuccess) return err
 
-    hipLaunchKernelGGL(combine_kernel, dim3(T, (L.H / 4 + kBlock - 1) / kBlock), dim3(kBlock), 0, st, y, rt.w, xres,
-                       out, L.top_k, L.H);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    // GEMV and MFMA segments side by side for large batches, which always
+    // have hot experts.  Below that the MFMA launches are often idle (they
+    // exit on the sort's maximum count), and an idle launch running beside
+    // the GEMV pass costs it more than it costs in order.  Not when the
+    // caller times the stages: then everything runs in order on its stream.
+    SideStream *sd = (mfma && !ev && T >= kMfmaWideTokens) ? side_stream(st) : nullptr;
+    if (sd) {
+        MOE_TRY(hipEventRecord(sd->fork, st));
+        MOE_TRY(hipStreamWaitEvent(sd->s, sd->fork, 0));
+        MOE_TRY(mfma_1(sd->s));
+        if (mfma2) MOE_TRY(mfma_2(sd->s));
+        MOE_TRY(gemv1(st));
+        // pass 2 of the DEDUP_PASS1 walk reads every segment's pass-1 rows
+        if (!mfma2) {
+            MOE_TRY(hipEventRecord(sd->join, sd->s));
+            MOE_TRY(hipStreamWaitEvent(st, sd->join, 0));
+        }
+        MOE_TRY(gemv2(st));
+        if (mfma2) {
+            MOE_TRY(hipEventRecord(sd->join, sd->s));
+            MOE_TRY(hipStreamWaitEvent(st, sd->join, 0));
+        }
+        return combine();
+    }
+    auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], st) : hipSuccess; };
+    MOE_TRY(gemv1(st));
+    MOE_TRY(mark(0));
+    if (mfma) MOE_TRY(mfma_1(st));
+    MOE_TRY(mark(1));
+    MOE_TRY(gemv2(st));
+    MOE_TRY(mark(2));
+    if (mfma2) MOE_TRY(mfma_2(st));
+    MOE_TRY(mark(3));
+    MOE_TRY(combine());
     return mark(4);
+#undef MOE_TRY
 }
 
 }  // namespace moe

@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kBlock) void route_kernel(RouteArgs a) {
                     ss = fmaf(v.z, v.z, ss);
                     ss = fmaf(v.w, v.w, ss);
                 }
-                ss = wave_sum(ss);
+                ss = wave_sum_dpp(ss);
                 const float rs = 1.0f / sqrtf(ss / (float)H + a.eps);
                 for (int q = lane; q < h4; q += kWave) {
                     float4 v = row[q];
@@ -150,14 +150,20 @@ __global__ __launch_bounds__(kBlock) void route_kernel(RouteArgs a) {
                     }
                 }
             }
-            reduce_slots<kRouteRows, 1, kWave>(acc0, lane);
-            reduce_slots<kRouteRows, 1, kWave>(acc1, lane);
-            const int r = reduced_slot<kRouteRows, kWave>(lane);
-            if (slot_leader<kRouteRows, kWave>(lane) && e0 + r < E) {
-                const float bias = a.bias ? a.bias[e0 + r] : 0.f;
-                store_shared(a.logits + (size_t)(t0 + t) * E + e0 + r, a.bias ? acc0[0][0] + bias : acc0[0][0]);
-                if (two)
-                    store_shared(a.logits + (size_t)(t0 + t + 1) * E + e0 + r, a.bias ? acc1[0][0] + bias : acc1[0][0]);
+            // one DPP sum over the wave per row and token; lane r stores row r
+            float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+            for (int r = 0; r < kRouteRows; ++r) {
+                const float s0 = wave_sum_dpp(acc0[r][0]), s1 = wave_sum_dpp(acc1[r][0]);
+                if (lane == r) {
+                    l0 = s0;
+                    l1 = s1;
+                }
+            }
+            if (lane < kRouteRows && e0 + lane < E) {
+                const float bias = a.bias ? a.bias[e0 + lane] : 0.f;
+                store_shared(a.logits + (size_t)(t0 + t) * E + e0 + lane, a.bias ? l0 + bias : l0);
+                if (two) store_shared(a.logits + (size_t)(t0 + t + 1) * E + e0 + lane, a.bias ? l1 + bias : l1);
             }
         }
         wait_vm_stores();
@@ -170,21 +176,25 @@ __global__ __launch_bounds__(kBlock) void route_kernel(RouteArgs a) {
         if (!s_last) return;
     }
 
-    // selection for the tile's tokens, one wave per token
+    // selection for the tile's tokens, one wave per token; with a single tile
+    // the ids also go to LDS, where the sort below reads them
     const float *lg = a.logits_in ? a.logits_in : a.logits;
+    int *lds_ids = a.counts && a.n_tblk == 1 ? reinterpret_cast<int *>(dyn_lds) + sort_lds_ints(E) : nullptr;
     for (int t = t0 + wave; t < t1; t += kBlock / kWave) {
+        int32_t *li = lds_ids ? lds_ids + (size_t)(t - t0) * a.k : nullptr;
         if (a.logits_in)
-            select_token<false>(lg + (size_t)t * E, E, a.k, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, lane);
+            select_token<false>(lg + (size_t)t * E, E, a.k, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, li, lane);
         else
-            select_token<true>(lg + (size_t)t * E, E, a.k, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, lane);
+            select_token<true>(lg + (size_t)t * E, E, a.k, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, li, lane);
     }
     if (!a.counts) return;
     if (a.n_tblk == 1) {
-        // one tile: this workgroup selected every token, no second arrival
-        wait_vm_stores();
+        // one tile: this workgroup selected every token, no second arrival;
+        // the sort reads the ids from LDS, so the global stores need not have
+        // completed
         __syncthreads();
-        sort_block<true>(a.ids, a.T * a.k, E, a.counts, a.offsets, a.sorted, a.uniq, a.n_uniq, a.stats,
-                          reinterpret_cast<int *>(dyn_lds), a.zero, a.n_zero);
+        sort_routes<false>(lds_ids, a.T * a.k, E, a.counts, a.offsets, a.sorted, a.uniq, a.n_uniq, a.stats,
+                           reinterpret_cast<int *>(dyn_lds), a.zero, a.n_zero);
         return;
     }
     wait_vm_stores();
@@ -195,8 +205,8 @@ __global__ __launch_bounds__(kBlock) void route_kernel(RouteArgs a) {
     }
     __syncthreads();
     if (!s_last) return;
-    sort_block<true>(a.ids, a.T * a.k, E, a.counts, a.offsets, a.sorted, a.uniq, a.n_uniq, a.stats,
-                     reinterpret_cast<int *>(dyn_lds), a.zero, a.n_zero);
+    sort_routes<true>(a.ids, a.T * a.k, E, a.counts, a.offsets, a.sorted, a.uniq, a.n_uniq, a.stats,
+                      reinterpret_cast<int *>(dyn_lds), a.zero, a.n_zero);
 }
 
 template <int RDT>
@@ -244,7 +254,8 @@ hipError_t launch_route(const moe_layer_t &L, const float *x, const float *logit
     a.tile = logits_in ? (kBlock / kWave) : route_tile_tokens(L.H);
     a.n_eblk = logits_in ? 1 : (L.E + kRouteExperts - 1) / kRouteExperts;
     a.n_tblk = (T + a.tile - 1) / a.tile;
-    size_t lds = (size_t)sort_lds_ints(L.E) * 4;
+    // the sort's LDS, then (single tile) the selected ids
+    size_t lds = ((size_t)sort_lds_ints(L.E) + (size_t)(logits_in ? kBlock / kWave : route_tile_tokens(L.H)) * L.top_k) * 4;
     if (!logits_in) {
         const size_t tb = (size_t)a.tile * L.H * 4;
         lds = tb > lds ? tb : lds;

@@ -14,11 +14,15 @@
 //
 // Sort ("perf(cpu-moe): dedup experts across the batch in pass 1", commit
 // message: a counting sort of the routes by expert id, built once per layer
-// and step).  Histogram with LDS integer atomics, exclusive scans for the
-// offsets and the unique-expert list, then a stable scatter in windows of 256
-// routes: each window sets one bit per route in a per-expert bitmask, and a
-// route's rank inside its expert is the expert's count in earlier windows
-// plus the bits below its own.
+// and step).  Up to kSortWaveRoutes routes, one wave sorts alone, with no
+// barrier (sort_wave): rounds of 64 routes in route order, each route's rank
+// among the equal ids of its round from ballots over the id bits, plus the
+// per-expert running count in LDS; then one scan over the experts.  Larger
+// sorts use the whole workgroup (sort_block): histogram with LDS integer
+// atomics, exclusive scans for the offsets and the unique-expert list, then a
+// stable scatter in windows of 256 routes: each window sets one bit per route
+// in a per-expert bitmask, and a route's rank inside its expert is the
+// expert's count in earlier windows plus the bits below its own.
 #pragma once
 
 #include "common.h"
@@ -68,21 +72,23 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 
 // One wave selects for one token.  l: the token's E logits (COHERENT: written
 // by other workgroups of this launch).  Writes ids[0..k) and w[0..k) with
-// device-scope stores.  Each lane sorts its own keys once (descending key,
-// ascending index); a round then takes the wave maximum of the lanes' heads,
+// device-scope stores, and the ids also to lds_ids[0..k) when it is set.
+// Each lane sorts its own keys once (descending key, ascending index); a
+// round then takes the wave maximum of the lanes' heads,
 // finds its lane by ballot, and only on an exact tie between lanes runs a
 // second reduction for the lowest index; the winning lane advances its head.
 template <bool COHERENT, int NCS>
-__device__ void select_token_n(const float *l, int E, int k, int32_t *ids, float *w, int lane) {
+__device__ __forceinline__ void select_token_n(const float *l, int E, int k, int32_t *ids, float *w, int32_t *lds_ids, int lane) {
     uint32_t key[NCS];
     uint32_t idx[NCS];
     const int nc = (E + kWave - 1) / kWave;
+    // unconditional loads (index clamped), all in flight at once
 #pragma unroll
     for (int c = 0; c < NCS; ++c) {
         const int e = lane + kWave * c;
         const bool valid = c < nc && e < E;
-        float v = 0.f;
-        if (valid) v = COHERENT ? load_shared(l + e) : l[e];
+        const int ec = min(e, E - 1);
+        const float v = COHERENT ? load_shared(l + ec) : l[ec];
         key[c] = valid ? logit_key(v) : 0u;  // 0: no expert
         idx[c] = (uint32_t)e;
     }
@@ -119,29 +125,31 @@ __device__ void select_token_n(const float *l, int E, int k, int32_t *ids, float
     if (lane < k) {
         store_shared(ids + lane, (int32_t)my_idx);
         store_shared(w + lane, p / sum);
+        if (lds_ids) lds_ids[lane] = (int32_t)my_idx;
     }
 }
 
 // Logits per lane instantiated for 1, 2, 4, 8 and 16 (E <= 1024).
 template <bool COHERENT>
-__device__ void select_token(const float *l, int E, int k, int32_t *ids, float *w, int lane) {
+__device__ __forceinline__ void select_token(const float *l, int E, int k, int32_t *ids, float *w, int32_t *lds_ids, int lane) {
     const int nc = (E + kWave - 1) / kWave;
-    if (nc <= 1) select_token_n<COHERENT, 1>(l, E, k, ids, w, lane);
-    else if (nc <= 2) select_token_n<COHERENT, 2>(l, E, k, ids, w, lane);
-    else if (nc <= 4) select_token_n<COHERENT, 4>(l, E, k, ids, w, lane);
-    else if (nc <= 8) select_token_n<COHERENT, 8>(l, E, k, ids, w, lane);
-    else select_token_n<COHERENT, 16>(l, E, k, ids, w, lane);
+    if (nc <= 1) select_token_n<COHERENT, 1>(l, E, k, ids, w, lds_ids, lane);
+    else if (nc <= 2) select_token_n<COHERENT, 2>(l, E, k, ids, w, lds_ids, lane);
+    else if (nc <= 4) select_token_n<COHERENT, 4>(l, E, k, ids, w, lds_ids, lane);
+    else if (nc <= 8) select_token_n<COHERENT, 8>(l, E, k, ids, w, lds_ids, lane);
+    else select_token_n<COHERENT, 16>(l, E, k, ids, w, lds_ids, lane);
 }
 
 // LDS ints needed by sort_block for E experts.
 __host__ __device__ constexpr int sort_lds_ints(int E) { return 11 * E; }
 
 // One workgroup sorts R routes.  ids COHERENT: written by other workgroups
-// of this launch.  lds: sort_lds_ints(E) ints.  Each thread loads its routes
+// of this launch; otherwise global memory written before the launch or this
+// workgroup's LDS.  lds: sort_lds_ints(E) ints.  Each thread loads its routes
 // r = tid + 256 w once (up to 16 windows held in registers).  Also zeroes
 // n_zero words at zero (counters of the kernels that follow).
 template <bool COHERENT>
-__device__ void sort_block(const int32_t *ids, int R, int E, int32_t *counts, int32_t *offsets, int32_t *sorted,
+__device__ __forceinline__ void sort_block(const int32_t *ids, int R, int E, int32_t *counts, int32_t *offsets, int32_t *sorted,
                            int32_t *uniq, int32_t *n_uniq, int32_t *stats, int *lds, unsigned *zero, int n_zero) {
     constexpr int kWin = 16;
     __shared__ int s_bad, s_max;
@@ -245,6 +253,127 @@ __device__ void sort_block(const int32_t *ids, int R, int E, int32_t *counts, in
             }
             __syncthreads();
         }
+    }
+}
+
+
+// Inclusive prefix sum over the wave by DPP (row_shr 1, 2, 4, 8 inside rows
+// of 16, then row_bcast15 and row_bcast31 across rows).
+__device__ __forceinline__ int wave_scan_incl(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return v;
+}
+
+constexpr int kSortWaveRounds = 16;
+constexpr int kSortWaveRoutes = kSortWaveRounds * kWave;  // routes sort_wave handles
+
+// LDS ints needed by sort_wave for E experts.
+__host__ __device__ constexpr int sort_wave_lds_ints(int E) { return 2 * E; }
+
+// One wave sorts R <= kSortWaveRoutes routes (same outputs as sort_block).
+// Route r = 64 j + lane is handled in round j.  Within a round, the lanes
+// holding the same id are found by ballots over the id bits; a route's rank
+// is the number of earlier routes with its id: the running count of that id
+// from earlier rounds (LDS, updated by the lowest lane of each group) plus
+// the group's lanes below it.  A wave's LDS accesses complete in program
+// order, so no barrier is needed.  lds: sort_wave_lds_ints(E) ints.
+template <bool COHERENT>
+__device__ __forceinline__ void sort_wave(const int32_t *ids, int R, int E, int32_t *counts, int32_t *offsets, int32_t *sorted,
+                          int32_t *uniq, int32_t *n_uniq, int32_t *stats, int *lds, int lane) {
+    int *s_run = lds, *s_off = lds + E;
+    const int nr = (R + kWave - 1) / kWave;
+    int id[kSortWaveRounds], rk[kSortWaveRounds];
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < kSortWaveRounds; ++j) {
+        const int r = j * kWave + lane;
+        id[j] = (j < nr && r < R) ? (COHERENT ? load_shared(ids + r) : ids[r]) : -1;
+        if (j < nr && r < R && (id[j] < 0 || id[j] >= E)) bad = true;
+    }
+    for (int e = lane; e < E; e += kWave) s_run[e] = 0;
+    if (__ballot(bad)) {
+        if (lane == 0) {
+            *n_uniq = -1;
+            if (stats) { stats[0] = -1; stats[1] = R; stats[2] = 0; stats[3] = 0; }
+        }
+        return;
+    }
+    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+    const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int j = 0; j < kSortWaveRounds; ++j) {
+        if (j < nr) {
+            const int v = id[j];
+            const bool valid = v >= 0;
+            unsigned long long same = __ballot(valid);
+            for (int b = 0; b < nbits; ++b) {
+                const bool bit = ((v >> b) & 1) != 0;
+                const unsigned long long on = __ballot(bit);
+                same &= bit ? on : ~on;
+            }
+            const int before = __popcll(same & below);
+            const int base = valid ? s_run[v] : 0;
+            rk[j] = base + before;
+            if (valid && before == 0) s_run[v] = base + __popcll(same);
+        }
+    }
+    // exclusive scans over the experts of the counts and of (count > 0); lane
+    // l owns experts [l * per, l * per + per)
+    const int per = (E + kWave - 1) / kWave;
+    const int lo = min(E, lane * per), hi = min(E, lo + per);
+    int csum = 0, usum = 0, cmax = 0;
+    for (int e = lo; e < hi; ++e) {
+        const int c = s_run[e];
+        csum += c;
+        usum += c > 0;
+        cmax = max(cmax, c);
+    }
+    const int cinc = wave_scan_incl(csum), uinc = wave_scan_incl(usum);
+    const int utot = __builtin_amdgcn_readlane(uinc, kWave - 1);
+    const int mx = (int)wave_reduce_u32<true>((uint32_t)cmax);
+    int cpre = cinc - csum, upre = uinc - usum;
+    for (int e = lo; e < hi; ++e) {
+        const int c = s_run[e];
+        s_off[e] = cpre;
+        offsets[e] = cpre;
+        counts[e] = c;
+        if (c > 0) uniq[upre++] = e;
+        cpre += c;
+    }
+    if (lane == 0) {
+        offsets[E] = R;
+        *n_uniq = utot;
+        if (stats) { stats[0] = utot; stats[1] = R; stats[2] = mx; stats[3] = 0; }
+    }
+#pragma unroll
+    for (int j = 0; j < kSortWaveRounds; ++j)
+        if (j < nr && id[j] >= 0) sorted[s_off[id[j]] + rk[j]] = j * kWave + lane;
+}
+
+// LDS ints needed by sort_routes for E experts and R routes.
+__host__ __device__ constexpr int sort_routes_lds_ints(int E, int R) {
+    return R <= kSortWaveRoutes ? sort_wave_lds_ints(E) : sort_lds_ints(E);
+}
+
+// Sort by one workgroup (every thread calls this): one wave when R fits,
+// the whole workgroup otherwise.  Also zeroes n_zero words at zero.
+template <bool COHERENT>
+__device__ __forceinline__ void sort_routes(const int32_t *ids, int R, int E, int32_t *counts, int32_t *offsets, int32_t *sorted,
+                            int32_t *uniq, int32_t *n_uniq, int32_t *stats, int *lds, unsigned *zero, int n_zero) {
+    if (R > kSortWaveRoutes) {
+        sort_block<COHERENT>(ids, R, E, counts, offsets, sorted, uniq, n_uniq, stats, lds, zero, n_zero);
+        return;
+    }
+    const int tid = threadIdx.x;
+    if (tid < kWave) {
+        sort_wave<COHERENT>(ids, R, E, counts, offsets, sorted, uniq, n_uniq, stats, lds, tid);
+    } else {
+        for (int i = tid - kWave; i < n_zero; i += kBlock - kWave) zero[i] = 0u;
     }
 }
 

@@ -10,8 +10,8 @@ __global__ __launch_bounds__(kBlock) void sort_kernel(const int32_t *__restrict_
                                                       int32_t *__restrict__ sorted, int32_t *__restrict__ uniq,
                                                       int32_t *__restrict__ n_uniq) {
     extern __shared__ float4 dyn_lds[];
-    sort_block<false>(ids, R, E, counts, offsets, sorted, uniq, n_uniq, nullptr, reinterpret_cast<int *>(dyn_lds),
-                      nullptr, 0);
+    sort_routes<false>(ids, R, E, counts, offsets, sorted, uniq, n_uniq, nullptr, reinterpret_cast<int *>(dyn_lds),
+                       nullptr, 0);
 }
 
 hipError_t launch_sort(const int32_t *ids, int R, int E, int32_t *counts, int32_t *offsets, int32_t *sorted,

@@ -83,7 +83,7 @@ def test_router_logits_from_x(spec, T, bias):
 # ----------------------------------------------------------------------- sort --
 
 @pytest.mark.parametrize("T,k,E", [(1, 1, 1), (4, 2, 8), (64, 8, 256), (37, 6, 100), (512, 8, 256), (300, 3, 1024),
-                                   (1, 8, 256), (2048, 2, 128)])
+                                   (1, 8, 256), (2048, 2, 128), (128, 8, 256), (205, 5, 64)])
 @pytest.mark.parametrize("kind", ["distinct", "repeats", "collide"])
 def test_sort_bit_exact(T, k, E, kind):
     note("sort T=%d k=%d E=%d %s" % (T, k, E, kind))
