@@ -101,12 +101,40 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 
+// Value of a butterfly partner of this lane at level `mask` (a power of two
+// below 64), without going through the LDS crossbar: the partner differs
+// from the lane in bit `mask` and in no bit above it.  32 and 16: the
+// partner is lane ^ mask (v_permlane32_swap / v_permlane16_swap, which
+// exchange the two halves of the wave / the rows of 16 lanes pairwise);
+// 8 and 4: lane ^ 15 and lane ^ 7 (DPP row_mirror, row_half_mirror); 2 and
+// 1: lane ^ 2, lane ^ 1 (DPP quad_perm).  Pairing lane with lane ^ (2 mask
+// - 1) instead of lane ^ mask still adds disjoint lane sets at every level
+// of a reduction that runs the masks from high to low.
+__device__ __forceinline__ float xor_partner(float v, int mask, int lane) {
+    const unsigned u = __float_as_uint(v);
+    switch (mask) {
+        case 32: {
+            const auto q = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+            return __uint_as_float((lane & 32) ? q[0] : q[1]);
+        }
+        case 16: {
+            const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+            return __uint_as_float((lane & 16) ? r[0] : r[1]);
+        }
+        case 8: return __int_as_float(__builtin_amdgcn_update_dpp(0, (int)u, 0x140, 0xF, 0xF, false));
+        case 4: return __int_as_float(__builtin_amdgcn_update_dpp(0, (int)u, 0x141, 0xF, 0xF, false));
+        case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, (int)u, 0x4E, 0xF, 0xF, false));
+        default: return __int_as_float(__builtin_amdgcn_update_dpp(0, (int)u, 0xB1, 0xF, 0xF, false));
+    }
+}
+
 // Reduce-scatter of NS slots of NW lane partials over the G lanes of a row:
 // level s (mask G/2 >> s) halves the live slots, each lane keeping the half
 // its lane bit selects and adding its partner's copy of that half; after
 // log2(NS) levels a lane holds slot (l % G) >> (log2 G - log2 NS), and a
 // butterfly over the remaining masks completes that slot's sum in every lane
-// of its group.  The order of the additions depends only on lane positions.
+// of its group (partners from xor_partner).  The order of the additions
+// depends only on lane positions.
 template <int NS, int NW, int G>
 __device__ __forceinline__ void reduce_slots(float (&p)[NS][NW], int lane) {
     constexpr int LOG = ilog2(NS);
@@ -129,13 +157,13 @@ __device__ __forceinline__ void reduce_slots(float (&p)[NS][NW], int lane) {
                 asm("" : "+v"(lo), "+v"(hi));
                 const float keep = upper ? hi : lo;
                 const float give = upper ? lo : hi;
-                p[i][v] = keep + __shfl_xor(give, mask, kWave);
+                p[i][v] = keep + xor_partner(give, mask, lane);
             }
     }
 #pragma unroll
     for (int mask = (G / 2) >> LOG; mask >= 1; mask >>= 1)
 #pragma unroll
-        for (int v = 0; v < NW; ++v) p[0][v] += __shfl_xor(p[0][v], mask, kWave);
+        for (int v = 0; v < NW; ++v) p[0][v] += xor_partner(p[0][v], mask, lane);
 }
 
 // Slot held by this lane after reduce_slots, and whether it writes it.
