@@ -91,6 +91,41 @@ __device__ __forceinline__ float chunk_dot<MOE_FP8_E4M3>(const u32x4 w, const fl
     return acc;
 }
 
+// A chunk decoded to fp32 (exact): EPC values in memory order.  fp8 codes
+// are decoded without their block scale.
+template <int WDT>
+__device__ __forceinline__ void chunk_decode(const u32x4 w, float *f);
+
+template <>
+__device__ __forceinline__ void chunk_decode<MOE_F32>(const u32x4 w, float *f) {
+    f[0] = __uint_as_float(w.x);
+    f[1] = __uint_as_float(w.y);
+    f[2] = __uint_as_float(w.z);
+    f[3] = __uint_as_float(w.w);
+}
+
+template <>
+__device__ __forceinline__ void chunk_decode<MOE_BF16>(const u32x4 w, float *f) {
+    f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x);
+    f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+    f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z);
+    f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+}
+
+template <>
+__device__ __forceinline__ void chunk_decode<MOE_FP8_E4M3>(const u32x4 w, float *f) {
+    const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[q], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[q], true);
+        f[4 * q] = lo[0];
+        f[4 * q + 1] = lo[1];
+        f[4 * q + 2] = hi[0];
+        f[4 * q + 3] = hi[1];
+    }
+}
+
 // Sum over the 64 lanes; every lane receives the same value (each butterfly
 // step adds the same two operands in both partner lanes).
 __device__ __forceinline__ float wave_sum(float v) {

@@ -12,6 +12,8 @@
 // every walk gives bitwise the same result.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -117,15 +119,18 @@ __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\
 // workgroup: the staged rows of every wave are in LDS after it.
 __device__ __forceinline__ void wait_loads_and_sync() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// acc[s] = this lane's partial of slot s . x, chunks in order, with x read
-// from an LDS row; fp8 chunks are scaled by their
-// block scale.  The weights stay packed in registers across the route loop:
-// the empty asm makes them opaque on every call, so the compiler cannot
-// hoist their decode out of the loop (which would double their register
-// footprint and halve the waves in flight).
-template <int WDT, int NC, int NS, int G>
-__device__ __forceinline__ void dot_rows(u32x4 (&w)[NS][NC], const float (&sc)[NS][NC], const float4 *xl, int nq,
-                                         int lane, float (&acc)[NS]) {
+// acc[r][s] = this lane's partial of slot s . x_r for RB routes, chunks in
+// order, with the x rows read from LDS; fp8 chunks are scaled by their block
+// scale.  Each weight chunk is decoded once for all RB routes; a route's
+// arithmetic (fp32 FMAs in element order per chunk, chunks in order) is the
+// same for any RB, so pairing routes changes no result bit.  The weights
+// stay packed in registers across the route loop: the empty asm makes them
+// opaque on every call, so the compiler cannot hoist their decode out of the
+// loop (which would double their register footprint and halve the waves in
+// flight).
+template <int WDT, int NC, int NS, int G, int RB>
+__device__ __forceinline__ void dot_rows(u32x4 (&w)[NS][NC], const float (&sc)[NS][NC],
+                                         const float4 *const (&xl)[RB], int nq, int lane, float (&acc)[RB][NS]) {
     constexpr int EPC = WT<WDT>::kEpc;
     const int sub = lane & (G - 1);
 #pragma unroll
@@ -133,21 +138,32 @@ __device__ __forceinline__ void dot_rows(u32x4 (&w)[NS][NC], const float (&sc)[N
 #pragma unroll
         for (int c = 0; c < NC; ++c) asm volatile("" : "+v"(w[s][c]));
 #pragma unroll
-    for (int s = 0; s < NS; ++s) acc[s] = 0.f;
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) acc[r][s] = 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         const int q = sub + G * c;
         if (q < nq) {
-            float xs[EPC];
+            float xs[RB][EPC];
 #pragma unroll
-            for (int v = 0; v < EPC / 4; ++v) {
-                const float4 f = xl[q * (EPC / 4) + v];
-                xs[4 * v] = f.x; xs[4 * v + 1] = f.y; xs[4 * v + 2] = f.z; xs[4 * v + 3] = f.w;
-            }
+            for (int r = 0; r < RB; ++r)
+#pragma unroll
+                for (int v = 0; v < EPC / 4; ++v) {
+                    const float4 f = xl[r][q * (EPC / 4) + v];
+                    xs[r][4 * v] = f.x; xs[r][4 * v + 1] = f.y; xs[r][4 * v + 2] = f.z; xs[r][4 * v + 3] = f.w;
+                }
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                if (WDT == MOE_FP8_E4M3) acc[s] = fmaf(sc[s][c], chunk_dot<WDT>(w[s][c], xs, 0.f), acc[s]);
-                else acc[s] = chunk_dot<WDT>(w[s][c], xs, acc[s]);
+                float wf[EPC];
+                chunk_decode<WDT>(w[s][c], wf);
+#pragma unroll
+                for (int r = 0; r < RB; ++r) {
+                    float t = WDT == MOE_FP8_E4M3 ? 0.f : acc[r][s];
+#pragma unroll
+                    for (int i = 0; i < EPC; ++i) t = fmaf(wf[i], xs[r][i], t);
+                    acc[r][s] = WDT == MOE_FP8_E4M3 ? fmaf(sc[s][c], t, acc[r][s]) : t;
+                }
             }
         }
     }
@@ -245,17 +261,32 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(Pass1Args a) {
                 return reinterpret_cast<const float4 *>(a.x + (size_t)(r / a.k) * H);
             });
             wait_loads_and_sync();
-            for (int m = 0; m < mb; ++m) {
-                const int r = segment_route_uniform(a.sa, first, m0 + m);
-                float acc[NS];
-                dot_rows<WDT, NC, NS, G>(w, sc, xl + (size_t)m * (H / 4), nq, lane, acc);
-                float gu[P][2];
+            // routes in pairs (one weight decode for both), then a single one
+            auto routes = [&](auto rb_tag, int m) {
+                constexpr int RB = decltype(rb_tag)::value;
+                const float4 *x[RB];
+                int r[RB];
 #pragma unroll
-                for (int p = 0; p < P; ++p) { gu[p][0] = acc[2 * p]; gu[p][1] = acc[2 * p + 1]; }
-                reduce_slots<P, 2, G>(gu, lane);
-                const int p = reduced_slot<P, G>(lane);
-                if (slot_leader<P, G>(lane) && i0 + p < I) a.act[(size_t)r * I + i0 + p] = silu(gu[0][0]) * gu[0][1];
-            }
+                for (int j = 0; j < RB; ++j) {
+                    r[j] = segment_route_uniform(a.sa, first, m0 + m + j);
+                    x[j] = xl + (size_t)(m + j) * (H / 4);
+                }
+                float acc[RB][NS];
+                dot_rows<WDT, NC, NS, G, RB>(w, sc, x, nq, lane, acc);
+#pragma unroll
+                for (int j = 0; j < RB; ++j) {
+                    float gu[P][2];
+#pragma unroll
+                    for (int p = 0; p < P; ++p) { gu[p][0] = acc[j][2 * p]; gu[p][1] = acc[j][2 * p + 1]; }
+                    reduce_slots<P, 2, G>(gu, lane);
+                    const int p = reduced_slot<P, G>(lane);
+                    if (slot_leader<P, G>(lane) && i0 + p < I)
+                        a.act[(size_t)r[j] * I + i0 + p] = silu(gu[0][0]) * gu[0][1];
+                }
+            };
+            int m = 0;
+            for (; m + 1 < mb; m += 2) routes(std::integral_constant<int, 2>{}, m);
+            if (m < mb) routes(std::integral_constant<int, 1>{}, m);
         };
         if (n > 0) batch(0, min(a.nb, n));
         for (int m0 = a.nb; m0 < n; m0 += a.nb) batch(m0, min(a.nb, n - m0));
@@ -328,18 +359,32 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Pass2Args a) {
                 return reinterpret_cast<const float4 *>(a.act + (size_t)r * I);
             });
             wait_loads_and_sync();
-            for (int m = 0; m < mb; ++m) {
-                const int r = segment_route_uniform(a.sa, first, m0 + m);
-                float acc[NS];
-                dot_rows<WDT, NC, NS, G>(w, sc, xl + (size_t)m * (I / 4), nq, lane, acc);
-                float v[NS][1];
+            // routes in pairs (one weight decode for both), then a single one
+            auto routes = [&](auto rb_tag, int m) {
+                constexpr int RB = decltype(rb_tag)::value;
+                const float4 *x[RB];
+                int r[RB];
 #pragma unroll
-                for (int j = 0; j < NS; ++j) v[j][0] = acc[j];
-                reduce_slots<NS, 1, G>(v, lane);
-                const int j = reduced_slot<NS, G>(lane);
-                const int h = h0 + j * RPS + half;
-                if (slot_leader<NS, G>(lane) && h < H) a.y[(size_t)r * H + h] = v[0][0];
-            }
+                for (int i = 0; i < RB; ++i) {
+                    r[i] = segment_route_uniform(a.sa, first, m0 + m + i);
+                    x[i] = xl + (size_t)(m + i) * (I / 4);
+                }
+                float acc[RB][NS];
+                dot_rows<WDT, NC, NS, G, RB>(w, sc, x, nq, lane, acc);
+#pragma unroll
+                for (int i = 0; i < RB; ++i) {
+                    float v[NS][1];
+#pragma unroll
+                    for (int j = 0; j < NS; ++j) v[j][0] = acc[i][j];
+                    reduce_slots<NS, 1, G>(v, lane);
+                    const int j = reduced_slot<NS, G>(lane);
+                    const int h = h0 + j * RPS + half;
+                    if (slot_leader<NS, G>(lane) && h < H) a.y[(size_t)r[i] * H + h] = v[0][0];
+                }
+            };
+            int m = 0;
+            for (; m + 1 < mb; m += 2) routes(std::integral_constant<int, 2>{}, m);
+            if (m < mb) routes(std::integral_constant<int, 1>{}, m);
         };
         if (n > 0) batch(0, min(a.nb, n));
         for (int m0 = a.nb; m0 < n; m0 += a.nb) batch(m0, min(a.nb, n - m0));
