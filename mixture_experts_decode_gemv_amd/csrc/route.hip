@@ -8,7 +8,8 @@
 // dispatches.  Here the router, the selection and the sort are one kernel:
 //
 //  * Workgroup (eb, tb) computes the logits of 16 experts (4 per wave, rows
-//    held in registers) for a tile of up to 8 tokens (32 KiB) staged in LDS
+//    held in registers) for a tile of up to 8 tokens (32 KiB, 64 KiB for
+//    batches of 128 tokens or more) staged in LDS
 //    (normalised there first for the RMSNorm form; workgroup eb = 0 also
 //    writes the normalised rows for the expert passes).
 //  * The last workgroup to finish a token tile (per-tile arrival counter)
@@ -26,9 +27,15 @@ namespace moe {
 constexpr int kRouteRows = 4;                      // router rows per wave
 constexpr int kRouteExperts = 4 * kRouteRows;      // experts per workgroup
 constexpr int kRouteTileFloats = 8192;             // token tile: 32 KiB of LDS
+constexpr int kRouteTileFloatsLarge = 16384;       // from kRouteLargeT tokens: 64 KiB
+constexpr int kRouteLargeT = 128;
 
-__host__ __device__ constexpr int route_tile_tokens(int H) {
-    return H >= kRouteTileFloats ? 1 : (kRouteTileFloats / H < 8 ? kRouteTileFloats / H : 8);
+// Tokens per tile: up to 8, in 32 KiB of LDS (64 KiB for large batches,
+// which have tiles enough to fill the chip and re-read the router rows once
+// per tile).
+__host__ __device__ constexpr int route_tile_tokens(int H, int T) {
+    const int f = T >= kRouteLargeT ? kRouteTileFloatsLarge : kRouteTileFloats;
+    return H >= f ? 1 : (f / H < 8 ? f / H : 8);
 }
 
 struct RouteArgs {
@@ -77,6 +84,10 @@ __global__ __launch_bounds__(kBlock) void route_kernel(RouteArgs a) {
                                                                                     (size_t)(e0 + r) * row_bytes) + q)
                                : u32x4{0u, 0u, 0u, 0u};
             }
+        // this lane's router bias (lane r stores row r of the wave), read
+        // before the token loop: a load inside it would wait behind the
+        // previous tokens' logit stores (vector memory counts in order)
+        const float bias_r = (a.bias && lane < kRouteRows && e0 + lane < E) ? a.bias[e0 + lane] : 0.f;
         // token tile -> LDS, 8 loads in flight per thread
         const int h4 = H / 4;
         {
@@ -85,9 +96,14 @@ __global__ __launch_bounds__(kBlock) void route_kernel(RouteArgs a) {
             float4 *dst = reinterpret_cast<float4 *>(tile);
             for (int base = 0; base < n4; base += 8 * kBlock) {
                 float4 v[8];
-                // unconditional loads (index clamped) keep v in registers
+                // unconditional loads (index clamped), all in flight at once:
+                // the empty asm uses every value before any store, so the
+                // compiler cannot sink a load under its store's condition
+                // (which would wait for each load in turn)
 #pragma unroll
                 for (int u = 0; u < 8; ++u) v[u] = src[min(base + u * kBlock + (int)threadIdx.x, n4 - 1)];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) asm volatile("" : "+v"(v[u].x), "+v"(v[u].y), "+v"(v[u].z), "+v"(v[u].w));
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const int idx = base + u * kBlock + threadIdx.x;
@@ -161,9 +177,8 @@ __global__ __launch_bounds__(kBlock) void route_kernel(RouteArgs a) {
                 }
             }
             if (lane < kRouteRows && e0 + lane < E) {
-                const float bias = a.bias ? a.bias[e0 + lane] : 0.f;
-                store_shared(a.logits + (size_t)(t0 + t) * E + e0 + lane, a.bias ? l0 + bias : l0);
-                if (two) store_shared(a.logits + (size_t)(t0 + t + 1) * E + e0 + lane, a.bias ? l1 + bias : l1);
+                store_shared(a.logits + (size_t)(t0 + t) * E + e0 + lane, a.bias ? l0 + bias_r : l0);
+                if (two) store_shared(a.logits + (size_t)(t0 + t + 1) * E + e0 + lane, a.bias ? l1 + bias_r : l1);
             }
         }
         wait_vm_stores();
@@ -251,11 +266,11 @@ hipError_t launch_route(const moe_layer_t &L, const float *x, const float *logit
     a.k = L.top_k;
     a.rmsnorm = rmsnorm ? 1 : 0;
     a.eps = 1e-6f;
-    a.tile = logits_in ? (kBlock / kWave) : route_tile_tokens(L.H);
+    a.tile = logits_in ? (kBlock / kWave) : route_tile_tokens(L.H, T);
     a.n_eblk = logits_in ? 1 : (L.E + kRouteExperts - 1) / kRouteExperts;
     a.n_tblk = (T + a.tile - 1) / a.tile;
     // the sort's LDS, then (single tile) the selected ids
-    size_t lds = ((size_t)sort_lds_ints(L.E) + (size_t)(logits_in ? kBlock / kWave : route_tile_tokens(L.H)) * L.top_k) * 4;
+    size_t lds = ((size_t)sort_lds_ints(L.E) + (size_t)a.tile * L.top_k) * 4;
     if (!logits_in) {
         const size_t tb = (size_t)a.tile * L.H * 4;
         lds = tb > lds ? tb : lds;
