@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0
 # (uniform routing, bs=64), from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
 # scaled by a 1 GiB copy calibration: profiles/pass_kernels_uniform_bs64_hbm_counters.md.
 # Reported only while the kernel source is the one that was measured.
-PASS1_TRAFFIC_BS64 = {"read_bytes": 1.3999e9, "write_bytes": 1.835e6, "source": "3559e2db0f1734b5"}
+PASS1_TRAFFIC_BS64 = {"read_bytes": 1.39999e9, "write_bytes": 1.83538e6, "source": "7ed2bc2be9be4d1a"}
 
 
 def pass1_source_fingerprint():

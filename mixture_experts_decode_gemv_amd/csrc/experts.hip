@@ -159,9 +159,12 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
     if (mfma) split.gemv_below = kMfmaMinRoutes;
 
     // pass 1 on the GEMV kernel: one wave item = P gate/up pairs of one segment
-    auto gemv1 = [&](hipStream_t s) {
+    // xb_first: the GEMV kernel writes the bf16 copy of x in its prologue
+    // (in-order path); otherwise mfma_1 converts it on its own stream
+    auto gemv1 = [&](hipStream_t s, bool xb_first) {
         Pass1Args p1{L.w_gate_up, L.s_gate_up, x, act, L.H, L.I, L.top_k,
-                     walk == MOE_WALK_PER_ROUTE ? per_route : split, lds_batch_rows(L.H)};
+                     walk == MOE_WALK_PER_ROUTE ? per_route : split,
+                     xb_first ? static_cast<uint32_t *>(xb) : nullptr, lds_batch_rows(L.H)};
         const int nq1 = L.H / epc;
         const int nc1 = nc_instance((nq1 + kWave - 1) / kWave);
         const int pairs = slots_for(nc1) / 2 * (kBlock / kWave);  // per workgroup item
@@ -172,14 +175,17 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
             default: return launch_pass1<MOE_FP8_E4M3>(nc1, persistent_grid(items1), s, p1);
         }
     };
-    // pass 1 of the MFMA segments, on a bf16 copy of x
-    auto mfma_1 = [&](hipStream_t s) {
-        const int npairs = T * L.H / 2;
-        const int g = std::max(1, std::min((npairs + kBlock - 1) / kBlock, num_cus() * 4));
-        hipLaunchKernelGGL(to_bf16_kernel, dim3(g), dim3(kBlock), 0, s, reinterpret_cast<const float2 *>(x),
-                           static_cast<float *>(xb), npairs);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+    // pass 1 of the MFMA segments, on a bf16 copy of x (converted here unless
+    // the GEMV pass 1 did it)
+    auto mfma_1 = [&](hipStream_t s, bool convert) {
+        if (convert) {
+            const int npairs = T * L.H / 2;
+            const int g = std::max(1, std::min((npairs + kBlock - 1) / kBlock, num_cus() * 4));
+            hipLaunchKernelGGL(to_bf16_kernel, dim3(g), dim3(kBlock), 0, s, reinterpret_cast<const float2 *>(x),
+                               static_cast<float *>(xb), npairs);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
         MfmaArgs m1{L.w_gate_up, L.s_gate_up, xb, act, L.H, L.I, L.top_k, kMfmaMinRoutes, mfma2 ? 1 : 0, grouped,
                     rt.max_count};
         return launch_mfma_pass(L, 1, T, m1, s);
@@ -221,9 +227,9 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
     if (sd) {
         MOE_TRY(hipEventRecord(sd->fork, st));
         MOE_TRY(hipStreamWaitEvent(sd->s, sd->fork, 0));
-        MOE_TRY(mfma_1(sd->s));
+        MOE_TRY(mfma_1(sd->s, true));
         if (mfma2) MOE_TRY(mfma_2(sd->s));
-        MOE_TRY(gemv1(st));
+        MOE_TRY(gemv1(st, false));
         // pass 2 of the DEDUP_PASS1 walk reads every segment's pass-1 rows
         if (!mfma2) {
             MOE_TRY(hipEventRecord(sd->join, sd->s));
@@ -237,9 +243,9 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
         return combine();
     }
     auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], st) : hipSuccess; };
-    MOE_TRY(gemv1(st));
+    MOE_TRY(gemv1(st, mfma));
     MOE_TRY(mark(0));
-    if (mfma) MOE_TRY(mfma_1(st));
+    if (mfma) MOE_TRY(mfma_1(st, false));
     MOE_TRY(mark(1));
     MOE_TRY(gemv2(st));
     MOE_TRY(mark(2));

@@ -190,7 +190,8 @@ struct Pass1Args {
     float *act;
     int H, I, k;
     SegArgs sa;
-    int nb;  // routes per LDS batch
+    uint32_t *xb;  // if set: bf16 copy of x [T, H] for the MFMA segments, written first
+    int nb;        // routes per LDS batch
 };
 
 template <int WDT, int NC>
@@ -206,6 +207,17 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(Pass1Args a) {
     const int items_per_seg = (I + P * WPB - 1) / (P * WPB);
     const int n_items = segment_count(a.sa) * items_per_seg;
     const size_t row_bytes = (size_t)H * WT<WDT>::kBytes;
+
+    if (a.xb) {  // the MFMA pass 1, launched after this kernel, reads x as bf16
+        const int npairs = a.sa.R / a.k * H / 2;
+        // stored as float-typed words: no store of this kernel may alias the
+        // int32 routing arrays, whose wave-uniform loads can then be scalar
+        float *xb = reinterpret_cast<float *>(a.xb);
+        for (int i = blockIdx.x * kBlock + threadIdx.x; i < npairs; i += gridDim.x * kBlock) {
+            const float2 v = reinterpret_cast<const float2 *>(a.x)[i];
+            xb[i] = __uint_as_float(bf16_pair_rne(v.x, v.y));
+        }
+    }
 
     // Items are strided over the workgroups, so at any time the grid streams
     // one narrow window of the weights.  The segment of the next item is
