@@ -18,8 +18,8 @@ import mixture_experts_decode_gemv_amd as moe  # noqa: E402
 import oracle  # noqa: E402
 import workload as wl  # noqa: E402
 
-from gpu_util import (check_layer_sampled, dev, gpu_expert_fwd, make_device_layer, max_rel,  # noqa: E402
-                      note, oracle_weights_for)
+from gpu_util import (check_layer_against_oracle, check_layer_sampled, dev, gpu_expert_fwd,  # noqa: E402
+                      gpu_layer_fwd, make_device_layer, max_rel, note, oracle_weights_for)
 
 NORTH_STAR_TOL = 2e-2
 MFMA_MIN = 16  # routes per expert from which a segment runs on MFMA
@@ -201,3 +201,20 @@ def test_large_bf16_sampled(large_bf16, T):
 def test_large_fp8_sampled(large_fp8, T):
     note("large fp8 T=%d" % T)
     _run_large(large_fp8, T)
+
+
+def test_mfma_narrow_many_experts():
+    """E = 1024 (the largest the library takes: 8 KiB of expert tables in the
+    narrow kernel's LDS), K = 128 (one stage), four hot experts on MFMA."""
+    note("mfma narrow E=1024")
+    spec = wl.LayerSpec(E=1024, top_k=2, H=128, I=128)
+    bias = np.zeros(spec.E, np.float32)
+    bias[[3, 500, 777, 1023]] = 6.0
+    w, layer, olayer = make_device_layer(spec, bias)
+    T = 64
+    x = wl.make_x(T, spec.H, draw=7)
+    err, apart = check_layer_against_oracle(layer, olayer, x, tol=NORTH_STAR_TOL)
+    g = gpu_layer_fwd(layer, x, 0, full=True)
+    assert g["counts"].max() >= MFMA_MIN
+    gemv = gpu_layer_fwd(layer, x, moe.MOE_NO_MFMA)
+    assert max_rel(g["out"], gemv) <= NORTH_STAR_TOL

@@ -325,3 +325,15 @@ def test_token_output_independent_of_batch_bitwise(sweep_layer, flags):
         assert np.array_equal(part, full[:T]), T
     again = gpu_layer_fwd(layer, x[:5], f)
     assert np.array_equal(again, full[:5])
+
+
+def test_stack_layer_large_batch_rmsnorm():
+    """The stack shape at 160 tokens: 64 KiB router tiles of 8 tokens,
+    RMSNorm on the tile, several tiles with a ragged last one, the workgroup
+    sort (R = 320 > one tile); GEMV segments only, so the fp32 bar holds."""
+    note("stack layer T=160")
+    T = 160
+    w, layer, olayer = make_device_layer(wl.STACK, layer_idx=4)
+    h = wl.make_x(T, wl.STACK.H, draw=301)
+    flags = moe.MOE_RMSNORM_IN | moe.MOE_ACCUM_RESIDUAL | moe.MOE_NO_MFMA
+    check_layer_against_oracle(layer, olayer, h, flags=flags, tol=1e-4, rmsnorm_in=True, residual=True)
