@@ -63,7 +63,7 @@ extern "C" {
 
 size_t moe_workspace_bytes(const moe_layer_t *layer, int32_t max_tokens) {
     if (check_layer(layer) != MOE_OK || max_tokens < 0) return 0;
-    return ws_layout(*layer, max_tokens).total;
+    return ws_bytes_for(*layer, max_tokens);
 }
 
 moe_status moe_workspace_init(const moe_layer_t *layer, int32_t max_tokens, void *ws, size_t ws_bytes,
@@ -71,10 +71,11 @@ moe_status moe_workspace_init(const moe_layer_t *layer, int32_t max_tokens, void
     moe_status s = check_layer(layer);
     if (s != MOE_OK) return s;
     if (max_tokens < 0 || !ws) return MOE_ERR_ARG;
-    const WsLayout wl = ws_layout(*layer, max_tokens);
-    if (ws_bytes < wl.total) return MOE_ERR_WORKSPACE;
+    const int64_t cap = ws_capacity(*layer, ws_bytes);
+    if (cap < max_tokens) return MOE_ERR_WORKSPACE;
+    const WsLayout wl = ws_layout(*layer, cap, cap);
     if (!aligned16(ws)) return MOE_ERR_ALIGN;
-    // stats and arrival counters sit at the front of the workspace
+    // stats and synchronisation words sit at the front of the workspace
     return hip_status(launch_zero(static_cast<unsigned *>(ws), (int)(wl.logits / 4), (hipStream_t)stream));
 }
 
@@ -96,8 +97,9 @@ moe_status moe_route(const moe_layer_t *layer, const float *x, const float *logi
     }
     if ((s = check_weights(layer, true, false)) != MOE_OK) return s;
     if (!aligned16(x)) return MOE_ERR_ALIGN;
-    const WsLayout wl = ws_layout(*layer, T);
-    if (!ws || ws_bytes < wl.total) return MOE_ERR_WORKSPACE;
+    const int64_t cap = ws ? ws_capacity(*layer, ws_bytes) : -1;
+    if (cap < T) return MOE_ERR_WORKSPACE;
+    const WsLayout wl = ws_layout(*layer, T, cap);
     if (!aligned16(ws)) return MOE_ERR_ALIGN;
     char *b = static_cast<char *>(ws);
     float *dst = logits_out ? logits_out : reinterpret_cast<float *>(b + wl.logits);
@@ -129,8 +131,9 @@ moe_status moe_expert_fwd(const moe_layer_t *layer, const float *x, int32_t T, c
     if ((flags & MOE_WALK_MASK) > MOE_WALK_DEDUP_PASS1) return MOE_ERR_ARG;
     if (!aligned16(x) || !aligned16(out)) return MOE_ERR_ALIGN;
     if (T == 0) return MOE_OK;
-    const WsLayout wl = ws_layout(*layer, T);
-    if (!ws || ws_bytes < wl.total) return MOE_ERR_WORKSPACE;
+    const int64_t cap = ws ? ws_capacity(*layer, ws_bytes) : -1;
+    if (cap < T) return MOE_ERR_WORKSPACE;
+    const WsLayout wl = ws_layout(*layer, T, cap);
     if (!aligned16(ws)) return MOE_ERR_ALIGN;
     char *b = static_cast<char *>(ws);
     Routing rt{topk_ids, counts, offsets, sorted_routes, uniq, n_uniq, topk_w, nullptr};
@@ -148,8 +151,9 @@ static moe_status layer_fwd(const moe_layer_t *layer, const float *x, int32_t T,
     if ((flags & MOE_WALK_MASK) > MOE_WALK_DEDUP_PASS1) return MOE_ERR_ARG;
     if (!aligned16(x) || !aligned16(out)) return MOE_ERR_ALIGN;
     if (T == 0) return MOE_OK;
-    const WsLayout wl = ws_layout(*layer, T);
-    if (!ws || ws_bytes < wl.total) return MOE_ERR_WORKSPACE;
+    const int64_t cap = ws ? ws_capacity(*layer, ws_bytes) : -1;
+    if (cap < T) return MOE_ERR_WORKSPACE;
+    const WsLayout wl = ws_layout(*layer, T, cap);
     if (!aligned16(ws)) return MOE_ERR_ALIGN;
     hipStream_t st = (hipStream_t)stream;
     char *b = static_cast<char *>(ws);
@@ -167,8 +171,8 @@ static moe_status layer_fwd(const moe_layer_t *layer, const float *x, int32_t T,
     if (ev && (s = hip_status(hipEventRecord(ev[1], st))) != MOE_OK) return s;
     Routing rt{I32(wl.ids),  I32(wl.counts), I32(wl.offsets), I32(wl.sorted),
                I32(wl.uniq), I32(wl.nuniq),  F(wl.w),         I32(wl.stats) + 2};
-    return hip_status(launch_experts(*layer, xin, (flags & MOE_ACCUM_RESIDUAL) ? x : nullptr, T, rt, b + wl.xb, F(wl.act),
-                                     F(wl.y), out, flags, st, ev ? ev + 2 : nullptr));
+    return hip_status(launch_experts(*layer, xin, (flags & MOE_ACCUM_RESIDUAL) ? x : nullptr, T, rt, b + wl.xb,
+                                     F(wl.act), F(wl.y), out, flags, st, ev ? ev + 2 : nullptr));
 }
 
 moe_status moe_layer_fwd(const moe_layer_t *layer, const float *x, int32_t T, float *out, uint32_t flags, void *ws,
@@ -190,8 +194,9 @@ moe_status moe_layer_routing(const moe_layer_t *layer, int32_t T, void *ws, size
     moe_status s = check_layer(layer);
     if (s != MOE_OK) return s;
     if (T < 0 || !ws) return MOE_ERR_ARG;
-    const WsLayout wl = ws_layout(*layer, T);
-    if (ws_bytes < wl.total) return MOE_ERR_WORKSPACE;
+    const int64_t cap = ws_capacity(*layer, ws_bytes);
+    if (cap < T) return MOE_ERR_WORKSPACE;
+    const WsLayout wl = ws_layout(*layer, T, cap);
     char *b = static_cast<char *>(ws);
     if (topk_ids) *topk_ids = reinterpret_cast<int32_t *>(b + wl.ids);
     if (topk_w) *topk_w = reinterpret_cast<float *>(b + wl.w);

@@ -248,13 +248,17 @@ struct WsLayout {
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-inline WsLayout ws_layout(const moe_layer_t &L, int64_t T) {
+// T tokens in a workspace that holds up to cap tokens (cap >= T).  The
+// synchronisation words are sized for cap, so they sit at the same offsets
+// for every batch size used with one workspace, and no data array of a
+// smaller batch ever lands on them.
+inline WsLayout ws_layout(const moe_layer_t &L, int64_t T, int64_t cap) {
     WsLayout s;
     const int64_t R = T * L.top_k;
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
     s.stats = take(16);
-    s.arrive = take((size_t)route_arrive_words((int)T) * 4);
+    s.arrive = take((size_t)route_arrive_words((int)cap) * 4);
     s.logits = take((size_t)T * L.E * 4);
     s.ids = take((size_t)R * 4);
     s.w = take((size_t)R * 4);
@@ -269,6 +273,28 @@ inline WsLayout ws_layout(const moe_layer_t &L, int64_t T) {
     s.y = take((size_t)R * L.H * 4);
     s.total = o;
     return s;
+}
+
+// Bytes for up to T tokens.
+inline size_t ws_bytes_for(const moe_layer_t &L, int64_t T) { return ws_layout(L, T, T).total; }
+
+// The largest token count a workspace of `bytes` bytes holds (-1 if none):
+// its capacity, which fixes where the synchronisation words sit.
+inline int64_t ws_capacity(const moe_layer_t &L, size_t bytes) {
+    if (bytes < ws_bytes_for(L, 0)) return -1;
+    int64_t lo = 0, hi = 1;
+    while (hi < (int64_t)1 << 30 && ws_bytes_for(L, hi) <= bytes) {
+        lo = hi;
+        hi *= 2;
+    }
+    while (hi - lo > 1) {
+        const int64_t mid = lo + (hi - lo) / 2;
+        if (ws_bytes_for(L, mid) <= bytes)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    return lo;
 }
 
 // ---- launchers (return hipSuccess or the launch error) -----------------------

@@ -96,3 +96,23 @@ def test_routing_accessor_points_into_the_workspace():
         assert 0x10000 <= v < 0x10000 + n
     with pytest.raises(moe.MoeError):
         moe.moe_layer_routing(L, 4, 0x10000, 8)
+
+
+def test_workspace_data_starts_at_a_fixed_offset_for_every_batch():
+    """The synchronisation words are laid out for the workspace's capacity
+    (fixed by its size), so the data region (logits first) starts at the same
+    offset for every batch size the workspace holds, and a batch larger than
+    the capacity is refused."""
+    L = _layer()
+    n = moe.moe_workspace_bytes(L, 64)
+    starts = set()
+    for T in (1, 3, 17, 64):
+        r = moe.moe_layer_routing(L, T, 0x10000, n)
+        starts.add(r["topk_ids"] - ((T * L.E * 4 + 255) // 256) * 256)
+    assert len(starts) == 1
+    big = 64
+    while moe.moe_workspace_bytes(L, big + 1) <= n:
+        big += 1
+    moe.moe_layer_routing(L, big, 0x10000, n)
+    with pytest.raises(moe.MoeError):
+        moe.moe_layer_routing(L, big + 1, 0x10000, n)

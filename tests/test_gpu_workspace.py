@@ -1,0 +1,64 @@
+"""One workspace serves every batch size up to its capacity: calls of
+different sizes in any order give bitwise the results of a fresh workspace,
+and the synchronisation words at its front are zero again after each call.
+
+The synchronisation words (the routing kernel's arrival counters) are laid
+out for the workspace's capacity, fixed by its size, so a small batch's
+logits or routing arrays never land on the counters a larger batch uses.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_decode_gemv_amd as moe
+import workload as wl
+from gpu_util import make_device_layer, note, stream, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(layer, x, T, flags, ws):
+    xd = to_dev(x.astype(np.float32))
+    out = torch.full_like(xd, float("nan"))
+    moe.moe_layer_fwd(layer.struct, xd, T, out, flags, ws, ws.numel(), stream())
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _front_is_clear(layer, T, ws):
+    """Every word between the statistics block and the logits is zero."""
+    s = layer.spec
+    r = moe.moe_layer_routing(layer.struct, T, ws, ws.numel())
+    logits_off = r["topk_ids"] - ws.data_ptr() - ((T * s.E * 4 + 255) // 256) * 256
+    front = ws[256:logits_off].view(torch.int32).cpu().numpy()
+    assert front.size > 0 and not front.any(), "%d synchronisation words left nonzero" % int((front != 0).sum())
+
+
+@pytest.mark.parametrize("spec,flags,sizes", [
+    (wl.SWEEP, 0, (64, 3, 64, 17, 1, 3, 64, 9)),
+    (wl.STACK, moe.MOE_RMSNORM_IN | moe.MOE_ACCUM_RESIDUAL, (4, 1, 4, 2, 1)),
+    (wl.TINY, 0, (37, 4, 1, 37, 12)),
+], ids=["sweep", "stack", "tiny"])
+def test_batch_sizes_interleaved_on_one_workspace(spec, flags, sizes):
+    w, layer, olayer = make_device_layer(spec)
+    cap = max(sizes)
+    xs = {T: wl.make_x(T, spec.H, draw=700 + T) for T in sizes}
+    ref = {}
+    for T in xs:
+        note("fresh workspace T=%d" % T)
+        ref[T] = _run(layer, xs[T], T, flags, layer.workspace(T))
+    ws = layer.workspace(cap)
+    for T in sizes:
+        note("shared workspace T=%d" % T)
+        assert np.array_equal(_run(layer, xs[T], T, flags, ws), ref[T]), "T=%d" % T
+        _front_is_clear(layer, T, ws)
+
+
+def test_larger_workspace_than_needed():
+    """A workspace bigger than moe_workspace_bytes(T) (its capacity is then
+    larger than the batch) gives the same bits."""
+    w, layer, olayer = make_device_layer(wl.SWEEP)
+    x = wl.make_x(8, wl.SWEEP.H, draw=990)
+    a = _run(layer, x, 8, 0, layer.workspace(8))
+    b = _run(layer, x, 8, 0, layer.workspace(200))
+    assert np.array_equal(a, b)
