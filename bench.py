@@ -36,21 +36,23 @@ HBM_PEAK_GBS = 8000.0
 # (uniform routing, bs=64), from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
 # scaled by a 1 GiB copy calibration: profiles/pass_kernels_uniform_bs64_hbm_counters.md.
 # Reported only while the kernel source is the one that was measured.
-PASS1_TRAFFIC_BS64 = {"read_bytes": 1.39999e9, "write_bytes": 1.83538e6, "source": "7ed2bc2be9be4d1a"}
+PASS1_TRAFFIC_BS64 = {"read_bytes": 1.39999e9, "write_bytes": 1.83501e6, "source": "8b28c7c3490d4561"}
 
 
 def pass1_source_fingerprint():
     """Hash of the pass-1 GEMV kernel source: the grouped-GEMV section of
-    experts_impl.h (segments through pass 1) and the chunk dot products of
-    common.h."""
+    experts_impl.h (segments through pass 1), the chunk dot products of
+    common.h and the persistent grid size of experts.hip."""
     import hashlib
 
     d = os.path.join(ROOT, "mixture_experts_decode_gemv_amd", "csrc")
     impl = open(os.path.join(d, "experts_impl.h")).read()
     common = open(os.path.join(d, "common.h")).read()
+    launch = open(os.path.join(d, "experts.hip")).read()
     a = impl[impl.index("struct SegArgs"):impl.index("// ---- pass 2: down rows")]
     b = common[common.index("// acc + sum_e w[e]"):common.index("// Sum over the 64 lanes")]
-    return hashlib.sha256((a + b).encode()).hexdigest()[:16]
+    c = launch[launch.index("static int persistent_grid"):launch.index("// Segments with at least kMfmaMinRoutes")]
+    return hashlib.sha256((a + b + c).encode()).hexdigest()[:16]
 MFMA_PEAK_TFS = 2500.0  # dense bf16
 
 

