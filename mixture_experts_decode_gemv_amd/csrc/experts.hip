@@ -89,13 +89,27 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const float *__restrict
     const int h = (blockIdx.y * kBlock + threadIdx.x) * 4;
     if (h >= H) return;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-        const float wj = w[(size_t)t * k + j];
-        const float4 v = *reinterpret_cast<const float4 *>(y + ((size_t)t * k + j) * H + h);
-        acc.x = fmaf(wj, v.x, acc.x);
-        acc.y = fmaf(wj, v.y, acc.y);
-        acc.z = fmaf(wj, v.z, acc.z);
-        acc.w = fmaf(wj, v.w, acc.w);
+    // routes in groups of 8 with every load of a group issued before its
+    // FMAs (j ascending): one memory round trip per group, not per route
+    constexpr int kG = 8;
+    for (int j0 = 0; j0 < k; j0 += kG) {
+        float wj[kG];
+        float4 v[kG];
+#pragma unroll
+        for (int u = 0; u < kG; ++u) {
+            const int j = min(j0 + u, k - 1);
+            wj[u] = w[(size_t)t * k + j];
+            v[u] = *reinterpret_cast<const float4 *>(y + ((size_t)t * k + j) * H + h);
+        }
+#pragma unroll
+        for (int u = 0; u < kG; ++u) {
+            if (j0 + u < k) {
+                acc.x = fmaf(wj[u], v[u].x, acc.x);
+                acc.y = fmaf(wj[u], v[u].y, acc.y);
+                acc.z = fmaf(wj[u], v[u].z, acc.z);
+                acc.w = fmaf(wj[u], v[u].w, acc.w);
+            }
+        }
     }
     if (xres) {
         const float4 r = *reinterpret_cast<const float4 *>(xres + (size_t)t * H + h);

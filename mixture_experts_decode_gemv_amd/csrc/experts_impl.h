@@ -12,6 +12,8 @@
 // every walk gives bitwise the same result.
 #pragma once
 
+#include <limits.h>
+
 #include <type_traits>
 
 #include "common.h"
@@ -70,6 +72,47 @@ __device__ __forceinline__ int segment_route_uniform(const SegArgs &sa, int firs
 __device__ __forceinline__ int segment_count(const SegArgs &sa) {
     const int n = sa.grouped ? *sa.n_uniq : sa.R;
     return n > 0 ? n : 0;
+}
+
+// The segment count and segment s for a workgroup's first item, with as few
+// dependent scalar round trips as possible before its weight loads can be
+// issued: n_uniq and uniq[s] are read together.  When no segment is left to
+// the MFMA kernels (every unique expert has at least one route here), the
+// expert alone addresses the weights: late is set, n is 1 for now, and the
+// caller reads first and n with segment_rest() once the loads are in flight.
+__device__ __forceinline__ int first_segment(const SegArgs &sa, int s, int &e, int &first, int &n, bool &late) {
+    late = false;
+    first = 0;
+    n = 0;
+    e = 0;
+    if (!sa.grouped) {
+        if (s < sa.R) segment(sa, s, e, first, n);
+        return sa.R;
+    }
+    int nu, ev;
+    asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&s"(nu), "=&s"(ev)
+                 : "s"(sa.n_uniq), "s"(sa.uniq + min(s, sa.E - 1))
+                 : "memory");
+    const int nseg = nu > 0 ? nu : 0;
+    if (s < nseg && ev >= 0 && ev < sa.E) {
+        e = ev;
+        if (sa.gemv_below == INT_MAX) {
+            late = true;
+            n = 1;
+        } else {
+            first = load_uniform(sa.offsets + e);
+            n = load_uniform(sa.counts + e);
+            if (n >= sa.gemv_below) n = 0;
+        }
+    }
+    return nseg;
+}
+
+// first and n of a unique expert's segment (after first_segment set late).
+__device__ __forceinline__ void segment_rest(const SegArgs &sa, int e, int &first, int &n) {
+    first = load_uniform(sa.offsets + e);
+    n = load_uniform(sa.counts + e);
 }
 
 // Loads chunk c of slot rows rows[s] (byte pointers of this lane's row), zero
@@ -205,7 +248,6 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(Pass1Args a) {
     const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
     const int H = a.H, I = a.I, nq = H / EPC;
     const int items_per_seg = (I + P * WPB - 1) / (P * WPB);
-    const int n_items = segment_count(a.sa) * items_per_seg;
     const size_t row_bytes = (size_t)H * WT<WDT>::kBytes;
 
     if (a.xb) {  // the MFMA pass 1, launched after this kernel, reads x as bf16
@@ -223,10 +265,12 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(Pass1Args a) {
     // one narrow window of the weights.  The segment of the next item is
     // fetched while the current one is processed.
     int e_nx = 0, first_nx = 0, n_nx = 0;
-    if (blockIdx.x < n_items) segment(a.sa, blockIdx.x / items_per_seg, e_nx, first_nx, n_nx);
+    bool late;
+    const int n_items = first_segment(a.sa, blockIdx.x / items_per_seg, e_nx, first_nx, n_nx, late) * items_per_seg;
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
         const int blk = item % items_per_seg;
-        const int e = e_nx, first = first_nx, n = n_nx;
+        const int e = e_nx;
+        int first = first_nx, n = n_nx;
         const int i0 = (blk * WPB + wv) * P;
         const char *rows[NS];
         bool ok[NS];
@@ -259,6 +303,10 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(Pass1Args a) {
         }
         u32x4 w[NS][NC];
         load_rows<NC, NS, G>(w, rows, ok, nq, lane);
+        if (late) {
+            segment_rest(a.sa, e, first, n);
+            late = false;
+        }
         if (item + gridDim.x < n_items) segment(a.sa, (item + gridDim.x) / items_per_seg, e_nx, first_nx, n_nx);
         // one batch of routes: rows into LDS, then every route of the batch
         // against the wave's rows.  The first batch (the whole segment when
@@ -328,14 +376,15 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Pass2Args a) {
     const int lane = threadIdx.x & (kWave - 1), half = lane / G, wv = threadIdx.x / kWave;
     const int H = a.H, I = a.I, nq = I / EPC;
     const int items_per_seg = (H + NR * WPB - 1) / (NR * WPB);
-    const int n_items = segment_count(a.sa) * items_per_seg;
     const size_t row_bytes = (size_t)I * WT<WDT>::kBytes;
 
     int e_nx = 0, first_nx = 0, n_nx = 0;
-    if (blockIdx.x < n_items) segment(a.sa, blockIdx.x / items_per_seg, e_nx, first_nx, n_nx);
+    bool late;
+    const int n_items = first_segment(a.sa, blockIdx.x / items_per_seg, e_nx, first_nx, n_nx, late) * items_per_seg;
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
         const int blk = item % items_per_seg;
-        const int e = e_nx, first = first_nx, n = n_nx;
+        const int e = e_nx;
+        int first = first_nx, n = n_nx;
         const int h0 = (blk * WPB + wv) * NR;
         // slot j, half hf: row h0 + j * RPS + hf
         const char *rows[NS];
@@ -363,6 +412,10 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Pass2Args a) {
         }
         u32x4 w[NS][NC];
         load_rows<NC, NS, G>(w, rows, ok, nq, lane);
+        if (late) {
+            segment_rest(a.sa, e, first, n);
+            late = false;
+        }
         if (item + gridDim.x < n_items) segment(a.sa, (item + gridDim.x) / items_per_seg, e_nx, first_nx, n_nx);
         auto batch = [&](int m0, int mb) {
             lds_sync();  // every wave is done reading the rows in LDS
