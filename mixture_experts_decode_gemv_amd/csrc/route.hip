@@ -13,13 +13,15 @@
 //    (normalised there first for the RMSNorm form; workgroup eb = 0 also
 //    writes the normalised rows for the expert passes).
 //  * The last workgroup to finish a token tile (per-tile arrival counter)
-//    selects the top k for those tokens, one wave per token.
+//    selects the top k for those tokens, two tokens per wave at once.
 //  * The last tile to be selected (arrival counter over tiles) runs the
 //    counting sort in that workgroup.
 // Nothing waits: a workgroup that is not last simply exits.  The arrival
 // counters are reset by the workgroup that consumed them, so they are zero
 // again when the launch ends (a fresh workspace is zeroed once by
 // moe_workspace_init).
+#include <type_traits>
+
 #include "route_impl.h"
 
 namespace moe {
@@ -195,13 +197,30 @@ __global__ __launch_bounds__(kBlock) void route_kernel(RouteArgs a) {
     // the ids also go to LDS, where the sort below reads them
     const float *lg = a.logits_in ? a.logits_in : a.logits;
     int *lds_ids = a.counts && a.n_tblk == 1 ? reinterpret_cast<int *>(dyn_lds) + sort_lds_ints(E) : nullptr;
-    for (int t = t0 + wave; t < t1; t += kBlock / kWave) {
-        int32_t *li = lds_ids ? lds_ids + (size_t)(t - t0) * a.k : nullptr;
+    // tokens t and t + 4 of a wave together (their chains overlap), then a
+    // last single one
+    constexpr int WPB = kBlock / kWave;
+    auto sel = [&](auto nt_tag, int t) {
+        constexpr int NT = decltype(nt_tag)::value;
+        const float *l[NT];
+        int32_t *ids[NT], *li[NT];
+        float *w[NT];
+#pragma unroll
+        for (int q = 0; q < NT; ++q) {
+            const int tq = t + q * WPB;
+            l[q] = lg + (size_t)tq * E;
+            ids[q] = a.ids + (size_t)tq * a.k;
+            w[q] = a.w + (size_t)tq * a.k;
+            li[q] = lds_ids ? lds_ids + (size_t)(tq - t0) * a.k : nullptr;
+        }
         if (a.logits_in)
-            select_token<false>(lg + (size_t)t * E, E, a.k, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, li, lane);
+            select_tokens<false, NT>(l, E, a.k, ids, w, li, lane);
         else
-            select_token<true>(lg + (size_t)t * E, E, a.k, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, li, lane);
-    }
+            select_tokens<true, NT>(l, E, a.k, ids, w, li, lane);
+    };
+    int t = t0 + wave;
+    for (; t + WPB < t1; t += 2 * WPB) sel(std::integral_constant<int, 2>{}, t);
+    if (t < t1) sel(std::integral_constant<int, 1>{}, t);
     if (!a.counts) return;
     if (a.n_tblk == 1) {
         // one tile: this workgroup selected every token, no second arrival;

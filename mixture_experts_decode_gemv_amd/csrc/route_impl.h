@@ -70,74 +70,103 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
 }
 
-// One wave selects for one token.  l: the token's E logits (COHERENT: written
-// by other workgroups of this launch).  Writes ids[0..k) and w[0..k) with
-// device-scope stores, and the ids also to lds_ids[0..k) when it is set.
-// Each lane sorts its own keys once (descending key, ascending index); a
-// round then takes the wave maximum of the lanes' heads,
-// finds its lane by ballot, and only on an exact tie between lanes runs a
-// second reduction for the lowest index; the winning lane advances its head.
-template <bool COHERENT, int NCS>
-__device__ __forceinline__ void select_token_n(const float *l, int E, int k, int32_t *ids, float *w, int32_t *lds_ids, int lane) {
-    uint32_t key[NCS];
-    uint32_t idx[NCS];
+// One wave selects for NT tokens at once (their chains are independent, so
+// their memory round trips and reduction latencies overlap).  l[q]: token
+// q's E logits (COHERENT: written by other workgroups of this launch).
+// Writes ids[q][0..k) and w[q][0..k) with device-scope stores, and the ids
+// also to lds_ids[q][0..k) when it is set.  Each lane sorts its own keys once
+// (descending key, ascending index); a round then takes the wave maximum of
+// the lanes' heads, finds its lane by ballot, and only on an exact tie
+// between lanes runs a second reduction for the lowest index; the winning
+// lane advances its head.  Every token's result is the same as when it is
+// selected alone.
+template <bool COHERENT, int NCS, int NT>
+__device__ __forceinline__ void select_tokens_n(const float *const (&l)[NT], int E, int k, int32_t *const (&ids)[NT],
+                                                float *const (&w)[NT], int32_t *const (&lds_ids)[NT], int lane) {
+    uint32_t key[NT][NCS];
+    uint32_t idx[NT][NCS];
     const int nc = (E + kWave - 1) / kWave;
     // unconditional loads (index clamped), all in flight at once
 #pragma unroll
-    for (int c = 0; c < NCS; ++c) {
-        const int e = lane + kWave * c;
-        const bool valid = c < nc && e < E;
-        const int ec = min(e, E - 1);
-        const float v = COHERENT ? load_shared(l + ec) : l[ec];
-        key[c] = valid ? logit_key(v) : 0u;  // 0: no expert
-        idx[c] = (uint32_t)e;
-    }
+    for (int q = 0; q < NT; ++q)
+#pragma unroll
+        for (int c = 0; c < NCS; ++c) {
+            const int e = lane + kWave * c;
+            const bool valid = c < nc && e < E;
+            const int ec = min(e, E - 1);
+            const float v = COHERENT ? load_shared(l[q] + ec) : l[q][ec];
+            key[q][c] = valid ? logit_key(v) : 0u;  // 0: no expert
+            idx[q][c] = (uint32_t)e;
+        }
     // per-lane insertion sort, descending key (stable: equal keys keep the
     // ascending index order they were generated in)
 #pragma unroll
-    for (int i = 1; i < NCS; ++i) {
+    for (int q = 0; q < NT; ++q)
 #pragma unroll
-        for (int j = i; j > 0; --j) {
-            if (key[j] > key[j - 1]) {
-                const uint32_t tk = key[j]; key[j] = key[j - 1]; key[j - 1] = tk;
-                const uint32_t ti = idx[j]; idx[j] = idx[j - 1]; idx[j - 1] = ti;
+        for (int i = 1; i < NCS; ++i) {
+#pragma unroll
+            for (int j = i; j > 0; --j) {
+                if (key[q][j] > key[q][j - 1]) {
+                    const uint32_t tk = key[q][j]; key[q][j] = key[q][j - 1]; key[q][j - 1] = tk;
+                    const uint32_t ti = idx[q][j]; idx[q][j] = idx[q][j - 1]; idx[q][j - 1] = ti;
+                }
             }
         }
-    }
-    int head = 0;
-    uint32_t my_key = 0u, my_idx = 0u, top = 0u;
-    for (int j = 0; j < k; ++j) {
-        uint32_t hk = 0u, hi = 0xFFFFFFFFu;
+    int head[NT];
+    uint32_t my_key[NT], my_idx[NT], top[NT];
 #pragma unroll
-        for (int c = 0; c < NCS; ++c)
-            if (c == head) { hk = key[c]; hi = idx[c]; }
-        const uint32_t m = wave_reduce_u32<true>(hk);
-        const unsigned long long holders = __ballot(hk == m);
-        uint32_t win;
-        if (__popcll(holders) == 1) win = (uint32_t)__shfl((int)hi, __ffsll((long long)holders) - 1, kWave);
-        else win = wave_reduce_u32<false>(hk == m ? hi : 0xFFFFFFFFu);
-        if (j == 0) top = m;
-        if (lane == j) { my_key = m; my_idx = win; }
-        if (hi == win) ++head;
+    for (int q = 0; q < NT; ++q) {
+        head[q] = 0;
+        my_key[q] = my_idx[q] = top[q] = 0u;
     }
-    const float p = lane < k ? expf(key_logit(my_key) - key_logit(top)) : 0.f;
-    const float sum = wave_sum_dpp(p);
+    for (int j = 0; j < k; ++j) {
+        uint32_t hk[NT], hi[NT], m[NT];
+#pragma unroll
+        for (int q = 0; q < NT; ++q) {
+            hk[q] = 0u;
+            hi[q] = 0xFFFFFFFFu;
+#pragma unroll
+            for (int c = 0; c < NCS; ++c)
+                if (c == head[q]) { hk[q] = key[q][c]; hi[q] = idx[q][c]; }
+        }
+#pragma unroll
+        for (int q = 0; q < NT; ++q) m[q] = wave_reduce_u32<true>(hk[q]);
+#pragma unroll
+        for (int q = 0; q < NT; ++q) {
+            const unsigned long long holders = __ballot(hk[q] == m[q]);
+            uint32_t win;
+            if (__popcll(holders) == 1) win = (uint32_t)__shfl((int)hi[q], __ffsll((long long)holders) - 1, kWave);
+            else win = wave_reduce_u32<false>(hk[q] == m[q] ? hi[q] : 0xFFFFFFFFu);
+            if (j == 0) top[q] = m[q];
+            if (lane == j) { my_key[q] = m[q]; my_idx[q] = win; }
+            if (hi[q] == win) ++head[q];
+        }
+    }
+    float p[NT], sum[NT];
+#pragma unroll
+    for (int q = 0; q < NT; ++q) p[q] = lane < k ? expf(key_logit(my_key[q]) - key_logit(top[q])) : 0.f;
+#pragma unroll
+    for (int q = 0; q < NT; ++q) sum[q] = wave_sum_dpp(p[q]);
     if (lane < k) {
-        store_shared(ids + lane, (int32_t)my_idx);
-        store_shared(w + lane, p / sum);
-        if (lds_ids) lds_ids[lane] = (int32_t)my_idx;
+#pragma unroll
+        for (int q = 0; q < NT; ++q) {
+            store_shared(ids[q] + lane, (int32_t)my_idx[q]);
+            store_shared(w[q] + lane, p[q] / sum[q]);
+            if (lds_ids[q]) lds_ids[q][lane] = (int32_t)my_idx[q];
+        }
     }
 }
 
 // Logits per lane instantiated for 1, 2, 4, 8 and 16 (E <= 1024).
-template <bool COHERENT>
-__device__ __forceinline__ void select_token(const float *l, int E, int k, int32_t *ids, float *w, int32_t *lds_ids, int lane) {
+template <bool COHERENT, int NT>
+__device__ __forceinline__ void select_tokens(const float *const (&l)[NT], int E, int k, int32_t *const (&ids)[NT],
+                                              float *const (&w)[NT], int32_t *const (&lds_ids)[NT], int lane) {
     const int nc = (E + kWave - 1) / kWave;
-    if (nc <= 1) select_token_n<COHERENT, 1>(l, E, k, ids, w, lds_ids, lane);
-    else if (nc <= 2) select_token_n<COHERENT, 2>(l, E, k, ids, w, lds_ids, lane);
-    else if (nc <= 4) select_token_n<COHERENT, 4>(l, E, k, ids, w, lds_ids, lane);
-    else if (nc <= 8) select_token_n<COHERENT, 8>(l, E, k, ids, w, lds_ids, lane);
-    else select_token_n<COHERENT, 16>(l, E, k, ids, w, lds_ids, lane);
+    if (nc <= 1) select_tokens_n<COHERENT, 1, NT>(l, E, k, ids, w, lds_ids, lane);
+    else if (nc <= 2) select_tokens_n<COHERENT, 2, NT>(l, E, k, ids, w, lds_ids, lane);
+    else if (nc <= 4) select_tokens_n<COHERENT, 4, NT>(l, E, k, ids, w, lds_ids, lane);
+    else if (nc <= 8) select_tokens_n<COHERENT, 8, NT>(l, E, k, ids, w, lds_ids, lane);
+    else select_tokens_n<COHERENT, 16, NT>(l, E, k, ids, w, lds_ids, lane);
 }
 
 // LDS ints needed by sort_block for E experts.
