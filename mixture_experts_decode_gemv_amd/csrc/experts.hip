@@ -119,11 +119,12 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const float *__restrict
 }
 
 // ---- launchers -------------------------------------------------------------------
-// GEMV grids: up to 16 workgroups per CU, of which 4 are resident at a time;
+// GEMV grids: up to 16 workgroups of 256 threads per CU (4096 threads), of
+// which a quarter are resident at a time;
 // the later ones start as the first finish, which evens out the tail (1 %
 // faster than 8 per CU at bs = 64, 2 % at bs = 8).
 static int persistent_grid(long long max_items) {
-    const long long cap = (long long)num_cus() * 16;
+    const long long cap = (long long)num_cus() * (16 * 256 / kGemvBlock);
     long long g = max_items < cap ? max_items : cap;
     return (int)(g < 1 ? 1 : g);
 }
@@ -184,7 +185,7 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
                      xb_first ? static_cast<uint32_t *>(xb) : nullptr, lds_batch_rows(L.H)};
         const int nq1 = L.H / epc;
         const int nc1 = nc_instance((nq1 + kWave - 1) / kWave);
-        const int pairs = slots_for(nc1) / 2 * (kBlock / kWave);  // per workgroup item
+        const int pairs = slots_for(nc1) / 2 * (kGemvBlock / kWave);  // per workgroup item
         const long long items1 = (long long)(p1.sa.grouped ? max_uniq : R) * ((L.I + pairs - 1) / pairs);
         switch (L.expert_dtype) {
             case MOE_F32: return launch_pass1<MOE_F32>(nc1, persistent_grid(items1), s, p1);
@@ -214,7 +215,7 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
         const int nq2 = L.I / epc;
         const int lanes = pass2_lanes(nq2);
         const int nc2 = nc_instance((nq2 + lanes - 1) / lanes);
-        const int rows2 = slots_for(nc2) * (kWave / lanes) * (kBlock / kWave);  // per workgroup item
+        const int rows2 = slots_for(nc2) * (kWave / lanes) * (kGemvBlock / kWave);  // per workgroup item
         const long long items2 = (long long)(p2.sa.grouped ? max_uniq : R) * ((L.H + rows2 - 1) / rows2);
         switch (L.expert_dtype) {
             case MOE_F32: return launch_pass2<MOE_F32>(nc2, lanes, persistent_grid(items2), s, p2);

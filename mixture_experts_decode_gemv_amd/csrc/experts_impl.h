@@ -139,6 +139,9 @@ __device__ __forceinline__ void load_rows(u32x4 (&w)[NS][NC], const char *const 
 // carry more x than weight traffic through the CU's vector memory path and
 // the weight stream slows down.
 
+// Threads per workgroup of the GEMV passes.
+constexpr int kGemvBlock = 256;
+
 // Issue the loads of rows m = 0..mb-1 (global rows src(m) of q4 float4s)
 // into LDS rows of q4 float4s at xl; the caller waits (vmcnt(0)) and syncs.
 template <typename RowOf>
@@ -146,7 +149,7 @@ __device__ __forceinline__ void stage_rows_lds(float4 *xl, int mb, int q4, RowOf
     const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
     for (int m = 0; m < mb; ++m) {
         const float4 *src = row_of(m);  // m is uniform: route lookups may shuffle
-        for (int u0 = wv * kWave; u0 < q4; u0 += kBlock)
+        for (int u0 = wv * kWave; u0 < q4; u0 += kGemvBlock)
             if (u0 + lane < q4)
                 __builtin_amdgcn_global_load_lds(static_cast<const void *>(src + u0 + lane),
                                                  (__attribute__((address_space(3))) void *)(xl + m * q4 + u0), 16, 0,
@@ -215,10 +218,10 @@ __device__ __forceinline__ void dot_rows(u32x4 (&w)[NS][NC], const float (&sc)[N
 // Slots per wave for NC chunks per lane: 32 to 64 VGPRs of weights.
 __host__ __device__ constexpr int slots_for(int nc) { return nc <= 2 ? 8 : 4; }
 
-// Routes staged per LDS batch for rows of K floats: 32 KiB of LDS per
-// workgroup, at most 16 rows.
+// Routes staged per LDS batch for rows of K floats: 32 KiB of LDS per 4
+// waves of a workgroup, at most 16 rows.
 inline int lds_batch_rows(int K) {
-    const int nb = (32 * 1024) / (K * 4);
+    const int nb = (32 * 1024 * (kGemvBlock / 256)) / (K * 4);
     return nb < 1 ? 1 : nb > 16 ? 16 : nb;
 }
 
@@ -238,13 +241,13 @@ struct Pass1Args {
 };
 
 template <int WDT, int NC>
-__global__ __launch_bounds__(kBlock) void pass1_kernel(Pass1Args a) {
+__global__ __launch_bounds__(kGemvBlock) void pass1_kernel(Pass1Args a) {
     extern __shared__ float4 xl[];  // nb rows of H floats
     constexpr int G = kWave;
     constexpr int NS = slots_for(NC);
     constexpr int P = NS / 2;  // gate/up pairs per wave
     constexpr int EPC = WT<WDT>::kEpc;
-    constexpr int WPB = kBlock / kWave;
+    constexpr int WPB = kGemvBlock / kWave;
     const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
     const int H = a.H, I = a.I, nq = H / EPC;
     const int items_per_seg = (I + P * WPB - 1) / (P * WPB);
@@ -255,7 +258,7 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(Pass1Args a) {
         // stored as float-typed words: no store of this kernel may alias the
         // int32 routing arrays, whose wave-uniform loads can then be scalar
         float *xb = reinterpret_cast<float *>(a.xb);
-        for (int i = blockIdx.x * kBlock + threadIdx.x; i < npairs; i += gridDim.x * kBlock) {
+        for (int i = blockIdx.x * kGemvBlock + threadIdx.x; i < npairs; i += gridDim.x * kGemvBlock) {
             const float2 v = reinterpret_cast<const float2 *>(a.x)[i];
             xb[i] = __uint_as_float(bf16_pair_rne(v.x, v.y));
         }
@@ -366,13 +369,13 @@ struct Pass2Args {
 };
 
 template <int WDT, int NC, int G>
-__global__ __launch_bounds__(kBlock) void pass2_kernel(Pass2Args a) {
+__global__ __launch_bounds__(kGemvBlock) void pass2_kernel(Pass2Args a) {
     extern __shared__ float4 xl[];  // nb rows of I floats
     constexpr int NS = slots_for(NC);
     constexpr int RPS = kWave / G;  // rows per slot
     constexpr int NR = NS * RPS;    // rows per wave
     constexpr int EPC = WT<WDT>::kEpc;
-    constexpr int WPB = kBlock / kWave;
+    constexpr int WPB = kGemvBlock / kWave;
     const int lane = threadIdx.x & (kWave - 1), half = lane / G, wv = threadIdx.x / kWave;
     const int H = a.H, I = a.I, nq = I / EPC;
     const int items_per_seg = (H + NR * WPB - 1) / (NR * WPB);
@@ -467,7 +470,7 @@ inline int pass2_lanes(int nq) { return (nq % 64 != 0 && nq % 32 == 0) ? 32 : 64
 template <int WDT>
 hipError_t launch_pass1(int nc, int grid, hipStream_t st, const Pass1Args &a) {
     const size_t lds = (size_t)a.nb * a.H * 4;
-#define MOE_P1(N) hipLaunchKernelGGL((pass1_kernel<WDT, N>), dim3(grid), dim3(kBlock), lds, st, a)
+#define MOE_P1(N) hipLaunchKernelGGL((pass1_kernel<WDT, N>), dim3(grid), dim3(kGemvBlock), lds, st, a)
     switch (nc_instance(nc)) {
         case 1: MOE_P1(1); break;
         case 2: MOE_P1(2); break;
@@ -483,7 +486,7 @@ hipError_t launch_pass1(int nc, int grid, hipStream_t st, const Pass1Args &a) {
 template <int WDT>
 hipError_t launch_pass2(int nc, int lanes, int grid, hipStream_t st, const Pass2Args &a) {
     const size_t lds = (size_t)a.nb * a.I * 4;
-#define MOE_P2(N, L) hipLaunchKernelGGL((pass2_kernel<WDT, N, L>), dim3(grid), dim3(kBlock), lds, st, a)
+#define MOE_P2(N, L) hipLaunchKernelGGL((pass2_kernel<WDT, N, L>), dim3(grid), dim3(kGemvBlock), lds, st, a)
     if (lanes == 32) {
         switch (nc_instance(nc)) {
             case 1: MOE_P2(1, 32); break;
