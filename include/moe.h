@@ -170,6 +170,18 @@ moe_status moe_layer_routing(const moe_layer_t *layer, int32_t T, void *ws, size
                              float **topk_w, int32_t **counts, int32_t **offsets, int32_t **sorted_routes,
                              int32_t **uniq, int32_t **n_uniq);
 
+/* Expert-usage telemetry: hist[e] += counts[e] for e < E, on `stream`, with
+ * hist a caller-owned device array of E uint64 counters (8-byte aligned) that
+ * accumulates across calls; nothing is added when *n_uniq < 0 (the sort
+ * rejected the routing).  counts and n_uniq are the outputs of moe_sort, or
+ * the addresses moe_layer_routing returns after a moe_layer_fwd call, so a
+ * recorded graph can add each layer's usage after its forward.
+ * "MoE Performance Optimization Analysis", Option 3 (expert caching) and
+ * Phase 3: track per-layer expert usage.  Errors: NULL pointer or E < 1
+ * (MOE_ERR_ARG), E > 1024 (MOE_ERR_SHAPE), misaligned hist (MOE_ERR_ALIGN). */
+moe_status moe_expert_usage(const int32_t *counts, const int32_t *n_uniq, int32_t E, uint64_t *hist,
+                            void *stream);
+
 /* Static text for a status code. */
 const char *moe_status_str(moe_status status);
 

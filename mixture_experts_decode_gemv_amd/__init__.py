@@ -6,9 +6,11 @@ used for device memory and streams.  There is no fallback: if the library is
 missing or fails to load, importing the functions raises.
 
 Entry points (same names as ``include/moe.h``): ``moe_workspace_bytes``,
-``moe_route``, ``moe_sort``, ``moe_expert_fwd``, ``moe_layer_fwd``,
-``moe_layer_fwd_events``, ``moe_layer_routing``, ``moe_status_str``.  Tensor arguments may be torch tensors (their
-``data_ptr()`` is passed), raw integer device addresses or None (NULL).
+``moe_workspace_init``, ``moe_route``, ``moe_sort``, ``moe_expert_fwd``,
+``moe_layer_fwd``, ``moe_layer_fwd_events``, ``moe_layer_routing``,
+``moe_expert_usage``, ``moe_status_str``.  Tensor arguments may be torch
+tensors (their ``data_ptr()`` is passed), raw integer device addresses or
+None (NULL).
 """
 from __future__ import annotations
 
@@ -28,7 +30,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE",
           5: "MOE_ERR_HIP", 6: "MOE_ERR_UNSUPPORTED", 7: "MOE_ERR_ALIGN"}
 
 EXPORTS = ("moe_workspace_bytes", "moe_workspace_init", "moe_route", "moe_sort", "moe_expert_fwd", "moe_layer_fwd",
-           "moe_layer_fwd_events", "moe_layer_routing", "moe_status_str")
+           "moe_layer_fwd_events", "moe_layer_routing", "moe_expert_usage", "moe_status_str")
 
 MOE_N_STAGES = 6
 STAGES = ("routing", "pass1_gemv", "pass1_mfma", "pass2_gemv", "pass2_mfma", "combine")
@@ -76,6 +78,8 @@ def lib():
         pp = ctypes.POINTER(ctypes.c_void_p)
         L.moe_layer_routing.restype = ctypes.c_int
         L.moe_layer_routing.argtypes = [P, i32, vp, sz, pp, pp, pp, pp, pp, pp, pp]
+        L.moe_expert_usage.restype = ctypes.c_int
+        L.moe_expert_usage.argtypes = [vp, vp, i32, vp, vp]
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_status_str.argtypes = [ctypes.c_int]
         _lib = L
@@ -166,6 +170,11 @@ def moe_layer_routing(layer, T, ws, ws_bytes) -> dict:
     _check("moe_layer_routing", lib().moe_layer_routing(ctypes.byref(layer), int(T), _p(ws), int(ws_bytes),
                                                         *[ctypes.byref(p) for p in ptrs]))
     return {n: p.value for n, p in zip(ROUTING_FIELDS, ptrs)}
+
+
+def moe_expert_usage(counts, n_uniq, E, hist, stream=None):
+    """hist[e] += counts[e] (uint64 device counters), skipped when *n_uniq < 0."""
+    _check("moe_expert_usage", lib().moe_expert_usage(_p(counts), _p(n_uniq), int(E), _p(hist), _s(stream)))
 
 
 class DeviceLayer:

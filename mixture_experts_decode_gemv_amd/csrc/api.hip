@@ -208,6 +208,16 @@ moe_status moe_layer_routing(const moe_layer_t *layer, int32_t T, void *ws, size
     return MOE_OK;
 }
 
+moe_status moe_expert_usage(const int32_t *counts, const int32_t *n_uniq, int32_t E, uint64_t *hist,
+                            void *stream) {
+    if (!counts || !n_uniq || !hist) return MOE_ERR_ARG;
+    if (E < 1) return MOE_ERR_ARG;
+    if (E > kMaxE) return MOE_ERR_SHAPE;
+    if (((uintptr_t)hist & 7u) != 0) return MOE_ERR_ALIGN;
+    return hip_status(launch_usage(counts, n_uniq, E, reinterpret_cast<unsigned long long *>(hist),
+                                   (hipStream_t)stream));
+}
+
 const char *moe_status_str(moe_status status) {
     switch (status) {
         case MOE_OK: return "ok";

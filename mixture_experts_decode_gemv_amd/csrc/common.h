@@ -309,6 +309,8 @@ hipError_t launch_route(const moe_layer_t &L, const float *x, const float *logit
 hipError_t launch_sort(const int32_t *ids, int R, int E, int32_t *counts, int32_t *offsets, int32_t *sorted,
                        int32_t *uniq, int32_t *n_uniq, hipStream_t st);
 hipError_t launch_zero(unsigned *p, int n, hipStream_t st);
+hipError_t launch_usage(const int32_t *counts, const int32_t *n_uniq, int E, unsigned long long *hist,
+                        hipStream_t st);
 
 struct Routing {
     const int32_t *ids, *counts, *offsets, *sorted, *uniq, *n_uniq;

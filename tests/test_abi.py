@@ -116,3 +116,13 @@ def test_workspace_data_starts_at_a_fixed_offset_for_every_batch():
     moe.moe_layer_routing(L, big, 0x10000, n)
     with pytest.raises(moe.MoeError):
         moe.moe_layer_routing(L, big + 1, 0x10000, n)
+
+
+def test_expert_usage_argument_errors():
+    lib = moe.lib()
+    assert lib.moe_expert_usage(None, 0x200, 8, 0x300, None) == 1
+    assert lib.moe_expert_usage(0x100, None, 8, 0x300, None) == 1
+    assert lib.moe_expert_usage(0x100, 0x200, 8, None, None) == 1
+    assert lib.moe_expert_usage(0x100, 0x200, 0, 0x300, None) == 1
+    assert lib.moe_expert_usage(0x100, 0x200, 2000, 0x300, None) == 2
+    assert lib.moe_expert_usage(0x100, 0x200, 8, 0x304, None) == 7
