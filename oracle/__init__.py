@@ -55,6 +55,10 @@ def lib():
         L.oracle_bf16_value.argtypes = [ctypes.c_uint16]
         L.oracle_e4m3_value.restype = dbl
         L.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.oracle_e2m1_value.restype = dbl
+        L.oracle_e2m1_value.argtypes = [ctypes.c_uint8]
+        L.oracle_e8m0_value.restype = dbl
+        L.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
         L.oracle_rmsnorm.restype = None
         L.oracle_rmsnorm.argtypes = [i32, i32, vp, dbl, vp]
         L.oracle_router_logits.restype = None
@@ -91,9 +95,9 @@ class Layer:
     """Weights of one layer, as host arrays, bound into the C struct.
 
     ``w`` holds ``w_router``, ``w_gate_up``, ``w_down`` (fp32 arrays, bf16 as
-    uint16 bit patterns or E4M3 codes as uint8) and ``s_gate_up``/``s_down``
-    (fp8 block scales) plus ``spec`` (E, top_k, H, I, expert_dtype,
-    router_dtype).
+    uint16 bit patterns, E4M3 codes as uint8, or MXFP4 codes packed two per
+    byte) and ``s_gate_up``/``s_down`` (fp8 block scales, or MXFP4 E8M0 scale
+    bytes) plus ``spec`` (E, top_k, H, I, expert_dtype, router_dtype).
     """
 
     def __init__(self, w: dict, router_bias=None):
@@ -122,6 +126,14 @@ def bf16_value(b: int) -> float:
 
 def e4m3_value(c: int) -> float:
     return lib().oracle_e4m3_value(int(c))
+
+
+def e2m1_value(c: int) -> float:
+    return lib().oracle_e2m1_value(int(c))
+
+
+def e8m0_value(s: int) -> float:
+    return lib().oracle_e8m0_value(int(s))
 
 
 def rmsnorm(x, eps=RMS_EPS):

@@ -9,7 +9,10 @@
  * Every sum is accumulated in double in ascending index order; outputs are
  * returned in double.  Weights are decoded exactly to double first: fp32 as
  * is, bf16 as the upper half of an fp32 bit pattern, OCP E4M3 from its bit
- * fields times the fp32 scale of its 128x128 block.
+ * fields times the fp32 scale of its 128x128 block, and MXFP4 (OCP
+ * microscaling: E2M1 elements, two per byte with the first in the low
+ * nibble, sharing an E8M0 scale per block of 32 along a row) from its bit
+ * fields times 2^(scale - 127).
  *
  * Sources (page title, section):
  *  - "MoE Performance Optimization Analysis" (markbaseengine), Root Cause:
@@ -38,7 +41,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8 = 2 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8 = 2, OR_MXFP4 = 3 };
 enum { OR_RMSNORM = 1, OR_RESIDUAL = 2 };
 
 typedef struct {
@@ -47,8 +50,8 @@ typedef struct {
     const void *w_router;     /* [E, H]                          */
     const void *w_gate_up;    /* [E, 2I, H]                      */
     const void *w_down;       /* [E, H, I]                       */
-    const float *s_gate_up;   /* fp8 only: [E, 2I/128, H/128]    */
-    const float *s_down;      /* fp8 only: [E, H/128, I/128]     */
+    const void *s_gate_up;    /* fp8: float [E, 2I/128, H/128]; mxfp4: uint8 [E, 2I, H/32] */
+    const void *s_down;       /* fp8: float [E, H/128, I/128];  mxfp4: uint8 [E, H, I/32]  */
     const float *router_bias; /* [E] or NULL                     */
 } oracle_layer;
 
@@ -70,19 +73,38 @@ double oracle_e4m3_value(uint8_t c) {
     return s ? -mag : mag;
 }
 
-static double decode(int dtype, const void *base, size_t idx) {
+/* OCP E2M1 (MX element): sign, 2 exponent bits (bias 1), 1 mantissa bit;
+ * exponent 0 is subnormal (m * 2^-1); no infinities or NaN. */
+double oracle_e2m1_value(uint8_t c) {
+    int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+    double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -mag : mag;
+}
+
+/* OCP E8M0 (MX shared scale): 2^(s - 127); 255 is NaN. */
+double oracle_e8m0_value(uint8_t s) { return s == 255 ? NAN : ldexp(1.0, (int)s - 127); }
+
+/* Element idx of a row-major matrix (idx = row * cols + col).  MXFP4: the
+ * code is nibble (idx & 1) of byte idx / 2, its scale byte idx / 32 (cols is
+ * a multiple of 32, so the blocks of 32 never cross a row). */
+static double decode(int dtype, const void *base, const void *scales, size_t idx) {
     if (dtype == OR_F32) return (double)((const float *)base)[idx];
     if (dtype == OR_BF16) return oracle_bf16_value(((const uint16_t *)base)[idx]);
+    if (dtype == OR_MXFP4) {
+        const uint8_t b = ((const uint8_t *)base)[idx / 2];
+        return oracle_e2m1_value((idx & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 15)) *
+               oracle_e8m0_value(((const uint8_t *)scales)[idx / 32]);
+    }
     return oracle_e4m3_value(((const uint8_t *)base)[idx]);
 }
 
 /* gate_up[e][row][h], row < 2I */
 static double w_gu(const oracle_layer *L, int e, int row, int h) {
     size_t idx = ((size_t)e * 2 * L->I + row) * L->H + h;
-    double v = decode(L->expert_dtype, L->w_gate_up, idx);
+    double v = decode(L->expert_dtype, L->w_gate_up, L->s_gate_up, idx);
     if (L->expert_dtype == OR_FP8) {
         size_t sb = ((size_t)e * (2 * L->I / 128) + row / 128) * (L->H / 128) + h / 128;
-        v *= (double)L->s_gate_up[sb];
+        v *= (double)((const float *)L->s_gate_up)[sb];
     }
     return v;
 }
@@ -90,10 +112,10 @@ static double w_gu(const oracle_layer *L, int e, int row, int h) {
 /* down[e][h][i] */
 static double w_dn(const oracle_layer *L, int e, int h, int i) {
     size_t idx = ((size_t)e * L->H + h) * L->I + i;
-    double v = decode(L->expert_dtype, L->w_down, idx);
+    double v = decode(L->expert_dtype, L->w_down, L->s_down, idx);
     if (L->expert_dtype == OR_FP8) {
         size_t sb = ((size_t)e * (L->H / 128) + h / 128) * (L->I / 128) + i / 128;
-        v *= (double)L->s_down[sb];
+        v *= (double)((const float *)L->s_down)[sb];
     }
     return v;
 }
@@ -102,7 +124,9 @@ int oracle_check_layer(const oracle_layer *L) {
     if (!L || L->E < 1 || L->top_k < 1 || L->top_k > L->E || L->H < 1 || L->I < 1) return 1;
     if (!L->w_router || !L->w_gate_up || !L->w_down) return 1;
     if (L->expert_dtype == OR_FP8 && (L->H % 128 || L->I % 128 || !L->s_gate_up || !L->s_down)) return 1;
-    if (L->router_dtype == OR_FP8) return 1;
+    if (L->expert_dtype == OR_MXFP4 && (L->H % 32 || L->I % 32 || !L->s_gate_up || !L->s_down)) return 1;
+    if (L->expert_dtype < OR_F32 || L->expert_dtype > OR_MXFP4) return 1;
+    if (L->router_dtype != OR_F32 && L->router_dtype != OR_BF16) return 1;
     return 0;
 }
 
@@ -124,7 +148,7 @@ void oracle_router_logits(const oracle_layer *L, int T, const double *x, double 
         for (int e = 0; e < L->E; ++e) {
             double acc = 0.0;
             for (int h = 0; h < L->H; ++h)
-                acc += decode(L->router_dtype, L->w_router, (size_t)e * L->H + h) * x[(size_t)t * L->H + h];
+                acc += decode(L->router_dtype, L->w_router, NULL, (size_t)e * L->H + h) * x[(size_t)t * L->H + h];
             if (L->router_bias) acc += (double)L->router_bias[e];
             logits[(size_t)t * L->E + e] = acc;
         }

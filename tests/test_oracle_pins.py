@@ -415,3 +415,73 @@ def test_e4m3_encoder_is_nearest_code():
         dv = oracle.e4m3_value(c)
         assert abs(min(abs(v), 448.0) - abs(dv)) <= np.min(np.abs(mags - min(abs(v), 448.0))) + 1e-15
         assert (dv < 0) == (v < 0) or dv == 0
+
+
+# ------------------------------------------------------------------- MXFP4 --
+
+def _e2m1_table():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "e2m1_values.txt")) if l.strip() and not l.startswith("#")]
+    return {int(c): float(v) for c, v in rows[1:]}
+
+
+def test_e2m1_decode_all_codes_match_the_specification_table():
+    tab = _e2m1_table()
+    assert sorted(tab) == list(range(16))
+    for c, v in tab.items():
+        got = oracle.e2m1_value(c)
+        assert got == v and np.signbit(got) == np.signbit(v), c
+
+
+def test_e8m0_decode_all_codes_match_torch():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    got = np.array([oracle.e8m0_value(s) for s in range(256)])
+    assert np.array_equal(got[:255], ref[:255])
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+
+
+def _mx_decode(q, s):
+    """MXFP4 [rows, cols/2] codes and [rows, cols/32] scale bytes to float64,
+    from the specification table and torch's E8M0 decode."""
+    tab = np.array([_e2m1_table()[c] for c in range(16)])
+    codes = np.stack([q & 15, q >> 4], axis=-1).reshape(q.shape[0], -1)
+    sc = torch.from_numpy(np.ascontiguousarray(s)).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    return tab[codes] * np.repeat(sc, 32, axis=1)
+
+
+def test_mxfp4_expert_matches_table_decode():
+    """MXFP4 experts (E2M1 codes, E8M0 scale per 32 elements along a row):
+    decode with the specification table and torch's E8M0, run the textbook
+    SwiGLU; a transposed or misaligned nibble or scale index fails this."""
+    spec = wl.LayerSpec(E=2, top_k=1, H=96, I=64, expert_dtype=wl.MXFP4, router_dtype=wl.BF16)
+    w = wl.make_layer(spec)
+    x = wl.make_x(3, spec.H)
+    L = oracle.Layer(w)
+    ids = np.array([[1], [0], [1]], np.int32)
+    got = oracle.expert_fwd(L, x, ids, np.ones((3, 1)))
+    for t in range(3):
+        e = ids[t, 0]
+        ref = _torch_swiglu(x[t:t + 1], _mx_decode(w["w_gate_up"][e], w["s_gate_up"][e]),
+                            _mx_decode(w["w_down"][e], w["s_down"][e]))
+        assert np.allclose(got[t], ref[0], rtol=1e-12, atol=1e-12)
+
+
+def test_mxfp4_generator_scales_and_codes():
+    """The generator's blocks: scale 2^(floor(log2 amax) - 2), every code the
+    nearest E2M1 value of w / scale (saturating at 6), ties to the even code."""
+    k = wl.key(0, 0, 1)
+    q, s = wl.mxfp4_matrices(k, 1, 8, 128, 0.1)
+    src = wl.normal_f32(k, 8 * 128, 1.0).astype(np.float64).reshape(8, 128) * 0.1
+    dec = _mx_decode(q[0], s[0])
+    tab = np.array(sorted(set(abs(v) for v in _e2m1_table().values())))
+    for r in range(8):
+        for b in range(4):
+            blk = src[r, 32 * b:32 * b + 32]
+            scale = 2.0 ** (np.floor(np.log2(np.abs(blk).max())) - 2)
+            assert int(s[0, r, b]) == int(np.log2(scale)) + 127
+            for c in range(32):
+                a = min(abs(blk[c]) / scale, 6.0)
+                best = np.min(np.abs(tab - a))
+                assert abs(abs(dec[r, 32 * b + c]) / scale - a) <= best + 1e-12
+    for v in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0):  # exact ties go to the even code
+        c = wl.e2m1_encode(v)
+        assert c % 2 == 0, (v, c)

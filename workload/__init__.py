@@ -39,8 +39,8 @@ SEED_X = 1          # + draw index
 SEED_ZIPF_PERM = 2
 SEED_LOGITS = 3     # + draw index (selection fed straight from i.i.d. N(0,1) logits)
 
-F32, BF16, FP8 = 0, 1, 2
-DTYPE_NAMES = {F32: "f32", BF16: "bf16", FP8: "fp8_e4m3"}
+F32, BF16, FP8, MXFP4 = 0, 1, 2, 3
+DTYPE_NAMES = {F32: "f32", BF16: "bf16", FP8: "fp8_e4m3", MXFP4: "mxfp4"}
 
 
 def build(force: bool = False) -> str:
@@ -70,6 +70,10 @@ def lib():
         L.moegen_normal_bf16.argtypes = [u64, u64, u64, dbl, vp, i32]
         L.moegen_fp8_matrix.restype = i32
         L.moegen_fp8_matrix.argtypes = [u64, u64, i32, i32, dbl, vp, vp, i32]
+        L.moegen_mxfp4_matrix.restype = i32
+        L.moegen_mxfp4_matrix.argtypes = [u64, u64, i32, i32, dbl, vp, vp, i32]
+        L.moegen_e2m1_encode.restype = ctypes.c_uint8
+        L.moegen_e2m1_encode.argtypes = [dbl]
         L.moegen_permutation.restype = None
         L.moegen_permutation.argtypes = [u64, i32, vp]
         L.moegen_normal_one.restype = dbl
@@ -114,6 +118,24 @@ def fp8_matrices(k: int, count: int, rows: int, cols: int, sigma: float, nthread
     return q, s
 
 
+def mxfp4_matrices(k: int, count: int, rows: int, cols: int, sigma: float, nthreads: int | None = None):
+    """``count`` consecutive [rows, cols] matrices of one stream as MXFP4:
+    (codes uint8 [count, rows, cols/2], two per byte with the even element in
+    the low nibble; E8M0 scale bytes uint8 [count, rows, cols/32])."""
+    q = np.empty((count, rows, cols // 2), dtype=np.uint8)
+    s = np.empty((count, rows, cols // 32), dtype=np.uint8)
+    for c in range(count):
+        rc = lib().moegen_mxfp4_matrix(k, c * rows * cols, rows, cols, sigma, q[c].ctypes.data, s[c].ctypes.data,
+                                       nthreads or default_threads())
+        if rc != 0:
+            raise ValueError("mxfp4 matrices need cols that are a multiple of 32")
+    return q, s
+
+
+def e2m1_encode(v: float) -> int:
+    return int(lib().moegen_e2m1_encode(float(v)))
+
+
 def e4m3_encode(v: float) -> int:
     return int(lib().moegen_e4m3_encode(float(v)))
 
@@ -144,17 +166,19 @@ def _dt_array(k, n, sigma, dtype, nthreads):
 
 def make_layer(spec: LayerSpec, layer: int = 0, seed: int = SEED_WEIGHTS, nthreads: int | None = None,
                experts: bool = True) -> dict:
-    """Weights of one layer as host arrays (bf16 as uint16 bit patterns, fp8 as uint8 codes)."""
+    """Weights of one layer as host arrays (bf16 as uint16 bit patterns, fp8 as uint8 codes, MXFP4 as packed
+    uint8 codes with E8M0 scale bytes)."""
     E, H, I = spec.E, spec.H, spec.I
     sh, si = 1.0 / math.sqrt(H), 1.0 / math.sqrt(I)
     out = {"spec": spec}
     out["w_router"] = _dt_array(key(seed, layer, T_ROUTER), E * H, sh, spec.router_dtype, nthreads).reshape(E, H)
     if not experts:
         return out
-    if spec.expert_dtype == FP8:
-        q, s = fp8_matrices(key(seed, layer, T_GATE_UP), E, 2 * I, H, sh, nthreads)
+    if spec.expert_dtype in (FP8, MXFP4):
+        mats = fp8_matrices if spec.expert_dtype == FP8 else mxfp4_matrices
+        q, s = mats(key(seed, layer, T_GATE_UP), E, 2 * I, H, sh, nthreads)
         out["w_gate_up"], out["s_gate_up"] = q, s
-        q, s = fp8_matrices(key(seed, layer, T_DOWN), E, H, I, si, nthreads)
+        q, s = mats(key(seed, layer, T_DOWN), E, H, I, si, nthreads)
         out["w_down"], out["s_down"] = q, s
     else:
         out["w_gate_up"] = _dt_array(key(seed, layer, T_GATE_UP), E * 2 * I * H, sh, spec.expert_dtype,

@@ -221,6 +221,84 @@ int moegen_fp8_matrix(uint64_t key, uint64_t start, int rows, int cols, double s
     return 0;
 }
 
+/* ---- MXFP4 (OCP microscaling: E2M1 elements, E8M0 scale per 32) -------- */
+static const double e2m1_mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+/* Nearest E2M1 code to v, ties to the even code, |v| >= 6 saturates. */
+static uint8_t e2m1_encode(double v) {
+    uint8_t sign = (v < 0 || (v == 0 && signbit(v))) ? 8 : 0;
+    double a = fabs(v);
+    if (!(a < 6.0)) return sign | 7;
+    int lo = 0;
+    while (lo < 6 && e2m1_mag[lo + 1] <= a) ++lo;
+    int hi = lo + 1;
+    double dlo = a - e2m1_mag[lo], dhi = e2m1_mag[hi] - a;
+    int c = dlo < dhi ? lo : dhi < dlo ? hi : ((lo & 1) ? hi : lo);
+    return sign | (uint8_t)c;
+}
+
+typedef struct {
+    uint64_t key, start;
+    int cols;
+    int64_t blk_lo, blk_hi;
+    double sigma;
+    uint8_t *q, *scales;
+} mx_job;
+
+static void *mx_worker(void *arg) {
+    mx_job *j = (mx_job *)arg;
+    double w[32];
+    for (int64_t b = j->blk_lo; b < j->blk_hi; ++b) {
+        double amax = 0.0;
+        for (int c = 0; c < 32; ++c) {
+            w[c] = j->sigma * normal_at(j->key, j->start + (uint64_t)b * 32 + (uint64_t)c);
+            if (fabs(w[c]) > amax) amax = fabs(w[c]);
+        }
+        /* shared exponent: floor(log2(amax)) minus the largest E2M1
+         * exponent (2), clamped to the E8M0 range */
+        int se = 0;
+        if (amax > 0.0) {
+            int ex;
+            frexp(amax, &ex); /* amax = f * 2^ex, f in [0.5, 1) */
+            se = (ex - 1) - 2;
+        }
+        if (se < -127) se = -127;
+        if (se > 127) se = 127;
+        j->scales[b] = (uint8_t)(se + 127);
+        for (int c = 0; c < 32; c += 2) {
+            uint8_t lo = e2m1_encode(ldexp(w[c], -se)), hi = e2m1_encode(ldexp(w[c + 1], -se));
+            j->q[b * 16 + c / 2] = (uint8_t)(lo | (hi << 4));
+        }
+    }
+    return NULL;
+}
+
+/*
+ * One [rows, cols] matrix (cols a multiple of 32) whose element (r, c) is
+ * sigma * z_{start + r*cols + c}, encoded as MXFP4: codes two per byte
+ * (q[(r*cols + c)/2], element c even in the low nibble) and one E8M0 scale
+ * byte per block of 32 along a row (scales[(r*cols + c)/32]).  The scale is
+ * 2^(floor(log2 amax) - 2); codes are the nearest E2M1 values of w / scale.
+ */
+int moegen_mxfp4_matrix(uint64_t key, uint64_t start, int rows, int cols, double sigma, uint8_t *q,
+                        uint8_t *scales, int nthreads) {
+    if (cols % 32 || rows <= 0 || cols <= 0) return 1;
+    int64_t nblk = (int64_t)rows * cols / 32;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (nthreads > nblk) nthreads = (int)nblk;
+    mx_job jobs[256];
+    pthread_t th[256];
+    for (int t = 0; t < nthreads; ++t)
+        jobs[t] = (mx_job){key, start, cols, nblk * t / nthreads, nblk * (t + 1) / nthreads, sigma, q, scales};
+    for (int t = 1; t < nthreads; ++t) pthread_create(&th[t], NULL, mx_worker, &jobs[t]);
+    mx_worker(&jobs[0]);
+    for (int t = 1; t < nthreads; ++t) pthread_join(th[t], NULL);
+    return 0;
+}
+
+uint8_t moegen_e2m1_encode(double v) { return e2m1_encode(v); }
+
 /* Seeded permutation of 0..n-1 (Fisher-Yates driven by the uniform stream). */
 void moegen_permutation(uint64_t key, int n, int32_t *perm) {
     for (int i = 0; i < n; ++i) perm[i] = i;
