@@ -43,8 +43,9 @@
  *    stream) and return.  They never synchronise or read device memory back,
  *    so they can be recorded into a HIP graph.
  *  - Layout is row-major and contiguous.  Activations, logits, weights of the
- *    combine and outputs are fp32; expert weights are fp32, bf16 or OCP fp8
- *    E4M3 with fp32 scales per 128x128 block; the router is fp32 or bf16.
+ *    combine and outputs are fp32; expert weights are fp32, bf16, OCP fp8
+ *    E4M3 with fp32 scales per 128x128 block, or OCP MXFP4; the router is
+ *    fp32 or bf16.
  *  - The status covers host-side validation and launch errors only.  A
  *    device fault shows up at the caller's next synchronisation.  Inputs must
  *    be finite: NaN or Inf give an unspecified routing.
@@ -71,12 +72,20 @@ typedef enum {
     MOE_ERR_ALIGN = 7        /* a pointer is not 16-byte aligned               */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3 } moe_dtype;
 
 /* One MoE layer.  Limits: 1 <= E <= 1024, 1 <= top_k <= min(E, 32);
- * H, I >= 1 with H, I multiples of 4 (fp32), 8 (bf16) or 128 (fp8), and at
- * most 512 16-byte chunks per weight row (H, I <= 2048 fp32, 4096 bf16,
- * 8192 fp8).  Weight pointers must be 16-byte aligned. */
+ * H, I >= 1 with H, I multiples of 4 (fp32), 8 (bf16), 128 (fp8) or 32
+ * (MXFP4), and at most 512 16-byte chunks per weight row (H, I <= 2048 fp32,
+ * 4096 bf16, 8192 fp8, 16384 MXFP4).  Weight pointers must be 16-byte
+ * aligned.
+ *
+ * MXFP4 expert weights (OCP microscaling): E2M1 codes, two per byte with the
+ * even element in the low nibble (a row of K elements is K/2 bytes), and one
+ * E8M0 scale byte, 2^(s - 127), per 32 consecutive elements of a row:
+ * s_gate_up uint8 [E, 2I, H/32], s_down uint8 [E, H, I/32].  Such experts
+ * always run on the GEMV kernels (fp32 accumulation of exactly decoded
+ * weights).  The router stays fp32 or bf16. */
 typedef struct {
     int32_t E, top_k, H, I;
     int32_t router_dtype;     /* MOE_F32 or MOE_BF16                          */
@@ -84,8 +93,8 @@ typedef struct {
     const void *w_router;     /* [E, H]                                       */
     const void *w_gate_up;    /* [E, 2I, H]: rows [0, I) gate, [I, 2I) up     */
     const void *w_down;       /* [E, H, I]                                    */
-    const float *s_gate_up;   /* fp8 only: [E, 2I/128, H/128] block scales    */
-    const float *s_down;      /* fp8 only: [E, H/128, I/128] block scales     */
+    const void *s_gate_up;    /* fp8: float [E, 2I/128, H/128]; MXFP4: uint8 [E, 2I, H/32] */
+    const void *s_down;       /* fp8: float [E, H/128, I/128]; MXFP4: uint8 [E, H, I/32]   */
     const float *router_bias; /* [E] added to the logits, or NULL             */
 } moe_layer_t;
 

@@ -31,7 +31,8 @@ static moe_status check_layer(const moe_layer_t *L) {
     if (L->E < 1 || L->top_k < 1 || L->top_k > L->E || L->H < 1 || L->I < 1) return MOE_ERR_ARG;
     if (L->E > kMaxE || L->top_k > kMaxK) return MOE_ERR_SHAPE;
     if (L->router_dtype != MOE_F32 && L->router_dtype != MOE_BF16) return MOE_ERR_DTYPE;
-    if (L->expert_dtype != MOE_F32 && L->expert_dtype != MOE_BF16 && L->expert_dtype != MOE_FP8_E4M3)
+    if (L->expert_dtype != MOE_F32 && L->expert_dtype != MOE_BF16 && L->expert_dtype != MOE_FP8_E4M3 &&
+        L->expert_dtype != MOE_MXFP4)
         return MOE_ERR_DTYPE;
     const int epc = elems_per_chunk(L->expert_dtype), repc = elems_per_chunk(L->router_dtype);
     if (L->H % epc || L->I % epc || L->H % repc || L->H % 4 || L->I % 4) return MOE_ERR_SHAPE;
@@ -48,7 +49,8 @@ static moe_status check_weights(const moe_layer_t *L, bool router, bool experts)
     if (experts) {
         if (!L->w_gate_up || !L->w_down) return MOE_ERR_ARG;
         if (!aligned16(L->w_gate_up) || !aligned16(L->w_down)) return MOE_ERR_ALIGN;
-        if (L->expert_dtype == MOE_FP8_E4M3 && (!L->s_gate_up || !L->s_down)) return MOE_ERR_ARG;
+        if ((L->expert_dtype == MOE_FP8_E4M3 || L->expert_dtype == MOE_MXFP4) && (!L->s_gate_up || !L->s_down))
+            return MOE_ERR_ARG;
     }
     return MOE_OK;
 }

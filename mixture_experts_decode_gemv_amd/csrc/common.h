@@ -23,12 +23,12 @@ template <int WDT> struct WT;
 template <> struct WT<MOE_F32> { static constexpr int kEpc = 4; static constexpr int kBytes = 4; };
 template <> struct WT<MOE_BF16> { static constexpr int kEpc = 8; static constexpr int kBytes = 2; };
 template <> struct WT<MOE_FP8_E4M3> { static constexpr int kEpc = 16; static constexpr int kBytes = 1; };
+// MXFP4: 32 E2M1 codes per chunk, one E8M0 scale block (kBytes is not used:
+// row bytes are chunks x 16 for every dtype).
+template <> struct WT<MOE_MXFP4> { static constexpr int kEpc = 32; static constexpr int kBytes = 0; };
 
 __host__ __device__ constexpr int elems_per_chunk(int dtype) {
-    return dtype == MOE_F32 ? 4 : dtype == MOE_BF16 ? 8 : 16;
-}
-__host__ __device__ constexpr int bytes_per_elem(int dtype) {
-    return dtype == MOE_F32 ? 4 : dtype == MOE_BF16 ? 2 : 1;
+    return dtype == MOE_F32 ? 4 : dtype == MOE_BF16 ? 8 : dtype == MOE_FP8_E4M3 ? 16 : 32;
 }
 
 // Two fp32 -> packed bf16 pair (element 0 in the low half), round to nearest even.
@@ -90,6 +90,24 @@ __device__ __forceinline__ float chunk_dot<MOE_FP8_E4M3>(const u32x4 w, const fl
     }
     return acc;
 }
+
+// 8 E2M1 codes of a 32-bit word (element 2b in the low nibble of byte b) to
+// 8 exact fp32 values in element order, without their E8M0 scale, by the
+// hardware conversion (OCP E2M1 on gfx950).
+__device__ __forceinline__ void e2m1x8_decode(uint32_t v, float *f) {
+    const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((int)v, 1.0f, 0);
+    const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((int)v, 1.0f, 1);
+    const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((int)v, 1.0f, 2);
+    const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((int)v, 1.0f, 3);
+    f[0] = p0[0]; f[1] = p0[1];
+    f[2] = p1[0]; f[3] = p1[1];
+    f[4] = p2[0]; f[5] = p2[1];
+    f[6] = p3[0]; f[7] = p3[1];
+}
+
+// E8M0 scale byte to fp32: 2^(s - 127) (s = 0 is the subnormal 2^-127; 255,
+// NaN in the format, is never produced by the encoder).
+__device__ __forceinline__ float e8m0_value(uint32_t s) { return __uint_as_float(s ? s << 23 : 0x00400000u); }
 
 // A chunk decoded to fp32 (exact): EPC values in memory order.  fp8 codes
 // are decoded without their block scale.

@@ -190,7 +190,8 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
         switch (L.expert_dtype) {
             case MOE_F32: return launch_pass1<MOE_F32>(nc1, persistent_grid(items1), s, p1);
             case MOE_BF16: return launch_pass1<MOE_BF16>(nc1, persistent_grid(items1), s, p1);
-            default: return launch_pass1<MOE_FP8_E4M3>(nc1, persistent_grid(items1), s, p1);
+            case MOE_FP8_E4M3: return launch_pass1<MOE_FP8_E4M3>(nc1, persistent_grid(items1), s, p1);
+            default: return launch_pass1<MOE_MXFP4>(nc1, persistent_grid(items1), s, p1);
         }
     };
     // pass 1 of the MFMA segments, on a bf16 copy of x (converted here unless
@@ -204,7 +205,7 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-        MfmaArgs m1{L.w_gate_up, L.s_gate_up, xb, act, L.H, L.I, L.top_k, kMfmaMinRoutes, mfma2 ? 1 : 0, grouped,
+        MfmaArgs m1{L.w_gate_up, static_cast<const float *>(L.s_gate_up), xb, act, L.H, L.I, L.top_k, kMfmaMinRoutes, mfma2 ? 1 : 0, grouped,
                     rt.max_count};
         return launch_mfma_pass(L, 1, T, m1, s);
     };
@@ -213,18 +214,19 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
         Pass2Args p2{L.w_down, L.s_down, act, y, L.H, L.I,
                      walk == MOE_WALK_DEDUP ? (mfma2 ? split : grouped) : per_route, lds_batch_rows(L.I)};
         const int nq2 = L.I / epc;
-        const int lanes = pass2_lanes(nq2);
+        const int lanes = pass2_lanes(nq2, L.expert_dtype);
         const int nc2 = nc_instance((nq2 + lanes - 1) / lanes);
         const int rows2 = slots_for(nc2) * (kWave / lanes) * (kGemvBlock / kWave);  // per workgroup item
         const long long items2 = (long long)(p2.sa.grouped ? max_uniq : R) * ((L.H + rows2 - 1) / rows2);
         switch (L.expert_dtype) {
             case MOE_F32: return launch_pass2<MOE_F32>(nc2, lanes, persistent_grid(items2), s, p2);
             case MOE_BF16: return launch_pass2<MOE_BF16>(nc2, lanes, persistent_grid(items2), s, p2);
-            default: return launch_pass2<MOE_FP8_E4M3>(nc2, lanes, persistent_grid(items2), s, p2);
+            case MOE_FP8_E4M3: return launch_pass2<MOE_FP8_E4M3>(nc2, lanes, persistent_grid(items2), s, p2);
+            default: return launch_pass2<MOE_MXFP4>(nc2, lanes, persistent_grid(items2), s, p2);
         }
     };
     auto mfma_2 = [&](hipStream_t s) {
-        MfmaArgs m2{L.w_down, L.s_down, act, y, L.H, L.I, L.top_k, kMfmaMinRoutes, 0, grouped, rt.max_count};
+        MfmaArgs m2{L.w_down, static_cast<const float *>(L.s_down), act, y, L.H, L.I, L.top_k, kMfmaMinRoutes, 0, grouped, rt.max_count};
         return launch_mfma_pass(L, 2, T, m2, s);
     };
     auto combine = [&]() {

@@ -187,6 +187,47 @@ __device__ __forceinline__ void dot_rows(u32x4 (&w)[NS][NC], const float (&sc)[N
     for (int r = 0; r < RB; ++r)
 #pragma unroll
         for (int s = 0; s < NS; ++s) acc[r][s] = 0.f;
+    if constexpr (WDT == MOE_MXFP4) {
+        // 32 codes per chunk, taken a 32-bit word (8 elements) at a time:
+        // per (route, slot) one fp32 chain over the chunk's elements in
+        // order, then scaled by the chunk's E8M0 scale
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int q = sub + G * c;
+            if (q < nq) {
+                float t[RB][NS];
+#pragma unroll
+                for (int r = 0; r < RB; ++r)
+#pragma unroll
+                    for (int s = 0; s < NS; ++s) t[r][s] = 0.f;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    float xs[RB][8];
+#pragma unroll
+                    for (int r = 0; r < RB; ++r) {
+                        const float4 f0 = xl[r][q * 8 + 2 * v], f1 = xl[r][q * 8 + 2 * v + 1];
+                        xs[r][0] = f0.x; xs[r][1] = f0.y; xs[r][2] = f0.z; xs[r][3] = f0.w;
+                        xs[r][4] = f1.x; xs[r][5] = f1.y; xs[r][6] = f1.z; xs[r][7] = f1.w;
+                    }
+#pragma unroll
+                    for (int s = 0; s < NS; ++s) {
+                        const uint32_t word = v == 0 ? w[s][c].x : v == 1 ? w[s][c].y : v == 2 ? w[s][c].z : w[s][c].w;
+                        float wf[8];
+                        e2m1x8_decode(word, wf);
+#pragma unroll
+                        for (int r = 0; r < RB; ++r)
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) t[r][s] = fmaf(wf[i], xs[r][i], t[r][s]);
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < RB; ++r)
+#pragma unroll
+                    for (int s = 0; s < NS; ++s) acc[r][s] = fmaf(sc[s][c], t[r][s], acc[r][s]);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         const int q = sub + G * c;
@@ -231,7 +272,7 @@ inline int lds_batch_rows(int K) {
 // workgroup item is one segment and 4 * P consecutive pairs (P per wave).
 struct Pass1Args {
     const void *gate_up;
-    const float *s_gate_up;
+    const void *s_gate_up;  // fp8: float block scales; MXFP4: E8M0 bytes
     const float *x;
     float *act;
     int H, I, k;
@@ -251,7 +292,7 @@ __global__ __launch_bounds__(kGemvBlock) void pass1_kernel(Pass1Args a) {
     const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
     const int H = a.H, I = a.I, nq = H / EPC;
     const int items_per_seg = (I + P * WPB - 1) / (P * WPB);
-    const size_t row_bytes = (size_t)H * WT<WDT>::kBytes;
+    const size_t row_bytes = (size_t)nq * 16;
 
     if (a.xb) {  // the MFMA pass 1, launched after this kernel, reads x as bf16
         const int npairs = a.sa.R / a.k * H / 2;
@@ -290,6 +331,19 @@ __global__ __launch_bounds__(kGemvBlock) void pass1_kernel(Pass1Args a) {
         for (int r = 0; r < NS; ++r)
 #pragma unroll
             for (int c = 0; c < NC; ++c) sc[r][c] = 1.f;
+        if (WDT == MOE_MXFP4) {  // one E8M0 byte per chunk of 32: [E, 2I, H/32]
+            const uint8_t *sg = reinterpret_cast<const uint8_t *>(a.s_gate_up);
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                const int i = min(i0 + p, I - 1);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    const int q = min(lane + G * c, nq - 1);
+                    sc[2 * p][c] = e8m0_value(sg[((size_t)e * 2 * I + i) * nq + q]);
+                    sc[2 * p + 1][c] = e8m0_value(sg[((size_t)e * 2 * I + I + i) * nq + q]);
+                }
+            }
+        }
         if (WDT == MOE_FP8_E4M3) {
             const int nbh = H / 128;
 #pragma unroll
@@ -298,9 +352,9 @@ __global__ __launch_bounds__(kGemvBlock) void pass1_kernel(Pass1Args a) {
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
                     const int hb = min((lane + G * c) * EPC / 128, nbh - 1);
-                    sc[2 * p][c] = a.s_gate_up[((size_t)e * (2 * I / 128) + i / 128) * nbh + hb];
+                    sc[2 * p][c] = static_cast<const float *>(a.s_gate_up)[((size_t)e * (2 * I / 128) + i / 128) * nbh + hb];
                     sc[2 * p + 1][c] =
-                        a.s_gate_up[((size_t)e * (2 * I / 128) + (I + i) / 128) * nbh + hb];
+                        static_cast<const float *>(a.s_gate_up)[((size_t)e * (2 * I / 128) + (I + i) / 128) * nbh + hb];
                 }
             }
         }
@@ -360,7 +414,7 @@ __global__ __launch_bounds__(kGemvBlock) void pass1_kernel(Pass1Args a) {
 // A workgroup item is one segment and 4 * NR consecutive down rows.
 struct Pass2Args {
     const void *down;
-    const float *s_down;
+    const void *s_down;  // fp8: float block scales; MXFP4: E8M0 bytes
     const float *act;
     float *y;
     int H, I;
@@ -379,7 +433,7 @@ __global__ __launch_bounds__(kGemvBlock) void pass2_kernel(Pass2Args a) {
     const int lane = threadIdx.x & (kWave - 1), half = lane / G, wv = threadIdx.x / kWave;
     const int H = a.H, I = a.I, nq = I / EPC;
     const int items_per_seg = (H + NR * WPB - 1) / (NR * WPB);
-    const size_t row_bytes = (size_t)I * WT<WDT>::kBytes;
+    const size_t row_bytes = (size_t)nq * 16;
 
     int e_nx = 0, first_nx = 0, n_nx = 0;
     bool late;
@@ -401,6 +455,18 @@ __global__ __launch_bounds__(kGemvBlock) void pass2_kernel(Pass2Args a) {
 #pragma unroll
             for (int c = 0; c < NC; ++c) sc[j][c] = 1.f;
         }
+        if (WDT == MOE_MXFP4) {  // one E8M0 byte per chunk of 32: [E, H, I/32]
+            const uint8_t *sd = reinterpret_cast<const uint8_t *>(a.s_down);
+#pragma unroll
+            for (int j = 0; j < NS; ++j) {
+                const int h = min(h0 + j * RPS + half, H - 1);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    const int q = min((lane & (G - 1)) + G * c, nq - 1);
+                    sc[j][c] = e8m0_value(sd[((size_t)e * H + h) * nq + q]);
+                }
+            }
+        }
         if (WDT == MOE_FP8_E4M3) {
             const int nbi = I / 128;
 #pragma unroll
@@ -409,7 +475,7 @@ __global__ __launch_bounds__(kGemvBlock) void pass2_kernel(Pass2Args a) {
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
                     const int ib = min(((lane & (G - 1)) + G * c) * EPC / 128, nbi - 1);
-                    sc[j][c] = a.s_down[((size_t)e * (H / 128) + h / 128) * nbi + ib];
+                    sc[j][c] = static_cast<const float *>(a.s_down)[((size_t)e * (H / 128) + h / 128) * nbi + ib];
                 }
             }
         }
@@ -464,8 +530,17 @@ __global__ __launch_bounds__(kGemvBlock) void pass2_kernel(Pass2Args a) {
 __host__ __device__ constexpr int nc_instance(int nc) { return nc <= 4 ? nc : 8; }
 
 // Lanes per down row: 32 when a row's 16-byte chunks are a multiple of 32 but
-// not of 64 (e.g. 768 bf16), so no lane idles; otherwise 64.
-inline int pass2_lanes(int nq) { return (nq % 64 != 0 && nq % 32 == 0) ? 32 : 64; }
+// not of 64 (e.g. 768 bf16), so no lane idles; otherwise 64.  MXFP4 rows are
+// short (I/32 chunks): 16 or 8 lanes per row when the chunks divide so.
+inline int pass2_lanes(int nq, int dtype) {
+    if (nq % 64 == 0) return 64;
+    if (nq % 32 == 0) return 32;
+    if (dtype == MOE_MXFP4) {
+        if (nq % 16 == 0) return 16;
+        if (nq % 8 == 0) return 8;
+    }
+    return 64;
+}
 
 template <int WDT>
 hipError_t launch_pass1(int nc, int grid, hipStream_t st, const Pass1Args &a) {
@@ -487,6 +562,24 @@ template <int WDT>
 hipError_t launch_pass2(int nc, int lanes, int grid, hipStream_t st, const Pass2Args &a) {
     const size_t lds = (size_t)a.nb * a.I * 4;
 #define MOE_P2(N, L) hipLaunchKernelGGL((pass2_kernel<WDT, N, L>), dim3(grid), dim3(kGemvBlock), lds, st, a)
+    if constexpr (WDT == MOE_MXFP4) {
+        if (lanes == 16 || lanes == 8) {
+            switch (nc_instance(nc) * 100 + lanes) {
+                case 116: MOE_P2(1, 16); break;
+                case 216: MOE_P2(2, 16); break;
+                case 316: MOE_P2(3, 16); break;
+                case 416: MOE_P2(4, 16); break;
+                case 816: MOE_P2(8, 16); break;
+                case 108: MOE_P2(1, 8); break;
+                case 208: MOE_P2(2, 8); break;
+                case 308: MOE_P2(3, 8); break;
+                case 408: MOE_P2(4, 8); break;
+                case 808: MOE_P2(8, 8); break;
+                default: return hipErrorInvalidValue;
+            }
+            return hipGetLastError();
+        }
+    }
     if (lanes == 32) {
         switch (nc_instance(nc)) {
             case 1: MOE_P2(1, 32); break;
@@ -549,5 +642,7 @@ extern template hipError_t launch_pass1<MOE_FP8_E4M3>(int, int, hipStream_t, con
 extern template hipError_t launch_pass2<MOE_F32>(int, int, int, hipStream_t, const Pass2Args &);
 extern template hipError_t launch_pass2<MOE_BF16>(int, int, int, hipStream_t, const Pass2Args &);
 extern template hipError_t launch_pass2<MOE_FP8_E4M3>(int, int, int, hipStream_t, const Pass2Args &);
+extern template hipError_t launch_pass1<MOE_MXFP4>(int, int, hipStream_t, const Pass1Args &);
+extern template hipError_t launch_pass2<MOE_MXFP4>(int, int, int, hipStream_t, const Pass2Args &);
 
 }  // namespace moe

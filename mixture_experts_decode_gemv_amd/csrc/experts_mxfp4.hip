@@ -1,0 +1,7 @@
+// Instances of the GEMV expert passes for MXFP4 expert weights.
+#include "experts_impl.h"
+
+namespace moe {
+template hipError_t launch_pass1<MOE_MXFP4>(int, int, hipStream_t, const Pass1Args &);
+template hipError_t launch_pass2<MOE_MXFP4>(int, int, int, hipStream_t, const Pass2Args &);
+}  // namespace moe

@@ -126,3 +126,16 @@ def test_expert_usage_argument_errors():
     assert lib.moe_expert_usage(0x100, 0x200, 0, 0x300, None) == 1
     assert lib.moe_expert_usage(0x100, 0x200, 2000, 0x300, None) == 2
     assert lib.moe_expert_usage(0x100, 0x200, 8, 0x304, None) == 7
+
+
+def test_mxfp4_layer_validation():
+    lib = moe.lib()
+    ok = dict(expert_dtype=moe.MOE_MXFP4, H=64, I=64, s_gate_up=0x7000, s_down=0x8000)
+    args = (0x4000, 4, 0x5000, 0, 0x6000, 1 << 30, None)
+    # H, I multiples of 32
+    assert lib.moe_layer_fwd(ctypes.byref(_layer(**dict(ok, H=48))), *args) == 2
+    assert lib.moe_layer_fwd(ctypes.byref(_layer(**dict(ok, I=80))), *args) == 2
+    # scales required
+    assert lib.moe_layer_fwd(ctypes.byref(_layer(**dict(ok, s_down=None))), *args) == 1
+    # at most 512 chunks of 32 codes per row
+    assert lib.moe_layer_fwd(ctypes.byref(_layer(**dict(ok, H=32 * 513, router_dtype=moe.MOE_BF16))), *args) == 2
