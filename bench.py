@@ -75,7 +75,8 @@ def parse():
                          "skewed: E=256 top_k=6 Zipf(1.1) routing, bs 1/8/32/64; "
                          "stack: 30-layer stack, one HIP graph vs a host-sync arm; "
                          "large: E=256 H=4096 I=1536 Zipf layer at bs 128/256/512 with MFMA segments")
-    ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp8"], help="expert weights (large workload)")
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp8", "mxfp4"],
+                    help="expert weights: bf16 or fp8 (large workload), bf16 or mxfp4 (sweep and skewed)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a device-to-device copy of this many MiB, 3 times (reference for HBM counters)")
     return ap.parse_args()
@@ -213,12 +214,20 @@ def main():
     torch.cuda.set_device(dev)
     skewed = args.workload == "skewed"
     spec = wl.SKEWED if skewed else wl.SWEEP
+    if args.dtype not in ("bf16", "mxfp4"):
+        print("bench.py: the %s workload takes bf16 or mxfp4 experts" % args.workload, file=sys.stderr)
+        sys.exit(2)
+    mx = args.dtype == "mxfp4"
+    if mx:
+        spec = wl.LayerSpec(E=spec.E, top_k=spec.top_k, H=spec.H, I=spec.I, expert_dtype=wl.MXFP4,
+                            router_dtype=spec.router_dtype)
+    wname = "MXFP4 (E2M1, E8M0 scale per 32)" if mx else "bf16"
     bias = wl.zipf_bias(spec.E) if skewed else None
     walk = {"dedup": moe.MOE_WALK_DEDUP, "per_route": moe.MOE_WALK_PER_ROUTE,
             "dedup_pass1": moe.MOE_WALK_DEDUP_PASS1}[args.walk]
     if args.no_mfma:
         walk |= moe.MOE_NO_MFMA
-    bpw = 2  # bf16
+    bpw = 17 / 32 if mx else 2  # bytes per weight: MXFP4 half a byte plus one scale byte per 32
     expert_bytes = 3 * spec.H * spec.I * bpw
     gate_up_bytes = 2 * spec.H * spec.I * bpw
 
@@ -262,7 +271,7 @@ def main():
     T = args.bs
     # experts that the GEMV kernel streams: those below the MFMA threshold
     # (all of them when the MFMA path is off or T < 16)
-    mfma_on = not args.no_mfma and T >= 16 and args.walk != "per_route"
+    mfma_on = not args.no_mfma and T >= 16 and args.walk != "per_route" and not mx
     u_gemv = [int((c > 0).sum() - ((c >= 16).sum() if mfma_on else 0)) for c in
               (head_run["counts"][i] for i in head_run["stage_steps"])]
     p1_ms = head_run["stage_ms"]["pass1_gemv"]
@@ -272,7 +281,7 @@ def main():
     # measured HBM bytes per pass-1 launch (headline configuration only, and
     # only for the kernel source the counters were taken on)
     traffic = None
-    if (not skewed and args.bs == 64 and args.walk == "dedup" and not args.no_mfma
+    if (not skewed and not mx and args.bs == 64 and args.walk == "dedup" and not args.no_mfma
             and pass1_source_fingerprint() == PASS1_TRAFFIC_BS64["source"]):
         traffic = PASS1_TRAFFIC_BS64["read_bytes"] + PASS1_TRAFFIC_BS64["write_bytes"]
 
@@ -291,14 +300,14 @@ def main():
                 break
         el = time.time() - t_start
         cpu = dict(value=done / el, unit="steps/s", cores=nthreads, kind="oracle",
-                   sample="%d whole layer steps at bs=%d (E=256, k=%d, H=2048, I=768, bf16%s), fp64 "
-                          "accumulation, %.1f s" % (done, T, spec.top_k, ", Zipf bias" if skewed else "", el))
+                   sample="%d whole layer steps at bs=%d (E=256, k=%d, H=2048, I=768, %s%s), fp64 "
+                          "accumulation, %.1f s" % (done, T, spec.top_k, wname, ", Zipf bias" if skewed else "", el))
 
     head = results[args.bs]
     line = {
-        "metric": "MoE layer steps/s at bs=%d (%s routing, E=256, top_k=%d, H=2048, I=768, bf16); "
+        "metric": "MoE layer steps/s at bs=%d (%s routing, E=256, top_k=%d, H=2048, I=768, %s); "
                   "achieved HBM GB/s on unique-expert bytes" % (args.bs, "Zipf(1.1)" if skewed else "uniform",
-                                                              spec.top_k),
+                                                              spec.top_k, "mxfp4" if mx else "bf16"),
         "value": head["steps_per_s"],
         "unit": "steps/s",
         "n_gpus": 1,
@@ -308,10 +317,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp4" if mx else "bf16",
         "data": "synthetic (seeded N(0, 1/sqrt(fan_in)) weights, N(0,1) activations)",
-        "config": {"workload": "single MoE layer, %s routing, E=256 top_k=%d H=2048 I=768 bf16 experts, batch "
-                               "sweep" % ("Zipf(1.1)" if skewed else "uniform", spec.top_k), "bs": args.bs,
+        "config": {"workload": "single MoE layer, %s routing, E=256 top_k=%d H=2048 I=768 %s experts, batch "
+                               "sweep" % ("Zipf(1.1)" if skewed else "uniform", spec.top_k, wname), "bs": args.bs,
                    "walk": args.walk, "mfma": not args.no_mfma, "resident_layers": args.layers,
                    "draws": args.draws, "graph": not args.no_graph, "parallelism": "none (1 GPU)"},
         "hbm_GBps_unique_expert_bytes": head["hbm_GBps"],
@@ -319,7 +328,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "pass1_kernel (grouped GEMV, gate_up rows x routes)",
                      "achieved": p1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": p1_gbs / HBM_PEAK_GBS,
                      "traffic": traffic, "avg_launch_us": p1_ms * 1e3, "bytes_per_launch": p1_bytes,
-                     "bytes_rule": "unique experts on the GEMV path x 2I x H x 2 B (gate_up, bf16)"},
+                     "bytes_rule": "unique experts on the GEMV path x 2I x H x %s (gate_up, %s)" %
+                                   ("17/32 B (codes and E8M0 scales)" if mx else "2 B", "mxfp4" if mx else "bf16")},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -336,6 +346,10 @@ def bench_large(args):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.dtype == "mxfp4":
+        print("bench.py: the large workload takes bf16 or fp8 experts (MXFP4 experts have no MFMA path)",
+              file=sys.stderr)
+        sys.exit(2)
     spec = wl.LARGE_FP8 if args.dtype == "fp8" else wl.LARGE
     fp8 = spec.expert_dtype == wl.FP8
     bpw = 1 if fp8 else 2
