@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0
 # (uniform routing, bs=64), from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
 # scaled by a 1 GiB copy calibration: profiles/pass_kernels_uniform_bs64_hbm_counters.md.
 # Reported only while the kernel source is the one that was measured.
-PASS1_TRAFFIC_BS64 = {"read_bytes": 1.39999e9, "write_bytes": 1.83501e6, "source": "b78d131ab1c224fe"}
+PASS1_TRAFFIC_BS64 = {"read_bytes": 1.39999e9, "write_bytes": 1.83531e6, "source": "3ce981aa6142f3dc"}
 
 
 def pass1_source_fingerprint():
