@@ -193,7 +193,7 @@ __global__ __launch_bounds__(kBlock) void route_kernel(RouteArgs a) {
         if (!s_last) return;
     }
 
-    // selection for the tile's tokens, one wave per token; with a single tile
+    // selection for the tile's tokens, two per wave; with a single tile
     // the ids also go to LDS, where the sort below reads them
     const float *lg = a.logits_in ? a.logits_in : a.logits;
     int *lds_ids = a.counts && a.n_tblk == 1 ? reinterpret_cast<int *>(dyn_lds) + sort_lds_ints(E) : nullptr;

@@ -3,7 +3,7 @@
 //
 // Selection ("MoE Performance Optimization Analysis", GPU Router Design:
 // router compute, argmax and selection on the device).  The k largest logits
-// by (logit descending, expert index ascending), one wave per token: logits
+// by (logit descending, expert index ascending), one or two tokens per wave: logits
 // map to order-preserving 32-bit keys (-0 and +0 share one key, as IEEE
 // comparison has them equal); each lane keeps its best untaken (key, index);
 // round j takes the wave maximum key and, among lanes holding it, the lowest
