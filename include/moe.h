@@ -37,8 +37,11 @@
  *    from the caller's workspace `ws` of `ws_bytes` bytes (see
  *    moe_workspace_bytes).  A new workspace is prepared once with
  *    moe_workspace_init; after that every call leaves its synchronisation
- *    words zero again, and the rest of the workspace is scratch.  Calls that
- *    share a workspace must be ordered on one stream.
+ *    words zero again, and the rest of the workspace is scratch.  A
+ *    workspace serves every batch size up to the largest its ws_bytes holds;
+ *    its synchronisation words sit at offsets fixed by ws_bytes, so every
+ *    call on one workspace (and its moe_workspace_init) must pass the same
+ *    ws_bytes.  Calls that share a workspace must be ordered on one stream.
  *  - Calls only enqueue work on `stream` (a hipStream_t; NULL = the null
  *    stream) and return.  They never synchronise or read device memory back,
  *    so they can be recorded into a HIP graph.
