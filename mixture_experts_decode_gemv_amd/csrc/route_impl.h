@@ -384,16 +384,135 @@ __device__ __forceinline__ void sort_wave(const int32_t *ids, int R, int E, int3
         if (j < nr && id[j] >= 0) sorted[s_off[id[j]] + rk[j]] = j * kWave + lane;
 }
 
+// Four waves sort R <= 4 * kSortWaveRoutes routes: wave w ranks the routes
+// of its contiguous quarter [w Q, w Q + Q) as sort_wave does (ballots over
+// the id bits per round of 64, a per-wave running count per expert in LDS),
+// with no barrier; then one barrier, and each expert's count is the sum of
+// the four per-wave counts, whose exclusive prefix over the waves is added to
+// a route's rank within its wave.  Earlier waves hold earlier routes, so the
+// order is the stable one.  Same outputs as sort_block.  lds: 5 E ints.
+template <bool COHERENT>
+__device__ __forceinline__ void sort_waves4(const int32_t *ids, int R, int E, int32_t *counts, int32_t *offsets,
+                                            int32_t *sorted, int32_t *uniq, int32_t *n_uniq, int32_t *stats, int *lds,
+                                            unsigned *zero, int n_zero) {
+    constexpr int kW = kBlock / kWave;
+    __shared__ int s_bad, s_max;
+    __shared__ int s_wc[kW], s_wu[kW];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    int *s_runw = lds + wave * E, *s_off = lds + kW * E;
+    const int q = ((R + kW - 1) / kW + kWave - 1) / kWave * kWave;  // routes per wave, a multiple of 64
+    const int r0 = wave * q, r1 = min(R, r0 + q);
+    const int nr = r1 > r0 ? (r1 - r0 + kWave - 1) / kWave : 0;
+    if (tid == 0) { s_bad = 0; s_max = 0; }
+    for (int i = tid; i < n_zero; i += kBlock) zero[i] = 0u;
+    int id[kSortWaveRounds], rk[kSortWaveRounds];
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < kSortWaveRounds; ++j) {
+        const int r = r0 + j * kWave + lane;
+        id[j] = (j < nr && r < r1) ? (COHERENT ? load_shared(ids + r) : ids[r]) : -1;
+        if (j < nr && r < r1 && (id[j] < 0 || id[j] >= E)) bad = true;
+    }
+    for (int e = lane; e < E; e += kWave) s_runw[e] = 0;
+    __syncthreads();  // s_bad, s_max initialised
+    if (__ballot(bad)) {
+        if (lane == 0) s_bad = 1;
+    } else {
+        const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+        const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+        for (int j = 0; j < kSortWaveRounds; ++j) {
+            if (j < nr) {
+                const int v = id[j];
+                const bool valid = v >= 0;
+                unsigned long long same = __ballot(valid);
+                for (int b = 0; b < nbits; ++b) {
+                    const bool bit = ((v >> b) & 1) != 0;
+                    const unsigned long long on = __ballot(bit);
+                    same &= bit ? on : ~on;
+                }
+                const int before = __popcll(same & below);
+                const int base = valid ? s_runw[v] : 0;
+                rk[j] = base + before;
+                if (valid && before == 0) s_runw[v] = base + __popcll(same);
+            }
+        }
+    }
+    __syncthreads();
+    if (s_bad) {
+        if (tid == 0) {
+            *n_uniq = -1;
+            if (stats) { stats[0] = -1; stats[1] = R; stats[2] = 0; stats[3] = 0; }
+        }
+        return;
+    }
+    // per expert: the count is the sum over the waves; the waves' counts
+    // become their exclusive prefixes; then exclusive scans over the experts
+    // of the counts and of (count > 0).  Thread tid owns experts [lo, hi).
+    const int per = (E + kBlock - 1) / kBlock;
+    const int lo = min(E, tid * per), hi = min(E, lo + per);
+    int csum = 0, usum = 0, cmax = 0;
+    for (int e = lo; e < hi; ++e) {
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < kW; ++w) {
+            const int cw = lds[w * E + e];
+            lds[w * E + e] = c;
+            c += cw;
+        }
+        s_off[e] = c;  // the count, for now
+        csum += c;
+        usum += c > 0;
+        cmax = max(cmax, c);
+    }
+    int cinc = csum, uinc = usum;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int oc = __shfl_up(cinc, d, kWave), ou = __shfl_up(uinc, d, kWave);
+        if (lane >= d) { cinc += oc; uinc += ou; }
+    }
+    if (lane == kWave - 1) { s_wc[wave] = cinc; s_wu[wave] = uinc; }
+    atomicMax(&s_max, cmax);
+    __syncthreads();
+    int cpre = cinc - csum, upre = uinc - usum, utot = 0;
+    for (int wv = 0; wv < kW; ++wv) {
+        if (wv < wave) { cpre += s_wc[wv]; upre += s_wu[wv]; }
+        utot += s_wu[wv];
+    }
+    for (int e = lo; e < hi; ++e) {
+        const int c = s_off[e];
+        s_off[e] = cpre;
+        offsets[e] = cpre;
+        counts[e] = c;
+        if (c > 0) uniq[upre++] = e;
+        cpre += c;
+    }
+    if (tid == 0) {
+        offsets[E] = R;
+        *n_uniq = utot;
+        if (stats) { stats[0] = utot; stats[1] = R; stats[2] = s_max; stats[3] = 0; }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kSortWaveRounds; ++j)
+        if (j < nr && id[j] >= 0) sorted[s_off[id[j]] + s_runw[id[j]] + rk[j]] = r0 + j * kWave + lane;
+}
+
 // LDS ints needed by sort_routes for E experts and R routes.
 __host__ __device__ constexpr int sort_routes_lds_ints(int E, int R) {
     return R <= kSortWaveRoutes ? sort_wave_lds_ints(E) : sort_lds_ints(E);
 }
 
 // Sort by one workgroup (every thread calls this): one wave when R fits,
-// the whole workgroup otherwise.  Also zeroes n_zero words at zero.
+// four waves up to four times that, the whole workgroup's windows otherwise.
+// Also zeroes n_zero words at zero.
 template <bool COHERENT>
 __device__ __forceinline__ void sort_routes(const int32_t *ids, int R, int E, int32_t *counts, int32_t *offsets, int32_t *sorted,
                             int32_t *uniq, int32_t *n_uniq, int32_t *stats, int *lds, unsigned *zero, int n_zero) {
+    if (R > kSortWaveRoutes && R <= (kBlock / kWave) * kSortWaveRoutes) {
+        sort_waves4<COHERENT>(ids, R, E, counts, offsets, sorted, uniq, n_uniq, stats, lds, zero, n_zero);
+        return;
+    }
     if (R > kSortWaveRoutes) {
         sort_block<COHERENT>(ids, R, E, counts, offsets, sorted, uniq, n_uniq, stats, lds, zero, n_zero);
         return;
