@@ -84,7 +84,7 @@ def test_router_logits_from_x(spec, T, bias):
 
 @pytest.mark.parametrize("T,k,E", [(1, 1, 1), (4, 2, 8), (64, 8, 256), (37, 6, 100), (512, 8, 256), (300, 3, 1024),
                                    (1, 8, 256), (2048, 2, 128), (128, 8, 256), (205, 5, 64), (585, 7, 1000),
-                                   (600, 8, 256)])
+                                   (600, 8, 256), (32, 8, 256), (257, 1, 16), (258, 1, 1)])
 @pytest.mark.parametrize("kind", ["distinct", "repeats", "collide"])
 def test_sort_bit_exact(T, k, E, kind):
     note("sort T=%d k=%d E=%d %s" % (T, k, E, kind))
@@ -102,10 +102,10 @@ def test_sort_bit_exact(T, k, E, kind):
     assert g["n_uniq"] == r["n_uniq"]
 
 
-@pytest.mark.parametrize("T", [2, 300, 700], ids=["one-wave", "four-waves", "workgroup"])
+@pytest.mark.parametrize("T", [2, 50, 300, 700], ids=["one-wave", "four-waves-small", "four-waves", "workgroup"])
 def test_sort_flags_bad_id(T):
     """An id out of range (8 for E = 8) in the last route, for each sort
-    variant (up to 1024, 4096 and more routes)."""
+    variant (up to 256, 4096 and more routes)."""
     note("sort bad id T=%d" % T)
     ids = np.tile(np.array([[0, 3, 2, 5, 1, 7]], np.int32), (T, 1))
     ids[-1, -1] = 8
