@@ -76,7 +76,7 @@ def parse():
                          "stack: 30-layer stack, one HIP graph vs a host-sync arm; "
                          "large: E=256 H=4096 I=1536 Zipf layer at bs 128/256/512 with MFMA segments")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp8", "mxfp4"],
-                    help="expert weights: bf16 or fp8 (large workload), bf16 or mxfp4 (sweep and skewed)")
+                    help="expert weights: bf16 or mxfp4 (every workload but stack), fp8 (large workload)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a device-to-device copy of this many MiB, 3 times (reference for HBM counters)")
     return ap.parse_args()
@@ -271,7 +271,7 @@ def main():
     T = args.bs
     # experts that the GEMV kernel streams: those below the MFMA threshold
     # (all of them when the MFMA path is off or T < 16)
-    mfma_on = not args.no_mfma and T >= 16 and args.walk != "per_route" and not mx
+    mfma_on = not args.no_mfma and T >= 16 and args.walk != "per_route"
     u_gemv = [int((c > 0).sum() - ((c >= 16).sum() if mfma_on else 0)) for c in
               (head_run["counts"][i] for i in head_run["stage_steps"])]
     p1_ms = head_run["stage_ms"]["pass1_gemv"]
@@ -337,8 +337,9 @@ def main():
 
 def bench_large(args):
     """Large-batch regime: one layer E=256, top_k=8, H=4096, I=1536 with
-    Zipf(1.1)-skewed routing, bs 128/256/512, bf16 or fp8 e4m3 experts with
-    128x128 block scales.  Experts holding >= 16 routes run on MFMA."""
+    Zipf(1.1)-skewed routing, bs 128/256/512, bf16, fp8 e4m3 experts with
+    128x128 block scales or MXFP4 experts.  Experts holding >= 16 routes run
+    on MFMA."""
     import torch
 
     import mixture_experts_decode_gemv_amd as moe
@@ -346,16 +347,12 @@ def bench_large(args):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    if args.dtype == "mxfp4":
-        print("bench.py: the large workload takes bf16 or fp8 experts (MXFP4 experts have no MFMA path)",
-              file=sys.stderr)
-        sys.exit(2)
-    spec = wl.LARGE_FP8 if args.dtype == "fp8" else wl.LARGE
-    fp8 = spec.expert_dtype == wl.FP8
-    bpw = 1 if fp8 else 2
+    spec = {"fp8": wl.LARGE_FP8, "mxfp4": wl.LARGE_MXFP4}.get(args.dtype, wl.LARGE)
+    # bytes per weight, scales included: fp8 1 (+ 4 per 128x128 block), MXFP4
+    # half a byte plus one scale byte per 32
+    bpw = {wl.FP8: 1 + 4 / (128 * 128), wl.MXFP4: 17 / 32}.get(spec.expert_dtype, 2)
     H, I = spec.H, spec.I
-    scale_bytes = (2 * I * H + H * I) // (128 * 128) * 4 if fp8 else 0
-    expert_bytes = 3 * H * I * bpw + scale_bytes
+    expert_bytes = 3 * H * I * bpw
     bias = wl.zipf_bias(spec.E)
     t0 = time.time()
     host = wl.make_layer(spec)
@@ -421,8 +418,7 @@ def bench_large(args):
     # algorithmic bytes of each stage at the headline batch: weights of the
     # experts it streams (GEMV: below 16 routes, MFMA: 16 or more)
     n_gemv = head["unique_ev"] - head["mfma_experts"]
-    per_expert = {"pass1": 2 * I * H * bpw + (2 * I * H // (128 * 128) * 4 if fp8 else 0),
-                  "pass2": H * I * bpw + (H * I // (128 * 128) * 4 if fp8 else 0)}
+    per_expert = {"pass1": 2 * I * H * bpw, "pass2": H * I * bpw}
     stage_bytes = {"pass1_gemv": n_gemv * per_expert["pass1"], "pass1_mfma": head["mfma_experts"] * per_expert["pass1"],
                    "pass2_gemv": n_gemv * per_expert["pass2"], "pass2_mfma": head["mfma_experts"] * per_expert["pass2"],
                    "routing": spec.E * H * 2, "combine": 0}
@@ -434,7 +430,8 @@ def bench_large(args):
                   "achieved HBM GB/s on unique-expert bytes; MFMA TFLOP/s" % (bs_head, spec_name(args.dtype)),
         "value": head["steps_per_s"], "unit": "steps/s", "n_gpus": 1, "steps": head["timed_steps"],
         "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16" if not fp8 else "fp8_e4m3 weights, bf16 MFMA operands",
+        "vs_baseline": None, "dtype": {"fp8": "fp8_e4m3 weights, bf16 MFMA operands",
+                                       "mxfp4": "mxfp4 weights, bf16 MFMA operands"}.get(args.dtype, "bf16"),
         "data": "synthetic (seeded)",
         "config": {"workload": "large-batch single MoE layer, Zipf(1.1) routing, E=256 top_k=8 H=4096 I=1536 "
                                "%s experts, MFMA for experts with >= 16 routes" % spec_name(args.dtype),
@@ -453,7 +450,7 @@ def bench_large(args):
 
 
 def spec_name(dtype):
-    return "fp8 e4m3 (128x128 block scales)" if dtype == "fp8" else "bf16"
+    return {"fp8": "fp8 e4m3 (128x128 block scales)", "mxfp4": "MXFP4 (E2M1, E8M0 scale per 32)"}.get(dtype, "bf16")
 
 
 def host_topk(logits, k):

@@ -86,13 +86,20 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3 } moe_
  * MXFP4 expert weights (OCP microscaling): E2M1 codes, two per byte with the
  * even element in the low nibble (a row of K elements is K/2 bytes), and one
  * E8M0 scale byte, 2^(s - 127), per 32 consecutive elements of a row:
- * s_gate_up uint8 [E, 2I, H/32], s_down uint8 [E, H, I/32].  Such experts
- * always run on the GEMV kernels (fp32 accumulation of exactly decoded
- * weights).  The router stays fp32 or bf16. */
+ * s_gate_up uint8 [E, 2I, H/32], s_down uint8 [E, H, I/32].  The router
+ * stays fp32 or bf16.
+ *
+ * Matrix cores: an expert that holds 16 or more routes of a call runs both
+ * passes as bf16 MFMA products with fp32 accumulation (the activations and
+ * the decoded weights rounded to bf16; decoded MXFP4 weights are exact in
+ * bf16) when the experts are bf16, fp8 or MXFP4 with H and I multiples of
+ * 128 (MXFP4 also needs 4-byte aligned scale arrays), unless the flags ask
+ * for MOE_NO_MFMA or the per-route walk.  Every other segment runs on the
+ * GEMV kernels (fp32 accumulation of exactly decoded weights). */
 typedef struct {
     int32_t E, top_k, H, I;
     int32_t router_dtype;     /* MOE_F32 or MOE_BF16                          */
-    int32_t expert_dtype;     /* MOE_F32, MOE_BF16 or MOE_FP8_E4M3            */
+    int32_t expert_dtype;     /* MOE_F32, MOE_BF16, MOE_FP8_E4M3 or MOE_MXFP4 */
     const void *w_router;     /* [E, H]                                       */
     const void *w_gate_up;    /* [E, 2I, H]: rows [0, I) gate, [I, 2I) up     */
     const void *w_down;       /* [E, H, I]                                    */

@@ -130,14 +130,18 @@ static int persistent_grid(long long max_items) {
 }
 
 // Segments with at least kMfmaMinRoutes routes go to the MFMA kernels when the
-// weights are bf16 or fp8 with H and I multiples of 128, unless the caller
-// asked for the GEMV path only.  A segment cannot hold more routes than there
-// are tokens, so below kMfmaMinRoutes tokens no MFMA kernel is launched.
+// weights are bf16, fp8 or MXFP4 with H and I multiples of 128, unless the
+// caller asked for the GEMV path only.  A segment cannot hold more routes than
+// there are tokens, so below kMfmaMinRoutes tokens no MFMA kernel is launched.
 static bool mfma_eligible(const moe_layer_t &L, int T, uint32_t flags) {
     // the narrow kernels address activation rows with 32-bit byte offsets
     const bool offsets32 = (unsigned long long)T * L.H * 2 < (1ull << 32) &&
                            (unsigned long long)T * L.top_k * L.I * 4 < (1ull << 32);
-    return (L.expert_dtype == MOE_BF16 || L.expert_dtype == MOE_FP8_E4M3) && L.H % 128 == 0 && L.I % 128 == 0 &&
+    // MXFP4 scale words are copied 4 bytes at a time
+    const bool fp4_ok = L.expert_dtype == MOE_MXFP4 && (reinterpret_cast<uintptr_t>(L.s_gate_up) & 3) == 0 &&
+                        (reinterpret_cast<uintptr_t>(L.s_down) & 3) == 0;
+    return (L.expert_dtype == MOE_BF16 || L.expert_dtype == MOE_FP8_E4M3 || fp4_ok) && L.H % 128 == 0 &&
+           L.I % 128 == 0 &&
            !(flags & MOE_NO_MFMA) && T >= kMfmaMinRoutes && (int)(flags & MOE_WALK_MASK) != MOE_WALK_PER_ROUTE &&
            offsets32;
 }
@@ -145,8 +149,9 @@ static bool mfma_eligible(const moe_layer_t &L, int T, uint32_t flags) {
 // Small batches have few hot experts: narrow items (32 weight rows) spread
 // them over the chip.  Large batches have many items anyway, and wide items
 // (128 weight rows) read each staged activation row for 4x more weights.
+// MXFP4 runs on narrow items at every batch size.
 static hipError_t launch_mfma_pass(const moe_layer_t &L, int pass, int T, const MfmaArgs &a, hipStream_t st) {
-    const bool wide = T >= kMfmaWideTokens;
+    const bool wide = T >= kMfmaWideTokens && L.expert_dtype != MOE_MXFP4;
     // items <= row blocks x (segments that can reach the threshold + extra token blocks)
     const long long R = (long long)T * L.top_k;
     const long long segs = std::min<long long>(L.E, R / kMfmaMinRoutes);
@@ -157,8 +162,11 @@ static hipError_t launch_mfma_pass(const moe_layer_t &L, int pass, int T, const 
     if (wide)
         return L.expert_dtype == MOE_BF16 ? launch_mfma_wide<MOE_BF16>(pass, grid, st, a)
                                           : launch_mfma_wide<MOE_FP8_E4M3>(pass, grid, st, a);
-    return L.expert_dtype == MOE_BF16 ? launch_mfma<MOE_BF16>(pass, grid, st, a)
-                                      : launch_mfma<MOE_FP8_E4M3>(pass, grid, st, a);
+    switch (L.expert_dtype) {
+        case MOE_BF16: return launch_mfma<MOE_BF16>(pass, grid, st, a);
+        case MOE_FP8_E4M3: return launch_mfma<MOE_FP8_E4M3>(pass, grid, st, a);
+        default: return launch_mfma<MOE_MXFP4>(pass, grid, st, a);
+    }
 }
 
 hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xres, int T, const Routing &rt,
@@ -205,7 +213,7 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-        MfmaArgs m1{L.w_gate_up, static_cast<const float *>(L.s_gate_up), xb, act, L.H, L.I, L.top_k, kMfmaMinRoutes, mfma2 ? 1 : 0, grouped,
+        MfmaArgs m1{L.w_gate_up, L.s_gate_up, xb, act, L.H, L.I, L.top_k, kMfmaMinRoutes, mfma2 ? 1 : 0, grouped,
                     rt.max_count};
         return launch_mfma_pass(L, 1, T, m1, s);
     };
@@ -226,7 +234,7 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
         }
     };
     auto mfma_2 = [&](hipStream_t s) {
-        MfmaArgs m2{L.w_down, static_cast<const float *>(L.s_down), act, y, L.H, L.I, L.top_k, kMfmaMinRoutes, 0, grouped, rt.max_count};
+        MfmaArgs m2{L.w_down, L.s_down, act, y, L.H, L.I, L.top_k, kMfmaMinRoutes, 0, grouped, rt.max_count};
         return launch_mfma_pass(L, 2, T, m2, s);
     };
     auto combine = [&]() {

@@ -612,7 +612,7 @@ constexpr int kMfmaTokens = 64;
 
 struct MfmaArgs {
     const void *w;        // pass 1: gate_up [E, 2I, H]; pass 2: down [E, H, I]
-    const float *scales;  // fp8 block scales of w, else null
+    const void *scales;   // fp8: float block scales of w; MXFP4: E8M0 bytes; else null
     const void *src;      // bf16 rows: pass 1 x [T, H]; pass 2 a[r] in the first half of fp32 row r of act
     float *dst;           // pass 1: act [R, I]; pass 2: y [R, H]
     int H, I, k;
@@ -630,6 +630,7 @@ template <int WDT>
 hipError_t launch_mfma(int pass, int grid, hipStream_t st, const MfmaArgs &a);
 extern template hipError_t launch_mfma<MOE_BF16>(int, int, hipStream_t, const MfmaArgs &);
 extern template hipError_t launch_mfma<MOE_FP8_E4M3>(int, int, hipStream_t, const MfmaArgs &);
+extern template hipError_t launch_mfma<MOE_MXFP4>(int, int, hipStream_t, const MfmaArgs &);
 template <int WDT>
 hipError_t launch_mfma_wide(int pass, int grid, hipStream_t st, const MfmaArgs &a);
 extern template hipError_t launch_mfma_wide<MOE_BF16>(int, int, hipStream_t, const MfmaArgs &);

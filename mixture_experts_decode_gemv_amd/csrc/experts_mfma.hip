@@ -41,6 +41,15 @@
 // fp8 e4m3 weights (W8A16): each code is converted to fp32 by the hardware
 // (OCP E4M3 on gfx950), multiplied by its 128x128 block scale and rounded to
 // bf16; the MFMA then runs on bf16 exactly as for bf16 weights.
+//
+// MXFP4 weights (W4A16; OCP Microscaling Formats v1.0, E2M1 elements with an
+// E8M0 scale per 32 along K): a wave's k-step of 32 is one scale block, so a
+// lane's 8 codes share one scale.  They are converted to fp32 by the
+// hardware, multiplied by the scale and rounded to bf16, which is exact (an
+// E2M1 value has 2 significant bits).  A 128-wide stage of a row is 64 bytes
+// of codes and 4 scale bytes (one aligned word: the rows' scale arrays are
+// K/32 bytes long and K is a multiple of 128); every wave copies the 32
+// rows' scale words of the stage into its own LDS area.
 #include "experts_impl.h"
 
 namespace moe {
@@ -63,13 +72,19 @@ static_assert(kTT <= kWaves, "one token tile per wave in the epilogue");
 template <int WDT>
 struct Stage {
     static constexpr bool kFp8 = WDT == MOE_FP8_E4M3;
-    static constexpr int kRowB = kKS * (kFp8 ? 1 : 2);       // bytes of a weight row per stage
+    static constexpr bool kFp4 = WDT == MOE_MXFP4;
+    static constexpr int kRowB = kFp4 ? kKS / 2 : kKS * (kFp8 ? 1 : 2);  // bytes of a weight row per stage
     static constexpr int kChunks = kRowB / 16;                // 16-byte chunks per weight row
     static constexpr int kWBytes = 32 * kRowB;                // weights of one stage
-    static constexpr int kWLoads = kWBytes / 1024 / kWaves;   // weight copies per wave per stage
+    static constexpr int kWLanes = kWBytes / kWaves / 16 < kWave ? kWBytes / kWaves / 16 : kWave;  // lanes per copy
+    static constexpr int kWLoads = kWBytes / (kWLanes * 16) / kWaves;  // weight copies per wave per stage
     static constexpr int kXLoads = kXBytes / 1024 / kWaves;   // activation copies per wave per stage
-    static constexpr int kLoads = kWLoads + kXLoads;          // copies per wave per stage
-    static constexpr int kBytes = kWBytes + kXBytes;
+    static constexpr int kSLoads = kFp4 ? 1 : 0;              // scale-word copies per wave per stage
+    static constexpr int kSBytes = kFp4 ? kWaves * 32 * 4 : 0;  // MXFP4: each wave's 32 scale words
+    static constexpr int kLoads = kWLoads + kXLoads + kSLoads;  // copies per wave per stage
+    static constexpr int kBytes = kWBytes + kXBytes + kSBytes;
+    static_assert(kWLoads >= 1 && kWLoads * kWLanes * 16 * kWaves == kWBytes, "weight copies cover the stage");
+    static_assert(kWLanes % kChunks == 0, "a copy covers whole rows");
 };
 
 __device__ __forceinline__ f32x4_t mfma16(const u32x4 &a, const u32x4 &b, const f32x4_t &c) {
@@ -83,6 +98,16 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16(unsigned w0, unsigned w1, float 
     const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
     const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
     const auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+    return u32x4{bf16_pair_rne(a[0] * s, a[1] * s), bf16_pair_rne(b[0] * s, b[1] * s),
+                 bf16_pair_rne(c[0] * s, c[1] * s), bf16_pair_rne(d[0] * s, d[1] * s)};
+}
+
+// 8 E2M1 codes (one word, element 0 in the low nibble) times s, as 8 bf16.
+__device__ __forceinline__ u32x4 e2m1x8_to_bf16(unsigned w, float s) {
+    const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((int)w, 1.0f, 0);
+    const auto b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((int)w, 1.0f, 1);
+    const auto c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((int)w, 1.0f, 2);
+    const auto d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((int)w, 1.0f, 3);
     return u32x4{bf16_pair_rne(a[0] * s, a[1] * s), bf16_pair_rne(b[0] * s, b[1] * s),
                  bf16_pair_rne(c[0] * s, c[1] * s), bf16_pair_rne(d[0] * s, d[1] * s)};
 }
@@ -104,6 +129,22 @@ __device__ __forceinline__ void copy_to_lds(const void *base, unsigned off, cons
         "s_mov_b32 m0, %3\n\t"
         "s_nop 0\n\t"
         "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off), "s"(base), "s"(l)
+        : "memory");
+}
+
+// The same for 4 bytes per lane (LDS at dst + 4 * lane).
+__device__ __forceinline__ void copy_word_to_lds(const void *base, unsigned off, const unsigned char *dst) {
+    const unsigned l = __builtin_amdgcn_readfirstlane(
+        (unsigned)(size_t)(const __attribute__((address_space(3))) unsigned char *)dst);
+    unsigned saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, %2\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
         : "v"(off), "s"(base), "s"(l)
@@ -199,7 +240,7 @@ __device__ int build_tables(const MfmaArgs &a, int n_rb, int *pre, int *off, int
 template <int WDT, int PASS>
 __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
     using S = Stage<WDT>;
-    constexpr bool kFp8 = S::kFp8;
+    constexpr bool kFp8 = S::kFp8, kFp4 = S::kFp4;
     static_assert(kRing == 3, "the prologue below fills two stages");
     __shared__ __align__(1024) unsigned char ring[kRing * S::kBytes];
     __shared__ int wsum[2 * kWaves];
@@ -217,7 +258,7 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
     const int nst = K / kKS;
     const int n_rb = PASS == 1 ? a.I / 16 : a.H / 32;
     const int w_rows = PASS == 1 ? 2 * a.I : a.H;
-    const unsigned row_bytes = (unsigned)K * WT<WDT>::kBytes;
+    const unsigned row_bytes = kFp4 ? (unsigned)K / 2 : (unsigned)K * WT<WDT>::kBytes;  // MXFP4: 2 codes a byte
     // bf16 activation rows: pass 1 reads xb [T, H]; pass 2 reads a[r] from the
     // first half of the fp32 activation row r (4I bytes apart)
     const unsigned src_stride = PASS == 1 ? (unsigned)a.H * 2 : (unsigned)a.I * 4;
@@ -248,24 +289,37 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
         lds_barrier();  // the previous item is done with the ring
 
         // weight rows of the item: row rho < 16 of tile 0, rho >= 16 of tile 1.
-        // This lane's weight copy c covers rows (64 / kChunks) apart; its chunk
-        // is the one that lands at its LDS position (position ^ row).
+        // This lane's weight copy c covers rows (kWLanes / kChunks) apart; its
+        // chunk is the one that lands at its LDS position (position ^ row).
         const int r0 = PASS == 1 ? rb * 16 : rb * 32;
         const int r1 = PASS == 1 ? a.I + r0 : r0 + 16;
         const char *wbase = uniform_ptr(static_cast<const char *>(a.w) + (size_t)e * w_rows * row_bytes);
         unsigned woff[S::kWLoads];
 #pragma unroll
         for (int c = 0; c < S::kWLoads; ++c) {
-            const int rho = (wv * S::kWLoads + c) * (kWave / S::kChunks) + lane / S::kChunks;
+            const int rho = (wv * S::kWLoads + c) * (S::kWLanes / S::kChunks) + (lane % S::kWLanes) / S::kChunks;
             const int pos = lane % S::kChunks;
             const int chunk = pos ^ (rho & (S::kChunks - 1));
             woff[c] = (unsigned)(rho < 16 ? r0 + rho : r1 + rho - 16) * row_bytes + chunk * 16;
         }
         auto issue_w = [&](int ks, int sl) {
             const unsigned char *wd = ring + sl * S::kBytes;
+            if (S::kWLanes == kWave || lane < S::kWLanes)
 #pragma unroll
-            for (int c = 0; c < S::kWLoads; ++c)
-                copy_to_lds(wbase + (size_t)ks * S::kRowB, woff[c], wd + (wv * S::kWLoads + c) * 1024);
+                for (int c = 0; c < S::kWLoads; ++c)
+                    copy_to_lds(wbase + (size_t)ks * S::kRowB, woff[c], wd + (wv * S::kWLoads + c) * S::kWLanes * 16);
+        };
+        // MXFP4 scale words: lane l < 32 copies the stage's word of row l
+        const int sk = K / 32;  // scale bytes per weight row
+        const unsigned char *sbase = nullptr;
+        unsigned soff = 0;
+        if (kFp4) {
+            sbase = uniform_ptr(static_cast<const unsigned char *>(a.scales) + (size_t)e * w_rows * sk);
+            soff = (unsigned)((lane < 16 ? r0 + lane : r1 + (lane & 31) - 16) * sk);
+        }
+        auto issue_s = [&](int ks, int sl) {
+            if (kFp4 && lane < 32)
+                copy_word_to_lds(sbase + (size_t)ks * 4, soff, ring + sl * S::kBytes + S::kWBytes + kXBytes + wv * 128);
         };
 
         // activation copy j covers tokens 4 apart; only the waves whose token
@@ -293,17 +347,19 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
         // for the route ids would wait for those copies as well.)
         issue_w(0, 0);
         issue_x(0, 0);
+        issue_s(0, 0);
         if (nst > 1) {
             issue_w(1, 1);
             issue_x(1, 1);
+            issue_s(1, 1);
         }
 
         // fp8 block scales of the two tiles, stage ks in lane ks (K <= 64 * 128)
         float sc0 = 1.f, sc1 = 1.f;
         if (kFp8) {
             const int kb = K / 128;
-            const float *sp0 = a.scales + ((size_t)e * (w_rows / 128) + r0 / 128) * kb;
-            const float *sp1 = a.scales + ((size_t)e * (w_rows / 128) + r1 / 128) * kb;
+            const float *sp0 = static_cast<const float *>(a.scales) + ((size_t)e * (w_rows / 128) + r0 / 128) * kb;
+            const float *sp1 = static_cast<const float *>(a.scales) + ((size_t)e * (w_rows / 128) + r1 / 128) * kb;
             if (lane < kb) {
                 sc0 = sp0[lane];
                 sc1 = sp1[lane];
@@ -319,20 +375,29 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
         // Every operand of the stage is read before the copies of a later
         // stage are issued and before the first MFMA, so the LDS latency is
         // paid once per stage; tiles past ntt read rows that feed no output.
-        const int aoff = kFp8 ? (((2 * wv + (g >> 1)) ^ (m & 7)) << 4) + ((g & 1) << 3) : ((4 * wv + g) ^ m) << 4;
+        const int aoff = kFp4   ? ((wv ^ (m & 3)) << 4) + (g << 2)
+                         : kFp8 ? (((2 * wv + (g >> 1)) ^ (m & 7)) << 4) + ((g & 1) << 3)
+                                : ((4 * wv + g) ^ m) << 4;
         const int boff = m * kXRowB + (((4 * wv + g) ^ m) << 4);
         int sl = 0;
         for (int ks = 0; ks < nst; ++ks) {
             // copies issued after the stage that is needed: stage ks + 1's
             if (ks + 1 >= nst) wait_copies_and_sync<0>();
             else if (xw) wait_copies_and_sync<S::kLoads>();
-            else wait_copies_and_sync<S::kWLoads>();
+            else wait_copies_and_sync<S::kWLoads + S::kSLoads>();
 
             const unsigned char *wd = ring + sl * S::kBytes;
             const unsigned char *xd = wd + S::kWBytes;
             u32x4 a0, a1, b[kTT];
             uint2 c0, c1;
-            if (kFp8) {
+            unsigned f0 = 0, f1 = 0, e0 = 0, e1 = 0;
+            if (kFp4) {
+                const unsigned char *sd = wd + S::kWBytes + kXBytes + wv * 128;
+                f0 = *reinterpret_cast<const unsigned *>(wd + m * S::kRowB + aoff);
+                f1 = *reinterpret_cast<const unsigned *>(wd + (16 + m) * S::kRowB + aoff);
+                e0 = sd[4 * m + wv];  // scale block 4 ks + wv of row m (tile 0) and 16 + m (tile 1)
+                e1 = sd[4 * (16 + m) + wv];
+            } else if (kFp8) {
                 c0 = *reinterpret_cast<const uint2 *>(wd + m * S::kRowB + aoff);
                 c1 = *reinterpret_cast<const uint2 *>(wd + (16 + m) * S::kRowB + aoff);
             } else {
@@ -346,6 +411,11 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
                 const int ns = sl == 0 ? kRing - 1 : sl - 1;
                 issue_w(ks + kRing - 1, ns);
                 issue_x(ks + kRing - 1, ns);
+                issue_s(ks + kRing - 1, ns);
+            }
+            if (kFp4) {
+                a0 = e2m1x8_to_bf16(f0, e8m0_value(e0));
+                a1 = e2m1x8_to_bf16(f1, e8m0_value(e1));
             }
             if (kFp8) {
                 a0 = e4m3x8_to_bf16(c0.x, c0.y, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc0), ks)));
@@ -414,5 +484,6 @@ hipError_t launch_mfma(int pass, int grid, hipStream_t st, const MfmaArgs &a) {
 
 template hipError_t launch_mfma<MOE_BF16>(int, int, hipStream_t, const MfmaArgs &);
 template hipError_t launch_mfma<MOE_FP8_E4M3>(int, int, hipStream_t, const MfmaArgs &);
+template hipError_t launch_mfma<MOE_MXFP4>(int, int, hipStream_t, const MfmaArgs &);
 
 }  // namespace moe

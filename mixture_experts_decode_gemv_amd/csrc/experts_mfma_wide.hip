@@ -200,8 +200,8 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
         const float *sp0 = nullptr, *sp1 = nullptr;
         if (kFp8) {
             const int kb = K / 128;
-            sp0 = a.scales + ((size_t)e * (w_rows / 128) + r0 / 128) * kb;
-            sp1 = a.scales + ((size_t)e * (w_rows / 128) + r1 / 128) * kb;
+            sp0 = static_cast<const float *>(a.scales) + ((size_t)e * (w_rows / 128) + r0 / 128) * kb;
+            sp1 = static_cast<const float *>(a.scales) + ((size_t)e * (w_rows / 128) + r1 / 128) * kb;
         }
         // activation rows this thread stages: chunk tid % 16 of tokens
         // tid / 16 + 16 j (16 lanes fill one 256-byte row segment: contiguous

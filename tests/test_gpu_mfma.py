@@ -3,7 +3,8 @@ CPU oracle, through the C ABI.
 
 The MFMA path rounds both operands of each product to bf16 and accumulates
 in fp32: the activations x (pass 1) and a (pass 2), and, for fp8 weights, the
-decoded code times its block scale.  Its bar is the 2e-2 max relative error
+decoded code times its block scale (for MXFP4 weights, code times its E8M0
+scale, which is exact in bf16).  Its bar is the 2e-2 max relative error
 (max abs error over max |ref|) stated for bf16 weights with fp32
 accumulation.  Segments below the threshold stay on the GEMV path, whose
 results must not change bit for bit when other segments of the same call
@@ -28,6 +29,7 @@ MFMA_MIN = 16  # routes per expert from which a segment runs on MFMA
 # blocks of 64 gate/up pairs, 3 pass-2 row blocks of 128 down rows
 MIXED = wl.LayerSpec(E=8, top_k=2, H=384, I=384)
 MIXED_FP8 = wl.LayerSpec(E=8, top_k=2, H=384, I=256, expert_dtype=wl.FP8)
+MIXED_FP4 = wl.LayerSpec(E=8, top_k=2, H=384, I=256, expert_dtype=wl.MXFP4)
 
 
 def _oracle_routing(olayer, x):
@@ -51,7 +53,7 @@ def _routing(kind, olayer, x):
     return ids, rw
 
 
-@pytest.mark.parametrize("spec", [MIXED, MIXED_FP8], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("spec", [MIXED, MIXED_FP8, MIXED_FP4], ids=["bf16", "fp8", "mxfp4"])
 @pytest.mark.parametrize("T,kind", [(16, "collide"), (31, "edge"), (45, "router"), (300, "router"),
                                     (300, "collide")])
 def test_mfma_expert_fwd(spec, T, kind):
@@ -82,11 +84,12 @@ def test_mfma_expert_fwd(spec, T, kind):
     assert np.array_equal(pr, gemv)
 
 
-@pytest.mark.parametrize("T", [64, 300], ids=["narrow", "wide"])
-def test_mfma_deterministic_and_token_permutation(T):
-    note("mfma determinism and token permutation, T=%d" % T)
-    w, layer, olayer = make_device_layer(MIXED)
-    x = wl.make_x(T, MIXED.H, draw=5)
+@pytest.mark.parametrize("T,spec", [(64, MIXED), (300, MIXED), (64, MIXED_FP4), (300, MIXED_FP4)],
+                         ids=["narrow", "wide", "mxfp4-64", "mxfp4-300"])
+def test_mfma_deterministic_and_token_permutation(T, spec):
+    note("mfma determinism and token permutation, T=%d %s" % (T, wl.DTYPE_NAMES[spec.expert_dtype]))
+    w, layer, olayer = make_device_layer(spec)
+    x = wl.make_x(T, spec.H, draw=5)
     ids, rw = _oracle_routing(olayer, x)
     a = gpu_expert_fwd(layer, x, ids, rw)
     b = gpu_expert_fwd(layer, x, ids, rw)
@@ -141,9 +144,60 @@ def test_mfma_fp8_every_code(T):
     assert not np.array_equal(got, gemv)
 
 
+def _pack_fp4(codes):
+    """[..., cols] E2M1 codes to [..., cols / 2] bytes, even element in the low nibble."""
+    c = np.asarray(codes, np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def _fp4_codes_layer():
+    """One MXFP4 expert, H = I = 128 (4 scale blocks per row).  Gate row i,
+    column p holds code (i + p) % 16 with scale 2^((i + p // 32) % 5 - 2);
+    up rows hold 1.0 (scale 1); down is the identity with scale
+    2^((3 h + h // 32) % 4 - 1) on row h.  For x = e_p:
+    out[h] = silu(value((h + p) % 16) * 2^((h + p // 32) % 5 - 2)) * 2^((3 h + h // 32) % 4 - 1)."""
+    H = I = 128
+    one = wl.e2m1_encode(1.0)
+    gate = np.array([[(i + p) % 16 for p in range(H)] for i in range(I)])
+    up = np.full((I, H), one)
+    gu = _pack_fp4(np.concatenate([gate, up]))[None]
+    s_gu = np.full((1, 2 * I, H // 32), 127, np.uint8)
+    for i in range(I):
+        for b in range(H // 32):
+            s_gu[0, i, b] = 127 + (i + b) % 5 - 2
+    dn = _pack_fp4(np.where(np.eye(H, I, dtype=bool), one, 0))[None]
+    s_dn = np.full((1, H, I // 32), 127, np.uint8)
+    for h in range(H):
+        s_dn[0, h, :] = 127 + (3 * h + h // 32) % 4 - 1
+    spec = wl.LayerSpec(E=1, top_k=1, H=H, I=I, expert_dtype=wl.MXFP4, router_dtype=wl.BF16)
+    return dict(spec=spec, w_router=np.zeros((1, H), np.uint16), w_gate_up=gu, w_down=dn, s_gate_up=s_gu,
+                s_down=s_dn)
+
+
+def test_mfma_mxfp4_every_code_every_position():
+    """Every E2M1 code at every column of a gate row, with a scale per
+    (row, block of 32), through the MFMA decode: code * scale is exact in
+    bf16, so the only rounding is that of the activation to bf16 before the
+    down projection (at most 2^-8 relative).  A swapped nibble, byte or
+    scale block, or a wrong row's scale, fails it."""
+    note("mfma mxfp4 all codes")
+    w = _fp4_codes_layer()
+    layer = moe.DeviceLayer(w, device=dev())
+    olayer = oracle.Layer(w)
+    T = 128
+    x = np.eye(T, 128, dtype=np.float32)
+    ids = np.zeros((T, 1), np.int32)
+    got = gpu_expert_fwd(layer, x, ids, np.ones((T, 1)))
+    ref = oracle.expert_fwd(olayer, x, ids, np.ones((T, 1)))
+    assert np.allclose(got, ref, rtol=2.0 ** -8 * 1.01, atol=1e-30)
+    gemv = gpu_expert_fwd(layer, x, ids, np.ones((T, 1)), flags=moe.MOE_NO_MFMA)
+    assert not np.array_equal(got, gemv)
+    assert np.allclose(gemv, ref, rtol=4e-7, atol=1e-30)
+
+
 # ---------------------------------------------------------------------------
 # The large-batch regime at its full size: E=256, top_k=8, H=4096, I=1536,
-# Zipf(1.1)-skewed routing, bf16 and fp8 e4m3 with 128x128 block scales.
+# Zipf(1.1)-skewed routing, bf16, fp8 e4m3 with 128x128 block scales, MXFP4.
 # Every token's routing is checked; outputs on sampled tokens.
 
 def _sample(g, T, n_random=6):
@@ -201,6 +255,18 @@ def test_large_bf16_sampled(large_bf16, T):
 def test_large_fp8_sampled(large_fp8, T):
     note("large fp8 T=%d" % T)
     _run_large(large_fp8, T)
+
+
+@pytest.fixture(scope="module")
+def large_mxfp4():
+    note("generating the E=256 H=4096 I=1536 MXFP4 layer")
+    yield _large(wl.LARGE_MXFP4)
+
+
+@pytest.mark.parametrize("T", [128, 512])
+def test_large_mxfp4_sampled(large_mxfp4, T):
+    note("large mxfp4 T=%d" % T)
+    _run_large(large_mxfp4, T)
 
 
 def test_mfma_narrow_many_experts():
