@@ -149,9 +149,8 @@ static bool mfma_eligible(const moe_layer_t &L, int T, uint32_t flags) {
 // Small batches have few hot experts: narrow items (32 weight rows) spread
 // them over the chip.  Large batches have many items anyway, and wide items
 // (128 weight rows) read each staged activation row for 4x more weights.
-// MXFP4 runs on narrow items at every batch size.
 static hipError_t launch_mfma_pass(const moe_layer_t &L, int pass, int T, const MfmaArgs &a, hipStream_t st) {
-    const bool wide = T >= kMfmaWideTokens && L.expert_dtype != MOE_MXFP4;
+    const bool wide = T >= kMfmaWideTokens;
     // items <= row blocks x (segments that can reach the threshold + extra token blocks)
     const long long R = (long long)T * L.top_k;
     const long long segs = std::min<long long>(L.E, R / kMfmaMinRoutes);
@@ -159,9 +158,11 @@ static hipError_t launch_mfma_pass(const moe_layer_t &L, int pass, int T, const 
     const long long items = n_rb * (segs + R / kMfmaTokens);
     const long long cap = (long long)num_cus() * 2;
     const int grid = (int)std::max<long long>(1, std::min(items, cap));
-    if (wide)
-        return L.expert_dtype == MOE_BF16 ? launch_mfma_wide<MOE_BF16>(pass, grid, st, a)
-                                          : launch_mfma_wide<MOE_FP8_E4M3>(pass, grid, st, a);
+    if (wide) switch (L.expert_dtype) {
+            case MOE_BF16: return launch_mfma_wide<MOE_BF16>(pass, grid, st, a);
+            case MOE_FP8_E4M3: return launch_mfma_wide<MOE_FP8_E4M3>(pass, grid, st, a);
+            default: return launch_mfma_wide<MOE_MXFP4>(pass, grid, st, a);
+        }
     switch (L.expert_dtype) {
         case MOE_BF16: return launch_mfma<MOE_BF16>(pass, grid, st, a);
         case MOE_FP8_E4M3: return launch_mfma<MOE_FP8_E4M3>(pass, grid, st, a);

@@ -39,6 +39,16 @@
 // fp8 e4m3 weights (W8A16): each code is converted to fp32 by the hardware
 // (OCP E4M3 on gfx950), multiplied by its 128x128 block scale and rounded to
 // bf16; the MFMA then runs on bf16 exactly as for bf16 weights.
+//
+// MXFP4 weights (W4A16; OCP Microscaling Formats v1.0: E2M1 codes, an E8M0
+// scale per 32 along K): a stage of a row is 64 bytes of codes, so one load
+// covers a whole 16-row tile (4 lanes per row), and each lane also loads its
+// row's 4 scale bytes of the stage (one aligned word: a row's scale array
+// is K/32 bytes and K is a multiple of 128).  MFMA k-step s of the stage is
+// scale block 4 ks + s; the codes are converted by the hardware, multiplied
+// by that scale and rounded to bf16, which is exact.
+#include <type_traits>
+
 #include "experts_impl.h"
 
 namespace moe {
@@ -64,6 +74,16 @@ constexpr int kWTile = 32 * kWRow;
 __device__ __forceinline__ f32x4_t mfma16(const u32x4 &a, const u32x4 &b, const f32x4_t &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
                                                    c, 0, 0, 0);
+}
+
+// 8 E2M1 codes (one word, element 0 in the low nibble) times s, as 8 bf16.
+__device__ __forceinline__ u32x4 e2m1x8_to_bf16(unsigned w, float s) {
+    const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((int)w, 1.0f, 0);
+    const auto b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((int)w, 1.0f, 1);
+    const auto c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((int)w, 1.0f, 2);
+    const auto d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((int)w, 1.0f, 3);
+    return u32x4{bf16_pair_rne(a[0] * s, a[1] * s), bf16_pair_rne(b[0] * s, b[1] * s),
+                 bf16_pair_rne(c[0] * s, c[1] * s), bf16_pair_rne(d[0] * s, d[1] * s)};
 }
 
 // 8 E4M3 codes (two words, element 0 in the low byte) times s, as 8 bf16.
@@ -131,8 +151,11 @@ __device__ int build_item_table(const MfmaArgs &a, int nu, int n_rb, int *pre, i
 
 template <int WDT, int PASS>
 __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
-    constexpr bool kFp8 = WDT == MOE_FP8_E4M3;
-    constexpr int NWL = kFp8 ? 2 : 4;  // 16-byte weight loads per tile per stage
+    constexpr bool kFp8 = WDT == MOE_FP8_E4M3, kFp4 = WDT == MOE_MXFP4;
+    constexpr int NWL = kFp4 ? 1 : kFp8 ? 2 : 4;  // 16-byte weight loads per tile per stage
+    constexpr int kStageB = kFp4 ? kKS / 2 : kKS * WT<WDT>::kBytes;  // bytes of a row per stage
+    // per tile and stage: fp8 its block scale; MXFP4 the lane's row's 4 scale bytes
+    using ScaleT = std::conditional_t<kFp4, unsigned, float>;
     __shared__ __align__(16) unsigned char xs[2 * kBufLds];
     __shared__ __align__(16) unsigned char wls[kBlock / kWave][kWTile];
     __shared__ int pre[kMaxE + 1];
@@ -147,7 +170,7 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
     const int nst = K / kKS;
     const int n_rb = PASS == 1 ? a.I / 64 : a.H / 128;
     const int w_rows = PASS == 1 ? 2 * a.I : a.H;
-    const size_t row_bytes = (size_t)K * WT<WDT>::kBytes;
+    const size_t row_bytes = kFp4 ? (size_t)K / 2 : (size_t)K * WT<WDT>::kBytes;  // MXFP4: 2 codes a byte
     // bf16 activation rows: pass 1 reads xb [T, H]; pass 2 reads a[r] from the
     // first half of the fp32 activation row r (4I bytes apart)
     const size_t src_stride = PASS == 1 ? (size_t)a.H * 2 : (size_t)a.I * 4;
@@ -183,10 +206,12 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
         const int r1 = PASS == 1 ? a.I + r0 : r0 + 16;
         const char *wbase = static_cast<const char *>(a.w) + (size_t)e * w_rows * row_bytes;
         // load c covers rows RPL*(c % (16/RPL)) + lane / (64/RPL) of tile c / (16/RPL):
-        // bf16 4 rows x 256 B (16 lanes per row), fp8 8 rows x 128 B (8 lanes per row)
-        constexpr int LPR = kFp8 ? 8 : 16;     // lanes per row segment
+        // bf16 4 rows x 256 B (16 lanes per row), fp8 8 rows x 128 B (8 lanes
+        // per row), MXFP4 16 rows x 64 B (4 lanes per row)
+        constexpr int LPR = kStageB / 16;      // lanes per row segment
         constexpr int RPL = kWave / LPR;       // rows per load
-        constexpr int WROW = kFp8 ? kKS + 16 : kWRow;
+        constexpr int WROW = kStageB + 16;     // padded LDS row of the wave's tile
+        static_assert(WROW <= kWRow && NWL * RPL == 16, "two 16-row tiles per wave");
         const char *wsrc[NWL * 2];
         int wdst[NWL * 2];
 #pragma unroll
@@ -197,11 +222,16 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
             wdst[c] = (t * 16 + rho) * WROW + (lane % LPR) * 16;
         }
         unsigned char *wl = wls[wv];
-        const float *sp0 = nullptr, *sp1 = nullptr;
-        if (kFp8) {
+        const ScaleT *sp0 = nullptr, *sp1 = nullptr;
+        if constexpr (kFp8) {
             const int kb = K / 128;
             sp0 = static_cast<const float *>(a.scales) + ((size_t)e * (w_rows / 128) + r0 / 128) * kb;
             sp1 = static_cast<const float *>(a.scales) + ((size_t)e * (w_rows / 128) + r1 / 128) * kb;
+        } else if constexpr (kFp4) {  // the scale words of rows r0 + lane % 16 and r1 + lane % 16
+            const size_t sk = (size_t)K / 32;
+            const unsigned char *sb = static_cast<const unsigned char *>(a.scales) + (size_t)e * w_rows * sk;
+            sp0 = reinterpret_cast<const unsigned *>(sb + (size_t)(r0 + (lane & 15)) * sk);
+            sp1 = reinterpret_cast<const unsigned *>(sb + (size_t)(r1 + (lane & 15)) * sk);
         }
         // activation rows this thread stages: chunk tid % 16 of tokens
         // tid / 16 + 16 j (16 lanes fill one 256-byte row segment: contiguous
@@ -228,11 +258,11 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
             for (int j = 0; j < kXChunks; ++j)
                 *reinterpret_cast<u32x4 *>(xdst + buf * kBufLds + kRowsPerPass * j * kRowLds) = X[j];
         };
-        auto load_w = [&](int ks, u32x4(&W)[2 * NWL], float(&S)[2]) {
-            const size_t off = (size_t)ks * kKS * WT<WDT>::kBytes;
+        auto load_w = [&](int ks, u32x4(&W)[2 * NWL], ScaleT(&S)[2]) {
+            const size_t off = (size_t)ks * kStageB;  // kKS elements
 #pragma unroll
             for (int c = 0; c < 2 * NWL; ++c) W[c] = load_weight_chunk(reinterpret_cast<const u32x4 *>(wsrc[c] + off));
-            if (kFp8) {
+            if (kFp8 || kFp4) {
                 S[0] = sp0[ks];
                 S[1] = sp1[ks];
             }
@@ -244,7 +274,7 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
 
         // the stage's weights into the wave's LDS tile, then the MFMAs reading
         // both operands from LDS (A: lane (m, g) row m, k-group g of the step)
-        auto compute = [&](int buf, const u32x4(&W)[2 * NWL], const float(&S)[2]) {
+        auto compute = [&](int buf, const u32x4(&W)[2 * NWL], const ScaleT(&S)[2]) {
 #pragma unroll
             for (int c = 0; c < 2 * NWL; ++c) *reinterpret_cast<u32x4 *>(wl + wdst[c]) = W[c];
             const unsigned char *xb = xs + buf * kBufLds + (lane & 15) * kRowLds;
@@ -255,7 +285,12 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
             for (int s = 0; s < 4; ++s) {
                 const int koff = 32 * s + 8 * g;  // k of this lane's 8 elements within the stage
                 u32x4 a0, a1;
-                if (kFp8) {
+                if constexpr (kFp4) {
+                    const unsigned c0 = *reinterpret_cast<const unsigned *>(wa0 + koff / 2);
+                    const unsigned c1 = *reinterpret_cast<const unsigned *>(wa1 + koff / 2);
+                    a0 = e2m1x8_to_bf16(c0, e8m0_value((S[0] >> (8 * s)) & 0xffu));
+                    a1 = e2m1x8_to_bf16(c1, e8m0_value((S[1] >> (8 * s)) & 0xffu));
+                } else if constexpr (kFp8) {
                     const uint2 c0 = *reinterpret_cast<const uint2 *>(wa0 + koff);
                     const uint2 c1 = *reinterpret_cast<const uint2 *>(wa1 + koff);
                     a0 = e4m3x8_to_bf16(c0.x, c0.y, S[0]);
@@ -278,7 +313,7 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
         // ring of three stages: W/X/S index ks % 3
         u32x4 W0[2 * NWL], W1[2 * NWL], W2[2 * NWL];
         u32x4 X0[kXChunks], X1[kXChunks], X2[kXChunks];
-        float S0[2] = {1.f, 1.f}, S1[2] = {1.f, 1.f}, S2[2] = {1.f, 1.f};
+        ScaleT S0[2] = {1, 1}, S1[2] = {1, 1}, S2[2] = {1, 1};
         // Every stage issues the same loads (stage indices past the end are
         // clamped to the last stage) and the loop runs a multiple of 3 stages,
         // so the compiler's wait counts see the same load sequence on every
@@ -289,8 +324,8 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
         load_w(min(1, nst - 1), W1, S1);
         store_x(0, X0);
         // one stage: issue stage ks+2, compute stage ks, stage ks+1 into LDS
-        auto stage = [&](int ks, const u32x4(&Wc)[2 * NWL], const float(&Sc)[2], const u32x4(&Xn)[kXChunks],
-                         u32x4(&Wn2)[2 * NWL], float(&Sn2)[2], u32x4(&Xn2)[kXChunks]) {
+        auto stage = [&](int ks, const u32x4(&Wc)[2 * NWL], const ScaleT(&Sc)[2], const u32x4(&Xn)[kXChunks],
+                         u32x4(&Wn2)[2 * NWL], ScaleT(&Sn2)[2], u32x4(&Xn2)[kXChunks]) {
             const int kl = min(ks + 2, nst - 1);
             load_x(kl, Xn2);
             load_w(kl, Wn2, Sn2);
@@ -343,5 +378,6 @@ hipError_t launch_mfma_wide(int pass, int grid, hipStream_t st, const MfmaArgs &
 
 template hipError_t launch_mfma_wide<MOE_BF16>(int, int, hipStream_t, const MfmaArgs &);
 template hipError_t launch_mfma_wide<MOE_FP8_E4M3>(int, int, hipStream_t, const MfmaArgs &);
+template hipError_t launch_mfma_wide<MOE_MXFP4>(int, int, hipStream_t, const MfmaArgs &);
 
 }  // namespace moe

@@ -174,17 +174,17 @@ def _fp4_codes_layer():
                 s_down=s_dn)
 
 
-def test_mfma_mxfp4_every_code_every_position():
-    """Every E2M1 code at every column of a gate row, with a scale per
-    (row, block of 32), through the MFMA decode: code * scale is exact in
-    bf16, so the only rounding is that of the activation to bf16 before the
-    down projection (at most 2^-8 relative).  A swapped nibble, byte or
-    scale block, or a wrong row's scale, fails it."""
-    note("mfma mxfp4 all codes")
+@pytest.mark.parametrize("T", [127, 128], ids=["narrow", "wide"])
+def test_mfma_mxfp4_every_code_every_position(T):
+    """Every E2M1 code at every column of a gate row (columns 0..T-1), with a
+    scale per (row, block of 32), through the MFMA decode: code * scale is
+    exact in bf16, so the only rounding is that of the activation to bf16
+    before the down projection (at most 2^-8 relative).  A swapped nibble,
+    byte or scale block, or a wrong row's scale, fails it."""
+    note("mfma mxfp4 all codes, T=%d" % T)
     w = _fp4_codes_layer()
     layer = moe.DeviceLayer(w, device=dev())
     olayer = oracle.Layer(w)
-    T = 128
     x = np.eye(T, 128, dtype=np.float32)
     ids = np.zeros((T, 1), np.int32)
     got = gpu_expert_fwd(layer, x, ids, np.ones((T, 1)))
