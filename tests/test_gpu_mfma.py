@@ -195,6 +195,36 @@ def test_mfma_mxfp4_every_code_every_position(T):
     assert np.allclose(gemv, ref, rtol=4e-7, atol=1e-30)
 
 
+def test_mxfp4_unaligned_scales_stay_on_gemv():
+    """MXFP4 scale arrays that are not 4-byte aligned cannot be copied a word
+    at a time, so every segment stays on the GEMV kernels: the output equals
+    the MOE_NO_MFMA output of the aligned layer bit for bit."""
+    import torch
+
+    note("mxfp4 unaligned scales")
+    spec = MIXED_FP4
+    w, layer, olayer = make_device_layer(spec)
+    T = 64
+    x = wl.make_x(T, spec.H, draw=11)
+    ids, rw = _routing("collide", olayer, x)
+    shifted = layer.with_bias(None)
+    for n in ("s_gate_up", "s_down"):
+        src = layer.tensors[n].reshape(-1)
+        buf = torch.zeros(src.numel() + 16, dtype=torch.uint8, device=src.device)
+        buf[1:1 + src.numel()] = src
+        shifted.tensors[n + "_buf"] = buf
+    t = shifted.tensors
+    shifted.struct = moe.moe_layer_t(spec.E, spec.top_k, spec.H, spec.I, spec.router_dtype, spec.expert_dtype,
+                                     t["w_router"].data_ptr(), t["w_gate_up"].data_ptr(), t["w_down"].data_ptr(),
+                                     t["s_gate_up_buf"].data_ptr() + 1, t["s_down_buf"].data_ptr() + 1, None)
+    got = gpu_expert_fwd(shifted, x, ids, rw)
+    gemv = gpu_expert_fwd(layer, x, ids, rw, flags=moe.MOE_NO_MFMA)
+    mfma = gpu_expert_fwd(layer, x, ids, rw)
+    assert np.array_equal(got, gemv)
+    assert not np.array_equal(mfma, gemv), "the aligned layer takes the MFMA path"
+    assert max_rel(got, oracle.expert_fwd(olayer, x, ids, rw)) <= 1e-4
+
+
 # ---------------------------------------------------------------------------
 # The large-batch regime at its full size: E=256, top_k=8, H=4096, I=1536,
 # Zipf(1.1)-skewed routing, bf16, fp8 e4m3 with 128x128 block scales, MXFP4.
