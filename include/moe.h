@@ -201,6 +201,26 @@ moe_status moe_layer_routing(const moe_layer_t *layer, int32_t T, void *ws, size
 moe_status moe_expert_usage(const int32_t *counts, const int32_t *n_uniq, int32_t E, uint64_t *hist,
                             void *stream);
 
+/* A stack of layers, h_{l+1} = h_l + MoE_l(RMSNorm(h_l)) for l = 0 ..
+ * n_layers - 1 with h_0 = x and out = h_{n_layers}: the same result, bit for
+ * bit, as n_layers moe_layer_fwd calls with MOE_RMSNORM_IN |
+ * MOE_ACCUM_RESIDUAL, in one launch fewer per layer: the combine and residual
+ * of layer l run inside the routing launch of layer l + 1, which forms its
+ * input rows from layer l's outputs (only the last layer launches a combine).
+ * "TEXT Generation Optimization Report" (markbaseengine), Phase 2: fuse the
+ * operations around each layer to cut dispatches per token.
+ * layers: n_layers >= 1 descriptions of one shape (E, top_k, H, I and dtypes
+ * equal; weights may differ), else MOE_ERR_SHAPE.  flags: a walk arm and
+ * MOE_NO_MFMA; MOE_RMSNORM_IN and MOE_ACCUM_RESIDUAL are implied.  out may
+ * alias x.  ws: moe_stack_workspace_bytes(layers, max_tokens) bytes, prepared
+ * once with moe_stack_workspace_init; every call on it passes the same
+ * ws_bytes, as for a layer workspace. */
+size_t moe_stack_workspace_bytes(const moe_layer_t *layer, int32_t max_tokens);
+moe_status moe_stack_workspace_init(const moe_layer_t *layer, int32_t max_tokens, void *ws, size_t ws_bytes,
+                                    void *stream);
+moe_status moe_stack_fwd(const moe_layer_t *layers, int32_t n_layers, const float *x, int32_t T, float *out,
+                         uint32_t flags, void *ws, size_t ws_bytes, void *stream);
+
 /* Static text for a status code. */
 const char *moe_status_str(moe_status status);
 

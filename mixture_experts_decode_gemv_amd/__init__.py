@@ -8,7 +8,8 @@ missing or fails to load, importing the functions raises.
 Entry points (same names as ``include/moe.h``): ``moe_workspace_bytes``,
 ``moe_workspace_init``, ``moe_route``, ``moe_sort``, ``moe_expert_fwd``,
 ``moe_layer_fwd``, ``moe_layer_fwd_events``, ``moe_layer_routing``,
-``moe_expert_usage``, ``moe_status_str``.  Tensor arguments may be torch
+``moe_expert_usage``, ``moe_stack_workspace_bytes``,
+``moe_stack_workspace_init``, ``moe_stack_fwd``, ``moe_status_str``.  Tensor arguments may be torch
 tensors (their ``data_ptr()`` is passed), raw integer device addresses or
 None (NULL).
 """
@@ -30,7 +31,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE",
           5: "MOE_ERR_HIP", 6: "MOE_ERR_UNSUPPORTED", 7: "MOE_ERR_ALIGN"}
 
 EXPORTS = ("moe_workspace_bytes", "moe_workspace_init", "moe_route", "moe_sort", "moe_expert_fwd", "moe_layer_fwd",
-           "moe_layer_fwd_events", "moe_layer_routing", "moe_expert_usage", "moe_status_str")
+           "moe_layer_fwd_events", "moe_layer_routing", "moe_expert_usage", "moe_stack_workspace_bytes",
+           "moe_stack_workspace_init", "moe_stack_fwd", "moe_status_str")
 
 MOE_N_STAGES = 6
 STAGES = ("routing", "pass1_gemv", "pass1_mfma", "pass2_gemv", "pass2_mfma", "combine")
@@ -80,6 +82,12 @@ def lib():
         L.moe_layer_routing.argtypes = [P, i32, vp, sz, pp, pp, pp, pp, pp, pp, pp]
         L.moe_expert_usage.restype = ctypes.c_int
         L.moe_expert_usage.argtypes = [vp, vp, i32, vp, vp]
+        L.moe_stack_workspace_bytes.restype = sz
+        L.moe_stack_workspace_bytes.argtypes = [P, i32]
+        L.moe_stack_workspace_init.restype = ctypes.c_int
+        L.moe_stack_workspace_init.argtypes = [P, i32, vp, sz, vp]
+        L.moe_stack_fwd.restype = ctypes.c_int
+        L.moe_stack_fwd.argtypes = [P, i32, vp, i32, vp, u32, vp, sz, vp]
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_status_str.argtypes = [ctypes.c_int]
         _lib = L
@@ -175,6 +183,26 @@ def moe_layer_routing(layer, T, ws, ws_bytes) -> dict:
 def moe_expert_usage(counts, n_uniq, E, hist, stream=None):
     """hist[e] += counts[e] (uint64 device counters), skipped when *n_uniq < 0."""
     _check("moe_expert_usage", lib().moe_expert_usage(_p(counts), _p(n_uniq), int(E), _p(hist), _s(stream)))
+
+
+def moe_stack_workspace_bytes(layer: moe_layer_t, max_tokens: int) -> int:
+    return int(lib().moe_stack_workspace_bytes(ctypes.byref(layer), int(max_tokens)))
+
+
+def moe_stack_workspace_init(layer, max_tokens, ws, ws_bytes, stream=None):
+    _check("moe_stack_workspace_init", lib().moe_stack_workspace_init(ctypes.byref(layer), int(max_tokens), _p(ws),
+                                                                      int(ws_bytes), _s(stream)))
+
+
+def moe_stack_fwd(layers, x, T, out, flags=0, ws=None, ws_bytes=0, stream=None):
+    """``layers``: a sequence of moe_layer_t (or None: NULL, for the error tests)."""
+    arr = None
+    n = 0
+    if layers is not None:
+        n = len(layers)
+        arr = (moe_layer_t * max(n, 1))(*layers)
+    _check("moe_stack_fwd", lib().moe_stack_fwd(arr, int(n), _p(x), int(T), _p(out), int(flags), _p(ws),
+                                                int(ws_bytes), _s(stream)))
 
 
 class DeviceLayer:

@@ -210,6 +210,109 @@ moe_status moe_layer_routing(const moe_layer_t *layer, int32_t T, void *ws, size
     return MOE_OK;
 }
 
+// ---- layer stack ----------------------------------------------------------------
+// A stack's workspace: two layer workspaces (layers alternate between them,
+// so layer l + 1's routing launch can read layer l's y and weights while
+// writing its own routing), then two residual buffers [cap, H] fp32; all laid
+// out for the capacity cap, the largest batch ws_bytes holds.
+
+static size_t stack_bytes_for(const moe_layer_t &L, int64_t T) {
+    return 2 * align256(ws_bytes_for(L, T)) + 2 * align256((size_t)T * L.H * 4);
+}
+
+static int64_t stack_capacity(const moe_layer_t &L, size_t bytes) {
+    if (bytes < stack_bytes_for(L, 0)) return -1;
+    int64_t lo = 0, hi = 1;
+    while (hi < (int64_t)1 << 30 && stack_bytes_for(L, hi) <= bytes) {
+        lo = hi;
+        hi *= 2;
+    }
+    while (hi - lo > 1) {
+        const int64_t mid = lo + (hi - lo) / 2;
+        if (stack_bytes_for(L, mid) <= bytes) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+size_t moe_stack_workspace_bytes(const moe_layer_t *layer, int32_t max_tokens) {
+    if (check_layer(layer) != MOE_OK || max_tokens < 0) return 0;
+    return stack_bytes_for(*layer, max_tokens);
+}
+
+moe_status moe_stack_workspace_init(const moe_layer_t *layer, int32_t max_tokens, void *ws, size_t ws_bytes,
+                                    void *stream) {
+    moe_status s = check_layer(layer);
+    if (s != MOE_OK) return s;
+    if (max_tokens < 0 || !ws) return MOE_ERR_ARG;
+    const int64_t cap = stack_capacity(*layer, ws_bytes);
+    if (cap < max_tokens) return MOE_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MOE_ERR_ALIGN;
+    const WsLayout wl = ws_layout(*layer, cap, cap);
+    const size_t half = align256(ws_bytes_for(*layer, cap));
+    for (int i = 0; i < 2; ++i)
+        if ((s = hip_status(launch_zero(reinterpret_cast<unsigned *>(static_cast<char *>(ws) + i * half),
+                                        (int)(wl.logits / 4), (hipStream_t)stream))) != MOE_OK)
+            return s;
+    return MOE_OK;
+}
+
+moe_status moe_stack_fwd(const moe_layer_t *layers, int32_t n_layers, const float *x, int32_t T, float *out,
+                         uint32_t flags, void *ws, size_t ws_bytes, void *stream) {
+    if (!layers || n_layers < 1) return MOE_ERR_ARG;
+    moe_status s;
+    const moe_layer_t &L0 = layers[0];
+    for (int l = 0; l < n_layers; ++l) {
+        const moe_layer_t &L = layers[l];
+        if ((s = check_layer(&L)) != MOE_OK) return s;
+        if ((s = check_weights(&L, true, true)) != MOE_OK) return s;
+        if (L.E != L0.E || L.top_k != L0.top_k || L.H != L0.H || L.I != L0.I || L.router_dtype != L0.router_dtype ||
+            L.expert_dtype != L0.expert_dtype)
+            return MOE_ERR_SHAPE;
+    }
+    if (T < 0 || !x || !out) return MOE_ERR_ARG;
+    if ((flags & MOE_WALK_MASK) > MOE_WALK_DEDUP_PASS1) return MOE_ERR_ARG;
+    if (!aligned16(x) || !aligned16(out)) return MOE_ERR_ALIGN;
+    if (T == 0) return MOE_OK;
+    const int64_t cap = ws ? stack_capacity(L0, ws_bytes) : -1;
+    if (cap < T) return MOE_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MOE_ERR_ALIGN;
+    hipStream_t st = (hipStream_t)stream;
+    const WsLayout wl = ws_layout(L0, T, cap);
+    const size_t half = align256(ws_bytes_for(L0, cap)), hb = align256((size_t)cap * L0.H * 4);
+    char *b = static_cast<char *>(ws);
+    char *wsl[2] = {b, b + half};
+    float *hbuf[2] = {reinterpret_cast<float *>(b + 2 * half), reinterpret_cast<float *>(b + 2 * half + hb)};
+    auto F = [](char *p, size_t o) { return reinterpret_cast<float *>(p + o); };
+    auto I32 = [](char *p, size_t o) { return reinterpret_cast<int32_t *>(p + o); };
+    const uint32_t lf = (flags & (MOE_WALK_MASK | MOE_NO_MFMA)) | MOE_RMSNORM_IN | MOE_ACCUM_RESIDUAL;
+
+    const float *h = x;  // the current layer's input, the residual of its combine
+    for (int l = 0; l < n_layers; ++l) {
+        const moe_layer_t &L = layers[l];
+        char *wb = wsl[l & 1];
+        PrevCombine pc{};
+        if (l > 0) {
+            char *pb = wsl[(l - 1) & 1];
+            pc = PrevCombine{F(pb, wl.y), F(pb, wl.w), h, hbuf[l & 1], L.top_k};
+            h = hbuf[l & 1];
+        }
+        if ((s = hip_status(launch_route(L, h, nullptr, T, F(wb, wl.xn), F(wb, wl.logits), I32(wb, wl.ids),
+                                         F(wb, wl.w), I32(wb, wl.counts), I32(wb, wl.offsets), I32(wb, wl.sorted),
+                                         I32(wb, wl.uniq), I32(wb, wl.nuniq), I32(wb, wl.stats),
+                                         reinterpret_cast<unsigned *>(wb + wl.arrive), true, nullptr, 0, st,
+                                         l > 0 ? &pc : nullptr))) != MOE_OK)
+            return s;
+        Routing rt{I32(wb, wl.ids),  I32(wb, wl.counts), I32(wb, wl.offsets), I32(wb, wl.sorted),
+                   I32(wb, wl.uniq), I32(wb, wl.nuniq),  F(wb, wl.w),         I32(wb, wl.stats) + 2};
+        // the last layer combines here; the others in the next routing launch
+        if ((s = hip_status(launch_experts(L, F(wb, wl.xn), h, T, rt, wb + wl.xb, F(wb, wl.act), F(wb, wl.y),
+                                           l == n_layers - 1 ? out : nullptr, lf, st))) != MOE_OK)
+            return s;
+    }
+    return MOE_OK;
+}
+
 moe_status moe_expert_usage(const int32_t *counts, const int32_t *n_uniq, int32_t E, uint64_t *hist,
                             void *stream) {
     if (!counts || !n_uniq || !hist) return MOE_ERR_ARG;

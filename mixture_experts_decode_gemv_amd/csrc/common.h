@@ -318,12 +318,24 @@ inline int64_t ws_capacity(const moe_layer_t &L, size_t bytes) {
 // ---- launchers (return hipSuccess or the launch error) -----------------------
 int num_cus();
 
+// The previous layer of a stack, combined inside the next routing launch:
+// rows h_out[t] = h[t] + sum_j w[t, j] * y[t * k + j] (j ascending), which
+// are then that layer's input.
+struct PrevCombine {
+    const float *y;  // [T * k, H]
+    const float *w;  // [T, k]
+    const float *h;  // [T, H] residual
+    float *h_out;    // [T, H]
+    int k;
+};
+
 // Routing: router GEMV (unless logits_in), selection and, if counts is not
-// null, the sort; xn non-null with rmsnorm writes the normalised rows.
+// null, the sort; xn non-null with rmsnorm writes the normalised rows.  With
+// prev, the input rows are prev's combine (x is not read).
 hipError_t launch_route(const moe_layer_t &L, const float *x, const float *logits_in, int T, float *xn,
                         float *logits, int32_t *ids, float *w, int32_t *counts, int32_t *offsets, int32_t *sorted,
                         int32_t *uniq, int32_t *n_uniq, int32_t *stats, unsigned *arrive, bool rmsnorm,
-                        unsigned *zero, int n_zero, hipStream_t st);
+                        unsigned *zero, int n_zero, hipStream_t st, const PrevCombine *prev = nullptr);
 hipError_t launch_sort(const int32_t *ids, int R, int E, int32_t *counts, int32_t *offsets, int32_t *sorted,
                        int32_t *uniq, int32_t *n_uniq, hipStream_t st);
 hipError_t launch_zero(unsigned *p, int n, hipStream_t st);
@@ -339,6 +351,7 @@ struct Routing {
 // pass 2 MFMA and the combine (ev[0..4]); a stage that does not run records
 // its event right after the previous one.
 // xb: scratch for a bf16 copy of x [T, H] (used when segments take the MFMA path).
+// out null: no combine (y and rt.w are left for the next layer of a stack).
 hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xres, int T, const Routing &rt,
                           void *xb, float *act, float *y, float *out, uint32_t flags, hipStream_t st,
                           const hipEvent_t *ev = nullptr);

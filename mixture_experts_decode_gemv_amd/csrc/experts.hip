@@ -239,6 +239,7 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
         return launch_mfma_pass(L, 2, T, m2, s);
     };
     auto combine = [&]() {
+        if (!out) return hipSuccess;  // a stack: the next layer's routing launch combines
         hipLaunchKernelGGL(combine_kernel, dim3(T, (L.H / 4 + kBlock - 1) / kBlock), dim3(kBlock), 0, st, y, rt.w,
                            xres, out, L.top_k, L.H);
         return hipGetLastError();

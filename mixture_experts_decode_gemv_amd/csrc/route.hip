@@ -11,7 +11,10 @@
 //    held in registers) for a tile of up to 8 tokens (32 KiB, 64 KiB for
 //    batches of 128 tokens or more) staged in LDS
 //    (normalised there first for the RMSNorm form; workgroup eb = 0 also
-//    writes the normalised rows for the expert passes).
+//    writes the normalised rows for the expert passes).  In a layer stack
+//    the staged rows can be the previous layer's combine plus its residual,
+//    formed here with the combine kernel's arithmetic (workgroup eb = 0
+//    writes them out as the next residual), which saves that kernel.
 //  * The last workgroup to finish a token tile (per-tile arrival counter)
 //    selects the top k for those tokens, two tokens per wave at once.
 //  * The last tile to be selected (arrival counter over tiles) runs the
@@ -46,6 +49,13 @@ struct RouteArgs {
     const float *x;          // [T, H]
     const float *logits_in;  // [T, E] or null
     float *xn;               // normalised rows [T, H] (RMSNorm form) or null
+    // previous layer's combine, fused (prev_y null: x is the input):
+    // rows = prev_h + sum_j prev_w[t, j] * prev_y[t * prev_k + j]
+    const float *prev_y;     // [T * prev_k, H]
+    const float *prev_w;     // [T, prev_k]
+    const float *prev_h;     // [T, H] residual
+    float *h_out;            // [T, H] the combined rows (written by eb = 0)
+    int prev_k;
     float *logits;           // [T, E] out (when computed)
     int32_t *ids;            // [T, k]
     float *w;                // [T, k]
@@ -92,7 +102,61 @@ __global__ __launch_bounds__(kBlock) void route_kernel(RouteArgs a) {
         const float bias_r = (a.bias && lane < kRouteRows && e0 + lane < E) ? a.bias[e0 + lane] : 0.f;
         // token tile -> LDS, 8 loads in flight per thread
         const int h4 = H / 4;
-        {
+        if (a.prev_y) {
+            // the previous layer's combine: per element the FMAs over its
+            // routes in slot order from zero, then the residual added, as in
+            // combine_kernel; 4 elements per thread and 2 routes at a time,
+            // with every load of a group issued before its FMAs (8 elements
+            // per thread took 241-290 VGPRs and was slower at bs=1)
+            constexpr int kU = 4, kJ = 2;
+            const int n4 = (t1 - t0) * h4, pk = a.prev_k;
+            const float4 *py = reinterpret_cast<const float4 *>(a.prev_y);
+            const float4 *ph = reinterpret_cast<const float4 *>(a.prev_h);
+            float4 *dst = reinterpret_cast<float4 *>(tile);
+            for (int base = 0; base < n4; base += kU * kBlock) {
+                int tq[kU], qq[kU];
+                float4 acc[kU], res[kU];
+#pragma unroll
+                for (int u = 0; u < kU; ++u) {
+                    const int idx = min(base + u * kBlock + (int)threadIdx.x, n4 - 1);
+                    tq[u] = t0 + idx / h4;
+                    qq[u] = idx - (idx / h4) * h4;
+                    acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+                    res[u] = ph[(size_t)tq[u] * h4 + qq[u]];
+                }
+                for (int j0 = 0; j0 < pk; j0 += kJ) {
+                    float wj[kU][kJ];
+                    float4 v[kU][kJ];
+#pragma unroll
+                    for (int u = 0; u < kU; ++u)
+#pragma unroll
+                        for (int jj = 0; jj < kJ; ++jj) {
+                            const size_t r = (size_t)tq[u] * pk + min(j0 + jj, pk - 1);
+                            wj[u][jj] = a.prev_w[r];
+                            v[u][jj] = py[r * h4 + qq[u]];
+                        }
+#pragma unroll
+                    for (int u = 0; u < kU; ++u)
+#pragma unroll
+                        for (int jj = 0; jj < kJ; ++jj)
+                            if (j0 + jj < pk) {
+                                acc[u].x = fmaf(wj[u][jj], v[u][jj].x, acc[u].x);
+                                acc[u].y = fmaf(wj[u][jj], v[u][jj].y, acc[u].y);
+                                acc[u].z = fmaf(wj[u][jj], v[u][jj].z, acc[u].z);
+                                acc[u].w = fmaf(wj[u][jj], v[u][jj].w, acc[u].w);
+                            }
+                }
+#pragma unroll
+                for (int u = 0; u < kU; ++u) {
+                    const int idx = base + u * kBlock + threadIdx.x;
+                    if (idx < n4) {
+                        acc[u].x += res[u].x; acc[u].y += res[u].y; acc[u].z += res[u].z; acc[u].w += res[u].w;
+                        dst[idx] = acc[u];
+                        if (eb == 0) reinterpret_cast<float4 *>(a.h_out)[(size_t)tq[u] * h4 + qq[u]] = acc[u];
+                    }
+                }
+            }
+        } else {
             const int n4 = (t1 - t0) * h4;
             const float4 *src = reinterpret_cast<const float4 *>(a.x + (size_t)t0 * H);
             float4 *dst = reinterpret_cast<float4 *>(tile);
@@ -260,8 +324,13 @@ int route_arrive_words(int T) { return T + 1; }
 hipError_t launch_route(const moe_layer_t &L, const float *x, const float *logits_in, int T, float *xn,
                         float *logits, int32_t *ids, float *w, int32_t *counts, int32_t *offsets, int32_t *sorted,
                         int32_t *uniq, int32_t *n_uniq, int32_t *stats, unsigned *arrive, bool rmsnorm,
-                        unsigned *zero, int n_zero, hipStream_t st) {
+                        unsigned *zero, int n_zero, hipStream_t st, const PrevCombine *prev) {
     RouteArgs a;
+    a.prev_y = prev ? prev->y : nullptr;
+    a.prev_w = prev ? prev->w : nullptr;
+    a.prev_h = prev ? prev->h : nullptr;
+    a.h_out = prev ? prev->h_out : nullptr;
+    a.prev_k = prev ? prev->k : 0;
     a.zero = zero;
     a.n_zero = n_zero;
     a.wr = L.w_router;

@@ -139,3 +139,37 @@ def test_mxfp4_layer_validation():
     assert lib.moe_layer_fwd(ctypes.byref(_layer(**dict(ok, s_down=None))), *args) == 1
     # at most 512 chunks of 32 codes per row
     assert lib.moe_layer_fwd(ctypes.byref(_layer(**dict(ok, H=32 * 513, router_dtype=moe.MOE_BF16))), *args) == 2
+
+
+def test_stack_workspace_and_argument_errors():
+    """Stack workspace size and the host-side checks of moe_stack_fwd."""
+    L = _layer()
+    n = moe.moe_stack_workspace_bytes(L, 4)
+    assert n >= 2 * moe.moe_workspace_bytes(L, 4) + 2 * 4 * 64 * 4
+    assert moe.moe_stack_workspace_bytes(_layer(top_k=9), 4) == 0
+    x = out = ws = 0x10000
+
+    def status(layers, T=4, ws_bytes=n, flags=0, xp=x, wsp=ws):
+        try:
+            moe.moe_stack_fwd(layers, xp, T, out, flags, wsp, ws_bytes)
+        except moe.MoeError as e:
+            return e.status
+        return 0
+
+    assert status(None) == 1                                  # no layers
+    assert status([]) == 1                                    # n_layers = 0
+    assert status([L, _layer(I=64)]) == 2                     # shapes differ
+    assert status([L, _layer(expert_dtype=moe.MOE_BF16)]) == 2
+    assert status([L, L], xp=None) == 1
+    assert status([L, L], flags=3) == 1                       # no such walk
+    assert status([L, L], xp=0x10004) == 7                    # misaligned x
+    assert status([L, L], ws_bytes=n - 1) == 4                # workspace too small for T = 4
+    assert status([L, L], wsp=None) == 4
+    assert status([L, L], T=0) == 0                           # no-op
+    for bad in (None, 0x10008):
+        try:
+            moe.moe_stack_workspace_init(L, 4, bad, n)
+            st = 0
+        except moe.MoeError as e:
+            st = e.status
+        assert st == (1 if bad is None else 7)

@@ -1,0 +1,118 @@
+"""moe_stack_fwd: a stack of layers (RMSNorm before the router, residual
+after the combine) in which each layer's combine runs inside the next
+layer's routing launch.  Its output must equal, bit for bit, the same layers
+run one moe_layer_fwd call at a time with MOE_RMSNORM_IN |
+MOE_ACCUM_RESIDUAL (whose parity with the oracle the other tests check):
+the fused rows are formed with the combine kernel's arithmetic in the same
+order.  Covered: the 30-layer stack's layer shape, several token tiles, an
+odd top_k (a route group of one), segments on the matrix cores (narrow
+tiles, and the wide tiles on the second stream), every walk arm, an output
+that aliases the input, and graph replays."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_decode_gemv_amd as moe
+import workload as wl
+from gpu_util import dev, note
+
+pytestmark = pytest.mark.gpu
+
+NORM_RES = moe.MOE_RMSNORM_IN | moe.MOE_ACCUM_RESIDUAL
+SMALL = wl.LayerSpec(E=16, top_k=5, H=512, I=256)  # 8 tokens per routing tile
+
+
+def _layers(spec, n, bias=None):
+    return [moe.DeviceLayer(wl.make_layer(spec, layer=l), bias, device=dev()) for l in range(n)]
+
+
+def _sequential(layers, x0, T, flags):
+    stream = torch.cuda.Stream(dev())
+    ws = layers[0].workspace(T, stream)
+    h = x0.clone()
+    with torch.cuda.stream(stream):
+        for L in layers:
+            moe.moe_layer_fwd(L.struct, h, T, h, flags | NORM_RES, ws, ws.numel(), stream)
+    stream.synchronize()
+    return h.cpu().numpy()
+
+
+def _stack_ws(layers, T, stream):
+    n = moe.moe_stack_workspace_bytes(layers[0].struct, T)
+    ws = torch.empty(n, dtype=torch.uint8, device=dev())
+    moe.moe_stack_workspace_init(layers[0].struct, T, ws, n, stream)
+    return ws
+
+
+def _fused(layers, x0, T, flags, in_place=False):
+    stream = torch.cuda.Stream(dev())
+    ws = _stack_ws(layers, T, stream)
+    out = x0.clone() if in_place else torch.full_like(x0, float("nan"))
+    src = out if in_place else x0
+    with torch.cuda.stream(stream):
+        moe.moe_stack_fwd([L.struct for L in layers], src, T, out, flags, ws, ws.numel(), stream)
+    stream.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.fixture(scope="module")
+def stack3():
+    note("generating 3 layers of the stack shape")
+    return _layers(wl.STACK, 3)
+
+
+@pytest.mark.parametrize("T", [1, 4, 5])
+def test_stack_fused_equals_layer_calls_stack_shape(stack3, T):
+    note("fused stack, stack shape, T=%d" % T)
+    x0 = torch.from_numpy(wl.make_x(T, wl.STACK.H, draw=31 + T)).to(dev())
+    ref = _sequential(stack3, x0, T, 0)
+    assert np.isfinite(ref).all()
+    assert np.array_equal(_fused(stack3, x0, T, 0), ref)
+    assert np.array_equal(_fused(stack3, x0, T, 0, in_place=True), ref)
+
+
+@pytest.mark.parametrize("T", [1, 9, 40, 130])
+@pytest.mark.parametrize("flags", [0, moe.MOE_WALK_PER_ROUTE, moe.MOE_WALK_DEDUP_PASS1, moe.MOE_NO_MFMA],
+                         ids=["dedup", "per_route", "dedup_pass1", "no_mfma"])
+def test_stack_fused_equals_layer_calls(T, flags):
+    note("fused stack, E=16 k=5 H=512 I=256, T=%d flags=%d" % (T, flags))
+    bias = np.zeros(SMALL.E, np.float32)
+    bias[:2] = 3.0  # two hot experts: segments of 16 or more routes from T = 16
+    layers = _layers(SMALL, 4, bias)
+    x0 = torch.from_numpy(wl.make_x(T, SMALL.H, draw=41 + T)).to(dev())
+    ref = _sequential(layers, x0, T, flags)
+    assert np.isfinite(ref).all()
+    assert np.array_equal(_fused(layers, x0, T, flags), ref)
+
+
+def test_stack_fused_single_layer():
+    note("fused stack of one layer")
+    layers = _layers(SMALL, 1)
+    x0 = torch.from_numpy(wl.make_x(3, SMALL.H, draw=51)).to(dev())
+    assert np.array_equal(_fused(layers, x0, 3, 0), _sequential(layers, x0, 3, 0))
+
+
+def test_stack_fused_graph_replays(stack3):
+    """Recorded in a HIP graph, with eager work of the program between the
+    replays: every replay equals the layer-by-layer run."""
+    T = 4
+    x0 = torch.from_numpy(wl.make_x(T, wl.STACK.H, draw=61)).to(dev())
+    ref = _sequential(stack3, x0, T, 0)
+    stream = torch.cuda.Stream(dev())
+    ws = _stack_ws(stack3, T, stream)
+    structs = [L.struct for L in stack3]
+    h = x0.clone()
+    with torch.cuda.stream(stream):
+        moe.moe_stack_fwd(structs, h, T, h, 0, ws, ws.numel(), stream)  # warm-up outside the capture
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        moe.moe_stack_fwd(structs, h, T, h, 0, ws, ws.numel(), stream)
+    for i in range(3):
+        note("fused stack graph replay %d" % i)
+        with torch.cuda.stream(stream):
+            h.copy_(x0)
+            graph.replay()
+        stream.synchronize()
+        assert np.array_equal(h.cpu().numpy(), ref), "replay %d" % i
+        assert np.array_equal(_sequential(stack3, x0, T, 0), ref)
