@@ -168,6 +168,19 @@ def time_layer(torch, moe, layers, xs, T, walk, steps, warmup, graph=True, stage
         e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / (reps * G)
+    # spread: a separate short run with an event between consecutive replays
+    # (G steps each), kept out of the timed region above
+    nsp = min(reps, 8)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nsp + 1)]
+    with torch.cuda.stream(stream):
+        evs[0].record(stream)
+        for r in range(nsp):
+            run(1)
+            evs[r + 1].record(stream)
+    torch.cuda.synchronize()
+    per_replay = np.array([evs[r].elapsed_time(evs[r + 1]) / G for r in range(nsp)])
+    spread = {"p10": float(np.percentile(per_replay, 10)), "p50": float(np.percentile(per_replay, 50)),
+              "p90": float(np.percentile(per_replay, 90))}
 
     # per-stage times: the same steps, eager, with events between the stages
     ns = stage_steps or G
@@ -185,7 +198,7 @@ def time_layer(torch, moe, layers, xs, T, walk, steps, warmup, graph=True, stage
     del g
     # stage_steps: index into uniq/counts of each event-timed step
     return dict(ms=ms, timed_steps=reps * G, uniq=uniq, counts=counts, plan=plan, stage_ms=stage_ms,
-                stage_steps=[i % G for i in range(ns)])
+                stage_steps=[i % G for i in range(ns)], spread_ms=spread)
 
 
 def main():
@@ -257,12 +270,15 @@ def main():
         results[T] = dict(bs=T, ms_per_step=ms, steps_per_s=1e3 / ms, unique_experts=mean_u,
                           reuse=T * spec.top_k / mean_u, unique_expert_MiB=mean_u * expert_bytes / 2 ** 20,
                           hbm_GBps=gbs, hbm_frac=gbs / HBM_PEAK_GBS, timed_steps=run["timed_steps"],
+                          us_per_step_over_replays={k: v * 1e3 for k, v in run["spread_ms"].items()},
                           stage_us={k: v * 1e3 for k, v in run["stage_ms"].items()})
         if T == args.bs:
             head_run = run
-        print("[bench] bs=%d  %.1f us/step  %.0f steps/s  U=%.1f  %.0f GB/s (%.1f%% of 8 TB/s)  stages(us) %s"
-              % (T, ms * 1e3, 1e3 / ms, mean_u, gbs, 100 * gbs / HBM_PEAK_GBS,
-                 " ".join("%s=%.1f" % (k, v * 1e3) for k, v in run["stage_ms"].items())),
+        sp = run["spread_ms"]
+        print("[bench] bs=%d  %.1f us/step (p10/p50/p90 %.1f/%.1f/%.1f)  %.0f steps/s  U=%.1f  %.0f GB/s (%.1f%% of 8 TB/s)"
+              "  stages(us) %s"
+              % (T, ms * 1e3, sp["p10"] * 1e3, sp["p50"] * 1e3, sp["p90"] * 1e3, 1e3 / ms, mean_u, gbs,
+                 100 * gbs / HBM_PEAK_GBS, " ".join("%s=%.1f" % (k, v * 1e3) for k, v in run["stage_ms"].items())),
               file=sys.stderr, flush=True)
         del xs
 
@@ -387,7 +403,8 @@ def bench_large(args):
                        stage_us={k: v * 1e3 for k, v in st.items()},
                        mfma_TFLOPs_useful=mfma_tf, mfma_frac_of_peak=mfma_tf / MFMA_PEAK_TFS,
                        mfma_issued_over_useful=flops_issued / max(flops_useful, 1.0),
-                       pass1_mfma_GBps=p1m_gbs, timed_steps=run["timed_steps"], unique_ev=u_ev)
+                       pass1_mfma_GBps=p1m_gbs, timed_steps=run["timed_steps"], unique_ev=u_ev,
+                       us_per_step_over_replays={k: v * 1e3 for k, v in run["spread_ms"].items()})
         print("[bench] large %s bs=%d  %.1f us/step  U=%.1f (MFMA %.1f, %.0f%% of routes)  %.0f GB/s (%.1f%%)  "
               "MFMA %.0f TF/s useful  stages(us) %s" %
               (args.dtype, T, ms * 1e3, u, n_big, 100 * routes_big / (T * spec.top_k), gbs,
