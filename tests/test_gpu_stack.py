@@ -85,6 +85,22 @@ def test_stack_fused_equals_layer_calls(T, flags):
     assert np.array_equal(_fused(layers, x0, T, flags), ref)
 
 
+@pytest.mark.parametrize("dtype", [wl.FP8, wl.MXFP4], ids=["fp8", "mxfp4"])
+@pytest.mark.parametrize("T", [3, 40])
+def test_stack_fused_equals_layer_calls_quantised(dtype, T):
+    """fp8 (128x128 block scales) and MXFP4 experts, below and above the
+    MFMA threshold."""
+    spec = wl.LayerSpec(E=16, top_k=5, H=512, I=256, expert_dtype=dtype, router_dtype=wl.BF16)
+    note("fused stack, %s, T=%d" % (wl.DTYPE_NAMES[dtype], T))
+    bias = np.zeros(spec.E, np.float32)
+    bias[:2] = 3.0
+    layers = _layers(spec, 3, bias)
+    x0 = torch.from_numpy(wl.make_x(T, spec.H, draw=71 + T)).to(dev())
+    ref = _sequential(layers, x0, T, 0)
+    assert np.isfinite(ref).all()
+    assert np.array_equal(_fused(layers, x0, T, 0), ref)
+
+
 def test_stack_fused_single_layer():
     note("fused stack of one layer")
     layers = _layers(SMALL, 1)
