@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kBlock) void route_kernel(RouteArgs a) {
         // before the token loop: a load inside it would wait behind the
         // previous tokens' logit stores (vector memory counts in order)
         const float bias_r = (a.bias && lane < kRouteRows && e0 + lane < E) ? a.bias[e0 + lane] : 0.f;
-        // token tile -> LDS, 8 loads in flight per thread
+        // token tile -> LDS
         const int h4 = H / 4;
         if (a.prev_y) {
             // the previous layer's combine: per element the FMAs over its
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kBlock) void route_kernel(RouteArgs a) {
                     }
                 }
             }
-        } else {
+        } else {  // the input rows, 8 loads in flight per thread
             const int n4 = (t1 - t0) * h4;
             const float4 *src = reinterpret_cast<const float4 *>(a.x + (size_t)t0 * H);
             float4 *dst = reinterpret_cast<float4 *>(tile);
