@@ -101,6 +101,17 @@ def test_stack_fused_equals_layer_calls_quantised(dtype, T):
     assert np.array_equal(_fused(layers, x0, T, 0), ref)
 
 
+def test_stack_fused_wide_router_rows():
+    """H = 4096 with a bf16 router: 8 router chunks per lane held in registers
+    beside the fused staging (the largest routing instantiation)."""
+    spec = wl.LayerSpec(E=8, top_k=2, H=4096, I=128)
+    note("fused stack, H=4096")
+    layers = _layers(spec, 3)
+    for T in (1, 3):
+        x0 = torch.from_numpy(wl.make_x(T, spec.H, draw=81 + T)).to(dev())
+        assert np.array_equal(_fused(layers, x0, T, 0), _sequential(layers, x0, T, 0))
+
+
 def test_stack_fused_single_layer():
     note("fused stack of one layer")
     layers = _layers(SMALL, 1)
