@@ -71,7 +71,7 @@ typedef enum {
     MOE_ERR_DTYPE = 3,       /* unknown dtype or combination                   */
     MOE_ERR_WORKSPACE = 4,   /* ws NULL or smaller than required               */
     MOE_ERR_HIP = 5,         /* a HIP launch reported an error                 */
-    MOE_ERR_UNSUPPORTED = 6, /* valid request this build does not implement    */
+    MOE_ERR_UNSUPPORTED = 6, /* valid request the library does not implement   */
     MOE_ERR_ALIGN = 7        /* a pointer is not 16-byte aligned               */
 } moe_status;
 

@@ -331,7 +331,7 @@ const char *moe_status_str(moe_status status) {
         case MOE_ERR_DTYPE: return "unsupported dtype";
         case MOE_ERR_WORKSPACE: return "workspace missing or too small";
         case MOE_ERR_HIP: return "HIP launch error";
-        case MOE_ERR_UNSUPPORTED: return "not supported by this build";
+        case MOE_ERR_UNSUPPORTED: return "not supported by this library";
         case MOE_ERR_ALIGN: return "pointer not 16-byte aligned";
     }
     return "unknown status";
