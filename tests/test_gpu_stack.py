@@ -112,6 +112,24 @@ def test_stack_fused_wide_router_rows():
         assert np.array_equal(_fused(layers, x0, T, 0), _sequential(layers, x0, T, 0))
 
 
+def test_stack_workspace_serves_smaller_batches():
+    """One stack workspace sized for 8 tokens, used at 3, 8 and 1 tokens in
+    turn: every call equals the layer calls (the synchronisation words sit
+    where the workspace's byte size puts them, whatever the batch)."""
+    layers = _layers(SMALL, 2)
+    stream = torch.cuda.Stream(dev())
+    ws = _stack_ws(layers, 8, stream)
+    structs = [L.struct for L in layers]
+    for T in (3, 8, 1, 3):
+        note("stack workspace for 8 tokens, T=%d" % T)
+        x0 = torch.from_numpy(wl.make_x(T, SMALL.H, draw=91 + T)).to(dev())
+        out = torch.full_like(x0, float("nan"))
+        with torch.cuda.stream(stream):
+            moe.moe_stack_fwd(structs, x0, T, out, 0, ws, ws.numel(), stream)
+        stream.synchronize()
+        assert np.array_equal(out.cpu().numpy(), _sequential(layers, x0, T, 0))
+
+
 def test_stack_fused_single_layer():
     note("fused stack of one layer")
     layers = _layers(SMALL, 1)
