@@ -36,12 +36,13 @@
  *    library never allocates, frees or caches device memory; scratch comes
  *    from the caller's workspace `ws` of `ws_bytes` bytes (see
  *    moe_workspace_bytes).  A new workspace is prepared once with
- *    moe_workspace_init; after that every call leaves its synchronisation
- *    words zero again, and the rest of the workspace is scratch.  A
- *    workspace serves every batch size up to the largest its ws_bytes holds;
- *    its synchronisation words sit at offsets fixed by ws_bytes, so every
- *    call on one workspace (and its moe_workspace_init) must pass the same
- *    ws_bytes.  Calls that share a workspace must be ordered on one stream.
+ *    moe_workspace_init, which zeroes its synchronisation words: a front of
+ *    fixed size and place (about 256 KiB) that depends on nothing else.
+ *    Every call leaves them zero again; the rest of the workspace is
+ *    scratch.  So one workspace serves any batch (up to what its ws_bytes
+ *    holds) and any layer shape, with any ws_bytes passed per call, as long
+ *    as calls that share it are ordered on one stream.
+ *  - Batches: 0 <= T <= 65536 tokens per call (MOE_ERR_SHAPE above).
  *  - Calls only enqueue work on `stream` (a hipStream_t; NULL = the null
  *    stream) and return.  They never synchronise or read device memory back,
  *    so they can be recorded into a HIP graph.
@@ -53,6 +54,15 @@
  *    device fault shows up at the caller's next synchronisation.  Inputs must
  *    be finite: NaN or Inf give an unspecified routing.
  *  - T == 0 is a no-op that returns MOE_OK.
+ *  - Threads: entry points may be called from several host threads at once.
+ *    Calls that share a workspace, or a stream, must not overlap: order them
+ *    on one stream, issued by one thread at a time.  For batches of 128
+ *    tokens or more whose experts run partly on the matrix cores, the
+ *    library keeps one side stream and two events per (device, caller
+ *    stream) pair, created on the first such call made outside a graph
+ *    capture and kept until the process ends; a call enqueues its whole
+ *    fork/join sequence under a lock.  Apart from that and the device's
+ *    compute-unit count, the library holds no state between calls.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -153,7 +163,9 @@ moe_status moe_sort(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, in
  * moe_sort on the same ids).  x [T, H] is the expert input; out [T, H] is
  * overwritten (flags MOE_ACCUM_RESIDUAL: out = x + combine).  The walk arm
  * comes from flags & MOE_WALK_MASK; all arms give bitwise the same output
- * when no segment takes the MFMA path.  out may alias x. */
+ * when no segment takes the MFMA path.  out may alias x.  A routing the sort
+ * rejected (*n_uniq < 0, read on the device) runs no expert work and leaves
+ * out untouched. */
 moe_status moe_expert_fwd(const moe_layer_t *layer, const float *x, int32_t T, const int32_t *topk_ids,
                           const float *topk_w, const int32_t *counts, const int32_t *offsets,
                           const int32_t *sorted_routes, const int32_t *uniq, const int32_t *n_uniq, float *out,
@@ -213,8 +225,9 @@ moe_status moe_expert_usage(const int32_t *counts, const int32_t *n_uniq, int32_
  * equal; weights may differ), else MOE_ERR_SHAPE.  flags: a walk arm and
  * MOE_NO_MFMA; MOE_RMSNORM_IN and MOE_ACCUM_RESIDUAL are implied.  out may
  * alias x.  ws: moe_stack_workspace_bytes(layers, max_tokens) bytes, prepared
- * once with moe_stack_workspace_init; every call on it passes the same
- * ws_bytes, as for a layer workspace. */
+ * once with moe_stack_workspace_init (it zeroes two fixed fronts of
+ * synchronisation words); as for a layer workspace, calls on it may pass
+ * any batch it holds. */
 size_t moe_stack_workspace_bytes(const moe_layer_t *layer, int32_t max_tokens);
 moe_status moe_stack_workspace_init(const moe_layer_t *layer, int32_t max_tokens, void *ws, size_t ws_bytes,
                                     void *stream);

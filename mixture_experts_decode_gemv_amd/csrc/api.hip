@@ -57,6 +57,14 @@ static moe_status check_weights(const moe_layer_t *L, bool router, bool experts)
 
 static moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// A layer workspace for T tokens: present, large enough and aligned.
+static moe_status check_ws(const moe_layer_t &L, int32_t T, const void *ws, size_t ws_bytes) {
+    if (T > kMaxTokens) return MOE_ERR_SHAPE;
+    if (!ws || ws_bytes < ws_bytes_for(L, T)) return MOE_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -64,7 +72,7 @@ using namespace moe;
 extern "C" {
 
 size_t moe_workspace_bytes(const moe_layer_t *layer, int32_t max_tokens) {
-    if (check_layer(layer) != MOE_OK || max_tokens < 0) return 0;
+    if (check_layer(layer) != MOE_OK || max_tokens < 0 || max_tokens > kMaxTokens) return 0;
     return ws_bytes_for(*layer, max_tokens);
 }
 
@@ -73,12 +81,9 @@ moe_status moe_workspace_init(const moe_layer_t *layer, int32_t max_tokens, void
     moe_status s = check_layer(layer);
     if (s != MOE_OK) return s;
     if (max_tokens < 0 || !ws) return MOE_ERR_ARG;
-    const int64_t cap = ws_capacity(*layer, ws_bytes);
-    if (cap < max_tokens) return MOE_ERR_WORKSPACE;
-    const WsLayout wl = ws_layout(*layer, cap, cap);
-    if (!aligned16(ws)) return MOE_ERR_ALIGN;
-    // stats and synchronisation words sit at the front of the workspace
-    return hip_status(launch_zero(static_cast<unsigned *>(ws), (int)(wl.logits / 4), (hipStream_t)stream));
+    if ((s = check_ws(*layer, max_tokens, ws, ws_bytes)) != MOE_OK) return s;
+    // the statistics and synchronisation words: the fixed front
+    return hip_status(launch_zero(static_cast<unsigned *>(ws), (int)(kWsFrontBytes / 4), (hipStream_t)stream));
 }
 
 moe_status moe_route(const moe_layer_t *layer, const float *x, const float *logits_in, int32_t T,
@@ -99,10 +104,8 @@ moe_status moe_route(const moe_layer_t *layer, const float *x, const float *logi
     }
     if ((s = check_weights(layer, true, false)) != MOE_OK) return s;
     if (!aligned16(x)) return MOE_ERR_ALIGN;
-    const int64_t cap = ws ? ws_capacity(*layer, ws_bytes) : -1;
-    if (cap < T) return MOE_ERR_WORKSPACE;
-    const WsLayout wl = ws_layout(*layer, T, cap);
-    if (!aligned16(ws)) return MOE_ERR_ALIGN;
+    if ((s = check_ws(*layer, T, ws, ws_bytes)) != MOE_OK) return s;
+    const WsLayout wl = ws_layout(*layer, T);
     char *b = static_cast<char *>(ws);
     float *dst = logits_out ? logits_out : reinterpret_cast<float *>(b + wl.logits);
     return hip_status(launch_route(*layer, x, nullptr, T, nullptr, dst, topk_ids, topk_w, nullptr, nullptr, nullptr,
@@ -133,12 +136,10 @@ moe_status moe_expert_fwd(const moe_layer_t *layer, const float *x, int32_t T, c
     if ((flags & MOE_WALK_MASK) > MOE_WALK_DEDUP_PASS1) return MOE_ERR_ARG;
     if (!aligned16(x) || !aligned16(out)) return MOE_ERR_ALIGN;
     if (T == 0) return MOE_OK;
-    const int64_t cap = ws ? ws_capacity(*layer, ws_bytes) : -1;
-    if (cap < T) return MOE_ERR_WORKSPACE;
-    const WsLayout wl = ws_layout(*layer, T, cap);
-    if (!aligned16(ws)) return MOE_ERR_ALIGN;
+    if ((s = check_ws(*layer, T, ws, ws_bytes)) != MOE_OK) return s;
+    const WsLayout wl = ws_layout(*layer, T);
     char *b = static_cast<char *>(ws);
-    Routing rt{topk_ids, counts, offsets, sorted_routes, uniq, n_uniq, topk_w, nullptr};
+    Routing rt{topk_ids, counts, offsets, sorted_routes, uniq, n_uniq, topk_w, nullptr, n_uniq};
     return hip_status(launch_experts(*layer, x, (flags & MOE_ACCUM_RESIDUAL) ? x : nullptr, T, rt, b + wl.xb,
                                      reinterpret_cast<float *>(b + wl.act), reinterpret_cast<float *>(b + wl.y), out,
                                      flags, (hipStream_t)stream));
@@ -153,10 +154,8 @@ static moe_status layer_fwd(const moe_layer_t *layer, const float *x, int32_t T,
     if ((flags & MOE_WALK_MASK) > MOE_WALK_DEDUP_PASS1) return MOE_ERR_ARG;
     if (!aligned16(x) || !aligned16(out)) return MOE_ERR_ALIGN;
     if (T == 0) return MOE_OK;
-    const int64_t cap = ws ? ws_capacity(*layer, ws_bytes) : -1;
-    if (cap < T) return MOE_ERR_WORKSPACE;
-    const WsLayout wl = ws_layout(*layer, T, cap);
-    if (!aligned16(ws)) return MOE_ERR_ALIGN;
+    if ((s = check_ws(*layer, T, ws, ws_bytes)) != MOE_OK) return s;
+    const WsLayout wl = ws_layout(*layer, T);
     hipStream_t st = (hipStream_t)stream;
     char *b = static_cast<char *>(ws);
     auto F = [&](size_t o) { return reinterpret_cast<float *>(b + o); };
@@ -172,7 +171,7 @@ static moe_status layer_fwd(const moe_layer_t *layer, const float *x, int32_t T,
         return s;
     if (ev && (s = hip_status(hipEventRecord(ev[1], st))) != MOE_OK) return s;
     Routing rt{I32(wl.ids),  I32(wl.counts), I32(wl.offsets), I32(wl.sorted),
-               I32(wl.uniq), I32(wl.nuniq),  F(wl.w),         I32(wl.stats) + 2};
+               I32(wl.uniq), I32(wl.nuniq),  F(wl.w),         I32(wl.stats) + 2, nullptr};
     return hip_status(launch_experts(*layer, xin, (flags & MOE_ACCUM_RESIDUAL) ? x : nullptr, T, rt, b + wl.xb,
                                      F(wl.act), F(wl.y), out, flags, st, ev ? ev + 2 : nullptr));
 }
@@ -196,9 +195,8 @@ moe_status moe_layer_routing(const moe_layer_t *layer, int32_t T, void *ws, size
     moe_status s = check_layer(layer);
     if (s != MOE_OK) return s;
     if (T < 0 || !ws) return MOE_ERR_ARG;
-    const int64_t cap = ws_capacity(*layer, ws_bytes);
-    if (cap < T) return MOE_ERR_WORKSPACE;
-    const WsLayout wl = ws_layout(*layer, T, cap);
+    if ((s = check_ws(*layer, T, ws, ws_bytes)) != MOE_OK) return s;
+    const WsLayout wl = ws_layout(*layer, T);
     char *b = static_cast<char *>(ws);
     if (topk_ids) *topk_ids = reinterpret_cast<int32_t *>(b + wl.ids);
     if (topk_w) *topk_w = reinterpret_cast<float *>(b + wl.w);
@@ -211,33 +209,37 @@ moe_status moe_layer_routing(const moe_layer_t *layer, int32_t T, void *ws, size
 }
 
 // ---- layer stack ----------------------------------------------------------------
-// A stack's workspace: two layer workspaces (layers alternate between them,
-// so layer l + 1's routing launch can read layer l's y and weights while
-// writing its own routing), then two residual buffers [cap, H] fp32; all laid
-// out for the capacity cap, the largest batch ws_bytes holds.
+// A stack's workspace: the fixed fronts of two layer workspaces, then their
+// data arrays (layers alternate between them, so layer l + 1's routing launch
+// can read layer l's y and weights while writing its own routing), then two
+// residual buffers [T, H] fp32.  Only the fronts must stay in place from call
+// to call; the rest is laid out for each call's batch.
 
-static size_t stack_bytes_for(const moe_layer_t &L, int64_t T) {
-    return 2 * align256(ws_bytes_for(L, T)) + 2 * align256((size_t)T * L.H * 4);
-}
+struct StackLayout {
+    WsLayout half[2];
+    size_t h[2], total;
+};
 
-static int64_t stack_capacity(const moe_layer_t &L, size_t bytes) {
-    if (bytes < stack_bytes_for(L, 0)) return -1;
-    int64_t lo = 0, hi = 1;
-    while (hi < (int64_t)1 << 30 && stack_bytes_for(L, hi) <= bytes) {
-        lo = hi;
-        hi *= 2;
-    }
-    while (hi - lo > 1) {
-        const int64_t mid = lo + (hi - lo) / 2;
-        if (stack_bytes_for(L, mid) <= bytes) lo = mid;
-        else hi = mid;
-    }
-    return lo;
+static StackLayout stack_layout(const moe_layer_t &L, int64_t T) {
+    StackLayout sl;
+    const size_t data = align256(ws_data_bytes(L, T)), hb = align256((size_t)T * L.H * 4);
+    for (int i = 0; i < 2; ++i) sl.half[i] = ws_layout_at(L, T, i * kWsFrontBytes, 2 * kWsFrontBytes + i * data);
+    sl.h[0] = 2 * kWsFrontBytes + 2 * data;
+    sl.h[1] = sl.h[0] + hb;
+    sl.total = sl.h[1] + hb;
+    return sl;
 }
 
 size_t moe_stack_workspace_bytes(const moe_layer_t *layer, int32_t max_tokens) {
-    if (check_layer(layer) != MOE_OK || max_tokens < 0) return 0;
-    return stack_bytes_for(*layer, max_tokens);
+    if (check_layer(layer) != MOE_OK || max_tokens < 0 || max_tokens > kMaxTokens) return 0;
+    return stack_layout(*layer, max_tokens).total;
+}
+
+static moe_status check_stack_ws(const moe_layer_t &L, int32_t T, const void *ws, size_t ws_bytes) {
+    if (T > kMaxTokens) return MOE_ERR_SHAPE;
+    if (!ws || ws_bytes < stack_layout(L, T).total) return MOE_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MOE_ERR_ALIGN;
+    return MOE_OK;
 }
 
 moe_status moe_stack_workspace_init(const moe_layer_t *layer, int32_t max_tokens, void *ws, size_t ws_bytes,
@@ -245,16 +247,8 @@ moe_status moe_stack_workspace_init(const moe_layer_t *layer, int32_t max_tokens
     moe_status s = check_layer(layer);
     if (s != MOE_OK) return s;
     if (max_tokens < 0 || !ws) return MOE_ERR_ARG;
-    const int64_t cap = stack_capacity(*layer, ws_bytes);
-    if (cap < max_tokens) return MOE_ERR_WORKSPACE;
-    if (!aligned16(ws)) return MOE_ERR_ALIGN;
-    const WsLayout wl = ws_layout(*layer, cap, cap);
-    const size_t half = align256(ws_bytes_for(*layer, cap));
-    for (int i = 0; i < 2; ++i)
-        if ((s = hip_status(launch_zero(reinterpret_cast<unsigned *>(static_cast<char *>(ws) + i * half),
-                                        (int)(wl.logits / 4), (hipStream_t)stream))) != MOE_OK)
-            return s;
-    return MOE_OK;
+    if ((s = check_stack_ws(*layer, max_tokens, ws, ws_bytes)) != MOE_OK) return s;
+    return hip_status(launch_zero(static_cast<unsigned *>(ws), (int)(2 * kWsFrontBytes / 4), (hipStream_t)stream));
 }
 
 moe_status moe_stack_fwd(const moe_layer_t *layers, int32_t n_layers, const float *x, int32_t T, float *out,
@@ -274,15 +268,11 @@ moe_status moe_stack_fwd(const moe_layer_t *layers, int32_t n_layers, const floa
     if ((flags & MOE_WALK_MASK) > MOE_WALK_DEDUP_PASS1) return MOE_ERR_ARG;
     if (!aligned16(x) || !aligned16(out)) return MOE_ERR_ALIGN;
     if (T == 0) return MOE_OK;
-    const int64_t cap = ws ? stack_capacity(L0, ws_bytes) : -1;
-    if (cap < T) return MOE_ERR_WORKSPACE;
-    if (!aligned16(ws)) return MOE_ERR_ALIGN;
+    if ((s = check_stack_ws(L0, T, ws, ws_bytes)) != MOE_OK) return s;
     hipStream_t st = (hipStream_t)stream;
-    const WsLayout wl = ws_layout(L0, T, cap);
-    const size_t half = align256(ws_bytes_for(L0, cap)), hb = align256((size_t)cap * L0.H * 4);
+    const StackLayout sl = stack_layout(L0, T);
     char *b = static_cast<char *>(ws);
-    char *wsl[2] = {b, b + half};
-    float *hbuf[2] = {reinterpret_cast<float *>(b + 2 * half), reinterpret_cast<float *>(b + 2 * half + hb)};
+    float *hbuf[2] = {reinterpret_cast<float *>(b + sl.h[0]), reinterpret_cast<float *>(b + sl.h[1])};
     auto F = [](char *p, size_t o) { return reinterpret_cast<float *>(p + o); };
     auto I32 = [](char *p, size_t o) { return reinterpret_cast<int32_t *>(p + o); };
     const uint32_t lf = (flags & (MOE_WALK_MASK | MOE_NO_MFMA)) | MOE_RMSNORM_IN | MOE_ACCUM_RESIDUAL;
@@ -290,23 +280,23 @@ moe_status moe_stack_fwd(const moe_layer_t *layers, int32_t n_layers, const floa
     const float *h = x;  // the current layer's input, the residual of its combine
     for (int l = 0; l < n_layers; ++l) {
         const moe_layer_t &L = layers[l];
-        char *wb = wsl[l & 1];
+        const WsLayout &wl = sl.half[l & 1];
         PrevCombine pc{};
         if (l > 0) {
-            char *pb = wsl[(l - 1) & 1];
-            pc = PrevCombine{F(pb, wl.y), F(pb, wl.w), h, hbuf[l & 1], L.top_k};
+            const WsLayout &pl = sl.half[(l - 1) & 1];
+            pc = PrevCombine{F(b, pl.y), F(b, pl.w), h, hbuf[l & 1], L.top_k};
             h = hbuf[l & 1];
         }
-        if ((s = hip_status(launch_route(L, h, nullptr, T, F(wb, wl.xn), F(wb, wl.logits), I32(wb, wl.ids),
-                                         F(wb, wl.w), I32(wb, wl.counts), I32(wb, wl.offsets), I32(wb, wl.sorted),
-                                         I32(wb, wl.uniq), I32(wb, wl.nuniq), I32(wb, wl.stats),
-                                         reinterpret_cast<unsigned *>(wb + wl.arrive), true, nullptr, 0, st,
+        if ((s = hip_status(launch_route(L, h, nullptr, T, F(b, wl.xn), F(b, wl.logits), I32(b, wl.ids),
+                                         F(b, wl.w), I32(b, wl.counts), I32(b, wl.offsets), I32(b, wl.sorted),
+                                         I32(b, wl.uniq), I32(b, wl.nuniq), I32(b, wl.stats),
+                                         reinterpret_cast<unsigned *>(b + wl.arrive), true, nullptr, 0, st,
                                          l > 0 ? &pc : nullptr))) != MOE_OK)
             return s;
-        Routing rt{I32(wb, wl.ids),  I32(wb, wl.counts), I32(wb, wl.offsets), I32(wb, wl.sorted),
-                   I32(wb, wl.uniq), I32(wb, wl.nuniq),  F(wb, wl.w),         I32(wb, wl.stats) + 2};
+        Routing rt{I32(b, wl.ids),  I32(b, wl.counts), I32(b, wl.offsets), I32(b, wl.sorted),
+                   I32(b, wl.uniq), I32(b, wl.nuniq),  F(b, wl.w),         I32(b, wl.stats) + 2, nullptr};
         // the last layer combines here; the others in the next routing launch
-        if ((s = hip_status(launch_experts(L, F(wb, wl.xn), h, T, rt, wb + wl.xb, F(wb, wl.act), F(wb, wl.y),
+        if ((s = hip_status(launch_experts(L, F(b, wl.xn), h, T, rt, b + wl.xb, F(b, wl.act), F(b, wl.y),
                                            l == n_layers - 1 ? out : nullptr, lf, st))) != MOE_OK)
             return s;
     }

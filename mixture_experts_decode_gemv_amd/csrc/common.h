@@ -256,27 +256,31 @@ __device__ __forceinline__ u32x4 load_weight_chunk(const u32x4 *p) { return __bu
 __host__ __device__ constexpr int rows_per_wave(int nc) { return nc <= 2 ? 8 : nc <= 4 ? 4 : 2; }
 
 // ---- workspace layout (all offsets 256-byte aligned) ----------------------
-// stats and the routing kernel's arrival counters come first, at offsets that
-// do not depend on the token count, so moe_workspace_init can zero them once.
-int route_arrive_words(int T);
+// A workspace starts with a front of fixed size: the statistics words and the
+// routing kernel's arrival counters, which must be zero when a call starts
+// and are zero again when it ends.  Their place and extent depend on nothing
+// (not on the batch, the layer shape or the workspace's byte size), so no
+// data array of any call ever lands on them, whatever sizes the calls on one
+// workspace pass.  The data arrays follow, laid out for the call's batch.
+constexpr int kMaxTokens = 65536;                  // tokens per call
+constexpr int kArriveWords = kMaxTokens + 1;       // per token tile (<= T) + 1
+inline constexpr size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+constexpr size_t kWsStats = 0;                     // 4 int32
+constexpr size_t kWsArrive = 256;
+constexpr size_t kWsFrontBytes = kWsArrive + align256((size_t)kArriveWords * 4);
 
 struct WsLayout {
     size_t stats, arrive, logits, ids, w, counts, offsets, sorted, uniq, nuniq, xn, xb, act, y, total;
 };
 
-inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
-
-// T tokens in a workspace that holds up to cap tokens (cap >= T).  The
-// synchronisation words are sized for cap, so they sit at the same offsets
-// for every batch size used with one workspace, and no data array of a
-// smaller batch ever lands on them.
-inline WsLayout ws_layout(const moe_layer_t &L, int64_t T, int64_t cap) {
+// T tokens: the front at `front`, the data arrays from `data` on.
+inline WsLayout ws_layout_at(const moe_layer_t &L, int64_t T, size_t front, size_t data) {
     WsLayout s;
     const int64_t R = T * L.top_k;
-    size_t o = 0;
+    s.stats = front + kWsStats;
+    s.arrive = front + kWsArrive;
+    size_t o = data;
     auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
-    s.stats = take(16);
-    s.arrive = take((size_t)route_arrive_words((int)cap) * 4);
     s.logits = take((size_t)T * L.E * 4);
     s.ids = take((size_t)R * 4);
     s.w = take((size_t)R * 4);
@@ -293,27 +297,13 @@ inline WsLayout ws_layout(const moe_layer_t &L, int64_t T, int64_t cap) {
     return s;
 }
 
-// Bytes for up to T tokens.
-inline size_t ws_bytes_for(const moe_layer_t &L, int64_t T) { return ws_layout(L, T, T).total; }
+inline size_t ws_data_bytes(const moe_layer_t &L, int64_t T) { return ws_layout_at(L, T, 0, 0).total; }
 
-// The largest token count a workspace of `bytes` bytes holds (-1 if none):
-// its capacity, which fixes where the synchronisation words sit.
-inline int64_t ws_capacity(const moe_layer_t &L, size_t bytes) {
-    if (bytes < ws_bytes_for(L, 0)) return -1;
-    int64_t lo = 0, hi = 1;
-    while (hi < (int64_t)1 << 30 && ws_bytes_for(L, hi) <= bytes) {
-        lo = hi;
-        hi *= 2;
-    }
-    while (hi - lo > 1) {
-        const int64_t mid = lo + (hi - lo) / 2;
-        if (ws_bytes_for(L, mid) <= bytes)
-            lo = mid;
-        else
-            hi = mid;
-    }
-    return lo;
-}
+// A layer workspace: the front, then the data arrays.
+inline WsLayout ws_layout(const moe_layer_t &L, int64_t T) { return ws_layout_at(L, T, 0, kWsFrontBytes); }
+
+// Bytes of a layer workspace for up to T tokens.
+inline size_t ws_bytes_for(const moe_layer_t &L, int64_t T) { return kWsFrontBytes + ws_data_bytes(L, T); }
 
 // ---- launchers (return hipSuccess or the launch error) -----------------------
 int num_cus();
@@ -346,6 +336,9 @@ struct Routing {
     const int32_t *ids, *counts, *offsets, *sorted, *uniq, *n_uniq;
     const float *w;
     const int32_t *max_count;  // largest count of one expert (from the sort), or null
+    // a caller-supplied routing's n_uniq (null for the library's own): when
+    // negative (rejected by the sort) the combine leaves out untouched
+    const int32_t *reject;
 };
 // ev (optional): events recorded after pass 1 GEMV, pass 1 MFMA, pass 2 GEMV,
 // pass 2 MFMA and the combine (ev[0..4]); a stage that does not run records

@@ -47,47 +47,65 @@ __global__ __launch_bounds__(kBlock) void to_bf16_kernel(const float2 *__restric
 // write disjoint routes, so for large batches the MFMA kernels run on a
 // second stream, forked from the caller's stream after routing and joined
 // before the combine; both halves then share the HBM bandwidth instead of
-// taking turns.  One stream and
-// two events per device, created on the first call made outside a graph
-// capture (until then the passes run in order on the caller's stream).  Calls
-// on one device share them: concurrent callers are serialised on the side
-// stream, which is still correct.
+// taking turns (2-4 % per step at 128-512 tokens).  Each (device, caller
+// stream) pair gets its own side stream and fork/join events, created on the
+// first such call made outside a graph capture and kept until the process
+// ends (at most kMaxSides pairs; further pairs, and a first call made under
+// capture, run the passes in order on the caller's stream).  The table
+// mutex is held from the lookup through the join, so the whole fork ->
+// record -> wait -> launches -> join sequence of one call is enqueued
+// without interleaving with another thread's; and since a side stream
+// serves a single caller stream, a caller stream under capture takes only
+// its own side stream into that capture.
 struct SideStream {
+    int dev = -1;
+    hipStream_t caller = nullptr;
     hipStream_t s = nullptr;
     hipEvent_t fork = nullptr, join = nullptr;
 };
 
-static SideStream *side_stream(hipStream_t st) {
-    static std::mutex mu;
-    static SideStream sides[64];
+constexpr int kMaxSides = 64;
+static std::mutex g_side_mu;
+static SideStream g_sides[kMaxSides];
+static int g_nsides = 0;
+
+// The side stream of (current device, caller stream st), created if needed;
+// null when none can be used.  The caller holds g_side_mu.
+static SideStream *side_stream_locked(hipStream_t st) {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-    std::lock_guard<std::mutex> lock(mu);
-    SideStream &sd = sides[dev];
-    if (sd.s) return &sd;
+    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+    for (int i = 0; i < g_nsides; ++i)
+        if (g_sides[i].dev == dev && g_sides[i].caller == st) return &g_sides[i];
+    if (g_nsides == kMaxSides) return nullptr;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
-    if (hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) != hipSuccess) {
-        sd.s = nullptr;
-        return nullptr;
-    }
+    SideStream sd;
+    sd.dev = dev;
+    sd.caller = st;
+    if (hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
     if (hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) != hipSuccess) {
-        if (sd.fork) hipEventDestroy(sd.fork);
-        hipStreamDestroy(sd.s);
-        sd = SideStream{};
+        if (sd.fork) (void)hipEventDestroy(sd.fork);
+        (void)hipStreamDestroy(sd.s);
         return nullptr;
     }
-    return &sd;
+    g_sides[g_nsides] = sd;
+    return &g_sides[g_nsides++];
 }
 
 // ---- combine ------------------------------------------------------------------
 // out may alias xres: each thread reads its residual before storing there.
+// reject (a caller-supplied routing's n_uniq, or null): when it is negative
+// the sort rejected the routing, no expert pass ran, and out is left as it
+// was.  It is read alongside the y rows and tested only before the store, so
+// it adds no round trip.
 __global__ __launch_bounds__(kBlock) void combine_kernel(const float *__restrict__ y, const float *__restrict__ w,
-                                                         const float *xres, float *out, int k, int H) {
+                                                         const float *xres, float *out, int k, int H,
+                                                         const int32_t *reject) {
     const int t = blockIdx.x;
     const int h = (blockIdx.y * kBlock + threadIdx.x) * 4;
     if (h >= H) return;
+    const int nu = reject ? __builtin_nontemporal_load(reject) : 0;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     // routes in groups of 8 with every load of a group issued before its
     // FMAs (j ascending): one memory round trip per group, not per route
@@ -115,6 +133,7 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const float *__restrict
         const float4 r = *reinterpret_cast<const float4 *>(xres + (size_t)t * H + h);
         acc.x += r.x; acc.y += r.y; acc.z += r.z; acc.w += r.w;
     }
+    if (nu < 0) return;
     *reinterpret_cast<float4 *>(out + (size_t)t * H + h) = acc;
 }
 
@@ -241,7 +260,7 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
     auto combine = [&]() {
         if (!out) return hipSuccess;  // a stack: the next layer's routing launch combines
         hipLaunchKernelGGL(combine_kernel, dim3(T, (L.H / 4 + kBlock - 1) / kBlock), dim3(kBlock), 0, st, y, rt.w,
-                           xres, out, L.top_k, L.H);
+                           xres, out, L.top_k, L.H, rt.reject);
         return hipGetLastError();
     };
     hipError_t err;
@@ -253,7 +272,13 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
     // exit on the sort's maximum count), and an idle launch running beside
     // the GEMV pass costs it more than it costs in order.  Not when the
     // caller times the stages: then everything runs in order on its stream.
-    SideStream *sd = (mfma && !ev && T >= kMfmaWideTokens) ? side_stream(st) : nullptr;
+    std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
+    SideStream *sd = nullptr;
+    if (mfma && !ev && T >= kMfmaWideTokens) {
+        side_lock.lock();  // held until this call's join is enqueued
+        sd = side_stream_locked(st);
+        if (!sd) side_lock.unlock();
+    }
     if (sd) {
         MOE_TRY(hipEventRecord(sd->fork, st));
         MOE_TRY(hipStreamWaitEvent(sd->s, sd->fork, 0));

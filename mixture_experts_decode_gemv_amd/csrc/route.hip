@@ -319,7 +319,6 @@ static hipError_t route_dispatch(int nc, dim3 g, size_t lds, hipStream_t st, con
     return hipGetLastError();
 }
 
-int route_arrive_words(int T) { return T + 1; }
 
 hipError_t launch_route(const moe_layer_t &L, const float *x, const float *logits_in, int T, float *xn,
                         float *logits, int32_t *ids, float *w, int32_t *counts, int32_t *offsets, int32_t *sorted,

@@ -98,24 +98,27 @@ def test_routing_accessor_points_into_the_workspace():
         moe.moe_layer_routing(L, 4, 0x10000, 8)
 
 
-def test_workspace_data_starts_at_a_fixed_offset_for_every_batch():
-    """The synchronisation words are laid out for the workspace's capacity
-    (fixed by its size), so the data region (logits first) starts at the same
-    offset for every batch size the workspace holds, and a batch larger than
-    the capacity is refused."""
-    L = _layer()
-    n = moe.moe_workspace_bytes(L, 64)
+def test_workspace_front_is_fixed():
+    """The synchronisation words sit in a front of fixed size at the start of
+    every workspace, whatever the batch, the layer shape or the byte size the
+    call passes: the data region (logits first) starts at the same offset
+    for all of them.  A batch larger than ws_bytes holds, or above 65536
+    tokens, is refused."""
     starts = set()
-    for T in (1, 3, 17, 64):
-        r = moe.moe_layer_routing(L, T, 0x10000, n)
-        starts.add(r["topk_ids"] - ((T * L.E * 4 + 255) // 256) * 256)
-    assert len(starts) == 1
-    big = 64
-    while moe.moe_workspace_bytes(L, big + 1) <= n:
-        big += 1
-    moe.moe_layer_routing(L, big, 0x10000, n)
-    with pytest.raises(moe.MoeError):
-        moe.moe_layer_routing(L, big + 1, 0x10000, n)
+    for L in (_layer(), _layer(E=256, top_k=8, H=2048, I=768, expert_dtype=moe.MOE_BF16,
+                               router_dtype=moe.MOE_BF16)):
+        for cap in (64, 300):
+            n = moe.moe_workspace_bytes(L, cap)
+            for T in (1, 3, 17, 64):
+                r = moe.moe_layer_routing(L, T, 0x10000, n)
+                starts.add(r["topk_ids"] - 0x10000 - ((T * L.E * 4 + 255) // 256) * 256)
+            with pytest.raises(moe.MoeError):
+                moe.moe_layer_routing(L, cap + 1, 0x10000, n)
+    assert len(starts) == 1 and starts.pop() >= 65537 * 4
+    L = _layer()
+    assert moe.moe_workspace_bytes(L, 65536) > 0
+    assert moe.moe_workspace_bytes(L, 65537) == 0
+    assert moe.moe_stack_workspace_bytes(L, 65537) == 0
 
 
 def test_expert_usage_argument_errors():

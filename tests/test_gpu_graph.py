@@ -94,3 +94,60 @@ def test_mfma_layer_graph_equals_eager_bitwise(T):
         moe.moe_layer_fwd_events(layer.struct, x0, T, out, 0, ws, ws.numel(), stream, [e.cuda_event for e in evs])
     stream.synchronize()
     assert np.array_equal(out.cpu().numpy(), ref)
+
+
+def test_forked_calls_from_two_threads_on_two_streams():
+    """Two host threads, each on its own stream and workspace, call the
+    large-batch path (MFMA segments on a side stream forked from the caller's)
+    many times at once, one of them also while capturing a graph: every
+    output equals the in-order run bitwise.  Each caller stream has its own
+    side stream and events, and one call's fork/join sequence is enqueued
+    without interleaving with the other thread's."""
+    import threading
+
+    T = 300
+    bias = np.zeros(MIXED.E, np.float32)
+    bias[:3] = 2.0
+    w, layer, olayer = make_device_layer(MIXED, bias)
+    xs = [torch.from_numpy(wl.make_x(T, MIXED.H, draw=40 + i)).to(dev()) for i in range(2)]
+    refs = []
+    for i in range(2):  # in-order reference (stage events requested)
+        s = torch.cuda.Stream(dev())
+        ws = layer.workspace(T, s)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(moe.MOE_N_STAGES + 1)]
+        for e in evs:
+            e.record(s)
+        out = torch.empty_like(xs[i])
+        with torch.cuda.stream(s):
+            moe.moe_layer_fwd_events(layer.struct, xs[i], T, out, 0, ws, ws.numel(), s, [e.cuda_event for e in evs])
+        s.synchronize()
+        refs.append(out.cpu().numpy())
+    note("two threads, T=%d" % T)
+    streams = [torch.cuda.Stream(dev()) for _ in range(2)]
+    wss = [layer.workspace(T, s) for s in streams]
+    outs = [[torch.empty_like(xs[i]) for _ in range(8)] for i in range(2)]
+    torch.cuda.synchronize()
+    errors = []
+    barrier = threading.Barrier(2)
+
+    def worker(i):
+        try:
+            torch.cuda.set_device(dev())
+            s = streams[i]
+            barrier.wait()
+            with torch.cuda.stream(s):
+                for o in outs[i]:
+                    moe.moe_layer_fwd(layer.struct, xs[i], T, o, 0, wss[i], wss[i].numel(), s)
+            s.synchronize()
+        except Exception as exc:  # noqa: BLE001 - reported below
+            errors.append(exc)
+
+    th = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    assert not errors, errors
+    for i in range(2):
+        for o in outs[i]:
+            assert np.array_equal(o.cpu().numpy(), refs[i])

@@ -1,10 +1,11 @@
-"""One workspace serves every batch size up to its capacity: calls of
-different sizes in any order give bitwise the results of a fresh workspace,
-and the synchronisation words at its front are zero again after each call.
+"""One workspace serves every batch size it holds: calls of different
+sizes in any order give bitwise the results of a fresh workspace, and the
+synchronisation words at its front are zero again after each call.
 
-The synchronisation words (the routing kernel's arrival counters) are laid
-out for the workspace's capacity, fixed by its size, so a small batch's
-logits or routing arrays never land on the counters a larger batch uses.
+The synchronisation words (the routing kernel's arrival counters) sit in a
+front of fixed size and place, so no call's logits or routing arrays ever
+land on them, whatever batch, layer shape or byte size the calls on one
+workspace pass.
 """
 import numpy as np
 import pytest
@@ -54,9 +55,33 @@ def test_batch_sizes_interleaved_on_one_workspace(spec, flags, sizes):
         _front_is_clear(layer, T, ws)
 
 
+def test_byte_sizes_and_layer_shapes_alternate_on_one_buffer():
+    """One buffer, passed with its full size and with the smaller sizes two
+    other batches need, and shared by layers of two shapes: every call equals
+    a fresh workspace bitwise, and the front is clear after each."""
+    wa, la, _ = make_device_layer(wl.SWEEP)
+    wb, lb, _ = make_device_layer(wl.TINY)
+    xa = {T: wl.make_x(T, wl.SWEEP.H, draw=720 + T) for T in (8, 2)}
+    xb = {T: wl.make_x(T, wl.TINY.H, draw=730 + T) for T in (5,)}
+    ref = {("a", T): _run(la, xa[T], T, 0, la.workspace(T)) for T in xa}
+    ref[("b", 5)] = _run(lb, xb[5], 5, 0, lb.workspace(5))
+    ws = la.workspace(8)
+    plan = [("a", 8, ws.numel()), ("a", 2, moe.moe_workspace_bytes(la.struct, 2)),
+            ("b", 5, moe.moe_workspace_bytes(lb.struct, 5)), ("a", 8, ws.numel()),
+            ("b", 5, ws.numel()), ("a", 2, moe.moe_workspace_bytes(la.struct, 2)), ("a", 8, ws.numel())]
+    for name, T, nbytes in plan:
+        note("shared buffer: layer %s T=%d ws_bytes=%d" % (name, T, nbytes))
+        layer, x = (la, xa[T]) if name == "a" else (lb, xb[T])
+        xd = to_dev(x.astype(np.float32))
+        out = torch.full_like(xd, float("nan"))
+        moe.moe_layer_fwd(layer.struct, xd, T, out, 0, ws, nbytes, stream())
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), ref[(name, T)]), (name, T, nbytes)
+        _front_is_clear(layer, T, ws)
+
+
 def test_larger_workspace_than_needed():
-    """A workspace bigger than moe_workspace_bytes(T) (its capacity is then
-    larger than the batch) gives the same bits."""
+    """A workspace bigger than moe_workspace_bytes(T) gives the same bits."""
     w, layer, olayer = make_device_layer(wl.SWEEP)
     x = wl.make_x(8, wl.SWEEP.H, draw=990)
     a = _run(layer, x, 8, 0, layer.workspace(8))
