@@ -275,13 +275,13 @@ def _run_large(fixture, T):
     assert (c >= MFMA_MIN).any()
 
 
-@pytest.mark.parametrize("T", [128, 512])
+@pytest.mark.parametrize("T", [128, 256, 512])
 def test_large_bf16_sampled(large_bf16, T):
     note("large bf16 T=%d" % T)
     _run_large(large_bf16, T)
 
 
-@pytest.mark.parametrize("T", [128, 512])
+@pytest.mark.parametrize("T", [128, 256, 512])
 def test_large_fp8_sampled(large_fp8, T):
     note("large fp8 T=%d" % T)
     _run_large(large_fp8, T)

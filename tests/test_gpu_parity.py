@@ -114,6 +114,41 @@ def test_sort_flags_bad_id(T):
 
 # -------------------------------------------------------------------- experts --
 
+@pytest.mark.parametrize("walk", [moe.MOE_WALK_DEDUP, moe.MOE_WALK_PER_ROUTE, moe.MOE_WALK_DEDUP_PASS1])
+@pytest.mark.parametrize("flags", [0, moe.MOE_ACCUM_RESIDUAL])
+def test_expert_fwd_rejected_routing_leaves_out_untouched(walk, flags):
+    """A routing that the sort rejects (an id outside [0, E): n_uniq = -1)
+    runs no expert work, and the combine leaves out as it was."""
+    note("expert_fwd rejected routing walk=%d flags=%d" % (walk, flags))
+    w, layer, olayer = make_device_layer(wl.TINY)
+    T, s = 4, wl.TINY
+    ids = np.tile(np.array([[0, 3]], np.int32), (T, 1))
+    ids[2, 1] = s.E  # out of range
+    d_ids = torch.from_numpy(ids).to(dev())
+    d_w = torch.full((T, s.top_k), 0.5, dtype=torch.float32, device=dev())
+    counts = torch.empty(s.E, dtype=torch.int32, device=dev())
+    offsets = torch.empty(s.E + 1, dtype=torch.int32, device=dev())
+    sorted_routes = torch.empty(T * s.top_k, dtype=torch.int32, device=dev())
+    uniq = torch.empty(s.E, dtype=torch.int32, device=dev())
+    n = torch.empty(1, dtype=torch.int32, device=dev())
+    st = torch.cuda.current_stream()
+    x = torch.from_numpy(wl.make_x(T, s.H, draw=5)).to(dev())
+    out = torch.full((T, s.H), 7.25, dtype=torch.float32, device=dev())
+    ws = layer.workspace(T)
+    # a valid routing first, so the workspace's y rows and the routing
+    # arrays hold plausible values
+    good = torch.from_numpy(np.tile(np.array([[0, 3]], np.int32), (T, 1))).to(dev())
+    moe.moe_sort(good, T, s.top_k, s.E, counts, offsets, sorted_routes, uniq, n, st)
+    moe.moe_expert_fwd(layer.struct, x, T, good, d_w, counts, offsets, sorted_routes, uniq, n,
+                       torch.empty_like(out), walk, ws, ws.numel(), st)
+    moe.moe_sort(d_ids, T, s.top_k, s.E, counts, offsets, sorted_routes, uniq, n, st)
+    moe.moe_expert_fwd(layer.struct, x, T, d_ids, d_w, counts, offsets, sorted_routes, uniq, n, out,
+                       walk | flags, ws, ws.numel(), st)
+    torch.cuda.synchronize()
+    assert int(n.item()) == -1
+    assert (out == 7.25).all()
+
+
 def _oracle_routing(olayer, x):
     lg = oracle.router_logits(olayer, x)
     return oracle.select(lg, olayer.k)
@@ -271,7 +306,7 @@ def test_sweep_token_permutation_bitwise(sweep_layer):
     assert np.array_equal(a[perm], b)
 
 
-@pytest.mark.parametrize("T", [1, 64])
+@pytest.mark.parametrize("T", [1, 8, 32, 64])
 def test_layer_skewed(T):
     note("layer skewed k=6 T=%d" % T)
     bias = wl.zipf_bias(wl.SKEWED.E)
@@ -300,6 +335,19 @@ def test_stack_layers_rmsnorm_residual_teacher_forced():
         flags = moe.MOE_RMSNORM_IN | moe.MOE_ACCUM_RESIDUAL
         check_layer_against_oracle(layer, olayer, h, flags=flags, tol=1e-4, rmsnorm_in=True, residual=True)
         h = gpu_layer_fwd(layer, h, flags)
+        del layer
+
+
+def test_stack_shape_layer_bs1_rmsnorm_residual():
+    """The 30-layer stack's layer shape (E=128, top_k=2, H=2048, I=1024) at
+    one token, RMSNorm before the router and the residual after the combine,
+    against the oracle (GEMV segments only at one token: fp32 bar)."""
+    flags = moe.MOE_RMSNORM_IN | moe.MOE_ACCUM_RESIDUAL
+    for l in (0, 7):
+        note("stack-shape layer %d T=1" % l)
+        w, layer, olayer = make_device_layer(wl.STACK, layer_idx=l)
+        x = wl.make_x(1, wl.STACK.H, draw=310 + l)
+        check_layer_against_oracle(layer, olayer, x, flags=flags, tol=1e-4, rmsnorm_in=True, residual=True)
         del layer
 
 

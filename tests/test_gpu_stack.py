@@ -13,8 +13,9 @@ import pytest
 import torch
 
 import mixture_experts_decode_gemv_amd as moe
+import oracle
 import workload as wl
-from gpu_util import dev, note
+from gpu_util import (ambiguous_tokens, dev, gpu_layer_fwd, max_rel, note, oracle_for_gpu_selection)
 
 pytestmark = pytest.mark.gpu
 
@@ -69,6 +70,41 @@ def test_stack_fused_equals_layer_calls_stack_shape(stack3, T):
     assert np.isfinite(ref).all()
     assert np.array_equal(_fused(stack3, x0, T, 0), ref)
     assert np.array_equal(_fused(stack3, x0, T, 0, in_place=True), ref)
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_stack_fused_against_oracle(stack3, T):
+    """moe_stack_fwd against the oracle, layer by layer and teacher-forced:
+    the fused stacks of the first l and l + 1 layers give the GPU's h_l and
+    h_{l+1}; the oracle layer (RMSNorm, router, top-k, experts, combine,
+    residual) applied to h_l must give h_{l+1}.  A token whose oracle logits
+    have a near tie may be routed either way; it is compared against the
+    oracle rerun with the GPU's ids for that layer (from a layer call on the
+    same h_l, which routes bitwise as the stack does)."""
+    x0 = torch.from_numpy(wl.make_x(T, wl.STACK.H, draw=131 + T)).to(dev())
+    hs = [x0.cpu().numpy()]
+    for n in range(1, len(stack3) + 1):
+        note("fused stack prefix of %d layers, T=%d" % (n, T))
+        hs.append(_fused(stack3[:n], x0, T, 0))
+    for l in range(len(stack3)):
+        note("oracle check of stack layer %d, T=%d" % (l, T))
+        olayer = oracle.Layer(wl.make_layer(wl.STACK, layer=l))
+        h_in, h_out = hs[l], hs[l + 1]
+        ref = oracle.moe_layer(olayer, h_in, rmsnorm_in=True, residual=True)
+        ids = gpu_layer_fwd(stack3[l], h_in, NORM_RES, full=True)["ids"]
+        amb = ambiguous_tokens(ref["logits"], wl.STACK.top_k)
+        same = (ids == ref["ids"]).all(1)
+        assert (same | amb).all(), "layer %d: selection differs on tokens with a clear gap" % l
+        expect = ref["out"].copy()
+        if (~same).any():
+            alt = oracle_for_gpu_selection(olayer, h_in, ref["logits"], ids, rmsnorm_in=True, residual=True)
+            expect[~same] = alt[~same]
+        assert np.isfinite(h_out).all()
+        assert max_rel(h_out, expect) <= 1e-4, "layer %d" % l
+        # the MoE part alone (the residual removed on both sides)
+        moe_gpu = h_out.astype(np.float64) - h_in
+        moe_ref = expect - h_in.astype(np.float64)
+        assert max_rel(moe_gpu, moe_ref) <= 1e-4, "layer %d (MoE part)" % l
 
 
 @pytest.mark.parametrize("T", [1, 9, 40, 130])

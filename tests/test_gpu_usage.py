@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import mixture_experts_decode_gemv_amd as moe
+import oracle
 import workload as wl
 from gpu_util import dev, gpu_layer_fwd, make_device_layer, note, stream, to_dev
 
@@ -28,7 +29,7 @@ def test_usage_accumulates_the_counts_of_every_step():
         torch.cuda.synchronize()
         ids = ws[r["topk_ids"] - ws.data_ptr():r["topk_ids"] - ws.data_ptr() + T * wl.SWEEP.top_k * 4]
         ids = ids.view(torch.int32).cpu().numpy()
-        expect += np.bincount(ids, minlength=wl.SWEEP.E)
+        expect += oracle.sort(ids.reshape(T, wl.SWEEP.top_k), wl.SWEEP.E)["counts"]
         assert np.array_equal(hist.cpu().numpy(), expect), "step %d" % d
     assert int(expect.sum()) == 5 * T * wl.SWEEP.top_k
 
