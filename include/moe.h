@@ -178,6 +178,26 @@ moe_status moe_expert_fwd(const moe_layer_t *layer, const float *x, int32_t T, c
 moe_status moe_layer_fwd(const moe_layer_t *layer, const float *x, int32_t T, float *out, uint32_t flags,
                          void *ws, size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the layer
+ * exactly as moe_layer_fwd computes it, bit for bit, with its scratch in a
+ * device array that the library holds instead of a caller workspace:
+ * MOE_STATIC_SCRATCH_BYTES (16 MiB) on each GPU the library runs on, kept
+ * until the process ends.  The caller passes inputs and outputs only.  A
+ * batch whose layer needs more scratch than that
+ * (moe_workspace_bytes(layer, T) > MOE_STATIC_SCRATCH_BYTES, e.g. beyond
+ * 159 tokens for E=256, top_k=8, H=2048, I=768) is refused with
+ * MOE_ERR_WORKSPACE before anything is enqueued.  No memory is allocated:
+ * the first call on a device looks the array's address up and clears its
+ * synchronisation words with a fill kernel on `stream`, and every call
+ * leaves them clear again.  All calls on one GPU share the array, which
+ * keeps the last call's contents, so calls that overlap on one GPU race:
+ * order them on one stream.  The matrix-core segments of large batches run
+ * in order on `stream` (no side stream). */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+moe_status moe_layer_fwd_static(const moe_layer_t *layer, const float *x, int32_t T, float *out, uint32_t flags,
+                                void *stream);
+
 /* moe_layer_fwd with per-stage timing: events[s] (hipEvent_t, created by
  * the caller with timing enabled) is recorded on `stream` before stage s and
  * events[MOE_N_STAGES] after the last, for the stages

@@ -7,7 +7,7 @@ missing or fails to load, importing the functions raises.
 
 Entry points (same names as ``include/moe.h``): ``moe_workspace_bytes``,
 ``moe_workspace_init``, ``moe_route``, ``moe_sort``, ``moe_expert_fwd``,
-``moe_layer_fwd``, ``moe_layer_fwd_events``, ``moe_layer_routing``,
+``moe_layer_fwd``, ``moe_layer_fwd_static``, ``moe_layer_fwd_events``, ``moe_layer_routing``,
 ``moe_expert_usage``, ``moe_stack_workspace_bytes``,
 ``moe_stack_workspace_init``, ``moe_stack_fwd``, ``moe_status_str``.  Tensor arguments may be torch
 tensors (their ``data_ptr()`` is passed), raw integer device addresses or
@@ -31,10 +31,11 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE",
           5: "MOE_ERR_HIP", 6: "MOE_ERR_UNSUPPORTED", 7: "MOE_ERR_ALIGN"}
 
 EXPORTS = ("moe_workspace_bytes", "moe_workspace_init", "moe_route", "moe_sort", "moe_expert_fwd", "moe_layer_fwd",
-           "moe_layer_fwd_events", "moe_layer_routing", "moe_expert_usage", "moe_stack_workspace_bytes",
+           "moe_layer_fwd_static", "moe_layer_fwd_events", "moe_layer_routing", "moe_expert_usage", "moe_stack_workspace_bytes",
            "moe_stack_workspace_init", "moe_stack_fwd", "moe_status_str")
 
 MOE_N_STAGES = 6
+MOE_STATIC_SCRATCH_BYTES = 16 << 20
 STAGES = ("routing", "pass1_gemv", "pass1_mfma", "pass2_gemv", "pass2_mfma", "combine")
 
 
@@ -75,6 +76,8 @@ def lib():
         L.moe_expert_fwd.argtypes = [P, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, u32, vp, sz, vp]
         L.moe_layer_fwd.restype = ctypes.c_int
         L.moe_layer_fwd.argtypes = [P, vp, i32, vp, u32, vp, sz, vp]
+        L.moe_layer_fwd_static.restype = ctypes.c_int
+        L.moe_layer_fwd_static.argtypes = [P, vp, i32, vp, u32, vp]
         L.moe_layer_fwd_events.restype = ctypes.c_int
         L.moe_layer_fwd_events.argtypes = [P, vp, i32, vp, u32, vp, sz, vp, ctypes.POINTER(ctypes.c_void_p)]
         pp = ctypes.POINTER(ctypes.c_void_p)
@@ -156,6 +159,12 @@ def moe_expert_fwd(layer, x, T, topk_ids, topk_w, counts, offsets, sorted_routes
 def moe_layer_fwd(layer, x, T, out, flags=0, ws=None, ws_bytes=0, stream=None):
     _check("moe_layer_fwd", lib().moe_layer_fwd(ctypes.byref(layer), _p(x), int(T), _p(out), int(flags), _p(ws),
                                                 int(ws_bytes), _s(stream)))
+
+
+def moe_layer_fwd_static(layer, x, T, out, flags=0, stream=None):
+    """moe_layer_fwd with the library's own device scratch (no workspace)."""
+    _check("moe_layer_fwd_static", lib().moe_layer_fwd_static(ctypes.byref(layer), _p(x), int(T), _p(out),
+                                                              int(flags), _s(stream)))
 
 
 def moe_layer_fwd_events(layer, x, T, out, flags=0, ws=None, ws_bytes=0, stream=None, events=None):

@@ -7,7 +7,17 @@
 // host read between router and experts).
 #include <stdint.h>
 
+#include <mutex>
+
 #include "common.h"
+
+// ---- scratch of the allocation-free entry point -----------------------------
+// Device memory the library holds for moe_layer_fwd_static: each GPU the
+// library runs on has its own copy, for as long as the process runs.  In host
+// code this name is only a stand-in for the symbol: its device address comes
+// from hipGetSymbolAddress (static_scratch below), and only that address is
+// ever passed to a kernel or a fill.
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_SCRATCH_BYTES];
 
 namespace moe {
 
@@ -146,7 +156,7 @@ moe_status moe_expert_fwd(const moe_layer_t *layer, const float *x, int32_t T, c
 }
 
 static moe_status layer_fwd(const moe_layer_t *layer, const float *x, int32_t T, float *out, uint32_t flags,
-                            void *ws, size_t ws_bytes, void *stream, const hipEvent_t *ev) {
+                            void *ws, size_t ws_bytes, void *stream, const hipEvent_t *ev, bool may_fork = true) {
     moe_status s = check_layer(layer);
     if (s != MOE_OK) return s;
     if ((s = check_weights(layer, true, true)) != MOE_OK) return s;
@@ -173,12 +183,48 @@ static moe_status layer_fwd(const moe_layer_t *layer, const float *x, int32_t T,
     Routing rt{I32(wl.ids),  I32(wl.counts), I32(wl.offsets), I32(wl.sorted),
                I32(wl.uniq), I32(wl.nuniq),  F(wl.w),         I32(wl.stats) + 2, nullptr};
     return hip_status(launch_experts(*layer, xin, (flags & MOE_ACCUM_RESIDUAL) ? x : nullptr, T, rt, b + wl.xb,
-                                     F(wl.act), F(wl.y), out, flags, st, ev ? ev + 2 : nullptr));
+                                     F(wl.act), F(wl.y), out, flags, st, ev ? ev + 2 : nullptr, may_fork));
 }
 
 moe_status moe_layer_fwd(const moe_layer_t *layer, const float *x, int32_t T, float *out, uint32_t flags, void *ws,
                          size_t ws_bytes, void *stream) {
     return layer_fwd(layer, x, T, out, flags, ws, ws_bytes, stream, nullptr);
+}
+
+// The device address of this GPU's scratch array, looked up on the first
+// call on the device (with the device current), when its synchronisation
+// front is also cleared by a fill kernel on `st`; kept per device after that.
+static moe_status static_scratch(hipStream_t st, void **out) {
+    static std::mutex mu;
+    static void *ptr[64] = {nullptr};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    if (dev < 0 || dev >= 64) return MOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+        if (launch_zero(static_cast<unsigned *>(p), (int)(kWsFrontBytes / 4), st) != hipSuccess) return MOE_ERR_HIP;
+        ptr[dev] = p;
+    }
+    *out = ptr[dev];
+    return MOE_OK;
+}
+
+moe_status moe_layer_fwd_static(const moe_layer_t *layer, const float *x, int32_t T, float *out, uint32_t flags,
+                                void *stream) {
+    moe_status s = check_layer(layer);
+    if (s != MOE_OK) return s;
+    if ((s = check_weights(layer, true, true)) != MOE_OK) return s;
+    if (T < 0 || !x || !out) return MOE_ERR_ARG;
+    if ((flags & MOE_WALK_MASK) > MOE_WALK_DEDUP_PASS1) return MOE_ERR_ARG;
+    if (!aligned16(x) || !aligned16(out)) return MOE_ERR_ALIGN;
+    if (T == 0) return MOE_OK;
+    if (T > kMaxTokens) return MOE_ERR_SHAPE;
+    if (ws_bytes_for(*layer, T) > MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if ((s = static_scratch((hipStream_t)stream, &ws)) != MOE_OK) return s;
+    return layer_fwd(layer, x, T, out, flags, ws, MOE_STATIC_SCRATCH_BYTES, stream, nullptr, false);
 }
 
 moe_status moe_layer_fwd_events(const moe_layer_t *layer, const float *x, int32_t T, float *out, uint32_t flags,

@@ -345,8 +345,10 @@ struct Routing {
 // its event right after the previous one.
 // xb: scratch for a bf16 copy of x [T, H] (used when segments take the MFMA path).
 // out null: no combine (y and rt.w are left for the next layer of a stack).
+// may_fork false: the MFMA segments of large batches stay on st (no side
+// stream is created or used).
 hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xres, int T, const Routing &rt,
                           void *xb, float *act, float *y, float *out, uint32_t flags, hipStream_t st,
-                          const hipEvent_t *ev = nullptr);
+                          const hipEvent_t *ev = nullptr, bool may_fork = true);
 
 }  // namespace moe

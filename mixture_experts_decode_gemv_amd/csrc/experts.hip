@@ -191,7 +191,7 @@ static hipError_t launch_mfma_pass(const moe_layer_t &L, int pass, int T, const 
 
 hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xres, int T, const Routing &rt,
                           void *xb, float *act, float *y, float *out, uint32_t flags, hipStream_t st,
-                          const hipEvent_t *ev) {
+                          const hipEvent_t *ev, bool may_fork) {
     const int R = T * L.top_k;
     const int walk = (int)(flags & MOE_WALK_MASK);
     const int epc = elems_per_chunk(L.expert_dtype);
@@ -274,7 +274,7 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
     // caller times the stages: then everything runs in order on its stream.
     std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
     SideStream *sd = nullptr;
-    if (mfma && !ev && T >= kMfmaWideTokens) {
+    if (mfma && !ev && may_fork && T >= kMfmaWideTokens) {
         side_lock.lock();  // held until this call's join is enqueued
         sd = side_stream_locked(st);
         if (!sd) side_lock.unlock();

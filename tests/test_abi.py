@@ -176,3 +176,21 @@ def test_stack_workspace_and_argument_errors():
         except moe.MoeError as e:
             st = e.status
         assert st == (1 if bad is None else 7)
+
+
+def test_static_entry_point_validation():
+    """moe_layer_fwd_static refuses bad arguments and a batch that needs more
+    than its 16 MiB of scratch on the host, before anything is enqueued."""
+    lib = moe.lib()
+    L = _layer(E=256, top_k=8, H=2048, I=768, expert_dtype=moe.MOE_BF16, router_dtype=moe.MOE_BF16)
+    x = out = 0x10000
+    assert moe.MOE_STATIC_SCRATCH_BYTES == 16 << 20
+    assert moe.moe_workspace_bytes(L, 159) <= moe.MOE_STATIC_SCRATCH_BYTES < moe.moe_workspace_bytes(L, 160)
+    assert lib.moe_layer_fwd_static(ctypes.byref(L), x, 160, out, 0, None) == 4   # scratch too small
+    assert lib.moe_layer_fwd_static(ctypes.byref(L), x, 70000, out, 0, None) == 2  # above 65536 tokens
+    assert lib.moe_layer_fwd_static(ctypes.byref(L), None, 4, out, 0, None) == 1
+    assert lib.moe_layer_fwd_static(ctypes.byref(L), x, -1, out, 0, None) == 1
+    assert lib.moe_layer_fwd_static(ctypes.byref(L), x, 4, out, 3, None) == 1     # no such walk
+    assert lib.moe_layer_fwd_static(ctypes.byref(L), 0x10004, 4, out, 0, None) == 7
+    assert lib.moe_layer_fwd_static(ctypes.byref(L), x, 0, out, 0, None) == 0     # no-op
+    assert lib.moe_layer_fwd_static(ctypes.byref(_layer(top_k=9)), x, 4, out, 0, None) == 1
