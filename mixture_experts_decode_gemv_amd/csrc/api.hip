@@ -323,12 +323,17 @@ moe_status moe_stack_fwd(const moe_layer_t *layers, int32_t n_layers, const floa
     auto I32 = [](char *p, size_t o) { return reinterpret_cast<int32_t *>(p + o); };
     const uint32_t lf = (flags & (MOE_WALK_MASK | MOE_NO_MFMA)) | MOE_RMSNORM_IN | MOE_ACCUM_RESIDUAL;
 
+    // Small batches: every layer writes its output rows itself (pass 2 and
+    // the combine in one launch).  Otherwise each layer's combine runs in the
+    // next layer's routing launch and only the last layer launches one.
+    const bool direct = fused_combine(L0, T);
     const float *h = x;  // the current layer's input, the residual of its combine
     for (int l = 0; l < n_layers; ++l) {
         const moe_layer_t &L = layers[l];
         const WsLayout &wl = sl.half[l & 1];
+        const bool last = l == n_layers - 1;
         PrevCombine pc{};
-        if (l > 0) {
+        if (l > 0 && !direct) {
             const WsLayout &pl = sl.half[(l - 1) & 1];
             pc = PrevCombine{F(b, pl.y), F(b, pl.w), h, hbuf[l & 1], L.top_k};
             h = hbuf[l & 1];
@@ -337,14 +342,15 @@ moe_status moe_stack_fwd(const moe_layer_t *layers, int32_t n_layers, const floa
                                          F(b, wl.w), I32(b, wl.counts), I32(b, wl.offsets), I32(b, wl.sorted),
                                          I32(b, wl.uniq), I32(b, wl.nuniq), I32(b, wl.stats),
                                          reinterpret_cast<unsigned *>(b + wl.arrive), true, nullptr, 0, st,
-                                         l > 0 ? &pc : nullptr))) != MOE_OK)
+                                         l > 0 && !direct ? &pc : nullptr))) != MOE_OK)
             return s;
         Routing rt{I32(b, wl.ids),  I32(b, wl.counts), I32(b, wl.offsets), I32(b, wl.sorted),
                    I32(b, wl.uniq), I32(b, wl.nuniq),  F(b, wl.w),         I32(b, wl.stats) + 2, nullptr};
-        // the last layer combines here; the others in the next routing launch
-        if ((s = hip_status(launch_experts(L, F(b, wl.xn), h, T, rt, b + wl.xb, F(b, wl.act), F(b, wl.y),
-                                           l == n_layers - 1 ? out : nullptr, lf, st))) != MOE_OK)
+        float *dst = last ? out : direct ? hbuf[l & 1] : nullptr;
+        if ((s = hip_status(launch_experts(L, F(b, wl.xn), h, T, rt, b + wl.xb, F(b, wl.act), F(b, wl.y), dst, lf,
+                                           st))) != MOE_OK)
             return s;
+        if (direct) h = dst;
     }
     return MOE_OK;
 }

@@ -345,6 +345,9 @@ struct Routing {
 // its event right after the previous one.
 // xb: scratch for a bf16 copy of x [T, H] (used when segments take the MFMA path).
 // out null: no combine (y and rt.w are left for the next layer of a stack).
+// Whether launch_experts runs pass 2 and the combine as one launch for T
+// tokens (small batches): then it needs out, and writes no y rows.
+bool fused_combine(const moe_layer_t &L, int T);
 // may_fork false: the MFMA segments of large batches stay on st (no side
 // stream is created or used).
 hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xres, int T, const Routing &rt,

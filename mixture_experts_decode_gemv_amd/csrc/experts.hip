@@ -165,6 +165,18 @@ static bool mfma_eligible(const moe_layer_t &L, int T, uint32_t flags) {
            offsets32;
 }
 
+// Pass 2 and the combine in one launch (pass2c_kernel) for small batches with
+// an output to write: the y block of a workgroup ([R][rows] floats) must fit
+// in 64 KiB of LDS.  The same predicate tells a layer stack whether each
+// layer writes its output rows itself.
+bool fused_combine(const moe_layer_t &L, int T) {
+    if (T > kPass2cMaxT) return false;
+    const int nq2 = L.I / elems_per_chunk(L.expert_dtype);
+    const int lanes = pass2_lanes(nq2, L.expert_dtype);
+    const int nr = pass2c_rows(nc_instance((nq2 + lanes - 1) / lanes), lanes);
+    return (size_t)T * L.top_k * nr * 4 <= 64 * 1024;
+}
+
 // Small batches have few hot experts: narrow items (32 weight rows) spread
 // them over the chip.  Large batches have many items anyway, and wide items
 // (128 weight rows) read each staged activation row for 4x more weights.
@@ -253,12 +265,27 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
             default: return launch_pass2<MOE_MXFP4>(nc2, lanes, persistent_grid(items2), s, p2);
         }
     };
+    // pass 2 with the combine (small batches): writes out directly
+    const bool p2c = out && !mfma && fused_combine(L, T);
+    auto gemv2c = [&](hipStream_t s) {
+        Pass2cArgs p{L.w_down, L.s_down, act, rt.w, xres, out, rt.reject, L.H, L.I, L.top_k, T,
+                     walk == MOE_WALK_DEDUP ? grouped : per_route};
+        const int nq2 = L.I / epc;
+        const int lanes = pass2_lanes(nq2, L.expert_dtype);
+        const int nc2 = (nq2 + lanes - 1) / lanes;
+        switch (L.expert_dtype) {
+            case MOE_F32: return launch_pass2c<MOE_F32>(nc2, lanes, s, p);
+            case MOE_BF16: return launch_pass2c<MOE_BF16>(nc2, lanes, s, p);
+            case MOE_FP8_E4M3: return launch_pass2c<MOE_FP8_E4M3>(nc2, lanes, s, p);
+            default: return launch_pass2c<MOE_MXFP4>(nc2, lanes, s, p);
+        }
+    };
     auto mfma_2 = [&](hipStream_t s) {
         MfmaArgs m2{L.w_down, L.s_down, act, y, L.H, L.I, L.top_k, kMfmaMinRoutes, 0, grouped, rt.max_count};
         return launch_mfma_pass(L, 2, T, m2, s);
     };
     auto combine = [&]() {
-        if (!out) return hipSuccess;  // a stack: the next layer's routing launch combines
+        if (!out || p2c) return hipSuccess;  // a stack: the next layer's routing launch combines
         hipLaunchKernelGGL(combine_kernel, dim3(T, (L.H / 4 + kBlock - 1) / kBlock), dim3(kBlock), 0, st, y, rt.w,
                            xres, out, L.top_k, L.H, rt.reject);
         return hipGetLastError();
@@ -302,7 +329,7 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
     MOE_TRY(mark(0));
     if (mfma) MOE_TRY(mfma_1(st, false));
     MOE_TRY(mark(1));
-    MOE_TRY(gemv2(st));
+    MOE_TRY(p2c ? gemv2c(st) : gemv2(st));
     MOE_TRY(mark(2));
     if (mfma2) MOE_TRY(mfma_2(st));
     MOE_TRY(mark(3));

@@ -38,6 +38,31 @@ __device__ __forceinline__ int load_uniform(const int32_t *p) {
     return v;
 }
 
+// Two / three / four wave-uniform int32 reads issued together, with one wait.
+__device__ __forceinline__ void load_uniform2(const int32_t *p0, const int32_t *p1, int &v0, int &v1) {
+    asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&s"(v0), "=&s"(v1)
+                 : "s"(p0), "s"(p1)
+                 : "memory");
+}
+__device__ __forceinline__ void load_uniform3(const int32_t *p0, const int32_t *p1, const int32_t *p2, int &v0,
+                                              int &v1, int &v2) {
+    asm volatile(
+        "s_load_dword %0, %3, 0x0\n\ts_load_dword %1, %4, 0x0\n\ts_load_dword %2, %5, 0x0\n\ts_waitcnt lgkmcnt(0)"
+        : "=&s"(v0), "=&s"(v1), "=&s"(v2)
+        : "s"(p0), "s"(p1), "s"(p2)
+        : "memory");
+}
+__device__ __forceinline__ void load_uniform4(const int32_t *p0, const int32_t *p1, const int32_t *p2,
+                                              const int32_t *p3, int &v0, int &v1, int &v2, int &v3) {
+    asm volatile(
+        "s_load_dword %0, %4, 0x0\n\ts_load_dword %1, %5, 0x0\n\ts_load_dword %2, %6, 0x0\n\t"
+        "s_load_dword %3, %7, 0x0\n\ts_waitcnt lgkmcnt(0)"
+        : "=&s"(v0), "=&s"(v1), "=&s"(v2), "=&s"(v3)
+        : "s"(p0), "s"(p1), "s"(p2), "s"(p3)
+        : "memory");
+}
+
 // Expert, first sorted slot and route count of segment s (s uniform).
 __device__ __forceinline__ void segment(const SegArgs &sa, int s, int &e, int &first, int &n) {
     first = 0;
@@ -411,6 +436,51 @@ __global__ __launch_bounds__(kGemvBlock) void pass1_kernel(Pass1Args a) {
 }
 
 // ---- pass 2: down rows -------------------------------------------------------
+// Slot j of a wave whose first row is h0 holds row h0 + j * RPS + half for
+// the lane's half (RPS = 64 / G rows per slot): its byte pointer in expert
+// e, whether it exists (and live), and the block scales of the lane's chunks.
+template <int WDT, int NC, int NS, int G>
+__device__ __forceinline__ void down_rows(const void *down, const void *s_down, int e, int h0, int H, int I,
+                                          bool live, int lane, const char *(&rows)[NS], bool (&ok)[NS],
+                                          float (&sc)[NS][NC]) {
+    constexpr int RPS = kWave / G;
+    constexpr int EPC = WT<WDT>::kEpc;
+    const int half = lane / G, nq = I / EPC;
+    const size_t row_bytes = (size_t)nq * 16;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        const int h = h0 + j * RPS + half;
+        ok[j] = h < H && live;
+        rows[j] = static_cast<const char *>(down) + ((size_t)e * H + min(h, H - 1)) * row_bytes;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) sc[j][c] = 1.f;
+    }
+    if (WDT == MOE_MXFP4) {  // one E8M0 byte per chunk of 32: [E, H, I/32]
+        const uint8_t *sd = reinterpret_cast<const uint8_t *>(s_down);
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            const int h = min(h0 + j * RPS + half, H - 1);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const int q = min((lane & (G - 1)) + G * c, nq - 1);
+                sc[j][c] = e8m0_value(sd[((size_t)e * H + h) * nq + q]);
+            }
+        }
+    }
+    if (WDT == MOE_FP8_E4M3) {
+        const int nbi = I / 128;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            const int h = min(h0 + j * RPS + half, H - 1);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const int ib = min(((lane & (G - 1)) + G * c) * EPC / 128, nbi - 1);
+                sc[j][c] = static_cast<const float *>(s_down)[((size_t)e * (H / 128) + h / 128) * nbi + ib];
+            }
+        }
+    }
+}
+
 // A workgroup item is one segment and 4 * NR consecutive down rows.
 struct Pass2Args {
     const void *down;
@@ -433,7 +503,6 @@ __global__ __launch_bounds__(kGemvBlock) void pass2_kernel(Pass2Args a) {
     const int lane = threadIdx.x & (kWave - 1), half = lane / G, wv = threadIdx.x / kWave;
     const int H = a.H, I = a.I, nq = I / EPC;
     const int items_per_seg = (H + NR * WPB - 1) / (NR * WPB);
-    const size_t row_bytes = (size_t)nq * 16;
 
     int e_nx = 0, first_nx = 0, n_nx = 0;
     bool late;
@@ -443,42 +512,10 @@ __global__ __launch_bounds__(kGemvBlock) void pass2_kernel(Pass2Args a) {
         const int e = e_nx;
         int first = first_nx, n = n_nx;
         const int h0 = (blk * WPB + wv) * NR;
-        // slot j, half hf: row h0 + j * RPS + hf
         const char *rows[NS];
         bool ok[NS];
         float sc[NS][NC];
-#pragma unroll
-        for (int j = 0; j < NS; ++j) {
-            const int h = h0 + j * RPS + half;
-            ok[j] = h < H && n > 0;
-            rows[j] = static_cast<const char *>(a.down) + ((size_t)e * H + min(h, H - 1)) * row_bytes;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) sc[j][c] = 1.f;
-        }
-        if (WDT == MOE_MXFP4) {  // one E8M0 byte per chunk of 32: [E, H, I/32]
-            const uint8_t *sd = reinterpret_cast<const uint8_t *>(a.s_down);
-#pragma unroll
-            for (int j = 0; j < NS; ++j) {
-                const int h = min(h0 + j * RPS + half, H - 1);
-#pragma unroll
-                for (int c = 0; c < NC; ++c) {
-                    const int q = min((lane & (G - 1)) + G * c, nq - 1);
-                    sc[j][c] = e8m0_value(sd[((size_t)e * H + h) * nq + q]);
-                }
-            }
-        }
-        if (WDT == MOE_FP8_E4M3) {
-            const int nbi = I / 128;
-#pragma unroll
-            for (int j = 0; j < NS; ++j) {
-                const int h = min(h0 + j * RPS + half, H - 1);
-#pragma unroll
-                for (int c = 0; c < NC; ++c) {
-                    const int ib = min(((lane & (G - 1)) + G * c) * EPC / 128, nbi - 1);
-                    sc[j][c] = static_cast<const float *>(a.s_down)[((size_t)e * (H / 128) + h / 128) * nbi + ib];
-                }
-            }
-        }
+        down_rows<WDT, NC, NS, G>(a.down, a.s_down, e, h0, H, I, n > 0, lane, rows, ok, sc);
         u32x4 w[NS][NC];
         load_rows<NC, NS, G>(w, rows, ok, nq, lane);
         if (late) {
@@ -522,6 +559,150 @@ __global__ __launch_bounds__(kGemvBlock) void pass2_kernel(Pass2Args a) {
         };
         if (n > 0) batch(0, min(a.nb, n));
         for (int m0 = a.nb; m0 < n; m0 += a.nb) batch(m0, min(a.nb, n - m0));
+    }
+}
+
+// ---- pass 2 with the combine, for small batches ------------------------------
+// The same per-(row, route) arithmetic as pass2_kernel (a wave's NR down rows
+// in NS slots of G lanes, the same rows per slot, lane -> chunk assignment and
+// reduce-scatter, so every y value is bitwise the one pass2_kernel writes), in
+// another order: a workgroup owns one NR-row block of down for every segment.
+// Its waves (16, four per SIMD, so that one wave's memory latency is hidden
+// by the others; fewer where the weights take more registers) take the
+// segments in turn, QS at a time with the
+// weight loads of all QS in flight at once, and read the activation rows
+// straight from memory (a few per segment at small batches).  The y values of the
+// block stay in LDS ([R][NR]); after a barrier the workgroup forms
+// out[t, h] = sum_j w[t, j] y[t * k + j, h] (+ x[t, h]) for its rows with the
+// combine kernel's arithmetic (FMAs in slot order from zero, then the
+// residual).  So there is no y in memory and no combine launch.
+constexpr int kPass2cSegs = 1;   // segments per wave with their loads in flight together
+constexpr int kPass2cMaxT = 8;   // batches up to this size take this kernel
+
+// Waves per pass2c workgroup for NC chunks per lane and G lanes per row: as
+// many as the weight registers of one wave allow without spilling (fp8 and
+// MXFP4 decode into more temporaries).
+__host__ __device__ constexpr int pass2c_waves(int WDT, int NC, int G) {
+    return (WDT == MOE_FP8_E4M3 || WDT == MOE_MXFP4) ? (NC >= 8 ? 4 : 8) : (NC == 8 || (NC == 2 && G < 64) ? 8 : 16);
+}
+
+struct Pass2cArgs {
+    const void *down;
+    const void *s_down;     // fp8: float block scales; MXFP4: E8M0 bytes
+    const float *act;       // [R, I] fp32
+    const float *w;         // [T, k] combine weights
+    const float *xres;      // [T, H] residual or null
+    float *out;             // [T, H]; may alias xres (same element, same thread)
+    const int32_t *reject;  // a caller-supplied routing's n_uniq, or null: out untouched when negative
+    int H, I, k, T;
+    SegArgs sa;
+};
+
+template <int WDT, int NC, int G, int QS>
+__global__ __launch_bounds__(pass2c_waves(WDT, NC, G) * kWave) void pass2c_kernel(Pass2cArgs a) {
+    static_assert(QS == 1 || QS == 2, "segments are fetched one or two at a time");
+    extern __shared__ float yl[];  // [R][NR]
+    constexpr int NS = slots_for(NC);
+    constexpr int RPS = kWave / G;
+    constexpr int NR = NS * RPS;
+    constexpr int EPC = WT<WDT>::kEpc;
+    constexpr int WPB = pass2c_waves(WDT, NC, G);
+    const int lane = threadIdx.x & (kWave - 1), half = lane / G;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int H = a.H, I = a.I, nq = I / EPC;
+    const int h0 = blockIdx.x * NR;
+    const SegArgs &sa = a.sa;
+    const int nu = a.reject ? __builtin_nontemporal_load(a.reject) : 0;
+    // The experts of a wave's QS segments come in one scalar round trip
+    // (with the segment count, for the first ones); the weight loads are
+    // issued with the experts alone, and the segments' first slots and counts
+    // are read while they are in flight.  ids / uniq indices are clamped: an
+    // entry past the segment count is read but not used.
+    const int lim = sa.grouped ? sa.E - 1 : sa.R - 1;
+    const int32_t *elist = sa.grouped ? sa.uniq : sa.ids;
+    int s0 = wv * QS, nseg, ev[2];
+    if (sa.grouped) {
+        load_uniform3(sa.n_uniq, elist + min(s0, lim), elist + min(s0 + 1, lim), nseg, ev[0], ev[1]);
+        nseg = nseg > 0 ? nseg : 0;
+    } else {
+        nseg = sa.R;
+        load_uniform2(elist + min(s0, lim), elist + min(s0 + 1, lim), ev[0], ev[1]);
+    }
+    for (; s0 < nseg; s0 += WPB * QS) {
+        int e[QS], first[QS], n[QS];
+        bool live[QS];
+#pragma unroll
+        for (int q = 0; q < QS; ++q) {
+            live[q] = s0 + q < nseg && ev[q] >= 0 && ev[q] < sa.E;
+            e[q] = live[q] ? ev[q] : 0;
+        }
+        u32x4 w[QS][NS][NC];
+        float sc[QS][NS][NC];
+#pragma unroll
+        for (int q = 0; q < QS; ++q) {
+            const char *rows[NS];
+            bool ok[NS];
+            down_rows<WDT, NC, NS, G>(a.down, a.s_down, e[q], h0, H, I, live[q], lane, rows, ok, sc[q]);
+            load_rows<NC, NS, G>(w[q], rows, ok, nq, lane);
+        }
+        if (sa.grouped) {
+            if constexpr (QS == 2)
+                load_uniform4(sa.offsets + e[0], sa.counts + e[0], sa.offsets + e[1], sa.counts + e[1], first[0],
+                              n[0], first[1], n[1]);
+            else
+                load_uniform2(sa.offsets + e[0], sa.counts + e[0], first[0], n[0]);
+        } else {
+#pragma unroll
+            for (int q = 0; q < QS; ++q) {
+                first[q] = s0 + q;
+                n[q] = 1;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < QS; ++q)
+            if (!live[q] || n[q] >= sa.gemv_below) n[q] = 0;
+        // the next pair's experts, while this pair's weights are in flight
+        const int s1 = s0 + WPB * QS;
+        if (s1 < nseg) load_uniform2(elist + min(s1, lim), elist + min(s1 + 1, lim), ev[0], ev[1]);
+#pragma unroll
+        for (int q = 0; q < QS; ++q) {
+            // routes in pairs (one weight decode for both), then a single one
+            auto routes = [&](auto rb_tag, int m) {
+                constexpr int RB = decltype(rb_tag)::value;
+                const float4 *x[RB];
+                int r[RB];
+#pragma unroll
+                for (int i = 0; i < RB; ++i) {
+                    r[i] = segment_route_uniform(sa, first[q], m + i);
+                    x[i] = reinterpret_cast<const float4 *>(a.act + (size_t)r[i] * I);
+                }
+                float acc[RB][NS];
+                dot_rows<WDT, NC, NS, G, RB>(w[q], sc[q], x, nq, lane, acc);
+#pragma unroll
+                for (int i = 0; i < RB; ++i) {
+                    float v[NS][1];
+#pragma unroll
+                    for (int j = 0; j < NS; ++j) v[j][0] = acc[i][j];
+                    reduce_slots<NS, 1, G>(v, lane);
+                    const int j = reduced_slot<NS, G>(lane);
+                    if (slot_leader<NS, G>(lane)) yl[r[i] * NR + j * RPS + half] = v[0][0];
+                }
+            };
+            int m = 0;
+            for (; m + 1 < n[q]; m += 2) routes(std::integral_constant<int, 2>{}, m);
+            if (m < n[q]) routes(std::integral_constant<int, 1>{}, m);
+        }
+    }
+    __syncthreads();
+    if (nu < 0) return;
+    const int T = a.T, k = a.k;
+    for (int idx = threadIdx.x; idx < T * NR; idx += WPB * kWave) {
+        const int t = idx / NR, i = idx - t * NR, h = h0 + i;
+        if (h >= H) continue;
+        float acc = 0.f;
+        for (int j = 0; j < k; ++j) acc = fmaf(a.w[(size_t)t * k + j], yl[(t * k + j) * NR + i], acc);
+        if (a.xres) acc += a.xres[(size_t)t * H + h];
+        a.out[(size_t)t * H + h] = acc;
     }
 }
 
@@ -603,6 +784,51 @@ hipError_t launch_pass2(int nc, int lanes, int grid, hipStream_t st, const Pass2
     return hipGetLastError();
 }
 
+// Rows of down per pass2c workgroup (one wave's NR) for chunks-per-lane
+// instance nc and lanes per row.
+inline int pass2c_rows(int nc, int lanes) { return slots_for(nc) * (kWave / lanes); }
+
+template <int WDT>
+hipError_t launch_pass2c(int nc, int lanes, hipStream_t st, const Pass2cArgs &a) {
+    const int nr = pass2c_rows(nc_instance(nc), lanes);
+    const dim3 grid((a.H + nr - 1) / nr);
+    const size_t lds = (size_t)a.T * a.k * nr * 4;
+#define MOE_P2C(N, L) \
+    hipLaunchKernelGGL((pass2c_kernel<WDT, N, L, kPass2cSegs>), grid, dim3(pass2c_waves(WDT, N, L) * kWave), lds, st, a)
+    switch (nc_instance(nc) * 100 + lanes) {
+        case 164: MOE_P2C(1, 64); break;
+        case 264: MOE_P2C(2, 64); break;
+        case 364: MOE_P2C(3, 64); break;
+        case 464: MOE_P2C(4, 64); break;
+        case 864: MOE_P2C(8, 64); break;
+        case 132: MOE_P2C(1, 32); break;
+        case 232: MOE_P2C(2, 32); break;
+        case 332: MOE_P2C(3, 32); break;
+        case 432: MOE_P2C(4, 32); break;
+        case 832: MOE_P2C(8, 32); break;
+        default:
+            if constexpr (WDT == MOE_MXFP4) {
+                switch (nc_instance(nc) * 100 + lanes) {
+                    case 116: MOE_P2C(1, 16); break;
+                    case 216: MOE_P2C(2, 16); break;
+                    case 316: MOE_P2C(3, 16); break;
+                    case 416: MOE_P2C(4, 16); break;
+                    case 816: MOE_P2C(8, 16); break;
+                    case 108: MOE_P2C(1, 8); break;
+                    case 208: MOE_P2C(2, 8); break;
+                    case 308: MOE_P2C(3, 8); break;
+                    case 408: MOE_P2C(4, 8); break;
+                    case 808: MOE_P2C(8, 8); break;
+                    default: return hipErrorInvalidValue;
+                }
+                break;
+            }
+            return hipErrorInvalidValue;
+    }
+#undef MOE_P2C
+    return hipGetLastError();
+}
+
 // ---- MFMA segments ------------------------------------------------------------
 // Segments with at least kMfmaMinRoutes routes run on the matrix cores (see
 // experts_mfma.hip and experts_mfma_wide.hip), in token blocks of
@@ -646,5 +872,9 @@ extern template hipError_t launch_pass2<MOE_BF16>(int, int, int, hipStream_t, co
 extern template hipError_t launch_pass2<MOE_FP8_E4M3>(int, int, int, hipStream_t, const Pass2Args &);
 extern template hipError_t launch_pass1<MOE_MXFP4>(int, int, hipStream_t, const Pass1Args &);
 extern template hipError_t launch_pass2<MOE_MXFP4>(int, int, int, hipStream_t, const Pass2Args &);
+extern template hipError_t launch_pass2c<MOE_F32>(int, int, hipStream_t, const Pass2cArgs &);
+extern template hipError_t launch_pass2c<MOE_BF16>(int, int, hipStream_t, const Pass2cArgs &);
+extern template hipError_t launch_pass2c<MOE_FP8_E4M3>(int, int, hipStream_t, const Pass2cArgs &);
+extern template hipError_t launch_pass2c<MOE_MXFP4>(int, int, hipStream_t, const Pass2cArgs &);
 
 }  // namespace moe

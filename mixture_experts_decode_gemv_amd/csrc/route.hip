@@ -8,7 +8,9 @@
 // dispatches.  Here the router, the selection and the sort are one kernel:
 //
 //  * Workgroup (eb, tb) computes the logits of 16 experts (4 per wave, rows
-//    held in registers) for a tile of up to 8 tokens (32 KiB, 64 KiB for
+//    held in registers; 4 experts, one per wave, for batches of up to
+//    kRouteSmallT tokens, so that four times as many workgroups stream the
+//    router rows) for a tile of up to 8 tokens (32 KiB, 64 KiB for
 //    batches of 128 tokens or more) staged in LDS
 //    (normalised there first for the RMSNorm form; workgroup eb = 0 also
 //    writes the normalised rows for the expert passes).  In a layer stack
@@ -30,7 +32,7 @@
 namespace moe {
 
 constexpr int kRouteRows = 4;                      // router rows per wave
-constexpr int kRouteExperts = 4 * kRouteRows;      // experts per workgroup
+constexpr int kRouteSmallT = 16;                   // up to here: one row per wave
 constexpr int kRouteTileFloats = 8192;             // token tile: 32 KiB of LDS
 constexpr int kRouteTileFloatsLarge = 16384;       // from kRouteLargeT tokens: 64 KiB
 constexpr int kRouteLargeT = 128;
@@ -68,7 +70,7 @@ struct RouteArgs {
     float eps;
 };
 
-template <int RDT, int NC>
+template <int RDT, int NC, int RR>
 __global__ __launch_bounds__(kBlock) void route_kernel(RouteArgs a) {
     extern __shared__ float4 dyn_lds[];
     float *tile = reinterpret_cast<float *>(dyn_lds);
@@ -80,14 +82,14 @@ __global__ __launch_bounds__(kBlock) void route_kernel(RouteArgs a) {
     const int H = a.H, E = a.E;
 
     if (!a.logits_in) {
-        // router rows e0 .. e0+3 of this wave, issued first (they do not
+        // router rows e0 .. e0+RR-1 of this wave, issued first (they do not
         // depend on the tokens)
-        const int e0 = eb * kRouteExperts + wave * kRouteRows;
+        const int e0 = (eb * (kBlock / kWave) + wave) * RR;
         const int nq = H / EPC;
         const size_t row_bytes = (size_t)H * WT<RDT>::kBytes;
-        u32x4 wr[kRouteRows][NC];
+        u32x4 wr[RR][NC];
 #pragma unroll
-        for (int r = 0; r < kRouteRows; ++r)
+        for (int r = 0; r < RR; ++r)
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 const int q = lane + kWave * c;
@@ -99,7 +101,7 @@ __global__ __launch_bounds__(kBlock) void route_kernel(RouteArgs a) {
         // this lane's router bias (lane r stores row r of the wave), read
         // before the token loop: a load inside it would wait behind the
         // previous tokens' logit stores (vector memory counts in order)
-        const float bias_r = (a.bias && lane < kRouteRows && e0 + lane < E) ? a.bias[e0 + lane] : 0.f;
+        const float bias_r = (a.bias && lane < RR && e0 + lane < E) ? a.bias[e0 + lane] : 0.f;
         // token tile -> LDS
         const int h4 = H / 4;
         if (a.prev_y) {
@@ -206,12 +208,12 @@ __global__ __launch_bounds__(kBlock) void route_kernel(RouteArgs a) {
         for (int t = 0; t < nt; t += 2) {
             const bool two = t + 1 < nt;
 #pragma unroll
-            for (int r = 0; r < kRouteRows; ++r)
+            for (int r = 0; r < RR; ++r)
 #pragma unroll
                 for (int c = 0; c < NC; ++c) asm volatile("" : "+v"(wr[r][c]));
-            float acc0[kRouteRows][1], acc1[kRouteRows][1];
+            float acc0[RR][1], acc1[RR][1];
 #pragma unroll
-            for (int r = 0; r < kRouteRows; ++r) { acc0[r][0] = 0.f; acc1[r][0] = 0.f; }
+            for (int r = 0; r < RR; ++r) { acc0[r][0] = 0.f; acc1[r][0] = 0.f; }
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 const int q = lane + kWave * c;
@@ -226,7 +228,7 @@ __global__ __launch_bounds__(kBlock) void route_kernel(RouteArgs a) {
                         xs1[4 * v] = f1.x; xs1[4 * v + 1] = f1.y; xs1[4 * v + 2] = f1.z; xs1[4 * v + 3] = f1.w;
                     }
 #pragma unroll
-                    for (int r = 0; r < kRouteRows; ++r) {
+                    for (int r = 0; r < RR; ++r) {
                         acc0[r][0] = chunk_dot<RDT>(wr[r][c], xs0, acc0[r][0]);
                         acc1[r][0] = chunk_dot<RDT>(wr[r][c], xs1, acc1[r][0]);
                     }
@@ -235,14 +237,14 @@ __global__ __launch_bounds__(kBlock) void route_kernel(RouteArgs a) {
             // one DPP sum over the wave per row and token; lane r stores row r
             float l0 = 0.f, l1 = 0.f;
 #pragma unroll
-            for (int r = 0; r < kRouteRows; ++r) {
+            for (int r = 0; r < RR; ++r) {
                 const float s0 = wave_sum_dpp(acc0[r][0]), s1 = wave_sum_dpp(acc1[r][0]);
                 if (lane == r) {
                     l0 = s0;
                     l1 = s1;
                 }
             }
-            if (lane < kRouteRows && e0 + lane < E) {
+            if (lane < RR && e0 + lane < E) {
                 store_shared(a.logits + (size_t)(t0 + t) * E + e0 + lane, a.bias ? l0 + bias_r : l0);
                 if (two) store_shared(a.logits + (size_t)(t0 + t + 1) * E + e0 + lane, a.bias ? l1 + bias_r : l1);
             }
@@ -307,18 +309,17 @@ __global__ __launch_bounds__(kBlock) void route_kernel(RouteArgs a) {
                       reinterpret_cast<int *>(dyn_lds), a.zero, a.n_zero);
 }
 
-template <int RDT>
+template <int RDT, int RR>
 static hipError_t route_dispatch(int nc, dim3 g, size_t lds, hipStream_t st, const RouteArgs &a) {
     switch (nc) {
 #define MOE_RC(N) \
-    case N: hipLaunchKernelGGL((route_kernel<RDT, N>), g, dim3(kBlock), lds, st, a); break;
+    case N: hipLaunchKernelGGL((route_kernel<RDT, N, RR>), g, dim3(kBlock), lds, st, a); break;
         MOE_RC(1) MOE_RC(2) MOE_RC(3) MOE_RC(4) MOE_RC(5) MOE_RC(6) MOE_RC(7) MOE_RC(8)
 #undef MOE_RC
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
-
 
 hipError_t launch_route(const moe_layer_t &L, const float *x, const float *logits_in, int T, float *xn,
                         float *logits, int32_t *ids, float *w, int32_t *counts, int32_t *offsets, int32_t *sorted,
@@ -354,7 +355,11 @@ hipError_t launch_route(const moe_layer_t &L, const float *x, const float *logit
     a.rmsnorm = rmsnorm ? 1 : 0;
     a.eps = 1e-6f;
     a.tile = logits_in ? (kBlock / kWave) : route_tile_tokens(L.H, T);
-    a.n_eblk = logits_in ? 1 : (L.E + kRouteExperts - 1) / kRouteExperts;
+    // router rows per wave: one for small batches (more workgroups stream the
+    // router rows), four otherwise (each row is re-read once per token tile)
+    const int rr = T <= kRouteSmallT ? 1 : kRouteRows;
+    const int experts_per_wg = rr * (kBlock / kWave);
+    a.n_eblk = logits_in ? 1 : (L.E + experts_per_wg - 1) / experts_per_wg;
     a.n_tblk = (T + a.tile - 1) / a.tile;
     // the sort's LDS, then (single tile) the selected ids
     size_t lds = ((size_t)sort_lds_ints(L.E) + (size_t)a.tile * L.top_k) * 4;
@@ -365,8 +370,11 @@ hipError_t launch_route(const moe_layer_t &L, const float *x, const float *logit
     const int epc = elems_per_chunk(L.router_dtype);
     const int nc = logits_in ? 1 : (L.H / epc + kWave - 1) / kWave;
     const dim3 g(a.n_eblk * a.n_tblk);
-    if (L.router_dtype == MOE_BF16) return route_dispatch<MOE_BF16>(nc, g, lds, st, a);
-    return route_dispatch<MOE_F32>(nc, g, lds, st, a);
+    if (L.router_dtype == MOE_BF16)
+        return rr == 1 ? route_dispatch<MOE_BF16, 1>(nc, g, lds, st, a)
+                       : route_dispatch<MOE_BF16, kRouteRows>(nc, g, lds, st, a);
+    return rr == 1 ? route_dispatch<MOE_F32, 1>(nc, g, lds, st, a)
+                   : route_dispatch<MOE_F32, kRouteRows>(nc, g, lds, st, a);
 }
 
 // ---- fill kernel (workspace initialisation) ----------------------------------
