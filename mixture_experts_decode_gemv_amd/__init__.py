@@ -249,13 +249,16 @@ class DeviceLayer:
         return moe_layer_t(s.E, s.top_k, s.H, s.I, s.router_dtype, s.expert_dtype, _p(t["w_router"]),
                            _p(t["w_gate_up"]), _p(t["w_down"]), _p(t["s_gate_up"]), _p(t["s_down"]), _p(bias))
 
-    def with_bias(self, router_bias):
-        """Same weights, another router bias (a shallow view sharing memory)."""
+    def with_bias(self, router_bias, top_k=None):
+        """Same weights, another router bias and optionally another top_k (a
+        shallow view sharing memory)."""
+        import dataclasses
+
         import numpy as np
         import torch
 
         other = DeviceLayer.__new__(DeviceLayer)
-        other.spec = self.spec
+        other.spec = self.spec if top_k is None else dataclasses.replace(self.spec, top_k=top_k)
         other.tensors = dict(self.tensors)
         other.tensors["router_bias"] = (None if router_bias is None else torch.from_numpy(
             np.ascontiguousarray(router_bias, np.float32)).to(self.tensors["w_router"].device))

@@ -1,4 +1,5 @@
-"""Build the gfx950 HIP library ``libmoe_gfx950.so`` in-tree with hipcc."""
+"""Build the gfx950 HIP library ``libmoe_gfx950.so`` in-tree with hipcc, and
+the benchmark's read-stream probe ``libmoe_probe_gfx950.so``."""
 from __future__ import annotations
 
 import concurrent.futures
@@ -10,6 +11,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_gfx950.so")
+PROBE_SRC = os.path.join(HERE, "probe", "read_stream.hip")
+PROBE_LIB = os.path.join(HERE, "libmoe_probe_gfx950.so")
 ROOT = os.path.dirname(HERE)
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -59,6 +62,9 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     os.replace(tmp, LIB)
     for o in objs:
         os.remove(o)
+    ptmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    _run([HIPCC, *FLAGS, PROBE_SRC, "-o", ptmp], verbose)
+    os.replace(ptmp, PROBE_LIB)
     return LIB
 
 
