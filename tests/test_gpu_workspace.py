@@ -87,3 +87,24 @@ def test_larger_workspace_than_needed():
     a = _run(layer, x, 8, 0, layer.workspace(8))
     b = _run(layer, x, 8, 0, layer.workspace(200))
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("spec,flags", [
+    (wl.TINY, 0),
+    (wl.LayerSpec(E=16, top_k=4, H=512, I=256), 0),
+    (wl.STACK, moe.MOE_RMSNORM_IN | moe.MOE_ACCUM_RESIDUAL),
+], ids=["tiny", "bf16-small", "stack"])
+def test_small_batch_calls_repeat_on_one_workspace(spec, flags):
+    """Calls that alternate two inputs on one workspace, at the batch sizes
+    whose pass 2 and combine run as one launch, give bitwise the results of
+    fresh workspaces every time: nothing a call leaves in the workspace (its
+    counters, its activation rows) reaches the next call's results."""
+    w, layer, olayer = make_device_layer(spec)
+    for T in (1, 2, 4):
+        xs = [wl.make_x(T, spec.H, draw=900 + 10 * T + i) for i in range(2)]
+        ref = [_run(layer, x, T, flags, layer.workspace(T)) for x in xs]
+        ws = layer.workspace(T)
+        for rep in range(6):
+            note("repeat %d on one workspace, T=%d" % (rep, T))
+            assert np.array_equal(_run(layer, xs[rep % 2], T, flags, ws), ref[rep % 2]), "T=%d call %d" % (T, rep)
+            _front_is_clear(layer, T, ws)
