@@ -237,6 +237,55 @@ __device__ int build_tables(const MfmaArgs &a, int n_rb, int *pre, int *off, int
 
 }  // namespace
 
+// The end of an item: the four waves' partial sums (acc0, acc1: this wave's
+// k-steps of the two weight tiles, per token tile) go through red (LDS,
+// 2 x kWaves x kTT x 64 x 16 bytes, free on entry) and are added in wave
+// order w = 0, 1, 2, 3; wave tt then writes token tile tt: pass 1 a[r, i] =
+// silu(gate) * up (fp32, or bf16 into the first half of the fp32 row for the
+// MFMA pass 2), pass 2 the y rows.  A lane (m, g) holds rows 4g .. 4g+3 of
+// both tiles for token m of its tile.
+template <int PASS>
+__device__ __forceinline__ void mfma_epilogue(const MfmaArgs &a, f32x4_t *red, const f32x4_t (&acc0)[kTT],
+                                              const f32x4_t (&acc1)[kTT], int ntt, int nv, const int32_t *routes,
+                                              int r0, int wv, int lane) {
+    const int m = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int tt = 0; tt < kTT; ++tt) {
+        if (tt < ntt) {
+            red[((wv * 2 + 0) * kTT + tt) * kWave + lane] = acc0[tt];
+            red[((wv * 2 + 1) * kTT + tt) * kWave + lane] = acc1[tt];
+        }
+    }
+    lds_barrier();
+    const int tt = wv;  // this wave's token tile in the epilogue (waves < kTT)
+    const int tok = tt * 16 + m;
+    if (tt < ntt && tok < nv) {
+        f32x4_t s0 = red[((0 * 2 + 0) * kTT + tt) * kWave + lane];
+        f32x4_t s1 = red[((0 * 2 + 1) * kTT + tt) * kWave + lane];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) {
+            s0 += red[((w * 2 + 0) * kTT + tt) * kWave + lane];
+            s1 += red[((w * 2 + 1) * kTT + tt) * kWave + lane];
+        }
+        const int r = routes[tok];
+        const int row = r0 + 4 * g;
+        if (PASS == 1) {
+            float o[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) o[v] = silu(s0[v]) * s1[v];
+            if (a.act_bf16) {  // bf16 into the first half of the fp32 row r
+                *reinterpret_cast<uint2 *>(reinterpret_cast<char *>(a.dst) + (size_t)r * a.I * 4 + row * 2) =
+                    make_uint2(bf16_pair_rne(o[0], o[1]), bf16_pair_rne(o[2], o[3]));
+            } else {
+                *reinterpret_cast<float4 *>(a.dst + (size_t)r * a.I + row) = make_float4(o[0], o[1], o[2], o[3]);
+            }
+        } else {
+            *reinterpret_cast<float4 *>(a.dst + (size_t)r * a.H + row) = make_float4(s0[0], s0[1], s0[2], s0[3]);
+            *reinterpret_cast<float4 *>(a.dst + (size_t)r * a.H + row + 16) = make_float4(s1[0], s1[1], s1[2], s1[3]);
+        }
+    }
+}
+
 template <int WDT, int PASS>
 __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
     using S = Stage<WDT>;
@@ -433,43 +482,7 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
 
         // partial sums of the four waves, added in wave order
         lds_barrier();  // every wave is done reading the ring
-        f32x4_t *red = reinterpret_cast<f32x4_t *>(ring);
-#pragma unroll
-        for (int tt = 0; tt < kTT; ++tt) {
-            if (tt < ntt) {
-                red[((wv * 2 + 0) * kTT + tt) * kWave + lane] = acc0[tt];
-                red[((wv * 2 + 1) * kTT + tt) * kWave + lane] = acc1[tt];
-            }
-        }
-        lds_barrier();
-        const int tt = wv;  // this wave's token tile in the epilogue (waves < kTT)
-        const int tok = tt * 16 + m;
-        if (tt < ntt && tok < nv) {
-            f32x4_t s0 = red[((0 * 2 + 0) * kTT + tt) * kWave + lane];
-            f32x4_t s1 = red[((0 * 2 + 1) * kTT + tt) * kWave + lane];
-#pragma unroll
-            for (int w = 1; w < kWaves; ++w) {
-                s0 += red[((w * 2 + 0) * kTT + tt) * kWave + lane];
-                s1 += red[((w * 2 + 1) * kTT + tt) * kWave + lane];
-            }
-            const int r = routes[tok];
-            const int row = r0 + 4 * g;  // lane holds rows 4g .. 4g+3 of both tiles for token m
-            if (PASS == 1) {
-                float o[4];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) o[v] = silu(s0[v]) * s1[v];
-                if (a.act_bf16) {  // bf16 into the first half of the fp32 row r
-                    *reinterpret_cast<uint2 *>(reinterpret_cast<char *>(a.dst) + (size_t)r * a.I * 4 + row * 2) =
-                        make_uint2(bf16_pair_rne(o[0], o[1]), bf16_pair_rne(o[2], o[3]));
-                } else {
-                    *reinterpret_cast<float4 *>(a.dst + (size_t)r * a.I + row) = make_float4(o[0], o[1], o[2], o[3]);
-                }
-            } else {
-                *reinterpret_cast<float4 *>(a.dst + (size_t)r * a.H + row) = make_float4(s0[0], s0[1], s0[2], s0[3]);
-                *reinterpret_cast<float4 *>(a.dst + (size_t)r * a.H + row + 16) =
-                    make_float4(s1[0], s1[1], s1[2], s1[3]);
-            }
-        }
+        mfma_epilogue<PASS>(a, reinterpret_cast<f32x4_t *>(ring), acc0, acc1, ntt, nv, routes, r0, wv, lane);
     }
 }
 

@@ -100,6 +100,31 @@ def test_mfma_deterministic_and_token_permutation(T, spec):
     assert max_rel(c[np.argsort(perm)], ref) <= BF16_OPERAND_TOL
 
 
+# bf16 with a long K: pass 1 runs 20 stages of 128 through the narrow
+# kernel's LDS ring (its steady state, not only the prologue), pass 2 runs 5
+LONG_K = wl.LayerSpec(E=8, top_k=2, H=2560, I=640)
+
+
+@pytest.mark.parametrize("T", [16, 31, 45, 64])
+def test_mfma_narrow_long_k(T):
+    """Narrow bf16 items over a long K, with 1 to 4 token tiles of 16 per
+    item (every token on experts 0 and 1): within the bar of the oracle,
+    deterministic, and bitwise unchanged when the tokens are permuted (a
+    route's arithmetic does not depend on its place in the token block)."""
+    note("mfma narrow long K, T=%d" % T)
+    w, layer, olayer = make_device_layer(LONG_K)
+    x = wl.make_x(T, LONG_K.H, draw=40 + T)
+    ids, rw = _routing("collide", olayer, x)
+    ref = oracle.expert_fwd(olayer, x, ids, rw)
+    got = gpu_expert_fwd(layer, x, ids, rw)
+    note("  max rel err %.3g" % max_rel(got, ref))
+    assert max_rel(got, ref) <= BF16_OPERAND_TOL
+    assert np.array_equal(gpu_expert_fwd(layer, x, ids, rw), got)
+    perm = np.random.default_rng(T).permutation(T)
+    c = gpu_expert_fwd(layer, x[perm], ids[perm], rw[perm])
+    assert np.array_equal(c[np.argsort(perm)], got)
+
+
 def _fp8_codes_layer():
     """Two fp8 experts, H = I = 128, whose gate rows carry every E4M3 code
     once (expert e, gate row i: code 128*e + i in column 0, zeros elsewhere;
