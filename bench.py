@@ -46,7 +46,7 @@ MFMA_PEAK_TFS = 2500.0  # dense bf16
 # (uniform routing, bs=64), from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
 # scaled by a 1 GiB copy calibration: profiles/pass_kernels_uniform_bs64_hbm_counters.md.
 # Reported only while the kernel source is the one that was measured.
-PASS1_TRAFFIC_BS64 = {"read_bytes": 1.39955e9, "write_bytes": 1.83501e6, "source": "4aa1c63b368a46ad"}
+PASS1_TRAFFIC_BS64 = {"read_bytes": 1.39838e9, "write_bytes": 1.83040e6, "source": "4aa1c63b368a46ad"}
 
 
 def pass1_source_fingerprint():
@@ -61,7 +61,7 @@ def pass1_source_fingerprint():
     launch = open(os.path.join(d, "experts.hip")).read()
     a = impl[impl.index("struct SegArgs"):impl.index("// ---- pass 2: down rows")]
     b = common[common.index("// acc + sum_e w[e]"):common.index("// Sum over the 64 lanes")]
-    c = launch[launch.index("static int persistent_grid"):launch.index("// Segments with at least kMfmaMinRoutes")]
+    c = launch[launch.index("static int persistent_grid"):launch.index("// Segments with at least mfma_min_routes")]
     return hashlib.sha256((a + b + c).encode()).hexdigest()[:16]
 
 
@@ -304,13 +304,14 @@ def walk_arms(torch, moe, wl, layers, spec, sizes, steps, warmup, draws, expert_
     return out
 
 
-def stage_roofline(head_run, spec, T, bpw, no_mfma, walk):
+def stage_roofline(head_run, spec, T, bpw, thr):
     """Roofline of pass1_kernel (the dominant kernel of the uniform sweep) at
     the headline batch: algorithmic bytes = gate_up bytes of the experts the
-    GEMV kernel streams, over its event-timed average launch."""
-    mfma_on = not no_mfma and T >= 16 and walk != "per_route"
+    GEMV kernel streams (those below the library's MFMA threshold thr for the
+    call, moe_mfma_min_routes; every expert when thr is 0), over its
+    event-timed average launch."""
     counts = [head_run["counts"][i] for i in head_run["stage_steps"]]
-    u_gemv = [int((c > 0).sum() - ((c >= 16).sum() if mfma_on else 0)) for c in counts]
+    u_gemv = [int((c > 0).sum() - ((c >= thr).sum() if thr > 0 else 0)) for c in counts]
     p1_ms = head_run["stage_ms"]["pass1_gemv"]
     p1_bytes = float(np.mean(u_gemv)) * 2 * spec.H * spec.I * bpw
     return p1_bytes / (p1_ms * 1e-3) / 1e9, p1_ms, p1_bytes
@@ -505,7 +506,7 @@ def spec_name(dtype):
 
 def large_rows(torch, moe, wl, dtype, sizes, steps, warmup, draws):
     """E=256, top_k=8, H=4096, I=1536 with Zipf(1.1)-skewed routing; experts
-    holding >= 16 routes run on MFMA.  Per batch size: steps/s, HBM GB/s on
+    holding moe_mfma_min_routes() routes or more run on MFMA.  Per batch size: steps/s, HBM GB/s on
     unique-expert bytes, MFMA TFLOP/s on the MFMA stages, and the roofline of
     the stage that dominates."""
     dev = torch.device("cuda:0")
@@ -529,7 +530,8 @@ def large_rows(torch, moe, wl, dtype, sizes, steps, warmup, draws):
         st = run["stage_ms"]
         cs = [run["counts"][i] for i in run["stage_steps"]]
         u_ev = float(np.mean([(c > 0).sum() for c in cs]))
-        big = [c[c >= 16] for c in cs]
+        thr = moe.moe_mfma_min_routes(layer.struct, T, 0)
+        big = [c[c >= thr] for c in cs]
         n_big = float(np.mean([len(b) for b in big]))
         routes_big = float(np.mean([b.sum() for b in big]))
         tiles_big = float(np.mean([(np.ceil(b / 16) * 16).sum() for b in big]))
@@ -540,7 +542,7 @@ def large_rows(torch, moe, wl, dtype, sizes, steps, warmup, draws):
         u = run["uniq_timed"]
         gbs = u * expert_bytes / (ms * 1e-3) / 1e9
         # algorithmic bytes of each stage: weights of the experts it streams
-        # (GEMV: below 16 routes, MFMA: 16 or more)
+        # (GEMV: below the threshold thr, MFMA: thr or more)
         n_gemv = u_ev - n_big
         per_expert = {"pass1": 2 * I * H * bpw, "pass2": H * I * bpw}
         stage_bytes = {"pass1_gemv": n_gemv * per_expert["pass1"], "pass1_mfma": n_big * per_expert["pass1"],
@@ -689,7 +691,7 @@ def main():
                       "mxfp4": "mxfp4 weights, bf16 MFMA operands"}.get(args.dtype, "bf16"),
             "data": "synthetic (seeded)",
             "config": {"workload": "large-batch single MoE layer, Zipf(1.1) routing, E=256 top_k=8 H=4096 I=1536 "
-                                   "%s experts, MFMA for experts with >= 16 routes" % spec_name(args.dtype),
+                                   "%s experts, MFMA for experts with >= 4 routes (moe_mfma_min_routes at 128+ tokens)" % spec_name(args.dtype),
                        "bs": bs_head, "draws": args.draws},
             "hbm_GBps_unique_expert_bytes": head["hbm_GBps"], "sweep": [rows[t] for t in sizes],
             "roofline": dict(head["roofline"], traffic=None), "mfma": head["mfma"], "cpu_baseline": None}),
@@ -729,7 +731,8 @@ def main():
     rows, runs = sweep_rows(torch, moe, wl, layers, spec, sizes, flags, args.steps, args.warmup, args.draws,
                             expert_bytes, graph=not args.no_graph)
     head_run = runs[args.bs]
-    p1_gbs, p1_ms, p1_bytes = stage_roofline(head_run, spec, args.bs, bpw, args.no_mfma, args.walk)
+    p1_gbs, p1_ms, p1_bytes = stage_roofline(head_run, spec, args.bs, bpw,
+                                             moe.moe_mfma_min_routes(layers[0].struct, args.bs, flags))
 
     # measured HBM bytes per pass-1 launch (headline configuration only, and
     # only for the kernel source the counters were taken on)
@@ -763,7 +766,7 @@ def main():
             r, _ = large_rows(torch, moe, wl, dt, [128], min(xsteps, 32), args.warmup, 4)
             large[dt] = r[128]
         extra["large"] = {"workload": "single MoE layer, Zipf(1.1) routing, E=256 top_k=8 H=4096 I=1536, MFMA for "
-                                      "experts with >= 16 routes (fp8: W8A16 with 128x128 block scales)",
+                                      "experts with >= 4 routes (fp8: W8A16 with 128x128 block scales)",
                           "bs128": large}
         extra["read_stream_probe"] = read_stream_probe(torch)
     else:

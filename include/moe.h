@@ -99,9 +99,10 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3 } moe_
  * s_gate_up uint8 [E, 2I, H/32], s_down uint8 [E, H, I/32].  The router
  * stays fp32 or bf16.
  *
- * Matrix cores: an expert that holds 16 or more routes of a call runs both
- * passes as bf16 MFMA products with fp32 accumulation (the activations and
- * the decoded weights rounded to bf16; decoded MXFP4 weights are exact in
+ * Matrix cores: in a call of 16 or more tokens, an expert that holds
+ * moe_mfma_min_routes() routes or more (8 below 128 tokens, 4 from 128) runs
+ * both passes as bf16 MFMA products with fp32 accumulation (the activations
+ * and the decoded weights rounded to bf16; decoded MXFP4 weights are exact in
  * bf16) when the experts are bf16, fp8 or MXFP4 with H and I multiples of
  * 128 (MXFP4 also needs 4-byte aligned scale arrays), unless the flags ask
  * for MOE_NO_MFMA or the per-route walk.  Every other segment runs on the
@@ -132,6 +133,18 @@ enum {
 /* Bytes of workspace needed for up to max_tokens tokens (max_tokens >= 0).
  * Returns 0 if the layer description is invalid. */
 size_t moe_workspace_bytes(const moe_layer_t *layer, int32_t max_tokens);
+
+/* Routes an expert must hold in a call of T tokens for its segment to run on
+ * the matrix cores (bf16 MFMA: the activations rounded to bf16, fp32
+ * accumulation; the GEMV kernels keep fp32 activations), or 0 when no
+ * segment of such a call does: weights not bf16 / fp8 / MXFP4 with H and I
+ * multiples of 128, T below 16, MOE_NO_MFMA or the per-route walk in flags.
+ * Which segments run where decides the rounding of their results, so callers
+ * and tests can tell.  Host only (no device work); -1 for an invalid layer,
+ * T < 0 or an unknown walk in flags.  The thresholds: 8 routes below 128
+ * tokens, 4 from 128 tokens (the workload definition leaves "dense enough"
+ * open; these are measured crossovers). */
+int32_t moe_mfma_min_routes(const moe_layer_t *layer, int32_t T, uint32_t flags);
 
 /* Zero the synchronisation words at the front of a workspace sized for up to
  * max_tokens tokens (one small fill kernel on `stream`; no memset, so it can

@@ -148,10 +148,11 @@ static int persistent_grid(long long max_items) {
     return (int)(g < 1 ? 1 : g);
 }
 
-// Segments with at least kMfmaMinRoutes routes go to the MFMA kernels when the
-// weights are bf16, fp8 or MXFP4 with H and I multiples of 128, unless the
-// caller asked for the GEMV path only.  A segment cannot hold more routes than
-// there are tokens, so below kMfmaMinRoutes tokens no MFMA kernel is launched.
+// Segments with at least mfma_min_routes routes go to the MFMA kernels when
+// the weights are bf16, fp8 or MXFP4 with H and I multiples of 128, unless the
+// caller asked for the GEMV path only, and from kMfmaMinTokens tokens on
+// (below that the MFMA launches would mostly be idle, and batches up to
+// kPass2cMaxT tokens run pass 2 with the combine, on GEMV segments only).
 static bool mfma_eligible(const moe_layer_t &L, int T, uint32_t flags) {
     // the narrow kernels address activation rows with 32-bit byte offsets
     const bool offsets32 = (unsigned long long)T * L.H * 2 < (1ull << 32) &&
@@ -161,8 +162,13 @@ static bool mfma_eligible(const moe_layer_t &L, int T, uint32_t flags) {
                         (reinterpret_cast<uintptr_t>(L.s_down) & 3) == 0;
     return (L.expert_dtype == MOE_BF16 || L.expert_dtype == MOE_FP8_E4M3 || fp4_ok) && L.H % 128 == 0 &&
            L.I % 128 == 0 &&
-           !(flags & MOE_NO_MFMA) && T >= kMfmaMinRoutes && (int)(flags & MOE_WALK_MASK) != MOE_WALK_PER_ROUTE &&
+           !(flags & MOE_NO_MFMA) && T >= kMfmaMinTokens && (int)(flags & MOE_WALK_MASK) != MOE_WALK_PER_ROUTE &&
            offsets32;
+}
+
+int mfma_min_routes(const moe_layer_t &L, int T, uint32_t flags) {
+    if (!mfma_eligible(L, T, flags)) return 0;
+    return T >= kMfmaWideTokens ? kMfmaMinRoutesWide : kMfmaMinRoutes;
 }
 
 // Pass 2 and the combine in one launch (pass2c_kernel) for small batches with
@@ -184,7 +190,7 @@ static hipError_t launch_mfma_pass(const moe_layer_t &L, int pass, int T, const 
     const bool wide = T >= kMfmaWideTokens;
     // items <= row blocks x (segments that can reach the threshold + extra token blocks)
     const long long R = (long long)T * L.top_k;
-    const long long segs = std::min<long long>(L.E, R / kMfmaMinRoutes);
+    const long long segs = std::min<long long>(L.E, R / a.min_n);
     const long long n_rb = pass == 1 ? L.I / (wide ? 64 : 16) : L.H / (wide ? 128 : 32);
     const long long items = n_rb * (segs + R / kMfmaTokens);
     const long long cap = (long long)num_cus() * 2;
@@ -208,13 +214,14 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
     const int walk = (int)(flags & MOE_WALK_MASK);
     const int epc = elems_per_chunk(L.expert_dtype);
     const int max_uniq = R < L.E ? R : L.E;
-    const bool mfma = mfma_eligible(L, T, flags);
+    const int min_n = mfma_min_routes(L, T, flags);  // 0: no MFMA segments
+    const bool mfma = min_n > 0;
     const bool mfma2 = mfma && walk == MOE_WALK_DEDUP;
     SegArgs grouped{rt.ids, rt.counts, rt.offsets, rt.sorted, rt.uniq, rt.n_uniq, 1, R, L.E, INT_MAX};
     SegArgs per_route = grouped;
     per_route.grouped = 0;
     SegArgs split = grouped;  // the GEMV share of a pass that also has MFMA segments
-    if (mfma) split.gemv_below = kMfmaMinRoutes;
+    if (mfma) split.gemv_below = min_n;
 
     // pass 1 on the GEMV kernel: one wave item = P gate/up pairs of one segment
     // xb_first: the GEMV kernel writes the bf16 copy of x in its prologue
@@ -245,7 +252,7 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-        MfmaArgs m1{L.w_gate_up, L.s_gate_up, xb, act, L.H, L.I, L.top_k, kMfmaMinRoutes, mfma2 ? 1 : 0, grouped,
+        MfmaArgs m1{L.w_gate_up, L.s_gate_up, xb, act, L.H, L.I, L.top_k, min_n, mfma2 ? 1 : 0, grouped,
                     rt.max_count};
         return launch_mfma_pass(L, 1, T, m1, s);
     };
@@ -281,7 +288,7 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
         }
     };
     auto mfma_2 = [&](hipStream_t s) {
-        MfmaArgs m2{L.w_down, L.s_down, act, y, L.H, L.I, L.top_k, kMfmaMinRoutes, 0, grouped, rt.max_count};
+        MfmaArgs m2{L.w_down, L.s_down, act, y, L.H, L.I, L.top_k, min_n, 0, grouped, rt.max_count};
         return launch_mfma_pass(L, 2, T, m2, s);
     };
     auto combine = [&]() {

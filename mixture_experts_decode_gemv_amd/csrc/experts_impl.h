@@ -830,10 +830,20 @@ hipError_t launch_pass2c(int nc, int lanes, hipStream_t st, const Pass2cArgs &a)
 }
 
 // ---- MFMA segments ------------------------------------------------------------
-// Segments with at least kMfmaMinRoutes routes run on the matrix cores (see
-// experts_mfma.hip and experts_mfma_wide.hip), in token blocks of
-// kMfmaTokens routes.
-constexpr int kMfmaMinRoutes = 16;
+// Segments with at least kMfmaMinRoutes routes (kMfmaMinRoutesWide from
+// kMfmaWideTokens tokens) run on the matrix cores (see experts_mfma.hip and
+// experts_mfma_wide.hip), in token blocks of kMfmaTokens routes.  Measured on
+// the large Zipf layer, the skewed sweep and the uniform sweep (graph
+// replays): from 5 routes an expert's GEMV walk is bound by its fp32 FMAs
+// rather than by HBM, so the matrix cores pay from there once batches are
+// large; below 128 tokens, experts of 4 to 7 routes stream slightly faster on
+// the GEMV kernels (uniform bs=16..64 +1..3 % with 4), so there the threshold
+// is 8.
+constexpr int kMfmaMinRoutes = 8;
+constexpr int kMfmaMinRoutesWide = 4;
+// MFMA launches are made from this many tokens on.
+constexpr int kMfmaMinTokens = 16;
+static_assert(kMfmaMinTokens > kPass2cMaxT, "pass 2 with the combine reads GEMV segments only");
 constexpr int kMfmaTokens = 64;
 
 struct MfmaArgs {

@@ -129,6 +129,19 @@ def gpu_layer_fwd(layer: moe.DeviceLayer, x, flags=0, full=False):
     return res
 
 
+BF16_OPERAND_TOL = 2e-2  # bar for paths with bf16 operands: max abs error over max |ref|
+
+
+def call_tol(layer: moe.DeviceLayer, x, flags=0, gemv_tol=1e-4):
+    """The bar for one moe_layer_fwd call: the bf16-operand bar when some
+    segment of it runs on the matrix cores (an expert of its routing holds
+    moe_mfma_min_routes() routes or more), else the GEMV path's gemv_tol."""
+    thr = moe.moe_mfma_min_routes(layer.struct, x.shape[0], flags)
+    if thr <= 0:
+        return gemv_tol
+    return BF16_OPERAND_TOL if gpu_layer_fwd(layer, x, flags, full=True)["counts"].max() >= thr else gemv_tol
+
+
 def oracle_for_gpu_selection(olayer: oracle.Layer, x, oracle_logits, gpu_ids, rmsnorm_in=False, residual=False):
     """Oracle output when the routing is the GPU's ids: weights are the
     softmax of the oracle's logits over the GPU-chosen experts."""

@@ -194,3 +194,25 @@ def test_static_entry_point_validation():
     assert lib.moe_layer_fwd_static(ctypes.byref(L), 0x10004, 4, out, 0, None) == 7
     assert lib.moe_layer_fwd_static(ctypes.byref(L), x, 0, out, 0, None) == 0     # no-op
     assert lib.moe_layer_fwd_static(ctypes.byref(_layer(top_k=9)), x, 4, out, 0, None) == 1
+
+
+def test_mfma_min_routes():
+    """The matrix-core threshold a call applies (host only): 8 routes below
+    128 tokens, 4 from 128, none below 16 tokens, for fp32 experts, for H or I
+    not a multiple of 128, with MOE_NO_MFMA or the per-route walk."""
+    L = _layer(H=256, I=128, expert_dtype=moe.MOE_BF16)
+    assert moe.moe_mfma_min_routes(L, 15) == 0
+    assert moe.moe_mfma_min_routes(L, 16) == 8
+    assert moe.moe_mfma_min_routes(L, 127) == 8
+    assert moe.moe_mfma_min_routes(L, 128) == 4
+    assert moe.moe_mfma_min_routes(L, 4096) == 4
+    assert moe.moe_mfma_min_routes(L, 64, moe.MOE_WALK_DEDUP_PASS1) == 8
+    assert moe.moe_mfma_min_routes(L, 64, moe.MOE_NO_MFMA) == 0
+    assert moe.moe_mfma_min_routes(L, 64, moe.MOE_WALK_PER_ROUTE) == 0
+    assert moe.moe_mfma_min_routes(_layer(H=256, I=128, expert_dtype=moe.MOE_FP8_E4M3, s_gate_up=0x4000,
+                                          s_down=0x5000), 64) == 8
+    assert moe.moe_mfma_min_routes(_layer(H=256, I=128), 64) == 0  # fp32 experts
+    assert moe.moe_mfma_min_routes(_layer(H=192, I=128, expert_dtype=moe.MOE_BF16), 64) == 0
+    assert moe.moe_mfma_min_routes(L, -1) == -1
+    assert moe.moe_mfma_min_routes(_layer(top_k=9), 64) == -1
+    assert moe.moe_mfma_min_routes(L, 64, 7) == -1  # unknown walk

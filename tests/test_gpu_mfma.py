@@ -1,5 +1,6 @@
-"""Parity of the MFMA segment path (experts that hold >= 16 routes) with the
-CPU oracle, through the C ABI.
+"""Parity of the MFMA segment path (experts that hold moe_mfma_min_routes()
+routes or more: 8 below 128 tokens, 4 from 128) with the CPU oracle, through
+the C ABI.
 
 The MFMA path rounds both operands of each product to bf16 and accumulates
 in fp32: the activations x (pass 1) and a (pass 2), and, for fp8 weights, the
@@ -23,7 +24,12 @@ from gpu_util import (check_layer_against_oracle, check_layer_sampled, dev, gpu_
                       gpu_layer_fwd, make_device_layer, max_rel, note, oracle_weights_for)
 
 BF16_OPERAND_TOL = 2e-2  # bar for paths with bf16 operands: max abs error over max |ref|
-MFMA_MIN = 16  # routes per expert from which a segment runs on MFMA
+MFMA_TOKENS = 16  # MFMA launches from this many tokens
+
+
+def _min_routes(layer, T, flags=0):
+    """Routes per expert from which a segment of a T-token call runs on MFMA."""
+    return moe.moe_mfma_min_routes(layer.struct, T, flags)
 
 # H = I = 384: 3 K-stages of 128 in both passes (an odd count), 6 pass-1 row
 # blocks of 64 gate/up pairs, 3 pass-2 row blocks of 128 down rows
@@ -38,7 +44,7 @@ def _oracle_routing(olayer, x):
     return ids, oracle_weights_for(logits, ids)
 
 
-def _routing(kind, olayer, x):
+def _routing(kind, olayer, x, thr=8):
     T = x.shape[0]
     if kind == "router":
         return _oracle_routing(olayer, x)
@@ -47,9 +53,11 @@ def _routing(kind, olayer, x):
     rw /= rw.sum(1, keepdims=True)
     if kind == "collide":  # every token on experts 0 and 1: T routes each
         return np.tile(np.array([[0, 1]], np.int32), (T, 1)), rw
-    # "edge": 16 tokens on {0, 1} (exactly the threshold), the rest on {2, 3}
-    ids = np.tile(np.array([[2, 3]], np.int32), (T, 1))
-    ids[:MFMA_MIN] = [0, 1]
+    # "edge": thr tokens on {0, 1} (exactly the threshold), thr - 1 on {2, 3}
+    # (one short of it), the rest on {4, 5}
+    ids = np.tile(np.array([[4, 5]], np.int32), (T, 1))
+    ids[:thr] = [0, 1]
+    ids[thr:2 * thr - 1] = [2, 3]
     return ids, rw
 
 
@@ -60,9 +68,10 @@ def test_mfma_expert_fwd(spec, T, kind):
     note("mfma expert_fwd %s T=%d %s" % (wl.DTYPE_NAMES[spec.expert_dtype], T, kind))
     w, layer, olayer = make_device_layer(spec)
     x = wl.make_x(T, spec.H, draw=T)
-    ids, rw = _routing(kind, olayer, x)
+    thr = _min_routes(layer, T)
+    ids, rw = _routing(kind, olayer, x, thr)
     counts = np.bincount(ids.ravel(), minlength=spec.E)
-    big = counts >= MFMA_MIN
+    big = counts >= thr
     ref = oracle.expert_fwd(olayer, x, ids, rw)
     got = gpu_expert_fwd(layer, x, ids, rw)
     gemv = gpu_expert_fwd(layer, x, ids, rw, flags=moe.MOE_NO_MFMA)
@@ -150,7 +159,7 @@ def _fp8_codes_layer():
                 s_down=s_dn)
 
 
-@pytest.mark.parametrize("T", [2 * MFMA_MIN, 256], ids=["narrow", "wide"])
+@pytest.mark.parametrize("T", [2 * MFMA_TOKENS, 256], ids=["narrow", "wide"])
 def test_mfma_fp8_every_code(T):
     """Every E4M3 code through the MFMA decode: code * 0.5 is exact in bf16,
     so the only rounding is that of the activation to bf16 before the down
@@ -255,7 +264,7 @@ def test_mxfp4_unaligned_scales_stay_on_gemv():
 # Zipf(1.1)-skewed routing, bf16, fp8 e4m3 with 128x128 block scales, MXFP4.
 # Every token's routing is checked; outputs on sampled tokens.
 
-def _sample(g, T, n_random=6):
+def _sample(g, T, thr, n_random=6):
     """Random tokens plus the last route of the hottest expert (the ragged
     end of its last token block) and a route of the coldest MFMA expert."""
     rng = np.random.default_rng(T)
@@ -264,7 +273,7 @@ def _sample(g, T, n_random=6):
     k = g["ids"].shape[1]
     hot = int(np.argmax(counts))
     pick.add(int(srt[offsets[hot + 1] - 1]) // k)
-    mf = np.where(counts >= MFMA_MIN)[0]
+    mf = np.where(counts >= thr)[0]
     if len(mf):
         cold = int(mf[np.argmin(counts[mf])])
         pick.add(int(srt[offsets[cold]]) // k)
@@ -291,13 +300,14 @@ def large_fp8():
 def _run_large(fixture, T):
     w, layer, olayer = fixture
     x = wl.make_x(T, layer.spec.H, draw=500 + T)
+    thr = _min_routes(layer, T)
     g0 = check_layer_sampled(layer, olayer, x, [0])[1]
-    sample = _sample(g0, T)
+    sample = _sample(g0, T, thr)
     err, g = check_layer_sampled(layer, olayer, x, sample)
     c = g["counts"]
     note("  T=%d: %d unique, max count %d, %d experts on MFMA, sampled %d tokens, max rel err %.3g" %
-         (T, g["n_uniq"], c.max(), (c >= MFMA_MIN).sum(), len(sample), err))
-    assert (c >= MFMA_MIN).any()
+         (T, g["n_uniq"], c.max(), (c >= thr).sum(), len(sample), err))
+    assert thr > 0 and (c >= thr).any()
 
 
 @pytest.mark.parametrize("T", [128, 256, 512])
@@ -336,6 +346,6 @@ def test_mfma_narrow_many_experts():
     x = wl.make_x(T, spec.H, draw=7)
     err, apart = check_layer_against_oracle(layer, olayer, x, tol=BF16_OPERAND_TOL)
     g = gpu_layer_fwd(layer, x, 0, full=True)
-    assert g["counts"].max() >= MFMA_MIN
+    assert g["counts"].max() >= _min_routes(layer, T)
     gemv = gpu_layer_fwd(layer, x, moe.MOE_NO_MFMA)
     assert max_rel(g["out"], gemv) <= BF16_OPERAND_TOL

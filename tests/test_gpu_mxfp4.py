@@ -1,7 +1,7 @@
 """MXFP4 expert weights (OCP microscaling: E2M1 codes two per byte, one E8M0
-scale per 32 elements of a row) on the GEMV path (MOE_NO_MFMA: segments of
-16 or more routes would otherwise run on the matrix cores, tested with the
-other MFMA paths), against the oracle.
+scale per 32 elements of a row) on the GEMV path (MOE_NO_MFMA: segments with
+moe_mfma_min_routes() routes or more would otherwise run on the matrix
+cores, tested with the other MFMA paths), against the oracle.
 
 The GPU converts codes with the hardware E2M1 conversion and applies each
 chunk's scale to the chunk's fp32 sum; every weight is exact in fp32, so the

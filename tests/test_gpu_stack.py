@@ -113,7 +113,7 @@ def test_stack_fused_against_oracle(stack3, T):
 def test_stack_fused_equals_layer_calls(T, flags):
     note("fused stack, E=16 k=5 H=512 I=256, T=%d flags=%d" % (T, flags))
     bias = np.zeros(SMALL.E, np.float32)
-    bias[:2] = 3.0  # two hot experts: segments of 16 or more routes from T = 16
+    bias[:2] = 3.0  # two hot experts: segments on the matrix cores from T = 16
     layers = _layers(SMALL, 4, bias)
     x0 = torch.from_numpy(wl.make_x(T, SMALL.H, draw=41 + T)).to(dev())
     ref = _sequential(layers, x0, T, flags)
