@@ -36,7 +36,7 @@ EXPORTS = ("moe_workspace_bytes", "moe_workspace_init", "moe_route", "moe_sort",
 
 MOE_N_STAGES = 6
 MOE_STATIC_SCRATCH_BYTES = 16 << 20
-STAGES = ("routing", "pass1_gemv", "pass1_mfma", "pass2_gemv", "pass2_mfma", "combine")
+STAGES = ("routing", "pass1_gemv", "pass1_mfma", "pass2_mfma", "pass2_gemv", "combine")
 
 
 class MoeError(RuntimeError):

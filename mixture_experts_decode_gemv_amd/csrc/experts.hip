@@ -272,11 +272,12 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
             default: return launch_pass2<MOE_MXFP4>(nc2, lanes, persistent_grid(items2), s, p2);
         }
     };
-    // pass 2 with the combine (small batches): writes out directly
-    const bool p2c = out && !mfma && fused_combine(L, T);
+    // pass 2 with the combine (small batches): writes out directly; the
+    // routes on the matrix cores come from y, written by mfma_2 before it
+    const bool p2c = out && fused_combine(L, T);
     auto gemv2c = [&](hipStream_t s) {
-        Pass2cArgs p{L.w_down, L.s_down, act, rt.w, xres, out, rt.reject, L.H, L.I, L.top_k, T,
-                     walk == MOE_WALK_DEDUP ? grouped : per_route};
+        Pass2cArgs p{L.w_down, L.s_down, act, rt.w, xres, out, rt.reject, mfma2 ? y : nullptr, L.H, L.I, L.top_k, T,
+                     walk == MOE_WALK_DEDUP ? (mfma2 ? split : grouped) : per_route};
         const int nq2 = L.I / epc;
         const int lanes = pass2_lanes(nq2, L.expert_dtype);
         const int nc2 = (nq2 + lanes - 1) / lanes;
@@ -331,14 +332,17 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
         }
         return combine();
     }
+    // In order: pass 2 on the matrix cores before pass 2 on the GEMV kernels
+    // (they write disjoint routes; pass 2 with the combine reads the MFMA
+    // routes' y rows).
     auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], st) : hipSuccess; };
     MOE_TRY(gemv1(st, mfma));
     MOE_TRY(mark(0));
     if (mfma) MOE_TRY(mfma_1(st, false));
     MOE_TRY(mark(1));
-    MOE_TRY(p2c ? gemv2c(st) : gemv2(st));
-    MOE_TRY(mark(2));
     if (mfma2) MOE_TRY(mfma_2(st));
+    MOE_TRY(mark(2));
+    MOE_TRY(p2c ? gemv2c(st) : gemv2(st));
     MOE_TRY(mark(3));
     MOE_TRY(combine());
     return mark(4);

@@ -575,9 +575,12 @@ __global__ __launch_bounds__(kGemvBlock) void pass2_kernel(Pass2Args a) {
 // block stay in LDS ([R][NR]); after a barrier the workgroup forms
 // out[t, h] = sum_j w[t, j] y[t * k + j, h] (+ x[t, h]) for its rows with the
 // combine kernel's arithmetic (FMAs in slot order from zero, then the
-// residual).  So there is no y in memory and no combine launch.
+// residual).  So there is no y in memory and no combine launch.  Segments on
+// the matrix cores (gemv_below) are skipped here; pass 2 on the MFMA kernel
+// runs before this launch and writes their y rows to memory (y), from where
+// the combine reads them.
 constexpr int kPass2cSegs = 1;   // segments per wave with their loads in flight together
-constexpr int kPass2cMaxT = 8;   // batches up to this size take this kernel
+constexpr int kPass2cMaxT = 64;  // batches up to this size take this kernel
 
 // Waves per pass2c workgroup for NC chunks per lane and G lanes per row: as
 // many as the weight registers of one wave allow without spilling (fp8 and
@@ -594,6 +597,7 @@ struct Pass2cArgs {
     const float *xres;      // [T, H] residual or null
     float *out;             // [T, H]; may alias xres (same element, same thread)
     const int32_t *reject;  // a caller-supplied routing's n_uniq, or null: out untouched when negative
+    const float *y;         // [R, H] rows of the routes on the matrix cores, or null (none)
     int H, I, k, T;
     SegArgs sa;
 };
@@ -700,7 +704,12 @@ __global__ __launch_bounds__(pass2c_waves(WDT, NC, G) * kWave) void pass2c_kerne
         const int t = idx / NR, i = idx - t * NR, h = h0 + i;
         if (h >= H) continue;
         float acc = 0.f;
-        for (int j = 0; j < k; ++j) acc = fmaf(a.w[(size_t)t * k + j], yl[(t * k + j) * NR + i], acc);
+        for (int j = 0; j < k; ++j) {
+            const int r = t * k + j;
+            // a route of an expert on the matrix cores: its y row is in memory
+            const bool mf = a.y && sa.counts[sa.ids[r]] >= sa.gemv_below;
+            acc = fmaf(a.w[r], mf ? a.y[(size_t)r * H + h] : yl[r * NR + i], acc);
+        }
         if (a.xres) acc += a.xres[(size_t)t * H + h];
         a.out[(size_t)t * H + h] = acc;
     }
@@ -843,7 +852,6 @@ constexpr int kMfmaMinRoutes = 8;
 constexpr int kMfmaMinRoutesWide = 4;
 // MFMA launches are made from this many tokens on.
 constexpr int kMfmaMinTokens = 16;
-static_assert(kMfmaMinTokens > kPass2cMaxT, "pass 2 with the combine reads GEMV segments only");
 constexpr int kMfmaTokens = 64;
 
 struct MfmaArgs {

@@ -109,6 +109,37 @@ def test_mfma_deterministic_and_token_permutation(T, spec):
     assert max_rel(c[np.argsort(perm)], ref) <= BF16_OPERAND_TOL
 
 
+@pytest.mark.parametrize("spec", [MIXED, MIXED_FP8], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("cold", [0, 7], ids=["hot-only", "hot-and-cold"])
+def test_pass2_with_combine_equals_separate_launches(spec, cold):
+    """Up to 64 tokens pass 2 runs with the combine in one launch, which reads
+    the y rows of the routes on the matrix cores from memory (pass 2 on the
+    MFMA kernel runs first); above 64 tokens pass 2 and the combine are
+    separate launches.  64 tokens (64 - cold on experts 0 and 1, on MFMA;
+    cold on experts 2 and 3, below the threshold of 8 so on the GEMV kernels)
+    alone and followed by 8 tokens on experts 4 and 5 give bitwise the same
+    rows, and the rows follow the oracle."""
+    note("pass 2 with the combine vs separate launches, %s, %d cold tokens" %
+         (wl.DTYPE_NAMES[spec.expert_dtype], cold))
+    w, layer, olayer = make_device_layer(spec)
+    x = wl.make_x(72, spec.H, draw=60 + cold)
+    ids = np.tile(np.array([[0, 1]], np.int32), (72, 1))
+    ids[64 - cold:64] = [2, 3]
+    ids[64:] = [4, 5]
+    rw = np.random.default_rng(60).uniform(0.1, 1.0, size=(72, 2)).astype(np.float32)
+    rw /= rw.sum(1, keepdims=True)
+    thr = _min_routes(layer, 64)
+    assert thr > 0 and thr == _min_routes(layer, 72) and cold < thr
+    full = gpu_expert_fwd(layer, x, ids, rw)
+    part = gpu_expert_fwd(layer, x[:64], ids[:64], rw[:64])
+    assert np.array_equal(part, full[:64])
+    ref = oracle.expert_fwd(olayer, x[:64], ids[:64], rw[:64])
+    assert max_rel(part, ref) <= BF16_OPERAND_TOL
+    if cold:
+        gemv = gpu_expert_fwd(layer, x[:64], ids[:64], rw[:64], flags=moe.MOE_NO_MFMA)
+        assert np.array_equal(part[64 - cold:], gemv[64 - cold:])  # cold tokens: GEMV rows only
+
+
 # bf16 with a long K: pass 1 runs 20 stages of 128 through the narrow
 # kernel's LDS ring (its steady state, not only the prologue), pass 2 runs 5
 LONG_K = wl.LayerSpec(E=8, top_k=2, H=2560, I=640)

@@ -380,6 +380,10 @@ def test_token_output_independent_of_batch_bitwise(sweep_layer, flags):
         assert np.array_equal(part, full[:T]), T
     again = gpu_layer_fwd(layer, x[:5], f)
     assert np.array_equal(again, full[:5])
+    # pass 2 with the combine in one launch (up to 64 tokens) against the
+    # separate pass-2 and combine launches (above 64)
+    x72 = wl.make_x(72, wl.SWEEP.H, draw=12)
+    assert np.array_equal(gpu_layer_fwd(layer, x72[:64], f), gpu_layer_fwd(layer, x72, f)[:64])
 
 
 def test_stack_layer_large_batch_rmsnorm():
