@@ -153,6 +153,9 @@ template <int WDT, int PASS>
 __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
     constexpr bool kFp8 = WDT == MOE_FP8_E4M3, kFp4 = WDT == MOE_MXFP4;
     constexpr int NWL = kFp4 ? 1 : kFp8 ? 2 : 4;  // 16-byte weight loads per tile per stage
+    // stages in the register ring (kD - 1 in flight); deeper rings for the
+    // narrower fp8 and MXFP4 stages measured slower (4 and 5 stages)
+    constexpr int kD = 3;
     constexpr int kStageB = kFp4 ? kKS / 2 : kKS * WT<WDT>::kBytes;  // bytes of a row per stage
     // per tile and stage: fp8 its block scale; MXFP4 the lane's row's 4 scale bytes
     using ScaleT = std::conditional_t<kFp4, unsigned, float>;
@@ -258,10 +261,14 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
             for (int j = 0; j < kXChunks; ++j)
                 *reinterpret_cast<u32x4 *>(xdst + buf * kBufLds + kRowsPerPass * j * kRowLds) = X[j];
         };
+        // Ordinary (not streaming) loads: the other token blocks of this row
+        // block read the same lines at about the same time on this XCD, and
+        // streaming loads leave them out of L2 (the experts with more than
+        // kTB routes were then read once per token block from HBM).
         auto load_w = [&](int ks, u32x4(&W)[2 * NWL], ScaleT(&S)[2]) {
             const size_t off = (size_t)ks * kStageB;  // kKS elements
 #pragma unroll
-            for (int c = 0; c < 2 * NWL; ++c) W[c] = load_weight_chunk(reinterpret_cast<const u32x4 *>(wsrc[c] + off));
+            for (int c = 0; c < 2 * NWL; ++c) W[c] = *reinterpret_cast<const u32x4 *>(wsrc[c] + off);
             if (kFp8 || kFp4) {
                 S[0] = sp0[ks];
                 S[1] = sp1[ks];
@@ -310,33 +317,33 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
             }
         };
 
-        // ring of three stages: W/X/S index ks % 3
-        u32x4 W0[2 * NWL], W1[2 * NWL], W2[2 * NWL];
-        u32x4 X0[kXChunks], X1[kXChunks], X2[kXChunks];
-        ScaleT S0[2] = {1, 1}, S1[2] = {1, 1}, S2[2] = {1, 1};
+        // ring of kD stages: W/X/S slot ks % kD
+        u32x4 W[kD][2 * NWL], X[kD][kXChunks];
+        ScaleT S[kD][2];
+#pragma unroll
+        for (int d = 0; d < kD; ++d) S[d][0] = S[d][1] = 1;
         // Every stage issues the same loads (stage indices past the end are
-        // clamped to the last stage) and the loop runs a multiple of 3 stages,
-        // so the compiler's wait counts see the same load sequence on every
-        // path and only wait for the stage being consumed.
-        load_x(0, X0);
-        load_w(0, W0, S0);
-        load_x(min(1, nst - 1), X1);
-        load_w(min(1, nst - 1), W1, S1);
-        store_x(0, X0);
-        // one stage: issue stage ks+2, compute stage ks, stage ks+1 into LDS
-        auto stage = [&](int ks, const u32x4(&Wc)[2 * NWL], const ScaleT(&Sc)[2], const u32x4(&Xn)[kXChunks],
-                         u32x4(&Wn2)[2 * NWL], ScaleT(&Sn2)[2], u32x4(&Xn2)[kXChunks]) {
-            const int kl = min(ks + 2, nst - 1);
-            load_x(kl, Xn2);
-            load_w(kl, Wn2, Sn2);
-            lds_barrier();
-            if (ks < nst) compute(ks & 1, Wc, Sc);
-            if (ks + 1 < nst) store_x((ks + 1) & 1, Xn);
-        };
-        for (int ks = 0; ks < nst; ks += 3) {
-            stage(ks, W0, S0, X1, W2, S2, X2);
-            stage(ks + 1, W1, S1, X2, W0, S0, X0);
-            stage(ks + 2, W2, S2, X0, W1, S1, X1);
+        // clamped to the last stage) and the loop runs a multiple of kD
+        // stages, so the compiler's wait counts see the same load sequence on
+        // every path and only wait for the stage being consumed.
+#pragma unroll
+        for (int d = 0; d + 1 < kD; ++d) {
+            load_x(min(d, nst - 1), X[d]);
+            load_w(min(d, nst - 1), W[d], S[d]);
+        }
+        store_x(0, X[0]);
+        for (int ks = 0; ks < nst; ks += kD) {
+            // stage k: issue stage k + kD - 1, compute stage k, stage k + 1's
+            // activations into LDS
+#pragma unroll
+            for (int d = 0; d < kD; ++d) {
+                const int k = ks + d, kl = min(k + kD - 1, nst - 1);
+                load_x(kl, X[(d + kD - 1) % kD]);
+                load_w(kl, W[(d + kD - 1) % kD], S[(d + kD - 1) % kD]);
+                lds_barrier();
+                if (k < nst) compute(k & 1, W[d], S[d]);
+                if (k + 1 < nst) store_x((k + 1) & 1, X[(d + 1) % kD]);
+            }
         }
 
         // epilogue: lane holds rows 4*(lane/16)+v of both tiles for token lane%16
