@@ -44,9 +44,9 @@
 //
 // MXFP4 weights (W4A16; OCP Microscaling Formats v1.0, E2M1 elements with an
 // E8M0 scale per 32 along K): a wave's k-step of 32 is one scale block, so a
-// lane's 8 codes share one scale.  They are converted to fp32 by the
-// hardware, multiplied by the scale and rounded to bf16, which is exact (an
-// E2M1 value has 2 significant bits).  A 128-wide stage of a row is 64 bytes
+// lane's 8 codes share one scale.  The hardware converts them to bf16 with
+// the scale applied (a power of two), which is exact (an E2M1 value has 2
+// significant bits).  A 128-wide stage of a row is 64 bytes
 // of codes and 4 scale bytes (one aligned word: the rows' scale arrays are
 // K/32 bytes long and K is a multiple of 128); every wave copies the 32
 // rows' scale words of the stage into its own LDS area.
@@ -102,14 +102,14 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16(unsigned w0, unsigned w1, float 
                  bf16_pair_rne(c[0] * s, c[1] * s), bf16_pair_rne(d[0] * s, d[1] * s)};
 }
 
-// 8 E2M1 codes (one word, element 0 in the low nibble) times s, as 8 bf16.
+// 8 E2M1 codes (one word, element 0 in the low nibble) times the E8M0 scale
+// s (a power of two, or NaN for the code 0xFF), as 8 bf16: the hardware
+// conversion applies the scale's exponent, which is exact.
 __device__ __forceinline__ u32x4 e2m1x8_to_bf16(unsigned w, float s) {
-    const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((int)w, 1.0f, 0);
-    const auto b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((int)w, 1.0f, 1);
-    const auto c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((int)w, 1.0f, 2);
-    const auto d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((int)w, 1.0f, 3);
-    return u32x4{bf16_pair_rne(a[0] * s, a[1] * s), bf16_pair_rne(b[0] * s, b[1] * s),
-                 bf16_pair_rne(c[0] * s, c[1] * s), bf16_pair_rne(d[0] * s, d[1] * s)};
+    return u32x4{__builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0)),
+                 __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1)),
+                 __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2)),
+                 __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3))};
 }
 
 // Copy of 16 bytes per lane from base + off (base wave-uniform, off this

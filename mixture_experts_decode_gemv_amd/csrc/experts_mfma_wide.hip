@@ -36,17 +36,19 @@
 // XCD b % 8), so the token blocks of one row block, which read the same
 // weights, run at the same time behind the same L2.
 //
-// fp8 e4m3 weights (W8A16): each code is converted to fp32 by the hardware
-// (OCP E4M3 on gfx950), multiplied by its 128x128 block scale and rounded to
-// bf16; the MFMA then runs on bf16 exactly as for bf16 weights.
+// fp8 e4m3 weights (W8A16): the codes are converted to bf16 by the hardware
+// (OCP E4M3 on gfx950), which is exact, and the MFMAs of a stage (128 along
+// K, one block of the 128x128 block scales) add into sums of their own that
+// are multiplied by the tile's block scale and added to the accumulator at
+// the stage's end.
 //
 // MXFP4 weights (W4A16; OCP Microscaling Formats v1.0: E2M1 codes, an E8M0
 // scale per 32 along K): a stage of a row is 64 bytes of codes, so one load
 // covers a whole 16-row tile (4 lanes per row), and each lane also loads its
 // row's 4 scale bytes of the stage (one aligned word: a row's scale array
 // is K/32 bytes and K is a multiple of 128).  MFMA k-step s of the stage is
-// scale block 4 ks + s; the codes are converted by the hardware, multiplied
-// by that scale and rounded to bf16, which is exact.
+// scale block 4 ks + s; the hardware converts the codes to bf16 with that
+// scale applied (a power of two), which is exact.
 #include <type_traits>
 
 #include "experts_impl.h"
@@ -76,24 +78,23 @@ __device__ __forceinline__ f32x4_t mfma16(const u32x4 &a, const u32x4 &b, const 
                                                    c, 0, 0, 0);
 }
 
-// 8 E2M1 codes (one word, element 0 in the low nibble) times s, as 8 bf16.
+// 8 E2M1 codes (one word, element 0 in the low nibble) times the E8M0 scale
+// s (a power of two, or NaN for the code 0xFF), as 8 bf16: the hardware
+// conversion applies the scale's exponent, which is exact.
 __device__ __forceinline__ u32x4 e2m1x8_to_bf16(unsigned w, float s) {
-    const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((int)w, 1.0f, 0);
-    const auto b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((int)w, 1.0f, 1);
-    const auto c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((int)w, 1.0f, 2);
-    const auto d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((int)w, 1.0f, 3);
-    return u32x4{bf16_pair_rne(a[0] * s, a[1] * s), bf16_pair_rne(b[0] * s, b[1] * s),
-                 bf16_pair_rne(c[0] * s, c[1] * s), bf16_pair_rne(d[0] * s, d[1] * s)};
+    return u32x4{__builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0)),
+                 __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1)),
+                 __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2)),
+                 __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3))};
 }
 
-// 8 E4M3 codes (two words, element 0 in the low byte) times s, as 8 bf16.
-__device__ __forceinline__ u32x4 e4m3x8_to_bf16(unsigned w0, unsigned w1, float s) {
-    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
-    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
-    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
-    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
-    return u32x4{bf16_pair_rne(a[0] * s, a[1] * s), bf16_pair_rne(b[0] * s, b[1] * s),
-                 bf16_pair_rne(c[0] * s, c[1] * s), bf16_pair_rne(d[0] * s, d[1] * s)};
+// 8 E4M3 codes (two words, element 0 in the low byte) as 8 bf16, exactly:
+// every E4M3 value is a bf16 value (the conversion's scale is 1).
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(unsigned w0, unsigned w1) {
+    return u32x4{__builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false)),
+                 __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true)),
+                 __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false)),
+                 __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true))};
 }
 
 // Workgroup barrier that waits for this wave's LDS traffic only: the global
@@ -288,6 +289,10 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
             const int g = lane >> 4;
             const unsigned char *wa0 = wl + (lane & 15) * WROW;
             const unsigned char *wa1 = wl + (16 + (lane & 15)) * WROW;
+            // fp8: the stage's products in sums of their own (from zero at
+            // k-step 0), scaled by the tiles' block scales at the stage's end
+            f32x4_t p0[kTT], p1[kTT];
+            const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int koff = 32 * s + 8 * g;  // k of this lane's 8 elements within the stage
@@ -300,18 +305,35 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
                 } else if constexpr (kFp8) {
                     const uint2 c0 = *reinterpret_cast<const uint2 *>(wa0 + koff);
                     const uint2 c1 = *reinterpret_cast<const uint2 *>(wa1 + koff);
-                    a0 = e4m3x8_to_bf16(c0.x, c0.y, S[0]);
-                    a1 = e4m3x8_to_bf16(c1.x, c1.y, S[1]);
+                    a0 = e4m3x8_to_bf16(c0.x, c0.y);
+                    a1 = e4m3x8_to_bf16(c1.x, c1.y);
                 } else {
                     a0 = *reinterpret_cast<const u32x4 *>(wa0 + koff * 2);
                     a1 = *reinterpret_cast<const u32x4 *>(wa1 + koff * 2);
                 }
+                // (fp8 runs every token tile, with no branch: tiles past ntt
+                // feed no output)
 #pragma unroll
                 for (int tt = 0; tt < kTT; ++tt) {
-                    if (tt < ntt) {
+                    if (kFp8 || tt < ntt) {
                         const u32x4 b = *reinterpret_cast<const u32x4 *>(xb + tt * 16 * kRowLds + koff * 2);
-                        acc0[tt] = mfma16(a0, b, acc0[tt]);
-                        acc1[tt] = mfma16(a1, b, acc1[tt]);
+                        if constexpr (kFp8) {
+                            p0[tt] = mfma16(a0, b, s == 0 ? zero : p0[tt]);
+                            p1[tt] = mfma16(a1, b, s == 0 ? zero : p1[tt]);
+                        } else {
+                            acc0[tt] = mfma16(a0, b, acc0[tt]);
+                            acc1[tt] = mfma16(a1, b, acc1[tt]);
+                        }
+                    }
+                }
+            }
+            if constexpr (kFp8) {
+#pragma unroll
+                for (int tt = 0; tt < kTT; ++tt) {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        acc0[tt][v] = fmaf(S[0], p0[tt][v], acc0[tt][v]);
+                        acc1[tt][v] = fmaf(S[1], p1[tt][v], acc1[tt][v]);
                     }
                 }
             }
