@@ -192,7 +192,7 @@ static hipError_t launch_mfma_pass(const moe_layer_t &L, int pass, int T, const 
     const long long R = (long long)T * L.top_k;
     const long long segs = std::min<long long>(L.E, R / a.min_n);
     const long long n_rb = pass == 1 ? L.I / (wide ? 64 : 16) : L.H / (wide ? 128 : 32);
-    const long long items = n_rb * (segs + R / kMfmaTokens);
+    const long long items = n_rb * (segs + R / (wide ? kMfmaTokens : kMfmaNarrowTokens));
     const long long cap = (long long)num_cus() * 2;
     const int grid = (int)std::max<long long>(1, std::min(items, cap));
     if (wide) switch (L.expert_dtype) {

@@ -841,7 +841,8 @@ hipError_t launch_pass2c(int nc, int lanes, hipStream_t st, const Pass2cArgs &a)
 // ---- MFMA segments ------------------------------------------------------------
 // Segments with at least kMfmaMinRoutes routes (kMfmaMinRoutesWide from
 // kMfmaWideTokens tokens) run on the matrix cores (see experts_mfma.hip and
-// experts_mfma_wide.hip), in token blocks of kMfmaTokens routes.  Measured on
+// experts_mfma_wide.hip), in token blocks of kMfmaNarrowTokens (narrow tiles)
+// or kMfmaTokens (wide tiles) routes.  Measured on
 // the large Zipf layer, the skewed sweep and the uniform sweep (graph
 // replays): from 5 routes an expert's GEMV walk is bound by its fp32 FMAs
 // rather than by HBM, so the matrix cores pay from there once batches are
@@ -853,6 +854,9 @@ constexpr int kMfmaMinRoutesWide = 4;
 // MFMA launches are made from this many tokens on.
 constexpr int kMfmaMinTokens = 16;
 constexpr int kMfmaTokens = 64;
+// Token blocks of the narrow tiles (batches below kMfmaWideTokens): half
+// the activation rows per LDS stage leave room for a deeper weight ring.
+constexpr int kMfmaNarrowTokens = 32;
 
 struct MfmaArgs {
     const void *w;        // pass 1: gate_up [E, 2I, H]; pass 2: down [E, H, I]

@@ -20,8 +20,10 @@
 // K runs in stages of 128.  Each stage of the weight tile and of the bf16
 // activation rows of the token block is copied from memory straight into LDS
 // (global_load_lds_dwordx4: no register staging, so the depth of the
-// pipeline is set by LDS, not by VGPRs), through a ring of three stages with
-// stage s+2 in flight while stage s is computed.  A lane's 16-byte chunk is
+// pipeline is set by LDS, not by VGPRs), through a ring of as many stages as
+// 72 KiB hold (4 for bf16 weights, 6 for fp8 and MXFP4; two workgroups per
+// CU), all but one in flight while a stage is computed.  Token blocks hold 32
+// routes, so a stage's activation rows take 8 KiB.  A lane's 16-byte chunk is
 // stored at chunk position (chunk ^ row) of its LDS row: the copies stay
 // coalesced (a row's 16 chunks are still read by 16 adjacent lanes) and the
 // operand reads (16 rows, same chunk) hit 16 different bank groups.
@@ -59,13 +61,12 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 namespace {
 
-constexpr int kTB = kMfmaTokens;      // routes per token block (32 or 64)
+constexpr int kTB = kMfmaNarrowTokens;  // routes per token block
 constexpr int kTT = kTB / 16;         // 16-token MFMA tiles per block
 constexpr int kKS = 128;              // K per stage
 constexpr int kWaves = kBlock / kWave;
-constexpr int kRing = 3;              // LDS stages
 constexpr int kXRowB = kKS * 2;       // bytes of a staged activation row (bf16)
-constexpr int kXBytes = kTB * kXRowB;  // activations of one stage (16 KiB)
+constexpr int kXBytes = kTB * kXRowB;  // activations of one stage (8 KiB)
 constexpr int kXcds = 8;
 static_assert(kTT <= kWaves, "one token tile per wave in the epilogue");
 
@@ -83,6 +84,9 @@ struct Stage {
     static constexpr int kSBytes = kFp4 ? kWaves * 32 * 4 : 0;  // MXFP4: each wave's 32 scale words
     static constexpr int kLoads = kWLoads + kXLoads + kSLoads;  // copies per wave per stage
     static constexpr int kBytes = kWBytes + kXBytes + kSBytes;
+    // LDS stages of the ring (kRing - 1 in flight), as many as 72 KiB hold
+    // (two workgroups per CU): 4 for bf16, 6 for fp8 and MXFP4
+    static constexpr int kRing = (72 * 1024) / kBytes < 6 ? (72 * 1024) / kBytes : 6;
     static_assert(kWLoads >= 1 && kWLoads * kWLanes * 16 * kWaves == kWBytes, "weight copies cover the stage");
     static_assert(kWLanes % kChunks == 0, "a copy covers whole rows");
 };
@@ -168,6 +172,21 @@ template <int N>
 __device__ __forceinline__ void wait_copies_and_sync() {
     static_assert(N >= 0 && N <= 63, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// wait_copies_and_sync for n (wave-uniform, 0 <= n <= MAXN) stages of P
+// copies each issued after the needed one.
+template <int MAXN, int P>
+__device__ __forceinline__ void wait_stages(int n) {
+    if constexpr (MAXN > 0) {
+        if (n == MAXN) {
+            wait_copies_and_sync<MAXN * P>();
+            return;
+        }
+        wait_stages<MAXN - 1, P>(n);
+    } else {
+        wait_copies_and_sync<0>();
+    }
 }
 
 // Workgroup barrier that waits for this wave's LDS traffic only.
@@ -290,7 +309,8 @@ template <int WDT, int PASS>
 __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
     using S = Stage<WDT>;
     constexpr bool kFp8 = S::kFp8, kFp4 = S::kFp4;
-    static_assert(kRing == 3, "the prologue below fills two stages");
+    constexpr int kRing = S::kRing;
+    static_assert(kRing >= 3 && (kRing - 2) * S::kLoads <= 63, "ring depth");
     __shared__ __align__(1024) unsigned char ring[kRing * S::kBytes];
     __shared__ int wsum[2 * kWaves];
     extern __shared__ int tables[];  // pre [E + 1], off [E + 1]
@@ -391,16 +411,16 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
                 for (int j = 0; j < S::kXLoads; ++j)
                     copy_to_lds(xbase + (size_t)ks * kXRowB, xoff[j], xd + (wv * S::kXLoads + j) * 1024);
         };
-        // stages 0 and 1 in flight.  (Copying the weights ahead of the route
-        // reads would gain nothing: loads complete in issue order, so the wait
-        // for the route ids would wait for those copies as well.)
-        issue_w(0, 0);
-        issue_x(0, 0);
-        issue_s(0, 0);
-        if (nst > 1) {
-            issue_w(1, 1);
-            issue_x(1, 1);
-            issue_s(1, 1);
+        // stages 0 .. kRing - 2 in flight.  (Copying the weights ahead of the
+        // route reads would gain nothing: loads complete in issue order, so
+        // the wait for the route ids would wait for those copies as well.)
+#pragma unroll
+        for (int s = 0; s + 1 < kRing; ++s) {
+            if (s < nst) {
+                issue_w(s, s);
+                issue_x(s, s);
+                issue_s(s, s);
+            }
         }
 
         // fp8 block scales of the two tiles, stage ks in lane ks (K <= 64 * 128)
@@ -430,10 +450,11 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
         const int boff = m * kXRowB + (((4 * wv + g) ^ m) << 4);
         int sl = 0;
         for (int ks = 0; ks < nst; ++ks) {
-            // copies issued after the stage that is needed: stage ks + 1's
-            if (ks + 1 >= nst) wait_copies_and_sync<0>();
-            else if (xw) wait_copies_and_sync<S::kLoads>();
-            else wait_copies_and_sync<S::kWLoads + S::kSLoads>();
+            // copies issued after the stage that is needed: those of stages
+            // ks + 1 .. ks + after
+            const int after = min(kRing - 2, nst - 1 - ks);
+            if (xw) wait_stages<kRing - 2, S::kLoads>(after);
+            else wait_stages<kRing - 2, S::kWLoads + S::kSLoads>(after);
 
             const unsigned char *wd = ring + sl * S::kBytes;
             const unsigned char *xd = wd + S::kWBytes;

@@ -140,20 +140,25 @@ def test_pass2_with_combine_equals_separate_launches(spec, cold):
         assert np.array_equal(part[64 - cold:], gemv[64 - cold:])  # cold tokens: GEMV rows only
 
 
-# bf16 with a long K: pass 1 runs 20 stages of 128 through the narrow
-# kernel's LDS ring (its steady state, not only the prologue), pass 2 runs 5
+# A long K: pass 1 runs 20 stages of 128 through the narrow kernel's LDS
+# ring (its steady state, not only the prologue), pass 2 runs 5, fewer than
+# the fp8 and MXFP4 rings hold
 LONG_K = wl.LayerSpec(E=8, top_k=2, H=2560, I=640)
+LONG_K_FP8 = wl.LayerSpec(E=8, top_k=2, H=2560, I=640, expert_dtype=wl.FP8)
+LONG_K_FP4 = wl.LayerSpec(E=8, top_k=2, H=2560, I=640, expert_dtype=wl.MXFP4)
 
 
-@pytest.mark.parametrize("T", [16, 31, 45, 64])
-def test_mfma_narrow_long_k(T):
-    """Narrow bf16 items over a long K, with 1 to 4 token tiles of 16 per
-    item (every token on experts 0 and 1): within the bar of the oracle,
-    deterministic, and bitwise unchanged when the tokens are permuted (a
-    route's arithmetic does not depend on its place in the token block)."""
-    note("mfma narrow long K, T=%d" % T)
-    w, layer, olayer = make_device_layer(LONG_K)
-    x = wl.make_x(T, LONG_K.H, draw=40 + T)
+@pytest.mark.parametrize("spec", [LONG_K, LONG_K_FP8, LONG_K_FP4], ids=["bf16", "fp8", "mxfp4"])
+@pytest.mark.parametrize("T", [16, 31, 45, 64, 100])
+def test_mfma_narrow_long_k(spec, T):
+    """Narrow items over a long K, every token on experts 0 and 1, so each
+    of them holds T routes: one to four token blocks, the last one ragged.
+    Within the bar of the oracle, deterministic, and bitwise unchanged when
+    the tokens are permuted (a route's arithmetic does not depend on its
+    place in the token block)."""
+    note("mfma narrow long K, %s T=%d" % (wl.DTYPE_NAMES[spec.expert_dtype], T))
+    w, layer, olayer = make_device_layer(spec)
+    x = wl.make_x(T, spec.H, draw=40 + T)
     ids, rw = _routing("collide", olayer, x)
     ref = oracle.expert_fwd(olayer, x, ids, rw)
     got = gpu_expert_fwd(layer, x, ids, rw)
