@@ -337,23 +337,45 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
     const int slots = per_xcd * kXcds;
     const int m = lane & 15, g = lane >> 4;
 
-    for (int it = blockIdx.x; it < slots; it += gridDim.x) {
-        const int item = (it % kXcds) * per_xcd + it / kXcds;
-        if (item >= total) continue;  // uniform over the workgroup
-        int lo = 0, hi = E;           // pre[lo] <= item < pre[hi]
+    // item -> (expert, row block, token block)
+    struct Item {
+        int e, first, rb, tb, nv;
+    };
+    auto decode = [&](int item) {
+        int lo = 0, hi = E;  // pre[lo] <= item < pre[hi]
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
             if (pre[mid] <= item) lo = mid;
             else hi = mid;
         }
-        const int e = __builtin_amdgcn_readfirstlane(lo);
-        const int local = item - pre[e];
-        const int first = off[e], n = off[e + 1] - first;
+        Item d;
+        d.e = __builtin_amdgcn_readfirstlane(lo);
+        const int local = item - pre[d.e];
+        d.first = off[d.e];
+        const int n = off[d.e + 1] - d.first;
         const int ntb = (n + kTB - 1) / kTB;
-        const int rb = local / ntb, tb = local - rb * ntb;
-        const int nv = min(kTB, n - tb * kTB);
+        d.rb = local / ntb;
+        d.tb = local - d.rb * ntb;
+        d.nv = min(kTB, n - d.tb * kTB);
+        return d;
+    };
+    // route ids of this lane's activation copies: copy j covers tokens 4
+    // apart; rows past the block's routes load the first route's row (their
+    // LDS rows only feed outputs that are never stored)
+    auto route_ids = [&](int nv, const int32_t *routes, int(&r)[S::kXLoads]) {
+#pragma unroll
+        for (int j = 0; j < S::kXLoads; ++j) {
+            const int tau = (wv * S::kXLoads + j) * 4 + (lane >> 4);
+            r[j] = routes[tau < nv ? tau : 0];
+        }
+    };
+    for (int it = blockIdx.x; it < slots; it += gridDim.x) {
+        const int item = (it % kXcds) * per_xcd + it / kXcds;
+        if (item >= total) continue;  // uniform over the workgroup
+        const Item d = decode(item);
+        const int e = d.e, rb = d.rb, nv = d.nv;
         const int ntt = (nv + 15) >> 4;
-        const int32_t *routes = a.sa.sorted + first + tb * kTB;
+        const int32_t *routes = a.sa.sorted + d.first + d.tb * kTB;
 
         lds_barrier();  // the previous item is done with the ring
 
@@ -391,19 +413,39 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
                 copy_word_to_lds(sbase + (size_t)ks * 4, soff, ring + sl * S::kBytes + S::kWBytes + kXBytes + wv * 128);
         };
 
-        // activation copy j covers tokens 4 apart; only the waves whose token
-        // tile holds routes copy.  Rows past the block's routes load the first
-        // route's row (their LDS rows only feed outputs that are never stored).
+        // activation copies: only the waves whose token tile holds routes copy
         const bool xw = wv * kTB / (16 * kWaves) < ntt;
         const char *xbase = uniform_ptr(static_cast<const char *>(a.src));
+
+        // fp8 block scales of the two tiles, stage ks in lane ks (K <= 64 *
+        // 128), loaded before the route ids and complete once those are
+        float sc0 = 1.f, sc1 = 1.f;
+        if (kFp8) {
+            const int kb = K / 128;
+            const float *sp0 = static_cast<const float *>(a.scales) + ((size_t)e * (w_rows / 128) + r0 / 128) * kb;
+            const float *sp1 = static_cast<const float *>(a.scales) + ((size_t)e * (w_rows / 128) + r1 / 128) * kb;
+            if (lane < kb) {
+                sc0 = sp0[lane];
+                sc1 = sp1[lane];
+            }
+        }
+        // route ids of this lane's activation copies
+        int rn[S::kXLoads];
+        route_ids(nv, routes, rn);
         unsigned xoff[S::kXLoads];
 #pragma unroll
         for (int j = 0; j < S::kXLoads; ++j) {
             const int tau = (wv * S::kXLoads + j) * 4 + (lane >> 4);
-            const int r = routes[tau < nv ? tau : 0];
             const int chunk = (lane & 15) ^ (tau & 15);
-            xoff[j] = (unsigned)(PASS == 1 ? r / a.k : r) * src_stride + chunk * 16;
+            xoff[j] = (unsigned)(PASS == 1 ? rn[j] / a.k : rn[j]) * src_stride + chunk * 16;
         }
+        // The scale loads are complete here (the route ids were loaded after
+        // them); redefining the values in an asm statement tells the compiler
+        // so.  Otherwise it waits for them (vmcnt) at their first use inside
+        // the stage loop, and its count, which does not know the copies,
+        // would drain the ring at every stage.
+        if (kFp8) asm volatile("s_waitcnt vmcnt(0)" : "+v"(sc0), "+v"(sc1));
+
         auto issue_x = [&](int ks, int sl) {
             const unsigned char *xd = ring + sl * S::kBytes + S::kWBytes;
             if (xw)
@@ -423,17 +465,6 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
             }
         }
 
-        // fp8 block scales of the two tiles, stage ks in lane ks (K <= 64 * 128)
-        float sc0 = 1.f, sc1 = 1.f;
-        if (kFp8) {
-            const int kb = K / 128;
-            const float *sp0 = static_cast<const float *>(a.scales) + ((size_t)e * (w_rows / 128) + r0 / 128) * kb;
-            const float *sp1 = static_cast<const float *>(a.scales) + ((size_t)e * (w_rows / 128) + r1 / 128) * kb;
-            if (lane < kb) {
-                sc0 = sp0[lane];
-                sc1 = sp1[lane];
-            }
-        }
 
         f32x4_t acc0[kTT], acc1[kTT];
 #pragma unroll

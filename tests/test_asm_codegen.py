@@ -28,3 +28,34 @@ def test_no_calls_no_scratch(tmp_path, src):
     sizes = [int(v) for v in re.findall(r"\.amdhsa_private_segment_fixed_size\s+(\d+)", text)]
     assert max(sizes, default=0) == 0, "%s: a kernel uses scratch memory" % src
     assert not re.search(r"^\s*(scratch|buffer)_(load|store)", text, re.M), src
+
+
+def _kernel_bodies(text, prefix):
+    """{kernel name: its instruction lines} for the kernels whose names start with prefix."""
+    out = {}
+    for m in re.finditer(r"^(%s\w*):" % re.escape(prefix), text, re.M):
+        end = text.index(".Lfunc_end", m.end())
+        lines = [l.split(";")[0].strip() for l in text[m.end():end].split("\n")]
+        out[m.group(1)] = [l for l in lines if l and not l.startswith(".")]
+    return out
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+def test_narrow_mfma_ring_is_not_drained(tmp_path):
+    """The narrow MFMA kernels wait for their LDS copies only through their
+    own counted waits (s_waitcnt vmcnt(N) then s_barrier).  A compiler wait on
+    a vector load (e.g. the fp8 block scales) placed inside the stage loop
+    would count without the copies and so drain the ring at every stage."""
+    out = tmp_path / "experts_mfma.s"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S",
+           os.path.join(CSRC, "experts_mfma.hip"), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    bodies = _kernel_bodies(out.read_text(), "_ZN3moe11mfma_kernel")
+    assert len(bodies) == 6, sorted(bodies)
+    for name, lines in bodies.items():
+        first = next(i for i, l in enumerate(lines) if l.startswith("global_load_lds"))
+        last = max(i for i, l in enumerate(lines) if l.startswith("v_mfma"))
+        for i in range(first, last):
+            if lines[i].startswith("s_waitcnt") and "vmcnt" in lines[i]:
+                assert lines[i + 1] == "s_barrier", "%s: %s inside the stage loop" % (name, lines[i])
