@@ -179,14 +179,18 @@ static moe_status layer_fwd(const moe_layer_t *layer, const float *x, int32_t T,
     const bool norm = (flags & MOE_RMSNORM_IN) != 0;
     const float *xin = norm ? F(wl.xn) : x;
     if (ev && (s = hip_status(hipEventRecord(ev[0], st))) != MOE_OK) return s;
+    // the routing launch also writes the bf16 copy of x when segments may
+    // take the MFMA path
+    const bool xb = mfma_min_routes(*layer, T, flags) > 0;
     if ((s = hip_status(launch_route(*layer, x, nullptr, T, norm ? F(wl.xn) : nullptr, F(wl.logits), I32(wl.ids),
                                      F(wl.w), I32(wl.counts), I32(wl.offsets), I32(wl.sorted), I32(wl.uniq),
                                      I32(wl.nuniq), I32(wl.stats), reinterpret_cast<unsigned *>(b + wl.arrive), norm,
-                                     nullptr, 0, st))) != MOE_OK)
+                                     nullptr, 0, st, nullptr,
+                                     xb ? reinterpret_cast<uint32_t *>(b + wl.xb) : nullptr))) != MOE_OK)
         return s;
     if (ev && (s = hip_status(hipEventRecord(ev[1], st))) != MOE_OK) return s;
     Routing rt{I32(wl.ids),  I32(wl.counts), I32(wl.offsets), I32(wl.sorted),
-               I32(wl.uniq), I32(wl.nuniq),  F(wl.w),         I32(wl.stats) + 2, nullptr};
+               I32(wl.uniq), I32(wl.nuniq),  F(wl.w),         I32(wl.stats) + 2, nullptr, xb};
     return hip_status(launch_experts(*layer, xin, (flags & MOE_ACCUM_RESIDUAL) ? x : nullptr, T, rt, b + wl.xb,
                                      F(wl.act), F(wl.y), out, flags, st, ev ? ev + 2 : nullptr, may_fork));
 }
@@ -343,14 +347,16 @@ moe_status moe_stack_fwd(const moe_layer_t *layers, int32_t n_layers, const floa
             pc = PrevCombine{F(b, pl.y), F(b, pl.w), h, hbuf[l & 1], L.top_k};
             h = hbuf[l & 1];
         }
+        const bool xb = mfma_min_routes(L, T, lf) > 0;
         if ((s = hip_status(launch_route(L, h, nullptr, T, F(b, wl.xn), F(b, wl.logits), I32(b, wl.ids),
                                          F(b, wl.w), I32(b, wl.counts), I32(b, wl.offsets), I32(b, wl.sorted),
                                          I32(b, wl.uniq), I32(b, wl.nuniq), I32(b, wl.stats),
                                          reinterpret_cast<unsigned *>(b + wl.arrive), true, nullptr, 0, st,
-                                         l > 0 && !direct ? &pc : nullptr))) != MOE_OK)
+                                         l > 0 && !direct ? &pc : nullptr,
+                                         xb ? reinterpret_cast<uint32_t *>(b + wl.xb) : nullptr))) != MOE_OK)
             return s;
         Routing rt{I32(b, wl.ids),  I32(b, wl.counts), I32(b, wl.offsets), I32(b, wl.sorted),
-                   I32(b, wl.uniq), I32(b, wl.nuniq),  F(b, wl.w),         I32(b, wl.stats) + 2, nullptr};
+                   I32(b, wl.uniq), I32(b, wl.nuniq),  F(b, wl.w),         I32(b, wl.stats) + 2, nullptr, xb};
         float *dst = last ? out : direct ? hbuf[l & 1] : nullptr;
         if ((s = hip_status(launch_experts(L, F(b, wl.xn), h, T, rt, b + wl.xb, F(b, wl.act), F(b, wl.y), dst, lf,
                                            st))) != MOE_OK)

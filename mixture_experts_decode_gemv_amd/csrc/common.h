@@ -325,7 +325,8 @@ struct PrevCombine {
 hipError_t launch_route(const moe_layer_t &L, const float *x, const float *logits_in, int T, float *xn,
                         float *logits, int32_t *ids, float *w, int32_t *counts, int32_t *offsets, int32_t *sorted,
                         int32_t *uniq, int32_t *n_uniq, int32_t *stats, unsigned *arrive, bool rmsnorm,
-                        unsigned *zero, int n_zero, hipStream_t st, const PrevCombine *prev = nullptr);
+                        unsigned *zero, int n_zero, hipStream_t st, const PrevCombine *prev = nullptr,
+                        uint32_t *xb = nullptr);
 hipError_t launch_sort(const int32_t *ids, int R, int E, int32_t *counts, int32_t *offsets, int32_t *sorted,
                        int32_t *uniq, int32_t *n_uniq, hipStream_t st);
 hipError_t launch_zero(unsigned *p, int n, hipStream_t st);
@@ -339,6 +340,8 @@ struct Routing {
     // a caller-supplied routing's n_uniq (null for the library's own): when
     // negative (rejected by the sort) the combine leaves out untouched
     const int32_t *reject;
+    // the routing launch wrote the bf16 copy of x into xb
+    bool xb_ready = false;
 };
 // ev (optional): events recorded after pass 1 GEMV, pass 1 MFMA, pass 2 GEMV,
 // pass 2 MFMA and the combine (ev[0..4]); a stage that does not run records

@@ -317,7 +317,7 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
     if (sd) {
         MOE_TRY(hipEventRecord(sd->fork, st));
         MOE_TRY(hipStreamWaitEvent(sd->s, sd->fork, 0));
-        MOE_TRY(mfma_1(sd->s, true));
+        MOE_TRY(mfma_1(sd->s, !rt.xb_ready));
         if (mfma2) MOE_TRY(mfma_2(sd->s));
         MOE_TRY(gemv1(st, false));
         // pass 2 of the DEDUP_PASS1 walk reads every segment's pass-1 rows
@@ -336,7 +336,7 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
     // (they write disjoint routes; pass 2 with the combine reads the MFMA
     // routes' y rows).
     auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], st) : hipSuccess; };
-    MOE_TRY(gemv1(st, mfma));
+    MOE_TRY(gemv1(st, mfma && !rt.xb_ready));
     MOE_TRY(mark(0));
     if (mfma) MOE_TRY(mfma_1(st, false));
     MOE_TRY(mark(1));

@@ -57,6 +57,7 @@ struct RouteArgs {
     const float *prev_w;     // [T, prev_k]
     const float *prev_h;     // [T, H] residual
     float *h_out;            // [T, H] the combined rows (written by eb = 0)
+    uint32_t *xb;            // bf16 copy of the staged rows [T, H] (written by eb = 0) or null
     int prev_k;
     float *logits;           // [T, E] out (when computed)
     int32_t *ids;            // [T, k]
@@ -202,6 +203,17 @@ __global__ __launch_bounds__(kBlock) void route_kernel(RouteArgs a) {
             }
             __syncthreads();
         }
+        // the bf16 copy of the rows the experts read (for their MFMA
+        // segments), pairs rounded to nearest even
+        if (a.xb && eb == 0) {
+            const int n2 = (t1 - t0) * H / 2;
+            const float2 *src2 = reinterpret_cast<const float2 *>(tile);
+            uint32_t *dst2 = a.xb + (size_t)t0 * H / 2;
+            for (int i = threadIdx.x; i < n2; i += kBlock) {
+                const float2 v = src2[i];
+                dst2[i] = bf16_pair_rne(v.x, v.y);
+            }
+        }
         // two tokens per pass (independent chains); each token reduced on its
         // own, so a logit never depends on its position in the tile
         const int nt = t1 - t0;
@@ -324,7 +336,7 @@ static hipError_t route_dispatch(int nc, dim3 g, size_t lds, hipStream_t st, con
 hipError_t launch_route(const moe_layer_t &L, const float *x, const float *logits_in, int T, float *xn,
                         float *logits, int32_t *ids, float *w, int32_t *counts, int32_t *offsets, int32_t *sorted,
                         int32_t *uniq, int32_t *n_uniq, int32_t *stats, unsigned *arrive, bool rmsnorm,
-                        unsigned *zero, int n_zero, hipStream_t st, const PrevCombine *prev) {
+                        unsigned *zero, int n_zero, hipStream_t st, const PrevCombine *prev, uint32_t *xb) {
     RouteArgs a;
     a.prev_y = prev ? prev->y : nullptr;
     a.prev_w = prev ? prev->w : nullptr;
@@ -338,6 +350,7 @@ hipError_t launch_route(const moe_layer_t &L, const float *x, const float *logit
     a.x = x;
     a.logits_in = logits_in;
     a.xn = xn;
+    a.xb = logits_in ? nullptr : xb;
     a.logits = logits;
     a.ids = ids;
     a.w = w;
