@@ -154,9 +154,10 @@ static int persistent_grid(long long max_items) {
 // (below that the MFMA launches would mostly be idle, and batches up to
 // kPass2cMaxT tokens run pass 2 with the combine, on GEMV segments only).
 static bool mfma_eligible(const moe_layer_t &L, int T, uint32_t flags) {
-    // the narrow kernels address activation rows with 32-bit byte offsets
-    const bool offsets32 = (unsigned long long)T * L.H * 2 < (1ull << 32) &&
-                           (unsigned long long)T * L.top_k * L.I * 4 < (1ull << 32);
+    // the MFMA kernels address activation rows with 32-bit byte offsets, and
+    // the wide ones mark unused rows with offsets from 2 GiB up
+    const bool offsets32 = (unsigned long long)T * L.H * 2 < (1ull << 31) &&
+                           (unsigned long long)T * L.top_k * L.I * 4 < (1ull << 31);
     // MXFP4 scale words are copied 4 bytes at a time
     const bool fp4_ok = L.expert_dtype == MOE_MXFP4 && (reinterpret_cast<uintptr_t>(L.s_gate_up) & 3) == 0 &&
                         (reinterpret_cast<uintptr_t>(L.s_down) & 3) == 0;

@@ -69,6 +69,10 @@ constexpr int kChunksPerRow = kKS * 2 / 16;           // 16-byte chunks of a sta
 constexpr int kRowsPerPass = kBlock / kChunksPerRow;  // rows staged per pass of the workgroup (16)
 constexpr int kXChunks = kTB / kRowsPerPass;          // rows (one chunk each) per thread per stage
 constexpr int kXcds = 8;
+// Buffer descriptor word 3 for raw 32-bit loads on gfx9 (CDNA), and a byte
+// offset beyond every activation buffer here (< 2 GiB, with room for K)
+constexpr int kBufferFlags = 0x00020000;
+constexpr unsigned kOutside = 0x80000000u;
 // wave-private weight tile of one stage: 32 rows (two 16-row MFMA tiles)
 constexpr int kWRow = kKS * 2 + 16;  // bf16 row segment + pad (bytes); fp8 uses kKS + 16
 constexpr int kWTile = 32 * kWRow;
@@ -178,6 +182,10 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
     // bf16 activation rows: pass 1 reads xb [T, H]; pass 2 reads a[r] from the
     // first half of the fp32 activation row r (4I bytes apart)
     const size_t src_stride = PASS == 1 ? (size_t)a.H * 2 : (size_t)a.I * 4;
+    // the activation rows as a buffer: pass 1 x [T, H] bf16, pass 2 R rows
+    // of 4I bytes (offsets from kOutside on read as zeros)
+    const unsigned src_bytes = PASS == 1 ? (unsigned)(a.sa.R / a.k) * a.H * 2 : (unsigned)a.sa.R * a.I * 4;
+    const auto xrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.src), 0, (int)src_bytes, kBufferFlags);
     const int nu = min(segment_count(a.sa), a.sa.E);
     const int total = build_item_table(a, nu, n_rb, pre, wsum);
     // contiguous item ranges per XCD (the grid is a multiple of kXcds)
@@ -239,23 +247,25 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
         }
         // activation rows this thread stages: chunk tid % 16 of tokens
         // tid / 16 + 16 j (16 lanes fill one 256-byte row segment: contiguous
-        // global reads and conflict-free LDS writes).  Rows past the block's
-        // routes load token 0's row (their LDS rows only feed output columns
-        // that are never stored), so every lane issues the same loads and the
-        // wait counts stay exact.
+        // global reads and conflict-free LDS writes).  They are buffer loads:
+        // rows past the block's routes take an offset outside the buffer,
+        // which reads zeros without touching memory (their LDS rows only
+        // feed output columns that are never stored), so every lane issues
+        // the same loads and the wait counts stay exact.
         const int xq = tid % kChunksPerRow, xt0 = tid / kChunksPerRow;
-        const char *xsrc[kXChunks];
+        unsigned xoff[kXChunks];
 #pragma unroll
         for (int j = 0; j < kXChunks; ++j) {
             const int tok = xt0 + kRowsPerPass * j;
             const int xr = rts[tok < nv ? tok : 0];
-            xsrc[j] = static_cast<const char *>(a.src) + xq * 16 + (size_t)(PASS == 1 ? xr / a.k : xr) * src_stride;
+            xoff[j] = tok < nv ? (unsigned)(xq * 16 + (size_t)(PASS == 1 ? xr / a.k : xr) * src_stride) : kOutside;
         }
         unsigned char *xdst = xs + xt0 * kRowLds + xq * 16;
 
         auto load_x = [&](int ks, u32x4(&X)[kXChunks]) {
 #pragma unroll
-            for (int j = 0; j < kXChunks; ++j) X[j] = *reinterpret_cast<const u32x4 *>(xsrc[j] + ks * kKS * 2);
+            for (int j = 0; j < kXChunks; ++j)
+                X[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, (int)(xoff[j] + ks * kKS * 2), 0, 0));
         };
         auto store_x = [&](int buf, const u32x4(&X)[kXChunks]) {
 #pragma unroll

@@ -199,7 +199,8 @@ def test_static_entry_point_validation():
 def test_mfma_min_routes():
     """The matrix-core threshold a call applies (host only): 8 routes below
     128 tokens, 4 from 128, none below 16 tokens, for fp32 experts, for H or I
-    not a multiple of 128, with MOE_NO_MFMA or the per-route walk."""
+    not a multiple of 128, with MOE_NO_MFMA or the per-route walk, or for
+    activation rows of 2 GiB or more."""
     L = _layer(H=256, I=128, expert_dtype=moe.MOE_BF16)
     assert moe.moe_mfma_min_routes(L, 15) == 0
     assert moe.moe_mfma_min_routes(L, 16) == 8
@@ -213,6 +214,10 @@ def test_mfma_min_routes():
                                           s_down=0x5000), 64) == 8
     assert moe.moe_mfma_min_routes(_layer(H=256, I=128), 64) == 0  # fp32 experts
     assert moe.moe_mfma_min_routes(_layer(H=192, I=128, expert_dtype=moe.MOE_BF16), 64) == 0
+    # activation rows of 2 GiB or more (R x I x 4 bytes) stay on the GEMV kernels
+    Lw = _layer(H=256, I=4096, expert_dtype=moe.MOE_BF16)
+    assert moe.moe_mfma_min_routes(Lw, 65535) == 4
+    assert moe.moe_mfma_min_routes(Lw, 65536) == 0
     assert moe.moe_mfma_min_routes(L, -1) == -1
     assert moe.moe_mfma_min_routes(_layer(top_k=9), 64) == -1
     assert moe.moe_mfma_min_routes(L, 64, 7) == -1  # unknown walk
