@@ -286,46 +286,48 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
             }
         };
 
-        f32x4_t acc0[kTT], acc1[kTT];
+        // The rest of the item for NT token tiles, a compile-time count: no
+        // tile past them costs a branch, an LDS read or an MFMA, and each
+        // count has its own accumulators.
+        auto run = [&](auto ntc) {
+            constexpr int NT = decltype(ntc)::value;
+            f32x4_t acc0[NT], acc1[NT];
 #pragma unroll
-        for (int tt = 0; tt < kTT; ++tt) acc0[tt] = acc1[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int tt = 0; tt < NT; ++tt) acc0[tt] = acc1[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        // the stage's weights into the wave's LDS tile, then the MFMAs reading
-        // both operands from LDS (A: lane (m, g) row m, k-group g of the step)
-        auto compute = [&](int buf, const u32x4(&W)[2 * NWL], const ScaleT(&S)[2]) {
+            // the stage's weights into the wave's LDS tile, then the MFMAs reading
+            // both operands from LDS (A: lane (m, g) row m, k-group g of the step)
+            auto compute = [&](int buf, const u32x4(&W)[2 * NWL], const ScaleT(&S)[2]) {
 #pragma unroll
-            for (int c = 0; c < 2 * NWL; ++c) *reinterpret_cast<u32x4 *>(wl + wdst[c]) = W[c];
-            const unsigned char *xb = xs + buf * kBufLds + (lane & 15) * kRowLds;
-            const int g = lane >> 4;
-            const unsigned char *wa0 = wl + (lane & 15) * WROW;
-            const unsigned char *wa1 = wl + (16 + (lane & 15)) * WROW;
-            // fp8: the stage's products in sums of their own (from zero at
-            // k-step 0), scaled by the tiles' block scales at the stage's end
-            f32x4_t p0[kTT], p1[kTT];
-            const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+                for (int c = 0; c < 2 * NWL; ++c) *reinterpret_cast<u32x4 *>(wl + wdst[c]) = W[c];
+                const unsigned char *xb = xs + buf * kBufLds + (lane & 15) * kRowLds;
+                const int g = lane >> 4;
+                const unsigned char *wa0 = wl + (lane & 15) * WROW;
+                const unsigned char *wa1 = wl + (16 + (lane & 15)) * WROW;
+                // fp8: the stage's products in sums of their own (from zero at
+                // k-step 0), scaled by the tiles' block scales at the stage's end
+                f32x4_t p0[NT], p1[NT];
+                const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int koff = 32 * s + 8 * g;  // k of this lane's 8 elements within the stage
-                u32x4 a0, a1;
-                if constexpr (kFp4) {
-                    const unsigned c0 = *reinterpret_cast<const unsigned *>(wa0 + koff / 2);
-                    const unsigned c1 = *reinterpret_cast<const unsigned *>(wa1 + koff / 2);
-                    a0 = e2m1x8_to_bf16(c0, e8m0_value((S[0] >> (8 * s)) & 0xffu));
-                    a1 = e2m1x8_to_bf16(c1, e8m0_value((S[1] >> (8 * s)) & 0xffu));
-                } else if constexpr (kFp8) {
-                    const uint2 c0 = *reinterpret_cast<const uint2 *>(wa0 + koff);
-                    const uint2 c1 = *reinterpret_cast<const uint2 *>(wa1 + koff);
-                    a0 = e4m3x8_to_bf16(c0.x, c0.y);
-                    a1 = e4m3x8_to_bf16(c1.x, c1.y);
-                } else {
-                    a0 = *reinterpret_cast<const u32x4 *>(wa0 + koff * 2);
-                    a1 = *reinterpret_cast<const u32x4 *>(wa1 + koff * 2);
-                }
-                // (fp8 runs every token tile, with no branch: tiles past ntt
-                // feed no output)
+                for (int s = 0; s < 4; ++s) {
+                    const int koff = 32 * s + 8 * g;  // k of this lane's 8 elements within the stage
+                    u32x4 a0, a1;
+                    if constexpr (kFp4) {
+                        const unsigned c0 = *reinterpret_cast<const unsigned *>(wa0 + koff / 2);
+                        const unsigned c1 = *reinterpret_cast<const unsigned *>(wa1 + koff / 2);
+                        a0 = e2m1x8_to_bf16(c0, e8m0_value((S[0] >> (8 * s)) & 0xffu));
+                        a1 = e2m1x8_to_bf16(c1, e8m0_value((S[1] >> (8 * s)) & 0xffu));
+                    } else if constexpr (kFp8) {
+                        const uint2 c0 = *reinterpret_cast<const uint2 *>(wa0 + koff);
+                        const uint2 c1 = *reinterpret_cast<const uint2 *>(wa1 + koff);
+                        a0 = e4m3x8_to_bf16(c0.x, c0.y);
+                        a1 = e4m3x8_to_bf16(c1.x, c1.y);
+                    } else {
+                        a0 = *reinterpret_cast<const u32x4 *>(wa0 + koff * 2);
+                        a1 = *reinterpret_cast<const u32x4 *>(wa1 + koff * 2);
+                    }
 #pragma unroll
-                for (int tt = 0; tt < kTT; ++tt) {
-                    if (kFp8 || tt < ntt) {
+                    for (int tt = 0; tt < NT; ++tt) {
                         const u32x4 b = *reinterpret_cast<const u32x4 *>(xb + tt * 16 * kRowLds + koff * 2);
                         if constexpr (kFp8) {
                             p0[tt] = mfma16(a0, b, s == 0 ? zero : p0[tt]);
@@ -336,73 +338,87 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
                         }
                     }
                 }
+                if constexpr (kFp8) {
+#pragma unroll
+                    for (int tt = 0; tt < NT; ++tt) {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            acc0[tt][v] = fmaf(S[0], p0[tt][v], acc0[tt][v]);
+                            acc1[tt][v] = fmaf(S[1], p1[tt][v], acc1[tt][v]);
+                        }
+                    }
+                }
+            };
+
+            // ring of kD stages: W/X/S slot ks % kD
+            u32x4 W[kD][2 * NWL], X[kD][kXChunks];
+            ScaleT S[kD][2];
+#pragma unroll
+            for (int d = 0; d < kD; ++d) S[d][0] = S[d][1] = 1;
+            // Every stage issues the same loads (stage indices past the end are
+            // clamped to the last stage) and the loop runs a multiple of kD
+            // stages, so the compiler's wait counts see the same load sequence on
+            // every path and only wait for the stage being consumed.
+            {
+#pragma unroll
+                for (int d = 0; d + 1 < kD; ++d) {
+                    load_x(min(d, nst - 1), X[d]);
+                    load_w(min(d, nst - 1), W[d], S[d]);
+                }
+                store_x(0, X[0]);
+                for (int ks = 0; ks < nst; ks += kD) {
+                    // stage k: issue stage k + kD - 1, compute stage k, stage k +
+                    // 1's activations into LDS
+#pragma unroll
+                    for (int d = 0; d < kD; ++d) {
+                        const int k = ks + d, kl = min(k + kD - 1, nst - 1);
+                        load_x(kl, X[(d + kD - 1) % kD]);
+                        load_w(kl, W[(d + kD - 1) % kD], S[(d + kD - 1) % kD]);
+                        lds_barrier();
+                        if (k < nst) compute(k & 1, W[d], S[d]);
+                        if (k + 1 < nst) store_x((k + 1) & 1, X[(d + 1) % kD]);
+                    }
+                }
             }
-            if constexpr (kFp8) {
+
+            // epilogue: lane holds rows 4*(lane/16)+v of both tiles for token lane%16
 #pragma unroll
-                for (int tt = 0; tt < kTT; ++tt) {
+            for (int tt = 0; tt < NT; ++tt) {
+                const int tok = tt * 16 + (lane & 15);
+                if (tok < nv) {
+                    const int r = rts[tok];
+                    const int row = r0 + 4 * (lane >> 4);
+                    if (PASS == 1) {
+                        float o[4];
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        acc0[tt][v] = fmaf(S[0], p0[tt][v], acc0[tt][v]);
-                        acc1[tt][v] = fmaf(S[1], p1[tt][v], acc1[tt][v]);
+                        for (int v = 0; v < 4; ++v) o[v] = silu(acc0[tt][v]) * acc1[tt][v];
+                        if (a.act_bf16) {  // bf16 into the first half of the fp32 row r
+                            *reinterpret_cast<uint2 *>(reinterpret_cast<char *>(a.dst) + (size_t)r * a.I * 4 + row * 2) =
+                                make_uint2(bf16_pair_rne(o[0], o[1]), bf16_pair_rne(o[2], o[3]));
+                        } else {
+                            *reinterpret_cast<float4 *>(a.dst + (size_t)r * a.I + row) =
+                                make_float4(o[0], o[1], o[2], o[3]);
+                        }
+                    } else {
+                        *reinterpret_cast<float4 *>(a.dst + (size_t)r * a.H + row) =
+                            make_float4(acc0[tt][0], acc0[tt][1], acc0[tt][2], acc0[tt][3]);
+                        *reinterpret_cast<float4 *>(a.dst + (size_t)r * a.H + row + 16) =
+                            make_float4(acc1[tt][0], acc1[tt][1], acc1[tt][2], acc1[tt][3]);
                     }
                 }
             }
         };
-
-        // ring of kD stages: W/X/S slot ks % kD
-        u32x4 W[kD][2 * NWL], X[kD][kXChunks];
-        ScaleT S[kD][2];
-#pragma unroll
-        for (int d = 0; d < kD; ++d) S[d][0] = S[d][1] = 1;
-        // Every stage issues the same loads (stage indices past the end are
-        // clamped to the last stage) and the loop runs a multiple of kD
-        // stages, so the compiler's wait counts see the same load sequence on
-        // every path and only wait for the stage being consumed.
-#pragma unroll
-        for (int d = 0; d + 1 < kD; ++d) {
-            load_x(min(d, nst - 1), X[d]);
-            load_w(min(d, nst - 1), W[d], S[d]);
-        }
-        store_x(0, X[0]);
-        for (int ks = 0; ks < nst; ks += kD) {
-            // stage k: issue stage k + kD - 1, compute stage k, stage k + 1's
-            // activations into LDS
-#pragma unroll
-            for (int d = 0; d < kD; ++d) {
-                const int k = ks + d, kl = min(k + kD - 1, nst - 1);
-                load_x(kl, X[(d + kD - 1) % kD]);
-                load_w(kl, W[(d + kD - 1) % kD], S[(d + kD - 1) % kD]);
-                lds_barrier();
-                if (k < nst) compute(k & 1, W[d], S[d]);
-                if (k + 1 < nst) store_x((k + 1) & 1, X[(d + 1) % kD]);
+        // (bf16: one body for all counts; four took more than 256 VGPRs)
+        static_assert(kTT == 4, "token tiles 1 to 4");
+        if constexpr (kFp8 || kFp4) {
+            switch (ntt) {
+                case 1: run(std::integral_constant<int, 1>{}); break;
+                case 2: run(std::integral_constant<int, 2>{}); break;
+                case 3: run(std::integral_constant<int, 3>{}); break;
+                default: run(std::integral_constant<int, 4>{}); break;
             }
-        }
-
-        // epilogue: lane holds rows 4*(lane/16)+v of both tiles for token lane%16
-#pragma unroll
-        for (int tt = 0; tt < kTT; ++tt) {
-            const int tok = tt * 16 + (lane & 15);
-            if (tt < ntt && tok < nv) {
-                const int r = rts[tok];
-                const int row = r0 + 4 * (lane >> 4);
-                if (PASS == 1) {
-                    float o[4];
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) o[v] = silu(acc0[tt][v]) * acc1[tt][v];
-                    if (a.act_bf16) {  // bf16 into the first half of the fp32 row r
-                        *reinterpret_cast<uint2 *>(reinterpret_cast<char *>(a.dst) + (size_t)r * a.I * 4 + row * 2) =
-                            make_uint2(bf16_pair_rne(o[0], o[1]), bf16_pair_rne(o[2], o[3]));
-                    } else {
-                        *reinterpret_cast<float4 *>(a.dst + (size_t)r * a.I + row) =
-                            make_float4(o[0], o[1], o[2], o[3]);
-                    }
-                } else {
-                    *reinterpret_cast<float4 *>(a.dst + (size_t)r * a.H + row) =
-                        make_float4(acc0[tt][0], acc0[tt][1], acc0[tt][2], acc0[tt][3]);
-                    *reinterpret_cast<float4 *>(a.dst + (size_t)r * a.H + row + 16) =
-                        make_float4(acc1[tt][0], acc1[tt][1], acc1[tt][2], acc1[tt][3]);
-                }
-            }
+        } else {
+            run(std::integral_constant<int, 4>{});
         }
     }
 }
