@@ -304,14 +304,20 @@ def walk_arms(torch, moe, wl, layers, spec, sizes, steps, warmup, draws, expert_
     return out
 
 
-def stage_roofline(head_run, spec, T, bpw, thr):
+def mfma_experts(c, thr, hot):
+    """Experts of one call's counts c on the matrix cores: those holding thr
+    routes or more (moe_mfma_min_routes), if the largest holds hot or more
+    (moe_mfma_hot_routes); none when thr is 0."""
+    return int((c >= thr).sum()) if thr > 0 and c.max() >= hot else 0
+
+
+def stage_roofline(head_run, spec, T, bpw, thr, hot):
     """Roofline of pass1_kernel (the dominant kernel of the uniform sweep) at
     the headline batch: algorithmic bytes = gate_up bytes of the experts the
-    GEMV kernel streams (those below the library's MFMA threshold thr for the
-    call, moe_mfma_min_routes; every expert when thr is 0), over its
-    event-timed average launch."""
+    GEMV kernel streams (those not on the matrix cores, see mfma_experts),
+    over its event-timed average launch."""
     counts = [head_run["counts"][i] for i in head_run["stage_steps"]]
-    u_gemv = [int((c > 0).sum() - ((c >= thr).sum() if thr > 0 else 0)) for c in counts]
+    u_gemv = [int((c > 0).sum()) - mfma_experts(c, thr, hot) for c in counts]
     p1_ms = head_run["stage_ms"]["pass1_gemv"]
     p1_bytes = float(np.mean(u_gemv)) * 2 * spec.H * spec.I * bpw
     return p1_bytes / (p1_ms * 1e-3) / 1e9, p1_ms, p1_bytes
@@ -531,7 +537,8 @@ def large_rows(torch, moe, wl, dtype, sizes, steps, warmup, draws):
         cs = [run["counts"][i] for i in run["stage_steps"]]
         u_ev = float(np.mean([(c > 0).sum() for c in cs]))
         thr = moe.moe_mfma_min_routes(layer.struct, T, 0)
-        big = [c[c >= thr] for c in cs]
+        hot = moe.moe_mfma_hot_routes(layer.struct, T, 0)
+        big = [c[c >= thr] if c.max() >= hot else c[:0] for c in cs]
         n_big = float(np.mean([len(b) for b in big]))
         routes_big = float(np.mean([b.sum() for b in big]))
         tiles_big = float(np.mean([(np.ceil(b / 16) * 16).sum() for b in big]))
@@ -732,7 +739,8 @@ def main():
                             expert_bytes, graph=not args.no_graph)
     head_run = runs[args.bs]
     p1_gbs, p1_ms, p1_bytes = stage_roofline(head_run, spec, args.bs, bpw,
-                                             moe.moe_mfma_min_routes(layers[0].struct, args.bs, flags))
+                                             moe.moe_mfma_min_routes(layers[0].struct, args.bs, flags),
+                                             moe.moe_mfma_hot_routes(layers[0].struct, args.bs, flags))
 
     # measured HBM bytes per pass-1 launch (headline configuration only, and
     # only for the kernel source the counters were taken on)

@@ -100,8 +100,10 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3 } moe_
  * stays fp32 or bf16.
  *
  * Matrix cores: in a call of 16 or more tokens, an expert that holds
- * moe_mfma_min_routes() routes or more (8 below 128 tokens, 4 from 128) runs
- * both passes as bf16 MFMA products with fp32 accumulation (the activations
+ * moe_mfma_min_routes() routes or more (5 below 128 tokens, 4 from 128) runs,
+ * in moe_layer_fwd and moe_stack_fwd when the call's largest expert holds
+ * moe_mfma_hot_routes() routes or more (8 below 128 tokens), both passes as
+ * bf16 MFMA products with fp32 accumulation (the activations
  * and the decoded weights rounded to bf16; decoded MXFP4 weights are exact in
  * bf16) when the experts are bf16, fp8 or MXFP4 with H and I multiples of
  * 128 (MXFP4 also needs 4-byte aligned scale arrays), unless the flags ask
@@ -138,13 +140,23 @@ size_t moe_workspace_bytes(const moe_layer_t *layer, int32_t max_tokens);
  * the matrix cores (bf16 MFMA: the activations rounded to bf16, fp32
  * accumulation; the GEMV kernels keep fp32 activations), or 0 when no
  * segment of such a call does: weights not bf16 / fp8 / MXFP4 with H and I
- * multiples of 128, T below 16, MOE_NO_MFMA or the per-route walk in flags.
- * Which segments run where decides the rounding of their results, so callers
- * and tests can tell.  Host only (no device work); -1 for an invalid layer,
- * T < 0 or an unknown walk in flags.  The thresholds: 8 routes below 128
- * tokens, 4 from 128 tokens (the workload definition leaves "dense enough"
- * open; these are measured crossovers). */
+ * multiples of 128, T below 16, activation rows of 2 GiB or more,
+ * MOE_NO_MFMA or the per-route walk in flags.  Which segments run where
+ * decides the rounding of their results, so callers and tests can tell.
+ * Host only (no device work); -1 for an invalid layer, T < 0 or an unknown
+ * walk in flags.  The thresholds: 5 routes below 128 tokens, 4 from 128
+ * tokens (the workload definition leaves "dense enough" open; these are
+ * measured crossovers). */
 int32_t moe_mfma_min_routes(const moe_layer_t *layer, int32_t T, uint32_t flags);
+
+/* In moe_layer_fwd and moe_stack_fwd (whose own sort knows the largest
+ * expert), the segments of moe_mfma_min_routes() routes or more take the
+ * MFMA path only if the call's largest expert holds this many routes or
+ * more: 8 below 128 tokens (an MFMA launch with a few small experts costs
+ * more than it saves), moe_mfma_min_routes() from 128; 0 when no segment
+ * does.  moe_expert_fwd, given its routing, applies moe_mfma_min_routes()
+ * alone.  Host only; -1 as for moe_mfma_min_routes. */
+int32_t moe_mfma_hot_routes(const moe_layer_t *layer, int32_t T, uint32_t flags);
 
 /* Zero the synchronisation words at the front of a workspace sized for up to
  * max_tokens tokens (one small fill kernel on `stream`; no memset, so it can

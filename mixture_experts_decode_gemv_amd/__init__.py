@@ -9,7 +9,8 @@ Entry points (same names as ``include/moe.h``): ``moe_workspace_bytes``,
 ``moe_workspace_init``, ``moe_route``, ``moe_sort``, ``moe_expert_fwd``,
 ``moe_layer_fwd``, ``moe_layer_fwd_static``, ``moe_layer_fwd_events``, ``moe_layer_routing``,
 ``moe_expert_usage``, ``moe_stack_workspace_bytes``,
-``moe_stack_workspace_init``, ``moe_stack_fwd``, ``moe_mfma_min_routes``, ``moe_status_str``.  Tensor arguments may be torch
+``moe_stack_workspace_init``, ``moe_stack_fwd``, ``moe_mfma_min_routes``, ``moe_mfma_hot_routes``,
+``moe_status_str``.  Tensor arguments may be torch
 tensors (their ``data_ptr()`` is passed), raw integer device addresses or
 None (NULL).
 """
@@ -32,7 +33,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE",
 
 EXPORTS = ("moe_workspace_bytes", "moe_workspace_init", "moe_route", "moe_sort", "moe_expert_fwd", "moe_layer_fwd",
            "moe_layer_fwd_static", "moe_layer_fwd_events", "moe_layer_routing", "moe_expert_usage", "moe_stack_workspace_bytes",
-           "moe_stack_workspace_init", "moe_stack_fwd", "moe_mfma_min_routes", "moe_status_str")
+           "moe_stack_workspace_init", "moe_stack_fwd", "moe_mfma_min_routes", "moe_mfma_hot_routes",
+           "moe_status_str")
 
 MOE_N_STAGES = 6
 MOE_STATIC_SCRATCH_BYTES = 16 << 20
@@ -68,6 +70,8 @@ def lib():
         L.moe_workspace_bytes.argtypes = [P, i32]
         L.moe_mfma_min_routes.restype = i32
         L.moe_mfma_min_routes.argtypes = [P, i32, u32]
+        L.moe_mfma_hot_routes.restype = i32
+        L.moe_mfma_hot_routes.argtypes = [P, i32, u32]
         L.moe_workspace_init.restype = ctypes.c_int
         L.moe_workspace_init.argtypes = [P, i32, vp, sz, vp]
         L.moe_route.restype = ctypes.c_int
@@ -140,6 +144,12 @@ def moe_mfma_min_routes(layer: moe_layer_t, T: int, flags: int = 0) -> int:
     the matrix cores; 0 when no segment of such a call does, -1 on bad
     arguments."""
     return int(lib().moe_mfma_min_routes(ctypes.byref(layer), int(T), int(flags)))
+
+
+def moe_mfma_hot_routes(layer: moe_layer_t, T: int, flags: int = 0) -> int:
+    """Routes the largest expert of a moe_layer_fwd / moe_stack_fwd call must
+    hold for any segment to take the MFMA path (0: never; -1: invalid)."""
+    return int(lib().moe_mfma_hot_routes(ctypes.byref(layer), int(T), int(flags)))
 
 
 def moe_workspace_init(layer, max_tokens, ws, ws_bytes, stream=None):

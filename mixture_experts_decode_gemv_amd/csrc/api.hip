@@ -128,6 +128,11 @@ int32_t moe_mfma_min_routes(const moe_layer_t *layer, int32_t T, uint32_t flags)
     return mfma_min_routes(*layer, T, flags);
 }
 
+int32_t moe_mfma_hot_routes(const moe_layer_t *layer, int32_t T, uint32_t flags) {
+    if (check_layer(layer) != MOE_OK || T < 0 || (flags & MOE_WALK_MASK) > MOE_WALK_DEDUP_PASS1) return -1;
+    return mfma_hot_routes(*layer, T, flags);
+}
+
 moe_status moe_sort(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int32_t *counts, int32_t *offsets,
                     int32_t *sorted_routes, int32_t *uniq, int32_t *n_uniq, void *stream) {
     if (T < 0 || k < 1 || E < 1 || k > E) return MOE_ERR_ARG;

@@ -354,6 +354,9 @@ bool fused_combine(const moe_layer_t &L, int T);
 // Routes an expert needs in a call of T tokens for its segment to run on the
 // MFMA kernels, or 0 when no segment of such a call does.
 int mfma_min_routes(const moe_layer_t &L, int T, uint32_t flags);
+// The largest segment's routes from which any segment of the call takes the
+// MFMA path (0: never).
+int mfma_hot_routes(const moe_layer_t &L, int T, uint32_t flags);
 // may_fork false: the MFMA segments of large batches stay on st (no side
 // stream is created or used).
 hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xres, int T, const Routing &rt,

@@ -172,6 +172,11 @@ int mfma_min_routes(const moe_layer_t &L, int T, uint32_t flags) {
     return T >= kMfmaWideTokens ? kMfmaMinRoutesWide : kMfmaMinRoutes;
 }
 
+int mfma_hot_routes(const moe_layer_t &L, int T, uint32_t flags) {
+    if (!mfma_eligible(L, T, flags)) return 0;
+    return T >= kMfmaWideTokens ? kMfmaMinRoutesWide : kMfmaHotRoutes;
+}
+
 // Pass 2 and the combine in one launch (pass2c_kernel) for small batches with
 // an output to write: the y block of a workgroup ([R][rows] floats) must fit
 // in 64 KiB of LDS.  The same predicate tells a layer stack whether each
@@ -218,11 +223,18 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
     const int min_n = mfma_min_routes(L, T, flags);  // 0: no MFMA segments
     const bool mfma = min_n > 0;
     const bool mfma2 = mfma && walk == MOE_WALK_DEDUP;
-    SegArgs grouped{rt.ids, rt.counts, rt.offsets, rt.sorted, rt.uniq, rt.n_uniq, 1, R, L.E, INT_MAX};
+    // without the sort's statistics (a caller-supplied routing) every segment
+    // of min_n routes or more takes the MFMA path
+    const int hot = rt.max_count ? mfma_hot_routes(L, T, flags) : min_n;
+    SegArgs grouped{rt.ids, rt.counts, rt.offsets, rt.sorted, rt.uniq, rt.n_uniq, 1, R, L.E, INT_MAX, nullptr, 0};
     SegArgs per_route = grouped;
     per_route.grouped = 0;
     SegArgs split = grouped;  // the GEMV share of a pass that also has MFMA segments
-    if (mfma) split.gemv_below = min_n;
+    if (mfma) {
+        split.gemv_below = min_n;
+        split.max_count = rt.max_count;
+        split.hot = hot;
+    }
 
     // pass 1 on the GEMV kernel: one wave item = P gate/up pairs of one segment
     // xb_first: the GEMV kernel writes the bf16 copy of x in its prologue
@@ -253,7 +265,7 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-        MfmaArgs m1{L.w_gate_up, L.s_gate_up, xb, act, L.H, L.I, L.top_k, min_n, mfma2 ? 1 : 0, grouped,
+        MfmaArgs m1{L.w_gate_up, L.s_gate_up, xb, act, L.H, L.I, L.top_k, min_n, hot, mfma2 ? 1 : 0, grouped,
                     rt.max_count};
         return launch_mfma_pass(L, 1, T, m1, s);
     };
@@ -290,7 +302,7 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
         }
     };
     auto mfma_2 = [&](hipStream_t s) {
-        MfmaArgs m2{L.w_down, L.s_down, act, y, L.H, L.I, L.top_k, min_n, 0, grouped, rt.max_count};
+        MfmaArgs m2{L.w_down, L.s_down, act, y, L.H, L.I, L.top_k, min_n, hot, 0, grouped, rt.max_count};
         return launch_mfma_pass(L, 2, T, m2, s);
     };
     auto combine = [&]() {

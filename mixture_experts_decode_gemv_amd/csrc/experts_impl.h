@@ -25,7 +25,12 @@ struct SegArgs {
     int grouped;  // 1: segment = unique expert, 0: segment = one route
     int R;        // routes
     int E;        // experts (ids outside [0, E) make an empty segment)
-    int gemv_below;  // segments with this many routes or more are left to the MFMA kernels
+    int gemv_below;  // segments with this many routes or more are left to the MFMA kernels,
+    // but only if the largest segment (*max_count, when set) holds at least
+    // hot routes; otherwise every segment stays here.  Kernels resolve this
+    // once, at their start, into gemv_below.
+    const int32_t *max_count;
+    int hot;
 };
 
 // A wave-uniform int32 read through the scalar cache (s_load_dword), waited
@@ -105,7 +110,7 @@ __device__ __forceinline__ int segment_count(const SegArgs &sa) {
 // the MFMA kernels (every unique expert has at least one route here), the
 // expert alone addresses the weights: late is set, n is 1 for now, and the
 // caller reads first and n with segment_rest() once the loads are in flight.
-__device__ __forceinline__ int first_segment(const SegArgs &sa, int s, int &e, int &first, int &n, bool &late) {
+__device__ __forceinline__ int first_segment(SegArgs &sa, int s, int &e, int &first, int &n, bool &late) {
     late = false;
     first = 0;
     n = 0;
@@ -115,10 +120,21 @@ __device__ __forceinline__ int first_segment(const SegArgs &sa, int s, int &e, i
         return sa.R;
     }
     int nu, ev;
-    asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
-                 : "=&s"(nu), "=&s"(ev)
-                 : "s"(sa.n_uniq), "s"(sa.uniq + min(s, sa.E - 1))
-                 : "memory");
+    if (sa.gemv_below != INT_MAX && sa.max_count) {  // the threshold too, in the same round trip
+        int mx;
+        asm volatile(
+            "s_load_dword %0, %3, 0x0\n\ts_load_dword %1, %4, 0x0\n\ts_load_dword %2, %5, 0x0\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&s"(nu), "=&s"(ev), "=&s"(mx)
+            : "s"(sa.n_uniq), "s"(sa.uniq + min(s, sa.E - 1)), "s"(sa.max_count)
+            : "memory");
+        if (mx < sa.hot) sa.gemv_below = INT_MAX;
+    } else {
+        asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&s"(nu), "=&s"(ev)
+                     : "s"(sa.n_uniq), "s"(sa.uniq + min(s, sa.E - 1))
+                     : "memory");
+    }
     const int nseg = nu > 0 ? nu : 0;
     if (s < nseg && ev >= 0 && ev < sa.E) {
         e = ev;
@@ -615,7 +631,7 @@ __global__ __launch_bounds__(pass2c_waves(WDT, NC, G) * kWave) void pass2c_kerne
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int H = a.H, I = a.I, nq = I / EPC;
     const int h0 = blockIdx.x * NR;
-    const SegArgs &sa = a.sa;
+    SegArgs sa = a.sa;
     const int nu = a.reject ? __builtin_nontemporal_load(a.reject) : 0;
     // The experts of a wave's QS segments come in one scalar round trip
     // (with the segment count, for the first ones); the weight loads are
@@ -626,7 +642,14 @@ __global__ __launch_bounds__(pass2c_waves(WDT, NC, G) * kWave) void pass2c_kerne
     const int32_t *elist = sa.grouped ? sa.uniq : sa.ids;
     int s0 = wv * QS, nseg, ev[2];
     if (sa.grouped) {
-        load_uniform3(sa.n_uniq, elist + min(s0, lim), elist + min(s0 + 1, lim), nseg, ev[0], ev[1]);
+        if (sa.gemv_below != INT_MAX && sa.max_count) {  // the threshold too, in the same round trip
+            int mx;
+            load_uniform4(sa.n_uniq, elist + min(s0, lim), elist + min(s0 + 1, lim), sa.max_count, nseg, ev[0],
+                          ev[1], mx);
+            if (mx < sa.hot) sa.gemv_below = INT_MAX;
+        } else {
+            load_uniform3(sa.n_uniq, elist + min(s0, lim), elist + min(s0 + 1, lim), nseg, ev[0], ev[1]);
+        }
         nseg = nseg > 0 ? nseg : 0;
     } else {
         nseg = sa.R;
@@ -842,14 +865,16 @@ hipError_t launch_pass2c(int nc, int lanes, hipStream_t st, const Pass2cArgs &a)
 // Segments with at least kMfmaMinRoutes routes (kMfmaMinRoutesWide from
 // kMfmaWideTokens tokens) run on the matrix cores (see experts_mfma.hip and
 // experts_mfma_wide.hip), in token blocks of kMfmaNarrowTokens (narrow tiles)
-// or kMfmaTokens (wide tiles) routes.  Measured on
-// the large Zipf layer, the skewed sweep and the uniform sweep (graph
-// replays): from 5 routes an expert's GEMV walk is bound by its fp32 FMAs
-// rather than by HBM, so the matrix cores pay from there once batches are
-// large; below 128 tokens, experts of 4 to 7 routes stream slightly faster on
-// the GEMV kernels (uniform bs=16..64 +1..3 % with 4), so there the threshold
-// is 8.
-constexpr int kMfmaMinRoutes = 8;
+// or kMfmaTokens (wide tiles) routes; below kMfmaWideTokens tokens, only
+// when the call's largest segment holds kMfmaHotRoutes or more (decided on
+// the device from the sort's statistics).  Measured on the large Zipf layer,
+// the skewed sweep and the uniform sweep (graph replays): from 5 routes an
+// expert's GEMV walk is bound by its fp32 FMAs rather than by HBM, so the
+// matrix cores pay from there, but below 128 tokens an MFMA launch that
+// holds only a few such experts costs more than it saves (uniform bs=32/64
+// +4/+3 us with the threshold at 5 for every call, skewed bs=16/64 -5/-4 us).
+constexpr int kMfmaMinRoutes = 5;
+constexpr int kMfmaHotRoutes = 8;
 constexpr int kMfmaMinRoutesWide = 4;
 // MFMA launches are made from this many tokens on.
 constexpr int kMfmaMinTokens = 16;
@@ -864,7 +889,8 @@ struct MfmaArgs {
     const void *src;      // bf16 rows: pass 1 x [T, H]; pass 2 a[r] in the first half of fp32 row r of act
     float *dst;           // pass 1: act [R, I]; pass 2: y [R, H]
     int H, I, k;
-    int min_n;            // segments with at least min_n routes
+    int min_n;            // segments with at least min_n routes (if the largest holds hot or more)
+    int hot;
     int act_bf16;         // pass 1: write a[r] as bf16 (for the MFMA pass 2) instead of fp32
     SegArgs sa;           // grouped segments
     const int32_t *max_count;  // if set: largest segment; below min_n the launch has no work

@@ -318,7 +318,7 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
 
     // no expert reaches the threshold (known from the sort's statistics), or
     // the routing was rejected: nothing to do
-    if (a.max_count && load_uniform(a.max_count) < a.min_n) return;
+    if (a.max_count && load_uniform(a.max_count) < a.hot) return;
     if (segment_count(a.sa) == 0) return;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
     const int E = a.sa.E;

@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
 
     // no expert reaches the threshold (known from the sort's statistics):
     // nothing to do, without building the item table
-    if (a.max_count && load_uniform(a.max_count) < a.min_n) return;
+    if (a.max_count && load_uniform(a.max_count) < a.hot) return;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
     const int K = PASS == 1 ? a.H : a.I;
     const int nst = K / kKS;

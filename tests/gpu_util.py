@@ -134,12 +134,13 @@ BF16_OPERAND_TOL = 2e-2  # bar for paths with bf16 operands: max abs error over 
 
 def call_tol(layer: moe.DeviceLayer, x, flags=0, gemv_tol=1e-4):
     """The bar for one moe_layer_fwd call: the bf16-operand bar when some
-    segment of it runs on the matrix cores (an expert of its routing holds
-    moe_mfma_min_routes() routes or more), else the GEMV path's gemv_tol."""
-    thr = moe.moe_mfma_min_routes(layer.struct, x.shape[0], flags)
-    if thr <= 0:
+    segment of it runs on the matrix cores (its largest expert holds
+    moe_mfma_hot_routes() routes or more, which is at least
+    moe_mfma_min_routes()), else the GEMV path's gemv_tol."""
+    hot = moe.moe_mfma_hot_routes(layer.struct, x.shape[0], flags)
+    if hot <= 0:
         return gemv_tol
-    return BF16_OPERAND_TOL if gpu_layer_fwd(layer, x, flags, full=True)["counts"].max() >= thr else gemv_tol
+    return BF16_OPERAND_TOL if gpu_layer_fwd(layer, x, flags, full=True)["counts"].max() >= hot else gemv_tol
 
 
 def oracle_for_gpu_selection(olayer: oracle.Layer, x, oracle_logits, gpu_ids, rmsnorm_in=False, residual=False):

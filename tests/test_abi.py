@@ -197,27 +197,28 @@ def test_static_entry_point_validation():
 
 
 def test_mfma_min_routes():
-    """The matrix-core threshold a call applies (host only): 8 routes below
-    128 tokens, 4 from 128, none below 16 tokens, for fp32 experts, for H or I
-    not a multiple of 128, with MOE_NO_MFMA or the per-route walk, or for
-    activation rows of 2 GiB or more."""
+    """The matrix-core thresholds a call applies (host only): experts of 5
+    routes or more below 128 tokens when the largest holds 8 or more, 4 from
+    128, none below 16 tokens, for fp32 experts, for H or I not a multiple of
+    128, with MOE_NO_MFMA or the per-route walk, or for activation rows of
+    2 GiB or more."""
     L = _layer(H=256, I=128, expert_dtype=moe.MOE_BF16)
-    assert moe.moe_mfma_min_routes(L, 15) == 0
-    assert moe.moe_mfma_min_routes(L, 16) == 8
-    assert moe.moe_mfma_min_routes(L, 127) == 8
-    assert moe.moe_mfma_min_routes(L, 128) == 4
-    assert moe.moe_mfma_min_routes(L, 4096) == 4
-    assert moe.moe_mfma_min_routes(L, 64, moe.MOE_WALK_DEDUP_PASS1) == 8
-    assert moe.moe_mfma_min_routes(L, 64, moe.MOE_NO_MFMA) == 0
+    assert moe.moe_mfma_min_routes(L, 15) == 0 and moe.moe_mfma_hot_routes(L, 15) == 0
+    assert moe.moe_mfma_min_routes(L, 16) == 5 and moe.moe_mfma_hot_routes(L, 16) == 8
+    assert moe.moe_mfma_min_routes(L, 127) == 5 and moe.moe_mfma_hot_routes(L, 127) == 8
+    assert moe.moe_mfma_min_routes(L, 128) == 4 and moe.moe_mfma_hot_routes(L, 128) == 4
+    assert moe.moe_mfma_min_routes(L, 4096) == 4 and moe.moe_mfma_hot_routes(L, 4096) == 4
+    assert moe.moe_mfma_min_routes(L, 64, moe.MOE_WALK_DEDUP_PASS1) == 5
+    assert moe.moe_mfma_min_routes(L, 64, moe.MOE_NO_MFMA) == 0 and moe.moe_mfma_hot_routes(L, 64, moe.MOE_NO_MFMA) == 0
     assert moe.moe_mfma_min_routes(L, 64, moe.MOE_WALK_PER_ROUTE) == 0
     assert moe.moe_mfma_min_routes(_layer(H=256, I=128, expert_dtype=moe.MOE_FP8_E4M3, s_gate_up=0x4000,
-                                          s_down=0x5000), 64) == 8
+                                          s_down=0x5000), 64) == 5
     assert moe.moe_mfma_min_routes(_layer(H=256, I=128), 64) == 0  # fp32 experts
     assert moe.moe_mfma_min_routes(_layer(H=192, I=128, expert_dtype=moe.MOE_BF16), 64) == 0
     # activation rows of 2 GiB or more (R x I x 4 bytes) stay on the GEMV kernels
     Lw = _layer(H=256, I=4096, expert_dtype=moe.MOE_BF16)
     assert moe.moe_mfma_min_routes(Lw, 65535) == 4
-    assert moe.moe_mfma_min_routes(Lw, 65536) == 0
-    assert moe.moe_mfma_min_routes(L, -1) == -1
+    assert moe.moe_mfma_min_routes(Lw, 65536) == 0 and moe.moe_mfma_hot_routes(Lw, 65536) == 0
+    assert moe.moe_mfma_min_routes(L, -1) == -1 and moe.moe_mfma_hot_routes(L, -1) == -1
     assert moe.moe_mfma_min_routes(_layer(top_k=9), 64) == -1
     assert moe.moe_mfma_min_routes(L, 64, 7) == -1  # unknown walk

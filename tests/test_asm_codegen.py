@@ -27,7 +27,9 @@ def test_no_calls_no_scratch(tmp_path, src):
     assert "s_swappc" not in text, "%s: a device function is called instead of inlined" % src
     sizes = [int(v) for v in re.findall(r"\.amdhsa_private_segment_fixed_size\s+(\d+)", text)]
     assert max(sizes, default=0) == 0, "%s: a kernel uses scratch memory" % src
-    assert not re.search(r"^\s*(scratch|buffer)_(load|store)", text, re.M), src
+    # (buffer loads are the wide MFMA kernels' activation reads; spills would
+    # be scratch accesses or buffer stores)
+    assert not re.search(r"^\s*(scratch_(load|store)|buffer_store)", text, re.M), src
 
 
 def _kernel_bodies(text, prefix):

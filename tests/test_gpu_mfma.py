@@ -110,13 +110,13 @@ def test_mfma_deterministic_and_token_permutation(T, spec):
 
 
 @pytest.mark.parametrize("spec", [MIXED, MIXED_FP8], ids=["bf16", "fp8"])
-@pytest.mark.parametrize("cold", [0, 7], ids=["hot-only", "hot-and-cold"])
+@pytest.mark.parametrize("cold", [0, 4], ids=["hot-only", "hot-and-cold"])
 def test_pass2_with_combine_equals_separate_launches(spec, cold):
     """Up to 64 tokens pass 2 runs with the combine in one launch, which reads
     the y rows of the routes on the matrix cores from memory (pass 2 on the
     MFMA kernel runs first); above 64 tokens pass 2 and the combine are
     separate launches.  64 tokens (64 - cold on experts 0 and 1, on MFMA;
-    cold on experts 2 and 3, below the threshold of 8 so on the GEMV kernels)
+    cold on experts 2 and 3, below the threshold of 5 so on the GEMV kernels)
     alone and followed by 8 tokens on experts 4 and 5 give bitwise the same
     rows, and the rows follow the oracle."""
     note("pass 2 with the combine vs separate launches, %s, %d cold tokens" %
@@ -385,3 +385,54 @@ def test_mfma_narrow_many_experts():
     assert g["counts"].max() >= _min_routes(layer, T)
     gemv = gpu_layer_fwd(layer, x, moe.MOE_NO_MFMA)
     assert max_rel(g["out"], gemv) <= BF16_OPERAND_TOL
+
+
+# ---------------------------------------------------------------------------
+# moe_layer_fwd below 128 tokens: experts of moe_mfma_min_routes() routes or
+# more take the MFMA path only when the call's largest expert holds
+# moe_mfma_hot_routes() or more.  The router picks each token's expert
+# exactly: token t is one-hot at column t, and router row e holds 1.0 at the
+# columns of the tokens assigned to e (top_k = 1).
+
+ONE_HOT = wl.LayerSpec(E=8, top_k=1, H=128, I=128, router_dtype=wl.BF16)
+
+
+def _assigned_layer(assign):
+    w = wl.make_layer(ONE_HOT)
+    wr = np.zeros((ONE_HOT.E, ONE_HOT.H), np.uint16)
+    for t, e in enumerate(assign):
+        wr[e, t] = 0x3F80  # bf16 1.0
+    w["w_router"] = wr
+    return w, moe.DeviceLayer(w, device=dev()), oracle.Layer(w)
+
+
+@pytest.mark.parametrize("largest", [6, 10], ids=["below-hot", "hot"])
+def test_layer_mfma_only_with_a_hot_expert(largest):
+    """32 tokens: `largest` on expert 0, 6 on expert 1, the rest at most 4 per
+    expert.  With the largest expert below moe_mfma_hot_routes() every row is
+    the GEMV path's, bitwise; with it at or above, experts 0 and 1 (both at
+    or above moe_mfma_min_routes()) run on the matrix cores and the other
+    rows stay the GEMV path's.  Both within the bar of the oracle."""
+    T = 32
+    L = _assigned_layer([0])[1]
+    thr, hot = moe.moe_mfma_min_routes(L.struct, T), moe.moe_mfma_hot_routes(L.struct, T)
+    assert thr <= 6 < hot <= largest or largest < hot
+    rest = [2 + i % 6 for i in range(T - largest - 6)]
+    assign = [0] * largest + [1] * 6 + rest
+    assert max(np.bincount(rest)) < thr
+    note("layer MFMA rule: largest %d, thr %d, hot %d" % (largest, thr, hot))
+    w, layer, olayer = _assigned_layer(assign)
+    x = np.eye(T, ONE_HOT.H, dtype=np.float32)
+    g = gpu_layer_fwd(layer, x, full=True)
+    assert np.array_equal(g["ids"][:, 0], np.array(assign, np.int32))
+    got = g["out"]
+    gemv = gpu_layer_fwd(layer, x, flags=moe.MOE_NO_MFMA)
+    ref = oracle.moe_layer(olayer, x)["out"]
+    mf = np.array(assign) < 2
+    if largest < hot:
+        assert np.array_equal(got, gemv)
+        assert max_rel(got, ref) <= 1e-4
+    else:
+        assert np.array_equal(got[~mf], gemv[~mf])
+        assert not np.array_equal(got[mf], gemv[mf])
+        assert max_rel(got, ref) <= BF16_OPERAND_TOL
