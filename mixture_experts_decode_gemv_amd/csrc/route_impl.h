@@ -301,12 +301,21 @@ __device__ __forceinline__ int wave_scan_incl(int v) {
 }
 
 constexpr int kSortWaveRounds = 16;
-constexpr int kSortWaveRoutes = kSortWaveRounds * kWave;  // routes sort_wave handles
+constexpr int kSortWaveRoutes = kSortWaveRounds * kWave;  // routes one wave of sort_waves4 handles
+// The sorts' per-lane route arrays and their unrolled rounds are sized at
+// compile time; fewer rounds make a much shorter code path, which the one
+// workgroup that sorts runs once per call (4 rounds instead of 16: -4.4 us
+// per step with 512 and 1024 routes), so short sorts get their own.
+constexpr int kSortShortRounds = 4;
+// Above this many routes four waves sort faster than one (measured with
+// moe_sort back to back: 1024 routes 9.7 -> 7.0 us, 512 routes 6.5 -> 6.2 us).
+constexpr int kSortOneWaveMax = 256;
+constexpr int kOneWaveRounds = kSortOneWaveMax / kWave;
 
 // LDS ints needed by sort_wave for E experts.
 __host__ __device__ constexpr int sort_wave_lds_ints(int E) { return 2 * E; }
 
-// One wave sorts R <= kSortWaveRoutes routes (same outputs as sort_block).
+// One wave sorts R <= kSortOneWaveMax routes (same outputs as sort_block).
 // Route r = 64 j + lane is handled in round j.  Within a round, the lanes
 // holding the same id are found by ballots over the id bits; a route's rank
 // is the number of earlier routes with its id: the running count of that id
@@ -318,10 +327,10 @@ __device__ __forceinline__ void sort_wave(const int32_t *ids, int R, int E, int3
                           int32_t *uniq, int32_t *n_uniq, int32_t *stats, int *lds, int lane) {
     int *s_run = lds, *s_off = lds + E;
     const int nr = (R + kWave - 1) / kWave;
-    int id[kSortWaveRounds], rk[kSortWaveRounds];
+    int id[kOneWaveRounds], rk[kOneWaveRounds];
     bool bad = false;
 #pragma unroll
-    for (int j = 0; j < kSortWaveRounds; ++j) {
+    for (int j = 0; j < kOneWaveRounds; ++j) {
         const int r = j * kWave + lane;
         id[j] = (j < nr && r < R) ? (COHERENT ? load_shared(ids + r) : ids[r]) : -1;
         if (j < nr && r < R && (id[j] < 0 || id[j] >= E)) bad = true;
@@ -337,7 +346,7 @@ __device__ __forceinline__ void sort_wave(const int32_t *ids, int R, int E, int3
     const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
     const unsigned long long below = (1ull << lane) - 1ull;
 #pragma unroll
-    for (int j = 0; j < kSortWaveRounds; ++j) {
+    for (int j = 0; j < kOneWaveRounds; ++j) {
         if (j < nr) {
             const int v = id[j];
             const bool valid = v >= 0;
@@ -382,18 +391,18 @@ __device__ __forceinline__ void sort_wave(const int32_t *ids, int R, int E, int3
         if (stats) { stats[0] = utot; stats[1] = R; stats[2] = mx; stats[3] = 0; }
     }
 #pragma unroll
-    for (int j = 0; j < kSortWaveRounds; ++j)
+    for (int j = 0; j < kOneWaveRounds; ++j)
         if (j < nr && id[j] >= 0) sorted[s_off[id[j]] + rk[j]] = j * kWave + lane;
 }
 
-// Four waves sort R <= 4 * kSortWaveRoutes routes: wave w ranks the routes
+// Four waves sort R <= 4 * ROUNDS * 64 routes: wave w ranks the routes
 // of its contiguous quarter [w Q, w Q + Q) as sort_wave does (ballots over
 // the id bits per round of 64, a per-wave running count per expert in LDS),
 // with no barrier; then one barrier, and each expert's count is the sum of
 // the four per-wave counts, whose exclusive prefix over the waves is added to
 // a route's rank within its wave.  Earlier waves hold earlier routes, so the
 // order is the stable one.  Same outputs as sort_block.  lds: 5 E ints.
-template <bool COHERENT>
+template <int ROUNDS, bool COHERENT>
 __device__ __forceinline__ void sort_waves4(const int32_t *ids, int R, int E, int32_t *counts, int32_t *offsets,
                                             int32_t *sorted, int32_t *uniq, int32_t *n_uniq, int32_t *stats, int *lds,
                                             unsigned *zero, int n_zero) {
@@ -407,10 +416,10 @@ __device__ __forceinline__ void sort_waves4(const int32_t *ids, int R, int E, in
     const int nr = r1 > r0 ? (r1 - r0 + kWave - 1) / kWave : 0;
     if (tid == 0) { s_bad = 0; s_max = 0; }
     for (int i = tid; i < n_zero; i += kBlock) zero[i] = 0u;
-    int id[kSortWaveRounds], rk[kSortWaveRounds];
+    int id[ROUNDS], rk[ROUNDS];
     bool bad = false;
 #pragma unroll
-    for (int j = 0; j < kSortWaveRounds; ++j) {
+    for (int j = 0; j < ROUNDS; ++j) {
         const int r = r0 + j * kWave + lane;
         id[j] = (j < nr && r < r1) ? (COHERENT ? load_shared(ids + r) : ids[r]) : -1;
         if (j < nr && r < r1 && (id[j] < 0 || id[j] >= E)) bad = true;
@@ -423,7 +432,7 @@ __device__ __forceinline__ void sort_waves4(const int32_t *ids, int R, int E, in
         const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
         const unsigned long long below = (1ull << lane) - 1ull;
 #pragma unroll
-        for (int j = 0; j < kSortWaveRounds; ++j) {
+        for (int j = 0; j < ROUNDS; ++j) {
             if (j < nr) {
                 const int v = id[j];
                 const bool valid = v >= 0;
@@ -496,13 +505,11 @@ __device__ __forceinline__ void sort_waves4(const int32_t *ids, int R, int E, in
     }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < kSortWaveRounds; ++j)
+    for (int j = 0; j < ROUNDS; ++j)
         if (j < nr && id[j] >= 0) sorted[s_off[id[j]] + s_runw[id[j]] + rk[j]] = r0 + j * kWave + lane;
 }
 
-// Above this many routes four waves sort faster than one (measured with
-// moe_sort back to back: 1024 routes 9.7 -> 7.0 us, 512 routes 6.5 -> 6.2 us).
-constexpr int kSortOneWaveMax = 256;
+
 
 // LDS ints needed by sort_routes for E experts and R routes (callers reserve
 // sort_lds_ints(E), the largest of the three).
@@ -522,8 +529,14 @@ static_assert(sort_routes_lds_ints(1, kSortOneWaveMax) <= sort_lds_ints(1) &&
 template <bool COHERENT>
 __device__ __forceinline__ void sort_routes(const int32_t *ids, int R, int E, int32_t *counts, int32_t *offsets, int32_t *sorted,
                             int32_t *uniq, int32_t *n_uniq, int32_t *stats, int *lds, unsigned *zero, int n_zero) {
+    if (R > kSortOneWaveMax && R <= (kBlock / kWave) * kSortShortRounds * kWave) {
+        sort_waves4<kSortShortRounds, COHERENT>(ids, R, E, counts, offsets, sorted, uniq, n_uniq, stats, lds, zero,
+                                                n_zero);
+        return;
+    }
     if (R > kSortOneWaveMax && R <= (kBlock / kWave) * kSortWaveRoutes) {
-        sort_waves4<COHERENT>(ids, R, E, counts, offsets, sorted, uniq, n_uniq, stats, lds, zero, n_zero);
+        sort_waves4<kSortWaveRounds, COHERENT>(ids, R, E, counts, offsets, sorted, uniq, n_uniq, stats, lds, zero,
+                                               n_zero);
         return;
     }
     if (R > kSortWaveRoutes) {
