@@ -186,7 +186,7 @@ bool fused_combine(const moe_layer_t &L, int T) {
     const int nq2 = L.I / elems_per_chunk(L.expert_dtype);
     const int lanes = pass2_lanes(nq2, L.expert_dtype);
     const int nr = pass2c_rows(nc_instance((nq2 + lanes - 1) / lanes), lanes);
-    return (size_t)T * L.top_k * nr * 4 <= 64 * 1024;
+    return (size_t)T * L.top_k * (nr * 4 + 1) <= 64 * 1024;
 }
 
 // Small batches have few hot experts: narrow items (32 weight rows) spread

@@ -594,7 +594,9 @@ __global__ __launch_bounds__(kGemvBlock) void pass2_kernel(Pass2Args a) {
 // residual).  So there is no y in memory and no combine launch.  Segments on
 // the matrix cores (gemv_below) are skipped here; pass 2 on the MFMA kernel
 // runs before this launch and writes their y rows to memory (y), from where
-// the combine reads them.
+// the combine reads them.  A byte per route in LDS, set by the wave that
+// computes the route, tells the combine which routes are in LDS, so it reads
+// no routing arrays (two dependent round trips per output).
 constexpr int kPass2cSegs = 1;   // segments per wave with their loads in flight together
 constexpr int kPass2cMaxT = 64;  // batches up to this size take this kernel
 
@@ -621,12 +623,15 @@ struct Pass2cArgs {
 template <int WDT, int NC, int G, int QS>
 __global__ __launch_bounds__(pass2c_waves(WDT, NC, G) * kWave) void pass2c_kernel(Pass2cArgs a) {
     static_assert(QS == 1 || QS == 2, "segments are fetched one or two at a time");
-    extern __shared__ float yl[];  // [R][NR]
+    extern __shared__ float yl[];  // [R][NR], then a byte per route: its y values are in yl
     constexpr int NS = slots_for(NC);
     constexpr int RPS = kWave / G;
     constexpr int NR = NS * RPS;
     constexpr int EPC = WT<WDT>::kEpc;
     constexpr int WPB = pass2c_waves(WDT, NC, G);
+    unsigned char *in_yl = reinterpret_cast<unsigned char *>(yl + a.T * a.k * NR);
+    for (int r = threadIdx.x; r < a.T * a.k; r += WPB * kWave) in_yl[r] = 0;
+    __syncthreads();
     const int lane = threadIdx.x & (kWave - 1), half = lane / G;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int H = a.H, I = a.I, nq = I / EPC;
@@ -713,6 +718,7 @@ __global__ __launch_bounds__(pass2c_waves(WDT, NC, G) * kWave) void pass2c_kerne
                     reduce_slots<NS, 1, G>(v, lane);
                     const int j = reduced_slot<NS, G>(lane);
                     if (slot_leader<NS, G>(lane)) yl[r[i] * NR + j * RPS + half] = v[0][0];
+                    if (lane == 0) in_yl[r[i]] = 1;
                 }
             };
             int m = 0;
@@ -730,7 +736,7 @@ __global__ __launch_bounds__(pass2c_waves(WDT, NC, G) * kWave) void pass2c_kerne
         for (int j = 0; j < k; ++j) {
             const int r = t * k + j;
             // a route of an expert on the matrix cores: its y row is in memory
-            const bool mf = a.y && sa.counts[sa.ids[r]] >= sa.gemv_below;
+            const bool mf = a.y && !in_yl[r];
             acc = fmaf(a.w[r], mf ? a.y[(size_t)r * H + h] : yl[r * NR + i], acc);
         }
         if (a.xres) acc += a.xres[(size_t)t * H + h];
@@ -824,7 +830,7 @@ template <int WDT>
 hipError_t launch_pass2c(int nc, int lanes, hipStream_t st, const Pass2cArgs &a) {
     const int nr = pass2c_rows(nc_instance(nc), lanes);
     const dim3 grid((a.H + nr - 1) / nr);
-    const size_t lds = (size_t)a.T * a.k * nr * 4;
+    const size_t lds = (size_t)a.T * a.k * (nr * 4 + 1);
 #define MOE_P2C(N, L) \
     hipLaunchKernelGGL((pass2c_kernel<WDT, N, L, kPass2cSegs>), grid, dim3(pass2c_waves(WDT, N, L) * kWave), lds, st, a)
     switch (nc_instance(nc) * 100 + lanes) {

@@ -21,7 +21,7 @@
 // activation rows of the token block is copied from memory straight into LDS
 // (global_load_lds_dwordx4: no register staging, so the depth of the
 // pipeline is set by LDS, not by VGPRs), through a ring of as many stages as
-// 72 KiB hold (4 for bf16 weights, 6 for fp8 and MXFP4; two workgroups per
+// 76 KiB hold (4 for bf16 weights, 6 for fp8 and MXFP4; two workgroups per
 // CU), all but one in flight while a stage is computed.  Token blocks hold 32
 // routes, so a stage's activation rows take 8 KiB.  A lane's 16-byte chunk is
 // stored at chunk position (chunk ^ row) of its LDS row: the copies stay
@@ -68,6 +68,7 @@ constexpr int kWaves = kBlock / kWave;
 constexpr int kXRowB = kKS * 2;       // bytes of a staged activation row (bf16)
 constexpr int kXBytes = kTB * kXRowB;  // activations of one stage (8 KiB)
 constexpr int kXcds = 8;
+constexpr int kRedBytes = kWaves * 2 * kTT * kWave * 16;  // partial sums of an item's four waves
 static_assert(kTT <= kWaves, "one token tile per wave in the epilogue");
 
 template <int WDT>
@@ -84,9 +85,11 @@ struct Stage {
     static constexpr int kSBytes = kFp4 ? kWaves * 32 * 4 : 0;  // MXFP4: each wave's 32 scale words
     static constexpr int kLoads = kWLoads + kXLoads + kSLoads;  // copies per wave per stage
     static constexpr int kBytes = kWBytes + kXBytes + kSBytes;
-    // LDS stages of the ring (kRing - 1 in flight), as many as 72 KiB hold
-    // (two workgroups per CU): 4 for bf16, 6 for fp8 and MXFP4
-    static constexpr int kRing = (72 * 1024) / kBytes < 6 ? (72 * 1024) / kBytes : 6;
+    // bytes past the last slot so that it holds the partial sums of an item
+    static constexpr int kPad = kRedBytes > kBytes ? kRedBytes - kBytes : 0;
+    // LDS stages of the ring (kRing - 1 in flight), as many as 76 KiB hold
+    // with the pad (two workgroups per CU): 4 for bf16, 6 for fp8 and MXFP4
+    static constexpr int kRing = (76 * 1024 - kPad) / kBytes < 6 ? (76 * 1024 - kPad) / kBytes : 6;
     static_assert(kWLoads >= 1 && kWLoads * kWLanes * 16 * kWaves == kWBytes, "weight copies cover the stage");
     static_assert(kWLanes % kChunks == 0, "a copy covers whole rows");
 };
@@ -175,17 +178,17 @@ __device__ __forceinline__ void wait_copies_and_sync() {
 }
 
 // wait_copies_and_sync for n (wave-uniform, 0 <= n <= MAXN) stages of P
-// copies each issued after the needed one.
-template <int MAXN, int P>
+// copies each, then X more copies, issued after the needed one.
+template <int MAXN, int P, int X>
 __device__ __forceinline__ void wait_stages(int n) {
     if constexpr (MAXN > 0) {
         if (n == MAXN) {
-            wait_copies_and_sync<MAXN * P>();
+            wait_copies_and_sync<MAXN * P + X>();
             return;
         }
-        wait_stages<MAXN - 1, P>(n);
+        wait_stages<MAXN - 1, P, X>(n);
     } else {
-        wait_copies_and_sync<0>();
+        wait_copies_and_sync<X>();
     }
 }
 
@@ -258,15 +261,15 @@ __device__ int build_tables(const MfmaArgs &a, int n_rb, int *pre, int *off, int
 
 // The end of an item: the four waves' partial sums (acc0, acc1: this wave's
 // k-steps of the two weight tiles, per token tile) go through red (LDS,
-// 2 x kWaves x kTT x 64 x 16 bytes, free on entry) and are added in wave
-// order w = 0, 1, 2, 3; wave tt then writes token tile tt: pass 1 a[r, i] =
+// 2 x kWaves x kTT x 64 x 16 bytes) and are added in wave order
+// w = 0, 1, 2, 3; wave tt then writes token tile tt: pass 1 a[r, i] =
 // silu(gate) * up (fp32, or bf16 into the first half of the fp32 row for the
 // MFMA pass 2), pass 2 the y rows.  A lane (m, g) holds rows 4g .. 4g+3 of
-// both tiles for token m of its tile.
+// both tiles for token m of its tile; r is that token's route.
 template <int PASS>
 __device__ __forceinline__ void mfma_epilogue(const MfmaArgs &a, f32x4_t *red, const f32x4_t (&acc0)[kTT],
-                                              const f32x4_t (&acc1)[kTT], int ntt, int nv, const int32_t *routes,
-                                              int r0, int wv, int lane) {
+                                              const f32x4_t (&acc1)[kTT], int ntt, int nv, int r, int r0, int wv,
+                                              int lane) {
     const int m = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt) {
@@ -286,7 +289,6 @@ __device__ __forceinline__ void mfma_epilogue(const MfmaArgs &a, f32x4_t *red, c
             s0 += red[((w * 2 + 0) * kTT + tt) * kWave + lane];
             s1 += red[((w * 2 + 1) * kTT + tt) * kWave + lane];
         }
-        const int r = routes[tok];
         const int row = r0 + 4 * g;
         if (PASS == 1) {
             float o[4];
@@ -305,16 +307,26 @@ __device__ __forceinline__ void mfma_epilogue(const MfmaArgs &a, f32x4_t *red, c
     }
 }
 
+// Items follow each other without a gap in the copy stream.  During the last
+// stages of an item, once its final copies are issued, each wave copies the
+// next item's route ids into its own LDS row (one 4-byte copy per lane, which
+// the stage waits count) and loads the next fp8 scales; after the item's
+// last stage, the next item's first kRing - 1 stages are issued into ring
+// slots 0 .. kRing - 2, and only then are the item's partial sums reduced,
+// in slot kRing - 1 (extended by kPad bytes where a stage is smaller than
+// the reduction).  So the route-id round trip and the ring's fill latency of
+// an item overlap the previous item's last stages and epilogue.
 template <int WDT, int PASS>
 __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
     using S = Stage<WDT>;
     constexpr bool kFp8 = S::kFp8, kFp4 = S::kFp4;
     constexpr int kRing = S::kRing;
-    static_assert(kRing >= 3 && (kRing - 2) * S::kLoads <= 63, "ring depth");
-    __shared__ __align__(1024) unsigned char ring[kRing * S::kBytes];
+    static_assert(kRing >= 3 && (kRing - 2) * S::kLoads + 1 <= 63, "ring depth");
+    __shared__ __align__(1024) unsigned char ring[kRing * S::kBytes + S::kPad];
+    __shared__ int ids[kWaves][kWave];  // each wave's copy of an item's route ids
     __shared__ int wsum[2 * kWaves];
     extern __shared__ int tables[];  // pre [E + 1], off [E + 1]
-    static_assert(kWaves * 2 * kTT * kWave * 16 <= kRing * S::kBytes, "partial sums fit in the ring");
+    static_assert(S::kBytes + S::kPad >= kRedBytes, "partial sums fit in the last slot");
 
     // no expert reaches the threshold (known from the sort's statistics), or
     // the routing was rejected: nothing to do
@@ -331,11 +343,13 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
     // bf16 activation rows: pass 1 reads xb [T, H]; pass 2 reads a[r] from the
     // first half of the fp32 activation row r (4I bytes apart)
     const unsigned src_stride = PASS == 1 ? (unsigned)a.H * 2 : (unsigned)a.I * 4;
-    const int total = build_tables(a, n_rb, pre, off, wsum);
-    // contiguous item ranges per XCD (the grid is a multiple of kXcds)
+    const int total = __builtin_amdgcn_readfirstlane(build_tables(a, n_rb, pre, off, wsum));
+    // contiguous item ranges per XCD (the grid is a multiple of kXcds, so a
+    // workgroup's items ascend and stay inside its XCD's range)
     const int per_xcd = (total + kXcds - 1) / kXcds;
     const int slots = per_xcd * kXcds;
     const int m = lane & 15, g = lane >> 4;
+    auto item_of = [&](int it) { return (it % kXcds) * per_xcd + it / kXcds; };
 
     // item -> (expert, row block, token block)
     struct Item {
@@ -359,133 +373,173 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
         d.nv = min(kTB, n - d.tb * kTB);
         return d;
     };
-    // route ids of this lane's activation copies: copy j covers tokens 4
-    // apart; rows past the block's routes load the first route's row (their
-    // LDS rows only feed outputs that are never stored)
-    auto route_ids = [&](int nv, const int32_t *routes, int(&r)[S::kXLoads]) {
-#pragma unroll
-        for (int j = 0; j < S::kXLoads; ++j) {
-            const int tau = (wv * S::kXLoads + j) * 4 + (lane >> 4);
-            r[j] = routes[tau < nv ? tau : 0];
+    // the item's route ids into this wave's row of ids: lane l copies route
+    // l & 31 of the token block; positions past its routes take the first
+    // route (their LDS rows only feed outputs that are never stored)
+    const char *sorted = uniform_ptr(reinterpret_cast<const char *>(a.sa.sorted));
+    const unsigned char *idrow = reinterpret_cast<const unsigned char *>(&ids[wv][0]);
+    auto copy_ids = [&](const Item &d) {
+        const int tau = lane & (kTB - 1);
+        copy_word_to_lds(sorted, (unsigned)(d.first + d.tb * kTB + (tau < d.nv ? tau : 0)) * 4u, idrow);
+    };
+    // fp8 block scales of the item's two tiles, stage ks in lane ks (K <= 64 *
+    // 128; lanes past the stages repeat the last).  Nothing else writes s0
+    // and s1 here: a register write while an earlier load into the same
+    // register may be in flight would make the compiler wait for every load.
+    auto load_scales = [&](const Item &d, float &s0, float &s1) {
+        if (kFp8) {
+            const int kb = K / 128;
+            const int q0 = PASS == 1 ? d.rb * 16 : d.rb * 32;
+            const int q1 = PASS == 1 ? a.I + q0 : q0 + 16;
+            const float *sp0 = static_cast<const float *>(a.scales) + ((size_t)d.e * (w_rows / 128) + q0 / 128) * kb;
+            const float *sp1 = static_cast<const float *>(a.scales) + ((size_t)d.e * (w_rows / 128) + q1 / 128) * kb;
+            const int l = lane < kb ? lane : kb - 1;
+            s0 = sp0[l];
+            s1 = sp1[l];
         }
     };
-    for (int it = blockIdx.x; it < slots; it += gridDim.x) {
-        const int item = (it % kXcds) * per_xcd + it / kXcds;
-        if (item >= total) continue;  // uniform over the workgroup
-        const Item d = decode(item);
-        const int e = d.e, rb = d.rb, nv = d.nv;
-        const int ntt = (nv + 15) >> 4;
-        const int32_t *routes = a.sa.sorted + d.first + d.tb * kTB;
 
-        lds_barrier();  // the previous item is done with the ring
-
+    // per-item state: the item, its copy offsets and its fp8 scales
+    struct St {
+        Item d;
+        int ntt, r0, r_out;
+        bool xw;
+        const char *wbase;
+        const unsigned char *sbase;
+        unsigned soff;
+        unsigned woff[S::kWLoads];
+        unsigned xoff[S::kXLoads];
+        float sc0, sc1;
+    };
+    const int sk = K / 32;  // MXFP4 scale bytes per weight row
+    const char *xbase = uniform_ptr(static_cast<const char *>(a.src));
+    // the state of item d once its id copy (and scale loads) are complete
+    auto setup = [&](const Item &d, float s0, float s1) {
+        St c;
+        c.d = d;
+        c.ntt = (d.nv + 15) >> 4;
+        c.sc0 = s0;
+        c.sc1 = s1;
+        int rn[S::kXLoads];
+#pragma unroll
+        for (int j = 0; j < S::kXLoads; ++j) rn[j] = ids[wv][(wv * S::kXLoads + j) * 4 + (lane >> 4)];
+        c.r_out = ids[wv][wv * 16 + m];  // this lane's route in the epilogue (waves < kTT)
+        // the reads are done before a later copy rewrites the row
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         // weight rows of the item: row rho < 16 of tile 0, rho >= 16 of tile 1.
         // This lane's weight copy c covers rows (kWLanes / kChunks) apart; its
         // chunk is the one that lands at its LDS position (position ^ row).
-        const int r0 = PASS == 1 ? rb * 16 : rb * 32;
-        const int r1 = PASS == 1 ? a.I + r0 : r0 + 16;
-        const char *wbase = uniform_ptr(static_cast<const char *>(a.w) + (size_t)e * w_rows * row_bytes);
-        unsigned woff[S::kWLoads];
+        c.r0 = PASS == 1 ? d.rb * 16 : d.rb * 32;
+        const int r1 = PASS == 1 ? a.I + c.r0 : c.r0 + 16;
+        c.wbase = uniform_ptr(static_cast<const char *>(a.w) + (size_t)d.e * w_rows * row_bytes);
 #pragma unroll
-        for (int c = 0; c < S::kWLoads; ++c) {
-            const int rho = (wv * S::kWLoads + c) * (S::kWLanes / S::kChunks) + (lane % S::kWLanes) / S::kChunks;
+        for (int q = 0; q < S::kWLoads; ++q) {
+            const int rho = (wv * S::kWLoads + q) * (S::kWLanes / S::kChunks) + (lane % S::kWLanes) / S::kChunks;
             const int pos = lane % S::kChunks;
             const int chunk = pos ^ (rho & (S::kChunks - 1));
-            woff[c] = (unsigned)(rho < 16 ? r0 + rho : r1 + rho - 16) * row_bytes + chunk * 16;
+            c.woff[q] = (unsigned)(rho < 16 ? c.r0 + rho : r1 + rho - 16) * row_bytes + chunk * 16;
         }
-        auto issue_w = [&](int ks, int sl) {
-            const unsigned char *wd = ring + sl * S::kBytes;
-            if (S::kWLanes == kWave || lane < S::kWLanes)
-#pragma unroll
-                for (int c = 0; c < S::kWLoads; ++c)
-                    copy_to_lds(wbase + (size_t)ks * S::kRowB, woff[c], wd + (wv * S::kWLoads + c) * S::kWLanes * 16);
-        };
         // MXFP4 scale words: lane l < 32 copies the stage's word of row l
-        const int sk = K / 32;  // scale bytes per weight row
-        const unsigned char *sbase = nullptr;
-        unsigned soff = 0;
+        c.sbase = nullptr;
+        c.soff = 0;
         if (kFp4) {
-            sbase = uniform_ptr(static_cast<const unsigned char *>(a.scales) + (size_t)e * w_rows * sk);
-            soff = (unsigned)((lane < 16 ? r0 + lane : r1 + (lane & 31) - 16) * sk);
+            c.sbase = uniform_ptr(static_cast<const unsigned char *>(a.scales) + (size_t)d.e * w_rows * sk);
+            c.soff = (unsigned)((lane < 16 ? c.r0 + lane : r1 + (lane & 31) - 16) * sk);
         }
-        auto issue_s = [&](int ks, int sl) {
-            if (kFp4 && lane < 32)
-                copy_word_to_lds(sbase + (size_t)ks * 4, soff, ring + sl * S::kBytes + S::kWBytes + kXBytes + wv * 128);
-        };
-
         // activation copies: only the waves whose token tile holds routes copy
-        const bool xw = wv * kTB / (16 * kWaves) < ntt;
-        const char *xbase = uniform_ptr(static_cast<const char *>(a.src));
-
-        // fp8 block scales of the two tiles, stage ks in lane ks (K <= 64 *
-        // 128), loaded before the route ids and complete once those are
-        float sc0 = 1.f, sc1 = 1.f;
-        if (kFp8) {
-            const int kb = K / 128;
-            const float *sp0 = static_cast<const float *>(a.scales) + ((size_t)e * (w_rows / 128) + r0 / 128) * kb;
-            const float *sp1 = static_cast<const float *>(a.scales) + ((size_t)e * (w_rows / 128) + r1 / 128) * kb;
-            if (lane < kb) {
-                sc0 = sp0[lane];
-                sc1 = sp1[lane];
-            }
-        }
-        // route ids of this lane's activation copies
-        int rn[S::kXLoads];
-        route_ids(nv, routes, rn);
-        unsigned xoff[S::kXLoads];
+        c.xw = wv * kTB / (16 * kWaves) < c.ntt;
 #pragma unroll
         for (int j = 0; j < S::kXLoads; ++j) {
             const int tau = (wv * S::kXLoads + j) * 4 + (lane >> 4);
             const int chunk = (lane & 15) ^ (tau & 15);
-            xoff[j] = (unsigned)(PASS == 1 ? rn[j] / a.k : rn[j]) * src_stride + chunk * 16;
+            c.xoff[j] = (unsigned)(PASS == 1 ? rn[j] / a.k : rn[j]) * src_stride + chunk * 16;
         }
-        // The scale loads are complete here (the route ids were loaded after
-        // them); redefining the values in an asm statement tells the compiler
-        // so.  Otherwise it waits for them (vmcnt) at their first use inside
-        // the stage loop, and its count, which does not know the copies,
-        // would drain the ring at every stage.
-        if (kFp8) asm volatile("s_waitcnt vmcnt(0)" : "+v"(sc0), "+v"(sc1));
+        return c;
+    };
+    // stage ks of item c into ring slot sl
+    auto issue = [&](const St &c, int ks, int sl) {
+        const unsigned char *wd = ring + sl * S::kBytes;
+        if (S::kWLanes == kWave || lane < S::kWLanes)
+#pragma unroll
+            for (int q = 0; q < S::kWLoads; ++q)
+                copy_to_lds(uniform_ptr(c.wbase) + (size_t)ks * S::kRowB, c.woff[q],
+                            wd + (wv * S::kWLoads + q) * S::kWLanes * 16);
+        if (c.xw)
+#pragma unroll
+            for (int j = 0; j < S::kXLoads; ++j)
+                copy_to_lds(xbase + (size_t)ks * kXRowB, c.xoff[j], wd + S::kWBytes + (wv * S::kXLoads + j) * 1024);
+        if (kFp4 && lane < 32)
+            copy_word_to_lds(uniform_ptr(c.sbase) + (size_t)ks * 4, c.soff, wd + S::kWBytes + kXBytes + wv * 128);
+    };
+    // stages 0 .. kRing - 2 of item c in flight, in slots 0 .. kRing - 2
+    auto prologue = [&](const St &c) {
+#pragma unroll
+        for (int s = 0; s + 1 < kRing; ++s)
+            if (s < nst) issue(c, s, s);
+    };
 
-        auto issue_x = [&](int ks, int sl) {
-            const unsigned char *xd = ring + sl * S::kBytes + S::kWBytes;
-            if (xw)
-#pragma unroll
-                for (int j = 0; j < S::kXLoads; ++j)
-                    copy_to_lds(xbase + (size_t)ks * kXRowB, xoff[j], xd + (wv * S::kXLoads + j) * 1024);
-        };
-        // stages 0 .. kRing - 2 in flight.  (Copying the weights ahead of the
-        // route reads would gain nothing: loads complete in issue order, so
-        // the wait for the route ids would wait for those copies as well.)
-#pragma unroll
-        for (int s = 0; s + 1 < kRing; ++s) {
-            if (s < nst) {
-                issue_w(s, s);
-                issue_x(s, s);
-                issue_s(s, s);
+    int it = blockIdx.x;
+    if (it >= slots || item_of(it) >= total) return;  // uniform over the workgroup
+    St cur;
+    {
+        const Item d = decode(item_of(it));
+        float s0 = 1.f, s1 = 1.f;
+        load_scales(d, s0, s1);
+        copy_ids(d);
+        // Redefining the values in an asm statement tells the compiler that
+        // the loads are complete; it would otherwise wait for them (vmcnt) at
+        // their first use inside the stage loop, and its count, which does
+        // not know the copies, would drain the ring there.
+        asm volatile("s_waitcnt vmcnt(0)" : "+v"(s0), "+v"(s1)::"memory");
+        cur = setup(d, s0, s1);
+    }
+    prologue(cur);
+
+    // k-step wv of stage ks from slot sl: A lane (m, g) holds row m of a
+    // tile at k 32 wv + 8 g .. +7, B lane (m, g) token m of a token tile.
+    // Every operand of the stage is read before the copies of a later stage
+    // are issued and before the first MFMA, so the LDS latency is paid once
+    // per stage; tiles past ntt read rows that feed no output.
+    const int aoff = kFp4   ? ((wv ^ (m & 3)) << 4) + (g << 2)
+                     : kFp8 ? (((2 * wv + (g >> 1)) ^ (m & 7)) << 4) + ((g & 1) << 3)
+                            : ((4 * wv + g) ^ m) << 4;
+    const int boff = m * kXRowB + (((4 * wv + g) ^ m) << 4);
+    // the next item's fp8 scales, written only by their loads inside the
+    // loop (see load_scales)
+    float n0 = 1.f, n1 = 1.f;
+    for (;;) {
+        // the next item of this workgroup, if any: its id copy (and scale
+        // loads) are issued once this item's last copies are
+        const int nit = it + (int)gridDim.x;
+        const bool more = nit < slots && item_of(nit) < total;
+        Item dn = cur.d;
+        bool pf = false;  // issued, and counted by the stage waits
+        auto prefetch = [&]() {
+            if (more) {
+                dn = decode(item_of(nit));
+                load_scales(dn, n0, n1);
+                copy_ids(dn);
+                pf = true;
             }
-        }
+        };
+        if (nst <= kRing - 1) prefetch();
 
-
+        const int ntt = cur.ntt;
         f32x4_t acc0[kTT], acc1[kTT];
 #pragma unroll
         for (int tt = 0; tt < kTT; ++tt) acc0[tt] = acc1[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-        // k-step wv of stage ks from slot sl: A lane (m, g) holds row m of a
-        // tile at k 32 wv + 8 g .. +7, B lane (m, g) token m of a token tile.
-        // Every operand of the stage is read before the copies of a later
-        // stage are issued and before the first MFMA, so the LDS latency is
-        // paid once per stage; tiles past ntt read rows that feed no output.
-        const int aoff = kFp4   ? ((wv ^ (m & 3)) << 4) + (g << 2)
-                         : kFp8 ? (((2 * wv + (g >> 1)) ^ (m & 7)) << 4) + ((g & 1) << 3)
-                                : ((4 * wv + g) ^ m) << 4;
-        const int boff = m * kXRowB + (((4 * wv + g) ^ m) << 4);
         int sl = 0;
         for (int ks = 0; ks < nst; ++ks) {
             // copies issued after the stage that is needed: those of stages
-            // ks + 1 .. ks + after
+            // ks + 1 .. ks + after, then the next item's id copy
             const int after = min(kRing - 2, nst - 1 - ks);
-            if (xw) wait_stages<kRing - 2, S::kLoads>(after);
-            else wait_stages<kRing - 2, S::kWLoads + S::kSLoads>(after);
+            if (pf) {
+                if (cur.xw) wait_stages<kRing - 2, S::kLoads, 1>(after);
+                else wait_stages<kRing - 2, S::kWLoads + S::kSLoads, 1>(after);
+            } else {
+                if (cur.xw) wait_stages<kRing - 2, S::kLoads, 0>(after);
+                else wait_stages<kRing - 2, S::kWLoads + S::kSLoads, 0>(after);
+            }
 
             const unsigned char *wd = ring + sl * S::kBytes;
             const unsigned char *xd = wd + S::kWBytes;
@@ -509,18 +563,18 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
             for (int tt = 0; tt < kTT; ++tt) b[tt] = *reinterpret_cast<const u32x4 *>(xd + tt * 16 * kXRowB + boff);
 
             if (ks + kRing - 1 < nst) {
-                const int ns = sl == 0 ? kRing - 1 : sl - 1;
-                issue_w(ks + kRing - 1, ns);
-                issue_x(ks + kRing - 1, ns);
-                issue_s(ks + kRing - 1, ns);
+                issue(cur, ks + kRing - 1, sl == 0 ? kRing - 1 : sl - 1);
+                if (ks + kRing == nst) prefetch();  // the item's last copies are issued
             }
             if (kFp4) {
                 a0 = e2m1x8_to_bf16(f0, e8m0_value(e0));
                 a1 = e2m1x8_to_bf16(f1, e8m0_value(e1));
             }
             if (kFp8) {
-                a0 = e4m3x8_to_bf16(c0.x, c0.y, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc0), ks)));
-                a1 = e4m3x8_to_bf16(c1.x, c1.y, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc1), ks)));
+                a0 = e4m3x8_to_bf16(c0.x, c0.y,
+                                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cur.sc0), ks)));
+                a1 = e4m3x8_to_bf16(c1.x, c1.y,
+                                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cur.sc1), ks)));
             }
 #pragma unroll
             for (int tt = 0; tt < kTT; ++tt) {
@@ -532,9 +586,21 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
             sl = sl == kRing - 1 ? 0 : sl + 1;
         }
 
-        // partial sums of the four waves, added in wave order
         lds_barrier();  // every wave is done reading the ring
-        mfma_epilogue<PASS>(a, reinterpret_cast<f32x4_t *>(ring), acc0, acc1, ntt, nv, routes, r0, wv, lane);
+        St nxt = cur;
+        if (more) {
+            // the next item's first stages go out before this item's partial
+            // sums are added: slots 0 .. kRing - 2, slot kRing - 1 is left
+            // for the sums
+            asm volatile("s_waitcnt vmcnt(0)" : "+v"(n0), "+v"(n1)::"memory");
+            nxt = setup(dn, n0, n1);
+            prologue(nxt);
+        }
+        mfma_epilogue<PASS>(a, reinterpret_cast<f32x4_t *>(ring + (kRing - 1) * S::kBytes), acc0, acc1, ntt,
+                            cur.d.nv, cur.r_out, cur.r0, wv, lane);
+        if (!more) break;
+        it = nit;
+        cur = nxt;
     }
 }
 

@@ -33,21 +33,35 @@ def test_no_calls_no_scratch(tmp_path, src):
 
 
 def _kernel_bodies(text, prefix):
-    """{kernel name: its instruction lines} for the kernels whose names start with prefix."""
+    """{kernel name: its instruction lines} for the kernels whose names start with prefix;
+    inline-asm blocks keep their #ASMSTART / #ASMEND markers."""
     out = {}
     for m in re.finditer(r"^(%s\w*):" % re.escape(prefix), text, re.M):
         end = text.index(".Lfunc_end", m.end())
-        lines = [l.split(";")[0].strip() for l in text[m.end():end].split("\n")]
-        out[m.group(1)] = [l for l in lines if l and not l.startswith(".")]
+        lines = []
+        for l in text[m.end():end].split("\n"):
+            l = l.strip()
+            if l.startswith(";;#ASMSTART") or l.startswith(";;#ASMEND"):
+                lines.append(l[2:])
+                continue
+            l = l.split(";")[0].strip()
+            if l and not l.startswith("."):
+                lines.append(l)
+        out[m.group(1)] = lines
     return out
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
 def test_narrow_mfma_ring_is_not_drained(tmp_path):
     """The narrow MFMA kernels wait for their LDS copies only through their
-    own counted waits (s_waitcnt vmcnt(N) then s_barrier).  A compiler wait on
-    a vector load (e.g. the fp8 block scales) placed inside the stage loop
-    would count without the copies and so drain the ring at every stage."""
+    own waits: the counted stage waits (s_waitcnt vmcnt(N) then s_barrier, in
+    one asm block) and, once per item, an asm s_waitcnt vmcnt(0) for the
+    item's route-id copy and fp8 scales, placed where all the previous item's
+    copies have completed (one for the first item, one for each next item).
+    A compiler wait on a vector load (e.g. the fp8 block scales) inside the
+    stage loop would count without the copies and so drain the ring there; a
+    compiler wait is allowed only right before an item wait, with no load or
+    MFMA between them."""
     out = tmp_path / "experts_mfma.s"
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
            "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S",
@@ -56,8 +70,30 @@ def test_narrow_mfma_ring_is_not_drained(tmp_path):
     bodies = _kernel_bodies(out.read_text(), "_ZN3moe11mfma_kernel")
     assert len(bodies) == 6, sorted(bodies)
     for name, lines in bodies.items():
+        in_asm, block = [], None
+        for l in lines:
+            if l == "#ASMSTART":
+                block = []
+            elif l == "#ASMEND":
+                block = None
+            elif block is not None:
+                block.append(l)
+            in_asm.append(block is not None and l not in ("#ASMSTART", "#ASMEND"))
+        item_waits = [i for i, l in enumerate(lines)
+                      if l == "s_waitcnt vmcnt(0)" and in_asm[i] and lines[i - 1] == "#ASMSTART"
+                      and lines[i + 1] == "#ASMEND"]
+        assert len(item_waits) == 2, "%s: item waits at %s" % (name, item_waits)
         first = next(i for i, l in enumerate(lines) if l.startswith("global_load_lds"))
         last = max(i for i, l in enumerate(lines) if l.startswith("v_mfma"))
         for i in range(first, last):
-            if lines[i].startswith("s_waitcnt") and "vmcnt" in lines[i]:
-                assert lines[i + 1] == "s_barrier", "%s: %s inside the stage loop" % (name, lines[i])
+            l = lines[i]
+            if not (l.startswith("s_waitcnt") and "vmcnt" in l) or i in item_waits:
+                continue
+            if in_asm[i]:
+                assert lines[i + 1] == "s_barrier", "%s: %s inside the stage loop" % (name, l)
+                continue
+            nxt = next((j for j in item_waits if j > i), None)
+            assert nxt is not None and nxt - i <= 12, "%s: compiler wait %s at %d" % (name, l, i)
+            between = lines[i + 1:nxt]
+            assert not any(b.startswith(("global_load", "buffer_load", "v_mfma")) for b in between), \
+                "%s: compiler wait %s at %d" % (name, l, i)
