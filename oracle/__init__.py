@@ -59,6 +59,8 @@ def lib():
         L.oracle_e2m1_value.argtypes = [ctypes.c_uint8]
         L.oracle_e8m0_value.restype = dbl
         L.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
+        L.oracle_f16_value.restype = dbl
+        L.oracle_f16_value.argtypes = [ctypes.c_uint16]
         L.oracle_rmsnorm.restype = None
         L.oracle_rmsnorm.argtypes = [i32, i32, vp, dbl, vp]
         L.oracle_router_logits.restype = None
@@ -95,9 +97,9 @@ class Layer:
     """Weights of one layer, as host arrays, bound into the C struct.
 
     ``w`` holds ``w_router``, ``w_gate_up``, ``w_down`` (fp32 arrays, bf16 as
-    uint16 bit patterns, E4M3 codes as uint8, or MXFP4 codes packed two per
-    byte) and ``s_gate_up``/``s_down`` (fp8 block scales, or MXFP4 E8M0 scale
-    bytes) plus ``spec`` (E, top_k, H, I, expert_dtype, router_dtype).
+    uint16 bit patterns, E4M3 codes as uint8, or MXFP4 / q4_0 codes packed
+    two per byte) and ``s_gate_up``/``s_down`` (fp8 block scales, MXFP4 E8M0
+    scale bytes, or q4_0 binary16 scales as uint16 bit patterns) plus ``spec`` (E, top_k, H, I, expert_dtype, router_dtype).
     """
 
     def __init__(self, w: dict, router_bias=None):
@@ -134,6 +136,10 @@ def e2m1_value(c: int) -> float:
 
 def e8m0_value(s: int) -> float:
     return lib().oracle_e8m0_value(int(s))
+
+
+def f16_value(h: int) -> float:
+    return lib().oracle_f16_value(int(h))
 
 
 def rmsnorm(x, eps=RMS_EPS):

@@ -12,7 +12,11 @@
  * fields times the fp32 scale of its 128x128 block, and MXFP4 (OCP
  * microscaling: E2M1 elements, two per byte with the first in the low
  * nibble, sharing an E8M0 scale per block of 32 along a row) from its bit
- * fields times 2^(scale - 127).
+ * fields times 2^(scale - 127), and q4_0 (blocks of 32 elements along a row
+ * with one IEEE binary16 scale d; element j of a block is the 4-bit code in
+ * the low nibble of the block's byte j, element j + 16 the code in its high
+ * nibble; the value is (code - 8) * d) from its codes and the binary16 bit
+ * fields of d.
  *
  * Sources (page title, section):
  *  - "MoE Performance Optimization Analysis" (markbaseengine), Root Cause:
@@ -41,7 +45,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8 = 2, OR_MXFP4 = 3 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8 = 2, OR_MXFP4 = 3, OR_Q4_0 = 4 };
 enum { OR_RMSNORM = 1, OR_RESIDUAL = 2 };
 
 typedef struct {
@@ -50,8 +54,8 @@ typedef struct {
     const void *w_router;     /* [E, H]                          */
     const void *w_gate_up;    /* [E, 2I, H]                      */
     const void *w_down;       /* [E, H, I]                       */
-    const void *s_gate_up;    /* fp8: float [E, 2I/128, H/128]; mxfp4: uint8 [E, 2I, H/32] */
-    const void *s_down;       /* fp8: float [E, H/128, I/128];  mxfp4: uint8 [E, H, I/32]  */
+    const void *s_gate_up;    /* fp8: float [E, 2I/128, H/128]; mxfp4: uint8, q4_0: binary16 [E, 2I, H/32] */
+    const void *s_down;       /* fp8: float [E, H/128, I/128];  mxfp4: uint8, q4_0: binary16 [E, H, I/32]  */
     const float *router_bias; /* [E] or NULL                     */
 } oracle_layer;
 
@@ -84,12 +88,32 @@ double oracle_e2m1_value(uint8_t c) {
 /* OCP E8M0 (MX shared scale): 2^(s - 127); 255 is NaN. */
 double oracle_e8m0_value(uint8_t s) { return s == 255 ? NAN : ldexp(1.0, (int)s - 127); }
 
+/* IEEE 754 binary16: sign, 5 exponent bits (bias 15), 10 fraction bits;
+ * exponent 0 is subnormal (f * 2^-24), exponent 31 is infinity (f = 0) or
+ * NaN. */
+double oracle_f16_value(uint16_t h) {
+    int s = h >> 15, e = (h >> 10) & 0x1F, f = h & 0x3FF;
+    double mag;
+    if (e == 0x1F) mag = f ? NAN : INFINITY;
+    else if (e == 0) mag = ldexp((double)f, -24);
+    else mag = ldexp(1.0 + (double)f / 1024.0, e - 15);
+    return s ? -mag : mag;
+}
+
 /* Element idx of a row-major matrix (idx = row * cols + col).  MXFP4: the
  * code is nibble (idx & 1) of byte idx / 2, its scale byte idx / 32 (cols is
  * a multiple of 32, so the blocks of 32 never cross a row). */
 static double decode(int dtype, const void *base, const void *scales, size_t idx) {
     if (dtype == OR_F32) return (double)((const float *)base)[idx];
     if (dtype == OR_BF16) return oracle_bf16_value(((const uint16_t *)base)[idx]);
+    if (dtype == OR_Q4_0) {
+        /* block idx / 32 is 16 code bytes; element j < 16 in the low nibble of
+         * byte j, element j >= 16 in the high nibble of byte j - 16 */
+        const size_t blk = idx / 32, j = idx % 32;
+        const uint8_t b = ((const uint8_t *)base)[blk * 16 + (j & 15)];
+        const int code = j < 16 ? (b & 15) : (b >> 4);
+        return (double)(code - 8) * oracle_f16_value(((const uint16_t *)scales)[blk]);
+    }
     if (dtype == OR_MXFP4) {
         const uint8_t b = ((const uint8_t *)base)[idx / 2];
         return oracle_e2m1_value((idx & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 15)) *
@@ -124,8 +148,10 @@ int oracle_check_layer(const oracle_layer *L) {
     if (!L || L->E < 1 || L->top_k < 1 || L->top_k > L->E || L->H < 1 || L->I < 1) return 1;
     if (!L->w_router || !L->w_gate_up || !L->w_down) return 1;
     if (L->expert_dtype == OR_FP8 && (L->H % 128 || L->I % 128 || !L->s_gate_up || !L->s_down)) return 1;
-    if (L->expert_dtype == OR_MXFP4 && (L->H % 32 || L->I % 32 || !L->s_gate_up || !L->s_down)) return 1;
-    if (L->expert_dtype < OR_F32 || L->expert_dtype > OR_MXFP4) return 1;
+    if ((L->expert_dtype == OR_MXFP4 || L->expert_dtype == OR_Q4_0) &&
+        (L->H % 32 || L->I % 32 || !L->s_gate_up || !L->s_down))
+        return 1;
+    if (L->expert_dtype < OR_F32 || L->expert_dtype > OR_Q4_0) return 1;
     if (L->router_dtype != OR_F32 && L->router_dtype != OR_BF16) return 1;
     return 0;
 }

@@ -485,3 +485,98 @@ def test_mxfp4_generator_scales_and_codes():
     for v in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0):  # exact ties go to the even code
         c = wl.e2m1_encode(v)
         assert c % 2 == 0, (v, c)
+
+
+# -------------------------------------------------------------------- q4_0 --
+
+def test_f16_decode_all_codes_match_numpy():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.f16_value(int(h)) for h in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def _q4_decode(q, s):
+    """q4_0 [rows, cols/2] code bytes and [rows, cols/32] binary16 scales to
+    float64: per block of 16 bytes the low nibbles are elements 0..15 and the
+    high nibbles elements 16..31; value (code - 8) * d, d from numpy's float16."""
+    rows = q.shape[0]
+    blk = q.reshape(rows, -1, 16).astype(np.int64)
+    codes = np.concatenate([blk & 15, blk >> 4], axis=-1).reshape(rows, -1)
+    d = np.ascontiguousarray(s).view(np.float16).astype(np.float64)
+    return (codes - 8) * np.repeat(d, 32, axis=1)
+
+
+def test_q4_0_expert_matches_reference_decode():
+    """q4_0 experts: decode with numpy's binary16 and the block layout (low
+    nibbles first), run the textbook SwiGLU; a swapped nibble half, a wrong
+    code offset or a misaligned scale index fails this."""
+    spec = wl.LayerSpec(E=2, top_k=1, H=96, I=64, expert_dtype=wl.Q4_0, router_dtype=wl.BF16)
+    w = wl.make_layer(spec)
+    x = wl.make_x(3, spec.H)
+    L = oracle.Layer(w)
+    ids = np.array([[1], [0], [1]], np.int32)
+    got = oracle.expert_fwd(L, x, ids, np.ones((3, 1)))
+    for t in range(3):
+        e = ids[t, 0]
+        ref = _torch_swiglu(x[t:t + 1], _q4_decode(w["w_gate_up"][e], w["s_gate_up"][e]),
+                            _q4_decode(w["w_down"][e], w["s_down"][e]))
+        assert np.allclose(got[t], ref[0], rtol=1e-12, atol=1e-12)
+
+
+def test_q4_0_layer_equals_fp32_layer_of_its_values():
+    """A q4_0 layer and the fp32 layer holding exactly its decoded weights
+    (powers-of-two scales, so every value is exact in fp32) give the same
+    output bit for bit: the element order of a block is that of the fp32 rows."""
+    E, k, H, I = 3, 2, 64, 32
+    rng = np.random.default_rng(7)
+    gu_codes = rng.integers(0, 16, size=(E, 2 * I, H))
+    dn_codes = rng.integers(0, 16, size=(E, H, I))
+    gu_exp = rng.integers(-9, -5, size=(E, 2 * I, H // 32))
+    dn_exp = rng.integers(-9, -5, size=(E, H, I // 32))
+
+    def pack(codes, exps):
+        r = codes.reshape(codes.shape[0], codes.shape[1], -1, 32)
+        q = (r[..., :16] | (r[..., 16:] << 4)).astype(np.uint8).reshape(codes.shape[0], codes.shape[1], -1)
+        s = np.ldexp(1.0, exps).astype(np.float16).view(np.uint16)
+        vals = (codes - 8) * np.repeat(np.ldexp(1.0, exps), 32, axis=-1)
+        return q, s, vals.astype(np.float32)
+
+    qg, sg, vg = pack(gu_codes, gu_exp)
+    qd, sd, vd = pack(dn_codes, dn_exp)
+    wr = (rng.standard_normal((E, H)) * 0.2).astype(np.float32)
+    x = rng.standard_normal((5, H)).astype(np.float32)
+    Lq = oracle.Layer(dict(spec=_spec(E, k, H, I, wl.Q4_0, wl.F32), w_router=wr, w_gate_up=qg, w_down=qd,
+                           s_gate_up=sg, s_down=sd))
+    Lf = _f32_layer(E, k, H, I, vg, vd, w_router=wr)
+    oq, of = oracle.moe_layer(Lq, x), oracle.moe_layer(Lf, x)
+    for n in ("out", "ids", "w", "logits"):
+        assert np.array_equal(oq[n], of[n]), n
+
+
+def test_f16_encode_matches_numpy_rounding():
+    rng = np.random.default_rng(3)
+    vals = np.concatenate([rng.standard_normal(2000) * 10.0 ** rng.integers(-8, 4, 2000),
+                           [0.0, -0.0, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26, 65504.0, 1.0 + 2.0 ** -11,
+                            1.0 + 3 * 2.0 ** -11, 2.0 ** -14 - 2.0 ** -25]])
+    for v in vals:
+        assert wl.f16_encode(float(v)) == int(np.float16(v).view(np.uint16)), v
+
+
+def test_q4_0_generator_scales_and_codes():
+    """The generator's blocks: scale = binary16(amax / 7), every code the
+    nearest integer to w / d plus 8 (ties to even), clamped to 0..15."""
+    k = wl.key(0, 0, 1)
+    q, s = wl.q4_0_matrices(k, 1, 8, 128, 0.1)
+    src = wl.normal_f32(k, 8 * 128, 1.0).astype(np.float64).reshape(8, 128) * 0.1
+    dec = _q4_decode(q[0], s[0])
+    for r in range(8):
+        for b in range(4):
+            blk = src[r, 32 * b:32 * b + 32]
+            d = float(np.float16(np.abs(blk).max() / 7.0))
+            assert float(np.ascontiguousarray(s[0, r, b:b + 1]).view(np.float16)[0]) == d
+            want = np.clip(np.rint(blk / d) + 8, 0, 15) - 8
+            assert np.array_equal(dec[r, 32 * b:32 * b + 32] / d, want)

@@ -39,8 +39,8 @@ SEED_X = 1          # + draw index
 SEED_ZIPF_PERM = 2
 SEED_LOGITS = 3     # + draw index (selection fed straight from i.i.d. N(0,1) logits)
 
-F32, BF16, FP8, MXFP4 = 0, 1, 2, 3
-DTYPE_NAMES = {F32: "f32", BF16: "bf16", FP8: "fp8_e4m3", MXFP4: "mxfp4"}
+F32, BF16, FP8, MXFP4, Q4_0 = 0, 1, 2, 3, 4
+DTYPE_NAMES = {F32: "f32", BF16: "bf16", FP8: "fp8_e4m3", MXFP4: "mxfp4", Q4_0: "q4_0"}
 
 
 def build(force: bool = False) -> str:
@@ -74,6 +74,10 @@ def lib():
         L.moegen_mxfp4_matrix.argtypes = [u64, u64, i32, i32, dbl, vp, vp, i32]
         L.moegen_e2m1_encode.restype = ctypes.c_uint8
         L.moegen_e2m1_encode.argtypes = [dbl]
+        L.moegen_q4_0_matrix.restype = i32
+        L.moegen_q4_0_matrix.argtypes = [u64, u64, i32, i32, dbl, vp, vp, i32]
+        L.moegen_f16_encode.restype = ctypes.c_uint16
+        L.moegen_f16_encode.argtypes = [dbl]
         L.moegen_permutation.restype = None
         L.moegen_permutation.argtypes = [u64, i32, vp]
         L.moegen_normal_one.restype = dbl
@@ -132,6 +136,26 @@ def mxfp4_matrices(k: int, count: int, rows: int, cols: int, sigma: float, nthre
     return q, s
 
 
+def q4_0_matrices(k: int, count: int, rows: int, cols: int, sigma: float, nthreads: int | None = None):
+    """``count`` consecutive [rows, cols] matrices of one stream as q4_0:
+    (codes uint8 [count, rows, cols/2], per block of 32 elements along a row
+    16 bytes with element j in the low nibble of byte j and element j + 16 in
+    its high nibble; binary16 scales as uint16 bit patterns
+    [count, rows, cols/32])."""
+    q = np.empty((count, rows, cols // 2), dtype=np.uint8)
+    s = np.empty((count, rows, cols // 32), dtype=np.uint16)
+    for c in range(count):
+        rc = lib().moegen_q4_0_matrix(k, c * rows * cols, rows, cols, sigma, q[c].ctypes.data, s[c].ctypes.data,
+                                      nthreads or default_threads())
+        if rc != 0:
+            raise ValueError("q4_0 matrices need cols that are a multiple of 32")
+    return q, s
+
+
+def f16_encode(v: float) -> int:
+    return int(lib().moegen_f16_encode(float(v)))
+
+
 def e2m1_encode(v: float) -> int:
     return int(lib().moegen_e2m1_encode(float(v)))
 
@@ -174,8 +198,8 @@ def make_layer(spec: LayerSpec, layer: int = 0, seed: int = SEED_WEIGHTS, nthrea
     out["w_router"] = _dt_array(key(seed, layer, T_ROUTER), E * H, sh, spec.router_dtype, nthreads).reshape(E, H)
     if not experts:
         return out
-    if spec.expert_dtype in (FP8, MXFP4):
-        mats = fp8_matrices if spec.expert_dtype == FP8 else mxfp4_matrices
+    if spec.expert_dtype in (FP8, MXFP4, Q4_0):
+        mats = {FP8: fp8_matrices, MXFP4: mxfp4_matrices, Q4_0: q4_0_matrices}[spec.expert_dtype]
         q, s = mats(key(seed, layer, T_GATE_UP), E, 2 * I, H, sh, nthreads)
         out["w_gate_up"], out["s_gate_up"] = q, s
         q, s = mats(key(seed, layer, T_DOWN), E, H, I, si, nthreads)

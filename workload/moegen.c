@@ -299,6 +299,91 @@ int moegen_mxfp4_matrix(uint64_t key, uint64_t start, int rows, int cols, double
 
 uint8_t moegen_e2m1_encode(double v) { return e2m1_encode(v); }
 
+/* ---- q4_0 (blocks of 32 with one binary16 scale, 4-bit codes offset by 8) */
+
+/* Nearest IEEE binary16 value of v as its bit pattern, ties to even
+ * (rint in the default rounding mode); beyond the largest finite value,
+ * the largest finite value. */
+static uint16_t f16_encode(double v) {
+    uint16_t sign = (v < 0 || (v == 0 && signbit(v))) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (a < ldexp(1.0, -14)) return sign | (uint16_t)rint(ldexp(a, 24)); /* subnormal (1024 carries into 2^-14) */
+    int ex;
+    double m = frexp(a, &ex); /* a = m * 2^ex, m in [0.5, 1) */
+    int e = ex - 1;
+    double frac = rint((2.0 * m - 1.0) * 1024.0);
+    if (frac == 1024.0) {
+        frac = 0.0;
+        ++e;
+    }
+    if (e > 15) return sign | 0x7BFF;
+    return sign | (uint16_t)((e + 15) << 10) | (uint16_t)frac;
+}
+
+static double f16_decode(uint16_t h) {
+    int e = (h >> 10) & 0x1F, f = h & 0x3FF;
+    double mag = e == 0 ? ldexp((double)f, -24) : ldexp(1.0 + f / 1024.0, e - 15);
+    return (h & 0x8000) ? -mag : mag;
+}
+
+typedef struct {
+    uint64_t key, start;
+    int64_t blk_lo, blk_hi;
+    double sigma;
+    uint8_t *q;
+    uint16_t *scales;
+} q4_job;
+
+static void *q4_worker(void *arg) {
+    q4_job *j = (q4_job *)arg;
+    double w[32];
+    for (int64_t b = j->blk_lo; b < j->blk_hi; ++b) {
+        double amax = 0.0;
+        for (int c = 0; c < 32; ++c) {
+            w[c] = j->sigma * normal_at(j->key, j->start + (uint64_t)b * 32 + (uint64_t)c);
+            if (fabs(w[c]) > amax) amax = fabs(w[c]);
+        }
+        /* the scale maps the largest magnitude to code 8 +- 7 */
+        const uint16_t h = f16_encode(amax / 7.0);
+        const double d = f16_decode(h);
+        j->scales[b] = h;
+        uint8_t code[32];
+        for (int c = 0; c < 32; ++c) {
+            double qv = d > 0.0 ? rint(w[c] / d) + 8.0 : 8.0;
+            code[c] = (uint8_t)(qv < 0.0 ? 0.0 : qv > 15.0 ? 15.0 : qv);
+        }
+        for (int c = 0; c < 16; ++c) j->q[b * 16 + c] = (uint8_t)(code[c] | (code[c + 16] << 4));
+    }
+    return NULL;
+}
+
+/*
+ * One [rows, cols] matrix (cols a multiple of 32) whose element (r, c) is
+ * sigma * z_{start + r*cols + c}, encoded as q4_0: per block of 32 along a row
+ * one binary16 scale d = amax / 7 (scales[(r*cols + c)/32]) and 16 code bytes
+ * (q[(r*cols + c)/32 * 16 + j]: element j of the block in the low nibble of
+ * byte j, element j + 16 in its high nibble); each code is the nearest
+ * integer to w / d plus 8 (ties to even), clamped to 0..15.
+ */
+int moegen_q4_0_matrix(uint64_t key, uint64_t start, int rows, int cols, double sigma, uint8_t *q,
+                       uint16_t *scales, int nthreads) {
+    if (cols % 32 || rows <= 0 || cols <= 0) return 1;
+    int64_t nblk = (int64_t)rows * cols / 32;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (nthreads > nblk) nthreads = (int)nblk;
+    q4_job jobs[256];
+    pthread_t th[256];
+    for (int t = 0; t < nthreads; ++t)
+        jobs[t] = (q4_job){key, start, nblk * t / nthreads, nblk * (t + 1) / nthreads, sigma, q, scales};
+    for (int t = 1; t < nthreads; ++t) pthread_create(&th[t], NULL, q4_worker, &jobs[t]);
+    q4_worker(&jobs[0]);
+    for (int t = 1; t < nthreads; ++t) pthread_join(th[t], NULL);
+    return 0;
+}
+
+uint16_t moegen_f16_encode(double v) { return f16_encode(v); }
+
 /* Seeded permutation of 0..n-1 (Fisher-Yates driven by the uniform stream). */
 void moegen_permutation(uint64_t key, int n, int32_t *perm) {
     for (int i = 0; i < n; ++i) perm[i] = i;
