@@ -46,7 +46,7 @@ MFMA_PEAK_TFS = 2500.0  # dense bf16
 # (uniform routing, bs=64), from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
 # scaled by a 1 GiB copy calibration: profiles/pass_kernels_uniform_bs64_hbm_counters.md.
 # Reported only while the kernel source is the one that was measured.
-PASS1_TRAFFIC_BS64 = {"read_bytes": 1.38556e+09, "write_bytes": 1.53467e+06, "source": "eddb8c158d3e998f"}
+PASS1_TRAFFIC_BS64 = {"read_bytes": 1.38556e+09, "write_bytes": 1.53467e+06, "source": "9f3897dbdb7a5356"}
 
 
 def pass1_source_fingerprint():
@@ -86,8 +86,9 @@ def parse():
                          "skewed: E=256 top_k=6 Zipf(1.1) routing, bs 1/8/32/64; "
                          "stack: 30-layer stack, one HIP graph vs a host-sync arm; "
                          "large: E=256 H=4096 I=1536 Zipf layer at bs 128/256/512 with MFMA segments")
-    ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp8", "mxfp4"],
-                    help="expert weights: bf16 or mxfp4 (every workload but stack), fp8 (large workload)")
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp8", "mxfp4", "q4_0"],
+                    help="expert weights: bf16 or mxfp4 (every workload but stack), fp8 (large workload), "
+                         "q4_0 (sweep and skewed workloads, GEMV kernels)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a device-to-device copy of this many MiB, 3 times (reference for HBM counters)")
     return ap.parse_args()
@@ -706,19 +707,22 @@ def main():
         return
 
     skewed = args.workload == "skewed"
-    if args.dtype not in ("bf16", "mxfp4"):
-        print("bench.py: the %s workload takes bf16 or mxfp4 experts" % args.workload, file=sys.stderr)
+    if args.dtype not in ("bf16", "mxfp4", "q4_0"):
+        print("bench.py: the %s workload takes bf16, mxfp4 or q4_0 experts" % args.workload, file=sys.stderr)
         sys.exit(2)
-    mx = args.dtype == "mxfp4"
+    mx = args.dtype != "bf16"  # a 4-bit format
     base = wl.SKEWED if skewed else wl.SWEEP
-    spec = base if not mx else wl.LayerSpec(E=base.E, top_k=base.top_k, H=base.H, I=base.I, expert_dtype=wl.MXFP4,
+    qdt = {"mxfp4": wl.MXFP4, "q4_0": wl.Q4_0}.get(args.dtype)
+    spec = base if not mx else wl.LayerSpec(E=base.E, top_k=base.top_k, H=base.H, I=base.I, expert_dtype=qdt,
                                             router_dtype=base.router_dtype)
-    wname = "MXFP4 (E2M1, E8M0 scale per 32)" if mx else "bf16"
+    wname = {"mxfp4": "MXFP4 (E2M1, E8M0 scale per 32)", "q4_0": "q4_0 (4-bit codes, binary16 scale per 32)"}.get(
+        args.dtype, "bf16")
     bias = wl.zipf_bias(spec.E) if skewed else None
     walk = {"dedup": moe.MOE_WALK_DEDUP, "per_route": moe.MOE_WALK_PER_ROUTE,
             "dedup_pass1": moe.MOE_WALK_DEDUP_PASS1}[args.walk]
     flags = walk | (moe.MOE_NO_MFMA if args.no_mfma else 0)
-    bpw = 17 / 32 if mx else 2  # bytes per weight: MXFP4 half a byte plus one scale byte per 32
+    # bytes per weight: MXFP4 half a byte plus one scale byte per 32, q4_0 two scale bytes per 32
+    bpw = {"mxfp4": 17 / 32, "q4_0": 18 / 32}.get(args.dtype, 2)
     expert_bytes = 3 * spec.H * spec.I * bpw
 
     t0 = time.time()
@@ -790,7 +794,7 @@ def main():
     line = {
         "metric": "MoE layer steps/s at bs=%d (%s routing, E=256, top_k=%d, H=2048, I=768, %s); "
                   "achieved HBM GB/s on unique-expert bytes" % (args.bs, "Zipf(1.1)" if skewed else "uniform",
-                                                              spec.top_k, "mxfp4" if mx else "bf16"),
+                                                              spec.top_k, args.dtype),
         "value": head["steps_per_s"],
         "unit": "steps/s",
         "n_gpus": 1,
@@ -800,7 +804,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4" if mx else "bf16",
+        "dtype": args.dtype,
         "data": "synthetic (seeded N(0, 1/sqrt(fan_in)) weights, N(0,1) activations)",
         "config": {"workload": "single MoE layer, %s routing, E=256 top_k=%d H=2048 I=768 %s experts, batch "
                                "sweep" % ("Zipf(1.1)" if skewed else "uniform", spec.top_k, wname), "bs": args.bs,
@@ -814,7 +818,9 @@ def main():
                      "traffic": traffic, "avg_launch_us": p1_ms * 1e3, "bytes_per_launch": p1_bytes,
                      "frac_of_read_stream_probe": p1_gbs / probe["GBps"] if probe else None,
                      "bytes_rule": "unique experts on the GEMV path x 2I x H x %s (gate_up, %s)" %
-                                   ("17/32 B (codes and E8M0 scales)" if mx else "2 B", "mxfp4" if mx else "bf16")},
+                                   ({"mxfp4": "17/32 B (codes and E8M0 scales)",
+                                     "q4_0": "18/32 B (codes and binary16 scales)"}.get(args.dtype, "2 B"),
+                                    args.dtype)},
         "cpu_baseline": cpu,
     }
     line.update(extra)

@@ -85,12 +85,12 @@ typedef enum {
     MOE_ERR_ALIGN = 7        /* a pointer is not 16-byte aligned               */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3, MOE_Q4_0 = 4 } moe_dtype;
 
 /* One MoE layer.  Limits: 1 <= E <= 1024, 1 <= top_k <= min(E, 32);
  * H, I >= 1 with H, I multiples of 4 (fp32), 8 (bf16), 128 (fp8) or 32
- * (MXFP4), and at most 512 16-byte chunks per weight row (H, I <= 2048 fp32,
- * 4096 bf16, 8192 fp8, 16384 MXFP4).  Weight pointers must be 16-byte
+ * (MXFP4, q4_0), and at most 512 16-byte chunks per weight row (H, I <= 2048
+ * fp32, 4096 bf16, 8192 fp8, 16384 MXFP4 and q4_0).  Weight pointers must be 16-byte
  * aligned.
  *
  * MXFP4 expert weights (OCP microscaling): E2M1 codes, two per byte with the
@@ -98,6 +98,15 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3 } moe_
  * E8M0 scale byte, 2^(s - 127), per 32 consecutive elements of a row:
  * s_gate_up uint8 [E, 2I, H/32], s_down uint8 [E, H, I/32].  The router
  * stays fp32 or bf16.
+ *
+ * q4_0 expert weights (the q4_0 format of the pages' list of formats on the
+ * pass-1 dot product: blocks of 32 consecutive elements of a row, one
+ * IEEE binary16 scale d per block, 4-bit codes q, value (q - 8) * d): a
+ * block is 16 code bytes, element j < 16 in the low nibble of byte j and
+ * element j + 16 in its high nibble (a row of K elements is K/2 bytes); the
+ * scales sit in their own arrays, binary16 bit patterns, 2-byte aligned:
+ * s_gate_up uint16 [E, 2I, H/32], s_down uint16 [E, H, I/32].  q4_0 experts
+ * run on the GEMV kernels only.
  *
  * Matrix cores: in a call of 16 or more tokens, an expert that holds
  * moe_mfma_min_routes() routes or more (5 below 128 tokens, 4 from 128) runs,
@@ -112,12 +121,12 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3 } moe_
 typedef struct {
     int32_t E, top_k, H, I;
     int32_t router_dtype;     /* MOE_F32 or MOE_BF16                          */
-    int32_t expert_dtype;     /* MOE_F32, MOE_BF16, MOE_FP8_E4M3 or MOE_MXFP4 */
+    int32_t expert_dtype;     /* MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 or MOE_Q4_0 */
     const void *w_router;     /* [E, H]                                       */
     const void *w_gate_up;    /* [E, 2I, H]: rows [0, I) gate, [I, 2I) up     */
     const void *w_down;       /* [E, H, I]                                    */
-    const void *s_gate_up;    /* fp8: float [E, 2I/128, H/128]; MXFP4: uint8 [E, 2I, H/32] */
-    const void *s_down;       /* fp8: float [E, H/128, I/128]; MXFP4: uint8 [E, H, I/32]   */
+    const void *s_gate_up;    /* fp8: float [E, 2I/128, H/128]; MXFP4: uint8, q4_0: uint16 [E, 2I, H/32] */
+    const void *s_down;       /* fp8: float [E, H/128, I/128]; MXFP4: uint8, q4_0: uint16 [E, H, I/32]   */
     const float *router_bias; /* [E] added to the logits, or NULL             */
 } moe_layer_t;
 

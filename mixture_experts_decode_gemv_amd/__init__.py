@@ -22,7 +22,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_gfx950.so")
 
-MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 = 0, 1, 2, 3
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4, MOE_Q4_0 = 0, 1, 2, 3, 4
 MOE_WALK_DEDUP, MOE_WALK_PER_ROUTE, MOE_WALK_DEDUP_PASS1 = 0, 1, 2
 MOE_ACCUM_RESIDUAL = 1 << 4
 MOE_RMSNORM_IN = 1 << 6

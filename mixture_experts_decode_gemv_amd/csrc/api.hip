@@ -42,13 +42,13 @@ static moe_status check_layer(const moe_layer_t *L) {
     if (L->E > kMaxE || L->top_k > kMaxK) return MOE_ERR_SHAPE;
     if (L->router_dtype != MOE_F32 && L->router_dtype != MOE_BF16) return MOE_ERR_DTYPE;
     if (L->expert_dtype != MOE_F32 && L->expert_dtype != MOE_BF16 && L->expert_dtype != MOE_FP8_E4M3 &&
-        L->expert_dtype != MOE_MXFP4)
+        L->expert_dtype != MOE_MXFP4 && L->expert_dtype != MOE_Q4_0)
         return MOE_ERR_DTYPE;
     const int epc = elems_per_chunk(L->expert_dtype), repc = elems_per_chunk(L->router_dtype);
     if (L->H % epc || L->I % epc || L->H % repc || L->H % 4 || L->I % 4) return MOE_ERR_SHAPE;
     if (L->expert_dtype == MOE_FP8_E4M3 && (L->H % 128 || L->I % 128)) return MOE_ERR_SHAPE;
-    if (L->H / epc > kWave * kMaxChunksPerLane || L->I / epc > kWave * kMaxChunksPerLane ||
-        L->H / repc > kWave * kMaxChunksPerLane)
+    const int mc = max_chunks_per_lane(L->expert_dtype);
+    if (L->H / epc > kWave * mc || L->I / epc > kWave * mc || L->H / repc > kWave * kMaxChunksPerLane)
         return MOE_ERR_SHAPE;
     return MOE_OK;
 }
@@ -59,8 +59,13 @@ static moe_status check_weights(const moe_layer_t *L, bool router, bool experts)
     if (experts) {
         if (!L->w_gate_up || !L->w_down) return MOE_ERR_ARG;
         if (!aligned16(L->w_gate_up) || !aligned16(L->w_down)) return MOE_ERR_ALIGN;
-        if ((L->expert_dtype == MOE_FP8_E4M3 || L->expert_dtype == MOE_MXFP4) && (!L->s_gate_up || !L->s_down))
+        if ((L->expert_dtype == MOE_FP8_E4M3 || L->expert_dtype == MOE_MXFP4 || L->expert_dtype == MOE_Q4_0) &&
+            (!L->s_gate_up || !L->s_down))
             return MOE_ERR_ARG;
+        // q4_0 scales are read as 2-byte words
+        if (L->expert_dtype == MOE_Q4_0 &&
+            (((uintptr_t)L->s_gate_up & 1u) != 0 || ((uintptr_t)L->s_down & 1u) != 0))
+            return MOE_ERR_ALIGN;
     }
     return MOE_OK;
 }

@@ -15,6 +15,9 @@ constexpr int kBlock = 256;  // 4 waves per workgroup everywhere
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
 constexpr int kMaxChunksPerLane = 8;  // 16-byte chunks per lane per weight row
+// q4_0 rows stop at 4 chunks per lane (K <= 8192): with 8, its decode made
+// the compiler call the route loop out of line (scratch and calls).
+__host__ __device__ constexpr int max_chunks_per_lane(int dtype) { return dtype == MOE_Q4_0 ? 4 : kMaxChunksPerLane; }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -26,6 +29,8 @@ template <> struct WT<MOE_FP8_E4M3> { static constexpr int kEpc = 16; static con
 // MXFP4: 32 E2M1 codes per chunk, one E8M0 scale block (kBytes is not used:
 // row bytes are chunks x 16 for every dtype).
 template <> struct WT<MOE_MXFP4> { static constexpr int kEpc = 32; static constexpr int kBytes = 0; };
+// q4_0: 32 codes per chunk, one block with one binary16 scale.
+template <> struct WT<MOE_Q4_0> { static constexpr int kEpc = 32; static constexpr int kBytes = 0; };
 
 __host__ __device__ constexpr int elems_per_chunk(int dtype) {
     return dtype == MOE_F32 ? 4 : dtype == MOE_BF16 ? 8 : dtype == MOE_FP8_E4M3 ? 16 : 32;
@@ -103,6 +108,25 @@ __device__ __forceinline__ void e2m1x8_decode(uint32_t v, float *f) {
     f[2] = p1[0]; f[3] = p1[1];
     f[4] = p2[0]; f[5] = p2[1];
     f[6] = p3[0]; f[7] = p3[1];
+}
+
+// 8 q4_0 codes of a 32-bit word (bytes b0..b3 of a block's word v) as the
+// exact fp32 values code - 8: f[0..3] the low nibbles (elements 4v .. 4v + 3
+// of the block), f[4..7] the high nibbles (elements 16 + 4v .. 16 + 4v + 3).
+// With every nibble's top bit flipped, a nibble read as a signed 4-bit field
+// is code - 8: one signed bitfield extract and one conversion per element.
+__device__ __forceinline__ void q4x8_decode(uint32_t v, float *f) {
+    const int s = (int)(v ^ 0x88888888u);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        f[b] = (float)((s << (28 - 8 * b)) >> 28);
+        f[4 + b] = (float)((s << (24 - 8 * b)) >> 28);
+    }
+}
+
+// IEEE binary16 bit pattern to fp32 (exact).
+__device__ __forceinline__ float f16_value(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)h);
 }
 
 // E8M0 scale byte to fp32: 2^(s - 127) (s = 0 is the subnormal 2^-127; 255,

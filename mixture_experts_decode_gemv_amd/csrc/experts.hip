@@ -179,12 +179,16 @@ int mfma_hot_routes(const moe_layer_t &L, int T, uint32_t flags) {
 
 // Pass 2 and the combine in one launch (pass2c_kernel) for small batches with
 // an output to write: the y block of a workgroup ([R][rows] floats) must fit
-// in 64 KiB of LDS.  The same predicate tells a layer stack whether each
-// layer writes its output rows itself.
+// in 64 KiB of LDS, and down rows must take 32 or 64 lanes.  Short rows (16
+// or 8 lanes, 4-bit formats) give a workgroup 4-8x more rows, so the launch
+// would cover a quarter of the CUs or less (H = 2048: 64 workgroups of 8
+// waves); they take pass2_kernel and the combine launch.  The same predicate
+// tells a layer stack whether each layer writes its output rows itself.
 bool fused_combine(const moe_layer_t &L, int T) {
     if (T > kPass2cMaxT) return false;
     const int nq2 = L.I / elems_per_chunk(L.expert_dtype);
     const int lanes = pass2_lanes(nq2, L.expert_dtype);
+    if (lanes < 32) return false;
     const int nr = pass2c_rows(nc_instance((nq2 + lanes - 1) / lanes), lanes);
     return (size_t)T * L.top_k * (nr * 4 + 1) <= 64 * 1024;
 }
@@ -251,7 +255,8 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
             case MOE_F32: return launch_pass1<MOE_F32>(nc1, persistent_grid(items1), s, p1);
             case MOE_BF16: return launch_pass1<MOE_BF16>(nc1, persistent_grid(items1), s, p1);
             case MOE_FP8_E4M3: return launch_pass1<MOE_FP8_E4M3>(nc1, persistent_grid(items1), s, p1);
-            default: return launch_pass1<MOE_MXFP4>(nc1, persistent_grid(items1), s, p1);
+            case MOE_MXFP4: return launch_pass1<MOE_MXFP4>(nc1, persistent_grid(items1), s, p1);
+            default: return launch_pass1<MOE_Q4_0>(nc1, persistent_grid(items1), s, p1);
         }
     };
     // pass 1 of the MFMA segments, on a bf16 copy of x (converted here unless
@@ -282,7 +287,8 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
             case MOE_F32: return launch_pass2<MOE_F32>(nc2, lanes, persistent_grid(items2), s, p2);
             case MOE_BF16: return launch_pass2<MOE_BF16>(nc2, lanes, persistent_grid(items2), s, p2);
             case MOE_FP8_E4M3: return launch_pass2<MOE_FP8_E4M3>(nc2, lanes, persistent_grid(items2), s, p2);
-            default: return launch_pass2<MOE_MXFP4>(nc2, lanes, persistent_grid(items2), s, p2);
+            case MOE_MXFP4: return launch_pass2<MOE_MXFP4>(nc2, lanes, persistent_grid(items2), s, p2);
+            default: return launch_pass2<MOE_Q4_0>(nc2, lanes, persistent_grid(items2), s, p2);
         }
     };
     // pass 2 with the combine (small batches): writes out directly; the
@@ -298,7 +304,8 @@ hipError_t launch_experts(const moe_layer_t &L, const float *x, const float *xre
             case MOE_F32: return launch_pass2c<MOE_F32>(nc2, lanes, s, p);
             case MOE_BF16: return launch_pass2c<MOE_BF16>(nc2, lanes, s, p);
             case MOE_FP8_E4M3: return launch_pass2c<MOE_FP8_E4M3>(nc2, lanes, s, p);
-            default: return launch_pass2c<MOE_MXFP4>(nc2, lanes, s, p);
+            case MOE_MXFP4: return launch_pass2c<MOE_MXFP4>(nc2, lanes, s, p);
+            default: return launch_pass2c<MOE_Q4_0>(nc2, lanes, s, p);
         }
     };
     auto mfma_2 = [&](hipStream_t s) {

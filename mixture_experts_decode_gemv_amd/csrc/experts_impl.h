@@ -228,10 +228,15 @@ __device__ __forceinline__ void dot_rows(u32x4 (&w)[NS][NC], const float (&sc)[N
     for (int r = 0; r < RB; ++r)
 #pragma unroll
         for (int s = 0; s < NS; ++s) acc[r][s] = 0.f;
-    if constexpr (WDT == MOE_MXFP4) {
+    if constexpr (WDT == MOE_MXFP4 || WDT == MOE_Q4_0) {
         // 32 codes per chunk, taken a 32-bit word (8 elements) at a time:
-        // per (route, slot) one fp32 chain over the chunk's elements in
-        // order, then scaled by the chunk's E8M0 scale
+        // per (route, slot) one fp32 chain over the chunk's elements, then
+        // scaled by the chunk's scale (E8M0, or q4_0's binary16).  MXFP4
+        // word v holds elements 8v .. 8v + 7; q4_0 word v elements
+        // 4v .. 4v + 3 (low nibbles) and 16 + 4v .. 16 + 4v + 3 (high).
+        // Each element's value is exact in fp32 (a q4_0 code minus 8: taking
+        // the offset out of the sums instead, as sum q x - 8 sum x, loses
+        // the low bits of a small sum to cancellation).
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const int q = sub + G * c;
@@ -246,7 +251,8 @@ __device__ __forceinline__ void dot_rows(u32x4 (&w)[NS][NC], const float (&sc)[N
                     float xs[RB][8];
 #pragma unroll
                     for (int r = 0; r < RB; ++r) {
-                        const float4 f0 = xl[r][q * 8 + 2 * v], f1 = xl[r][q * 8 + 2 * v + 1];
+                        const float4 f0 = WDT == MOE_Q4_0 ? xl[r][q * 8 + v] : xl[r][q * 8 + 2 * v];
+                        const float4 f1 = WDT == MOE_Q4_0 ? xl[r][q * 8 + 4 + v] : xl[r][q * 8 + 2 * v + 1];
                         xs[r][0] = f0.x; xs[r][1] = f0.y; xs[r][2] = f0.z; xs[r][3] = f0.w;
                         xs[r][4] = f1.x; xs[r][5] = f1.y; xs[r][6] = f1.z; xs[r][7] = f1.w;
                     }
@@ -254,7 +260,8 @@ __device__ __forceinline__ void dot_rows(u32x4 (&w)[NS][NC], const float (&sc)[N
                     for (int s = 0; s < NS; ++s) {
                         const uint32_t word = v == 0 ? w[s][c].x : v == 1 ? w[s][c].y : v == 2 ? w[s][c].z : w[s][c].w;
                         float wf[8];
-                        e2m1x8_decode(word, wf);
+                        if constexpr (WDT == MOE_Q4_0) q4x8_decode(word, wf);
+                        else e2m1x8_decode(word, wf);
 #pragma unroll
                         for (int r = 0; r < RB; ++r)
 #pragma unroll
@@ -269,28 +276,30 @@ __device__ __forceinline__ void dot_rows(u32x4 (&w)[NS][NC], const float (&sc)[N
         }
         return;
     }
+    if constexpr (WDT != MOE_MXFP4 && WDT != MOE_Q4_0) {  // 4 to 16 elements per chunk
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const int q = sub + G * c;
-        if (q < nq) {
-            float xs[RB][EPC];
+        for (int c = 0; c < NC; ++c) {
+            const int q = sub + G * c;
+            if (q < nq) {
+                float xs[RB][EPC];
 #pragma unroll
-            for (int r = 0; r < RB; ++r)
+                for (int r = 0; r < RB; ++r)
 #pragma unroll
-                for (int v = 0; v < EPC / 4; ++v) {
-                    const float4 f = xl[r][q * (EPC / 4) + v];
-                    xs[r][4 * v] = f.x; xs[r][4 * v + 1] = f.y; xs[r][4 * v + 2] = f.z; xs[r][4 * v + 3] = f.w;
-                }
+                    for (int v = 0; v < EPC / 4; ++v) {
+                        const float4 f = xl[r][q * (EPC / 4) + v];
+                        xs[r][4 * v] = f.x; xs[r][4 * v + 1] = f.y; xs[r][4 * v + 2] = f.z; xs[r][4 * v + 3] = f.w;
+                    }
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                float wf[EPC];
-                chunk_decode<WDT>(w[s][c], wf);
+                for (int s = 0; s < NS; ++s) {
+                    float wf[EPC];
+                    chunk_decode<WDT>(w[s][c], wf);
 #pragma unroll
-                for (int r = 0; r < RB; ++r) {
-                    float t = WDT == MOE_FP8_E4M3 ? 0.f : acc[r][s];
+                    for (int r = 0; r < RB; ++r) {
+                        float t = WDT == MOE_FP8_E4M3 ? 0.f : acc[r][s];
 #pragma unroll
-                    for (int i = 0; i < EPC; ++i) t = fmaf(wf[i], xs[r][i], t);
-                    acc[r][s] = WDT == MOE_FP8_E4M3 ? fmaf(sc[s][c], t, acc[r][s]) : t;
+                        for (int i = 0; i < EPC; ++i) t = fmaf(wf[i], xs[r][i], t);
+                        acc[r][s] = WDT == MOE_FP8_E4M3 ? fmaf(sc[s][c], t, acc[r][s]) : t;
+                    }
                 }
             }
         }
@@ -372,6 +381,19 @@ __global__ __launch_bounds__(kGemvBlock) void pass1_kernel(Pass1Args a) {
         for (int r = 0; r < NS; ++r)
 #pragma unroll
             for (int c = 0; c < NC; ++c) sc[r][c] = 1.f;
+        if (WDT == MOE_Q4_0) {  // one binary16 scale per chunk of 32: [E, 2I, H/32]
+            const uint16_t *sg = reinterpret_cast<const uint16_t *>(a.s_gate_up);
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                const int i = min(i0 + p, I - 1);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    const int q = min(lane + G * c, nq - 1);
+                    sc[2 * p][c] = f16_value(sg[((size_t)e * 2 * I + i) * nq + q]);
+                    sc[2 * p + 1][c] = f16_value(sg[((size_t)e * 2 * I + I + i) * nq + q]);
+                }
+            }
+        }
         if (WDT == MOE_MXFP4) {  // one E8M0 byte per chunk of 32: [E, 2I, H/32]
             const uint8_t *sg = reinterpret_cast<const uint8_t *>(a.s_gate_up);
 #pragma unroll
@@ -470,6 +492,18 @@ __device__ __forceinline__ void down_rows(const void *down, const void *s_down, 
         rows[j] = static_cast<const char *>(down) + ((size_t)e * H + min(h, H - 1)) * row_bytes;
 #pragma unroll
         for (int c = 0; c < NC; ++c) sc[j][c] = 1.f;
+    }
+    if (WDT == MOE_Q4_0) {  // one binary16 scale per chunk of 32: [E, H, I/32]
+        const uint16_t *sd = reinterpret_cast<const uint16_t *>(s_down);
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            const int h = min(h0 + j * RPS + half, H - 1);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const int q = min((lane & (G - 1)) + G * c, nq - 1);
+                sc[j][c] = f16_value(sd[((size_t)e * H + h) * nq + q]);
+            }
+        }
     }
     if (WDT == MOE_MXFP4) {  // one E8M0 byte per chunk of 32: [E, H, I/32]
         const uint8_t *sd = reinterpret_cast<const uint8_t *>(s_down);
@@ -604,7 +638,8 @@ constexpr int kPass2cMaxT = 64;  // batches up to this size take this kernel
 // many as the weight registers of one wave allow without spilling (fp8 and
 // MXFP4 decode into more temporaries).
 __host__ __device__ constexpr int pass2c_waves(int WDT, int NC, int G) {
-    return (WDT == MOE_FP8_E4M3 || WDT == MOE_MXFP4) ? (NC >= 8 ? 4 : 8) : (NC == 8 || (NC == 2 && G < 64) ? 8 : 16);
+    return (WDT == MOE_FP8_E4M3 || WDT == MOE_MXFP4 || WDT == MOE_Q4_0) ? (NC >= 8 ? 4 : 8)
+                                                                        : (NC == 8 || (NC == 2 && G < 64) ? 8 : 16);
 }
 
 struct Pass2cArgs {
@@ -749,14 +784,18 @@ __global__ __launch_bounds__(pass2c_waves(WDT, NC, G) * kWave) void pass2c_kerne
 __host__ __device__ constexpr int nc_instance(int nc) { return nc <= 4 ? nc : 8; }
 
 // Lanes per down row: 32 when a row's 16-byte chunks are a multiple of 32 but
-// not of 64 (e.g. 768 bf16), so no lane idles; otherwise 64.  MXFP4 rows are
-// short (I/32 chunks): 16 or 8 lanes per row when the chunks divide so.
+// not of 64 (e.g. 768 bf16), so no lane idles; otherwise 64.  MXFP4 and q4_0
+// rows are short (I/32 chunks): 16 or 8 lanes per row when the chunks divide so.
+// Fewer lanes than 64 only while a lane's chunks stay within the kernels'
+// largest instance (8 chunks, 4 for q4_0): 288 bf16 chunks (I = 2304) take
+// 64 lanes of 5 chunks, not 32 of 9.
 inline int pass2_lanes(int nq, int dtype) {
+    const int max_nc = max_chunks_per_lane(dtype);
     if (nq % 64 == 0) return 64;
-    if (nq % 32 == 0) return 32;
-    if (dtype == MOE_MXFP4) {
-        if (nq % 16 == 0) return 16;
-        if (nq % 8 == 0) return 8;
+    if (nq % 32 == 0 && nq / 32 <= max_nc) return 32;
+    if (dtype == MOE_MXFP4 || dtype == MOE_Q4_0) {
+        if (nq % 16 == 0 && nq / 16 <= max_nc) return 16;
+        if (nq % 8 == 0 && nq / 8 <= max_nc) return 8;
     }
     return 64;
 }
@@ -770,7 +809,10 @@ hipError_t launch_pass1(int nc, int grid, hipStream_t st, const Pass1Args &a) {
         case 2: MOE_P1(2); break;
         case 3: MOE_P1(3); break;
         case 4: MOE_P1(4); break;
-        case 8: MOE_P1(8); break;
+        case 8:
+            if constexpr (WDT == MOE_Q4_0) return hipErrorInvalidValue;
+            else MOE_P1(8);
+            break;
         default: return hipErrorInvalidValue;
     }
 #undef MOE_P1
@@ -781,19 +823,25 @@ template <int WDT>
 hipError_t launch_pass2(int nc, int lanes, int grid, hipStream_t st, const Pass2Args &a) {
     const size_t lds = (size_t)a.nb * a.I * 4;
 #define MOE_P2(N, L) hipLaunchKernelGGL((pass2_kernel<WDT, N, L>), dim3(grid), dim3(kGemvBlock), lds, st, a)
-    if constexpr (WDT == MOE_MXFP4) {
+    if constexpr (WDT == MOE_MXFP4 || WDT == MOE_Q4_0) {
         if (lanes == 16 || lanes == 8) {
             switch (nc_instance(nc) * 100 + lanes) {
                 case 116: MOE_P2(1, 16); break;
                 case 216: MOE_P2(2, 16); break;
                 case 316: MOE_P2(3, 16); break;
                 case 416: MOE_P2(4, 16); break;
-                case 816: MOE_P2(8, 16); break;
+                case 816:
+                    if constexpr (WDT == MOE_Q4_0) return hipErrorInvalidValue;
+                    else MOE_P2(8, 16);
+                    break;
                 case 108: MOE_P2(1, 8); break;
                 case 208: MOE_P2(2, 8); break;
                 case 308: MOE_P2(3, 8); break;
                 case 408: MOE_P2(4, 8); break;
-                case 808: MOE_P2(8, 8); break;
+                case 808:
+                    if constexpr (WDT == MOE_Q4_0) return hipErrorInvalidValue;
+                    else MOE_P2(8, 8);
+                    break;
                 default: return hipErrorInvalidValue;
             }
             return hipGetLastError();
@@ -805,7 +853,10 @@ hipError_t launch_pass2(int nc, int lanes, int grid, hipStream_t st, const Pass2
             case 2: MOE_P2(2, 32); break;
             case 3: MOE_P2(3, 32); break;
             case 4: MOE_P2(4, 32); break;
-            case 8: MOE_P2(8, 32); break;
+            case 8:
+                if constexpr (WDT == MOE_Q4_0) return hipErrorInvalidValue;
+                else MOE_P2(8, 32);
+                break;
             default: return hipErrorInvalidValue;
         }
     } else {
@@ -814,7 +865,10 @@ hipError_t launch_pass2(int nc, int lanes, int grid, hipStream_t st, const Pass2
             case 2: MOE_P2(2, 64); break;
             case 3: MOE_P2(3, 64); break;
             case 4: MOE_P2(4, 64); break;
-            case 8: MOE_P2(8, 64); break;
+            case 8:
+                if constexpr (WDT == MOE_Q4_0) return hipErrorInvalidValue;
+                else MOE_P2(8, 64);
+                break;
             default: return hipErrorInvalidValue;
         }
     }
@@ -838,29 +892,19 @@ hipError_t launch_pass2c(int nc, int lanes, hipStream_t st, const Pass2cArgs &a)
         case 264: MOE_P2C(2, 64); break;
         case 364: MOE_P2C(3, 64); break;
         case 464: MOE_P2C(4, 64); break;
-        case 864: MOE_P2C(8, 64); break;
+        case 864:
+            if constexpr (WDT == MOE_Q4_0) return hipErrorInvalidValue;
+            else MOE_P2C(8, 64);
+            break;
         case 132: MOE_P2C(1, 32); break;
         case 232: MOE_P2C(2, 32); break;
         case 332: MOE_P2C(3, 32); break;
         case 432: MOE_P2C(4, 32); break;
-        case 832: MOE_P2C(8, 32); break;
-        default:
-            if constexpr (WDT == MOE_MXFP4) {
-                switch (nc_instance(nc) * 100 + lanes) {
-                    case 116: MOE_P2C(1, 16); break;
-                    case 216: MOE_P2C(2, 16); break;
-                    case 316: MOE_P2C(3, 16); break;
-                    case 416: MOE_P2C(4, 16); break;
-                    case 816: MOE_P2C(8, 16); break;
-                    case 108: MOE_P2C(1, 8); break;
-                    case 208: MOE_P2C(2, 8); break;
-                    case 308: MOE_P2C(3, 8); break;
-                    case 408: MOE_P2C(4, 8); break;
-                    case 808: MOE_P2C(8, 8); break;
-                    default: return hipErrorInvalidValue;
-                }
-                break;
-            }
+        case 832:
+            if constexpr (WDT == MOE_Q4_0) return hipErrorInvalidValue;
+            else MOE_P2C(8, 32);
+            break;
+        default:  // 16 or 8 lanes per row take pass2_kernel and the combine launch
             return hipErrorInvalidValue;
     }
 #undef MOE_P2C
@@ -930,5 +974,8 @@ extern template hipError_t launch_pass2c<MOE_F32>(int, int, hipStream_t, const P
 extern template hipError_t launch_pass2c<MOE_BF16>(int, int, hipStream_t, const Pass2cArgs &);
 extern template hipError_t launch_pass2c<MOE_FP8_E4M3>(int, int, hipStream_t, const Pass2cArgs &);
 extern template hipError_t launch_pass2c<MOE_MXFP4>(int, int, hipStream_t, const Pass2cArgs &);
+extern template hipError_t launch_pass1<MOE_Q4_0>(int, int, hipStream_t, const Pass1Args &);
+extern template hipError_t launch_pass2<MOE_Q4_0>(int, int, int, hipStream_t, const Pass2Args &);
+extern template hipError_t launch_pass2c<MOE_Q4_0>(int, int, hipStream_t, const Pass2cArgs &);
 
 }  // namespace moe

@@ -144,6 +144,22 @@ def test_mxfp4_layer_validation():
     assert lib.moe_layer_fwd(ctypes.byref(_layer(**dict(ok, H=32 * 513, router_dtype=moe.MOE_BF16))), *args) == 2
 
 
+
+def test_q4_0_layer_validation():
+    lib = moe.lib()
+    ok = dict(expert_dtype=moe.MOE_Q4_0, H=64, I=64, s_gate_up=0x7000, s_down=0x8000)
+    args = (0x4000, 4, 0x5000, 0, 0x6000, 1 << 30, None)
+    # H, I multiples of 32
+    assert lib.moe_layer_fwd(ctypes.byref(_layer(**dict(ok, H=48))), *args) == 2
+    assert lib.moe_layer_fwd(ctypes.byref(_layer(**dict(ok, I=80))), *args) == 2
+    # scales required, 2-byte aligned
+    assert lib.moe_layer_fwd(ctypes.byref(_layer(**dict(ok, s_gate_up=None))), *args) == 1
+    assert lib.moe_layer_fwd(ctypes.byref(_layer(**dict(ok, s_down=0x8001))), *args) == 7
+    # at most 256 blocks of 32 codes per row (4 chunks per lane)
+    assert lib.moe_layer_fwd(ctypes.byref(_layer(**dict(ok, I=32 * 257))), *args) == 2
+    # an unknown expert dtype
+    assert lib.moe_layer_fwd(ctypes.byref(_layer(**dict(ok, expert_dtype=5))), *args) == 3
+
 def test_stack_workspace_and_argument_errors():
     """Stack workspace size and the host-side checks of moe_stack_fwd."""
     L = _layer()
