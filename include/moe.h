@@ -237,7 +237,9 @@ moe_status moe_layer_fwd_static(const moe_layer_t *layer, const float *x, int32_
  * events[MOE_N_STAGES] after the last, for the stages
  *   0 routing (RMSNorm, router, selection, sort), 1 pass 1 GEMV segments,
  *   2 pass 1 MFMA segments, 3 pass 2 MFMA segments, 4 pass 2 GEMV segments
- *   (with the combine for batches up to 64 tokens), 5 combine.
+ *   (with the combine for batches up to 64 tokens whose down rows take 32
+ *   or 64 lanes: not MXFP4 or q4_0 rows with I not a multiple of 1024),
+ *   5 combine.
  * A stage that does not run for this call takes no time between its two
  * events.  events == NULL behaves as moe_layer_fwd; a NULL entry is
  * MOE_ERR_ARG.  For kernel timing in benchmarks; the extra event records
