@@ -955,6 +955,7 @@ hipError_t launch_mfma(int pass, int grid, hipStream_t st, const MfmaArgs &a);
 extern template hipError_t launch_mfma<MOE_BF16>(int, int, hipStream_t, const MfmaArgs &);
 extern template hipError_t launch_mfma<MOE_FP8_E4M3>(int, int, hipStream_t, const MfmaArgs &);
 extern template hipError_t launch_mfma<MOE_MXFP4>(int, int, hipStream_t, const MfmaArgs &);
+extern template hipError_t launch_mfma<MOE_Q4_0>(int, int, hipStream_t, const MfmaArgs &);
 template <int WDT>
 hipError_t launch_mfma_wide(int pass, int grid, hipStream_t st, const MfmaArgs &a);
 extern template hipError_t launch_mfma_wide<MOE_BF16>(int, int, hipStream_t, const MfmaArgs &);

@@ -75,14 +75,18 @@ template <int WDT>
 struct Stage {
     static constexpr bool kFp8 = WDT == MOE_FP8_E4M3;
     static constexpr bool kFp4 = WDT == MOE_MXFP4;
-    static constexpr int kRowB = kFp4 ? kKS / 2 : kKS * (kFp8 ? 1 : 2);  // bytes of a weight row per stage
+    static constexpr bool kQ4 = WDT == MOE_Q4_0;
+    static constexpr int kRowB = kFp4 || kQ4 ? kKS / 2 : kKS * (kFp8 ? 1 : 2);  // bytes of a weight row per stage
     static constexpr int kChunks = kRowB / 16;                // 16-byte chunks per weight row
     static constexpr int kWBytes = 32 * kRowB;                // weights of one stage
     static constexpr int kWLanes = kWBytes / kWaves / 16 < kWave ? kWBytes / kWaves / 16 : kWave;  // lanes per copy
     static constexpr int kWLoads = kWBytes / (kWLanes * 16) / kWaves;  // weight copies per wave per stage
     static constexpr int kXLoads = kXBytes / 1024 / kWaves;   // activation copies per wave per stage
-    static constexpr int kSLoads = kFp4 ? 1 : 0;              // scale-word copies per wave per stage
-    static constexpr int kSBytes = kFp4 ? kWaves * 32 * 4 : 0;  // MXFP4: each wave's 32 scale words
+    static constexpr int kSLoads = kFp4 || kQ4 ? 1 : 0;       // scale-word copies per wave per stage
+    // MXFP4: each wave's 32 scale words (4 E8M0 bytes a row); q4_0: 64 words
+    // (4 binary16 scales a row)
+    static constexpr int kSWave = kFp4 ? 32 * 4 : kQ4 ? 32 * 8 : 0;
+    static constexpr int kSBytes = kWaves * kSWave;
     static constexpr int kLoads = kWLoads + kXLoads + kSLoads;  // copies per wave per stage
     static constexpr int kBytes = kWBytes + kXBytes + kSBytes;
     // bytes past the last slot so that it holds the partial sums of an item
@@ -119,6 +123,31 @@ __device__ __forceinline__ u32x4 e2m1x8_to_bf16(unsigned w, float s) {
                  __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3))};
 }
 
+// 8 q4_0 codes of a word (bytes b0..b3 of a block's word g) as 8 bf16 values
+// code - 8 (exact): the low nibbles (block elements 4g .. 4g + 3), then the
+// high nibbles (16 + 4g .. 16 + 4g + 3).  A nibble with its top bit flipped,
+// read as a signed 4-bit field, is code - 8.
+__device__ __forceinline__ u32x4 q4x8_to_bf16(unsigned w) {
+    const int s = (int)(w ^ 0x88888888u);
+    float v[8];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        v[b] = (float)((s << (28 - 8 * b)) >> 28);
+        v[4 + b] = (float)((s << (24 - 8 * b)) >> 28);
+    }
+    return u32x4{bf16_pair_rne(v[0], v[1]), bf16_pair_rne(v[2], v[3]), bf16_pair_rne(v[4], v[5]),
+                 bf16_pair_rne(v[6], v[7])};
+}
+
+// A wave-uniform pointer (kept in scalar registers).
+template <typename P>
+__device__ __forceinline__ P *uniform_ptr(P *p) {
+    const unsigned long long v = (unsigned long long)p;
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+    return reinterpret_cast<P *>(((unsigned long long)hi << 32) | lo);
+}
+
 // Copy of 16 bytes per lane from base + off (base wave-uniform, off this
 // lane's byte offset) into LDS at dst + 16 * lane (dst wave-uniform; M0
 // carries it and is restored afterwards).  Issued from asm: the compiler,
@@ -138,7 +167,7 @@ __device__ __forceinline__ void copy_to_lds(const void *base, unsigned off, cons
         "global_load_lds_dwordx4 %1, %2\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "v"(off), "s"(base), "s"(l)
+        : "v"(off), "s"(uniform_ptr(base)), "s"(l)
         : "memory");
 }
 
@@ -154,18 +183,10 @@ __device__ __forceinline__ void copy_word_to_lds(const void *base, unsigned off,
         "global_load_lds_dword %1, %2\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "v"(off), "s"(base), "s"(l)
+        : "v"(off), "s"(uniform_ptr(base)), "s"(l)
         : "memory");
 }
 
-// A wave-uniform pointer (kept in scalar registers).
-template <typename P>
-__device__ __forceinline__ P *uniform_ptr(P *p) {
-    const unsigned long long v = (unsigned long long)p;
-    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
-    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
-    return reinterpret_cast<P *>(((unsigned long long)hi << 32) | lo);
-}
 
 // Wait until at most N of this wave's global loads are outstanding and all
 // of its LDS operations are done, then meet the other waves.  The copies
@@ -319,7 +340,7 @@ __device__ __forceinline__ void mfma_epilogue(const MfmaArgs &a, f32x4_t *red, c
 template <int WDT, int PASS>
 __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
     using S = Stage<WDT>;
-    constexpr bool kFp8 = S::kFp8, kFp4 = S::kFp4;
+    constexpr bool kFp8 = S::kFp8, kFp4 = S::kFp4, kQ4 = S::kQ4;
     constexpr int kRing = S::kRing;
     static_assert(kRing >= 3 && (kRing - 2) * S::kLoads + 1 <= 63, "ring depth");
     __shared__ __align__(1024) unsigned char ring[kRing * S::kBytes + S::kPad];
@@ -339,7 +360,8 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
     const int nst = K / kKS;
     const int n_rb = PASS == 1 ? a.I / 16 : a.H / 32;
     const int w_rows = PASS == 1 ? 2 * a.I : a.H;
-    const unsigned row_bytes = kFp4 ? (unsigned)K / 2 : (unsigned)K * WT<WDT>::kBytes;  // MXFP4: 2 codes a byte
+    // MXFP4 and q4_0: 2 codes a byte
+    const unsigned row_bytes = kFp4 || kQ4 ? (unsigned)K / 2 : (unsigned)K * WT<WDT>::kBytes;
     // bf16 activation rows: pass 1 reads xb [T, H]; pass 2 reads a[r] from the
     // first half of the fp32 activation row r (4I bytes apart)
     const unsigned src_stride = PASS == 1 ? (unsigned)a.H * 2 : (unsigned)a.I * 4;
@@ -439,12 +461,19 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
             const int chunk = pos ^ (rho & (S::kChunks - 1));
             c.woff[q] = (unsigned)(rho < 16 ? c.r0 + rho : r1 + rho - 16) * row_bytes + chunk * 16;
         }
-        // MXFP4 scale words: lane l < 32 copies the stage's word of row l
+        // MXFP4 scale words: lane l < 32 copies the stage's word of row l;
+        // q4_0: lane l copies word l & 1 of row l / 2 (a row's 4 binary16
+        // scales of the stage are two words)
         c.sbase = nullptr;
         c.soff = 0;
         if (kFp4) {
             c.sbase = uniform_ptr(static_cast<const unsigned char *>(a.scales) + (size_t)d.e * w_rows * sk);
             c.soff = (unsigned)((lane < 16 ? c.r0 + lane : r1 + (lane & 31) - 16) * sk);
+        }
+        if (kQ4) {
+            const int rho = lane >> 1;
+            c.sbase = uniform_ptr(static_cast<const unsigned char *>(a.scales) + (size_t)d.e * w_rows * (2 * sk));
+            c.soff = (unsigned)((rho < 16 ? c.r0 + rho : r1 + rho - 16) * (2 * sk) + (lane & 1) * 4);
         }
         // activation copies: only the waves whose token tile holds routes copy
         c.xw = wv * kTB / (16 * kWaves) < c.ntt;
@@ -469,7 +498,9 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
             for (int j = 0; j < S::kXLoads; ++j)
                 copy_to_lds(xbase + (size_t)ks * kXRowB, c.xoff[j], wd + S::kWBytes + (wv * S::kXLoads + j) * 1024);
         if (kFp4 && lane < 32)
-            copy_word_to_lds(uniform_ptr(c.sbase) + (size_t)ks * 4, c.soff, wd + S::kWBytes + kXBytes + wv * 128);
+            copy_word_to_lds(uniform_ptr(c.sbase) + (size_t)ks * 4, c.soff, wd + S::kWBytes + kXBytes + wv * S::kSWave);
+        if (kQ4)
+            copy_word_to_lds(uniform_ptr(c.sbase) + (size_t)ks * 8, c.soff, wd + S::kWBytes + kXBytes + wv * S::kSWave);
     };
     // stages 0 .. kRing - 2 of item c in flight, in slots 0 .. kRing - 2
     auto prologue = [&](const St &c) {
@@ -500,10 +531,14 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
     // Every operand of the stage is read before the copies of a later stage
     // are issued and before the first MFMA, so the LDS latency is paid once
     // per stage; tiles past ntt read rows that feed no output.
-    const int aoff = kFp4   ? ((wv ^ (m & 3)) << 4) + (g << 2)
+    const int aoff = kFp4 || kQ4 ? ((wv ^ (m & 3)) << 4) + (g << 2)
                      : kFp8 ? (((2 * wv + (g >> 1)) ^ (m & 7)) << 4) + ((g & 1) << 3)
                             : ((4 * wv + g) ^ m) << 4;
     const int boff = m * kXRowB + (((4 * wv + g) ^ m) << 4);
+    // q4_0: the activations of block elements 4g .. 4g + 3 and 16 + 4g ..
+    // 16 + 4g + 3 of k-step wv, in the order of the lane's weight codes
+    const int boffq0 = m * kXRowB + (((4 * wv + (g >> 1)) ^ m) << 4) + ((g & 1) << 3);
+    const int boffq1 = m * kXRowB + (((4 * wv + 2 + (g >> 1)) ^ m) << 4) + ((g & 1) << 3);
     // the next item's fp8 scales, written only by their loads inside the
     // loop (see load_scales)
     float n0 = 1.f, n1 = 1.f;
@@ -546,7 +581,17 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
             u32x4 a0, a1, b[kTT];
             uint2 c0, c1;
             unsigned f0 = 0, f1 = 0, e0 = 0, e1 = 0;
-            if (kFp4) {
+            float d0[4], d1[4];  // q4_0: scales of rows 4g .. 4g + 3 of both tiles, block wv
+            if (kQ4) {
+                const unsigned char *sd = wd + S::kWBytes + kXBytes + wv * S::kSWave;
+                f0 = *reinterpret_cast<const unsigned *>(wd + m * S::kRowB + aoff);
+                f1 = *reinterpret_cast<const unsigned *>(wd + (16 + m) * S::kRowB + aoff);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    d0[v] = f16_value(*reinterpret_cast<const unsigned short *>(sd + (4 * g + v) * 8 + 2 * wv));
+                    d1[v] = f16_value(*reinterpret_cast<const unsigned short *>(sd + (16 + 4 * g + v) * 8 + 2 * wv));
+                }
+            } else if (kFp4) {
                 const unsigned char *sd = wd + S::kWBytes + kXBytes + wv * 128;
                 f0 = *reinterpret_cast<const unsigned *>(wd + m * S::kRowB + aoff);
                 f1 = *reinterpret_cast<const unsigned *>(wd + (16 + m) * S::kRowB + aoff);
@@ -560,7 +605,15 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
                 a1 = *reinterpret_cast<const u32x4 *>(wd + (16 + m) * S::kRowB + aoff);
             }
 #pragma unroll
-            for (int tt = 0; tt < kTT; ++tt) b[tt] = *reinterpret_cast<const u32x4 *>(xd + tt * 16 * kXRowB + boff);
+            for (int tt = 0; tt < kTT; ++tt) {
+                if (kQ4) {
+                    const uint2 u0 = *reinterpret_cast<const uint2 *>(xd + tt * 16 * kXRowB + boffq0);
+                    const uint2 u1 = *reinterpret_cast<const uint2 *>(xd + tt * 16 * kXRowB + boffq1);
+                    b[tt] = u32x4{u0.x, u0.y, u1.x, u1.y};
+                } else {
+                    b[tt] = *reinterpret_cast<const u32x4 *>(xd + tt * 16 * kXRowB + boff);
+                }
+            }
 
             if (ks + kRing - 1 < nst) {
                 issue(cur, ks + kRing - 1, sl == 0 ? kRing - 1 : sl - 1);
@@ -569,6 +622,10 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
             if (kFp4) {
                 a0 = e2m1x8_to_bf16(f0, e8m0_value(e0));
                 a1 = e2m1x8_to_bf16(f1, e8m0_value(e1));
+            }
+            if (kQ4) {
+                a0 = q4x8_to_bf16(f0);
+                a1 = q4x8_to_bf16(f1);
             }
             if (kFp8) {
                 a0 = e4m3x8_to_bf16(c0.x, c0.y,
@@ -579,8 +636,18 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_kernel(MfmaArgs a) {
 #pragma unroll
             for (int tt = 0; tt < kTT; ++tt) {
                 if (tt < ntt) {
-                    acc0[tt] = mfma16(a0, b[tt], acc0[tt]);
-                    acc1[tt] = mfma16(a1, b[tt], acc1[tt]);
+                    if (kQ4) {  // one block per row: the k-step's sums times the rows' scales
+                        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+                        const f32x4_t p0 = mfma16(a0, b[tt], zero), p1 = mfma16(a1, b[tt], zero);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            acc0[tt][v] = fmaf(d0[v], p0[v], acc0[tt][v]);
+                            acc1[tt][v] = fmaf(d1[v], p1[v], acc1[tt][v]);
+                        }
+                    } else {
+                        acc0[tt] = mfma16(a0, b[tt], acc0[tt]);
+                        acc1[tt] = mfma16(a1, b[tt], acc1[tt]);
+                    }
                 }
             }
             sl = sl == kRing - 1 ? 0 : sl + 1;
@@ -616,5 +683,6 @@ hipError_t launch_mfma(int pass, int grid, hipStream_t st, const MfmaArgs &a) {
 template hipError_t launch_mfma<MOE_BF16>(int, int, hipStream_t, const MfmaArgs &);
 template hipError_t launch_mfma<MOE_FP8_E4M3>(int, int, hipStream_t, const MfmaArgs &);
 template hipError_t launch_mfma<MOE_MXFP4>(int, int, hipStream_t, const MfmaArgs &);
+template hipError_t launch_mfma<MOE_Q4_0>(int, int, hipStream_t, const MfmaArgs &);
 
 }  // namespace moe

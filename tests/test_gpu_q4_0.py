@@ -8,7 +8,8 @@ products in fp32 and applies the chunk's scale to the sum; every weight is
 exact in fp32, so the outputs follow the oracle to fp32 rounding (bar 1e-4,
 as for the other GEMV paths).  The per-code test places every code at every
 element position of a block, so a swapped nibble half or code offset fails
-it.  q4_0 experts never run on the matrix cores.
+it.  Below 128 tokens, segments at the matrix-core threshold run on the narrow
+MFMA kernels (tested against the oracle at the bf16-operand bar, 2e-2).
 
 Also here: down rows whose chunks would exceed a lane's largest instance at
 32 or 16 lanes per row (bf16 I = 2304, MXFP4 I = 7680), which take 64 lanes."""
@@ -18,7 +19,7 @@ import pytest
 import mixture_experts_decode_gemv_amd as moe
 import oracle
 import workload as wl
-from gpu_util import check_layer_against_oracle, dev, gpu_expert_fwd, gpu_layer_fwd, make_device_layer, note
+from gpu_util import call_tol, check_layer_against_oracle, dev, gpu_expert_fwd, gpu_layer_fwd, make_device_layer, note
 
 pytestmark = pytest.mark.gpu
 
@@ -81,11 +82,12 @@ def test_q4_0_layer_against_oracle(shape, T):
     spec = wl.LayerSpec(E=E, top_k=k, H=H, I=I, expert_dtype=wl.Q4_0, router_dtype=wl.BF16)
     w, layer, olayer = make_device_layer(spec)
     x = wl.make_x(T, H, draw=50 + T)
-    check_layer_against_oracle(layer, olayer, x, tol=1e-4)
-    outs = [gpu_layer_fwd(layer, x, f) for f in (moe.MOE_WALK_DEDUP, moe.MOE_WALK_PER_ROUTE,
-                                                  moe.MOE_WALK_DEDUP_PASS1, moe.MOE_NO_MFMA)]
+    check_layer_against_oracle(layer, olayer, x, tol=call_tol(layer, x))
+    check_layer_against_oracle(layer, olayer, x, flags=moe.MOE_NO_MFMA, tol=1e-4)
+    outs = [gpu_layer_fwd(layer, x, f | moe.MOE_NO_MFMA) for f in (moe.MOE_WALK_DEDUP, moe.MOE_WALK_PER_ROUTE,
+                                                                    moe.MOE_WALK_DEDUP_PASS1)]
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
-    assert moe.moe_mfma_min_routes(layer.struct, T, 0) == 0
+    assert (moe.moe_mfma_min_routes(layer.struct, T, 0) > 0) == (16 <= T < 128)
 
 
 @pytest.mark.parametrize("dtype,I", [(wl.BF16, 2304), (wl.MXFP4, 7680)], ids=["bf16-I2304", "mxfp4-I7680"])
@@ -100,3 +102,152 @@ def test_down_rows_beyond_eight_chunks_at_fewer_lanes(dtype, I, T):
     w, layer, olayer = make_device_layer(spec)
     x = wl.make_x(T, H, draw=60 + T)
     check_layer_against_oracle(layer, olayer, x, flags=moe.MOE_NO_MFMA, tol=1e-4)
+
+
+# ---------------------------------------------------------------------------
+# q4_0 segments on the matrix cores (narrow tiles, below 128 tokens): codes
+# minus 8 as exact bf16 operands, each k-step (one block per row) summed
+# fresh and scaled by the rows' binary16 scales.
+
+MIXED_Q4 = wl.LayerSpec(E=8, top_k=2, H=384, I=256, expert_dtype=wl.Q4_0)
+LONG_K_Q4 = wl.LayerSpec(E=8, top_k=2, H=2560, I=640, expert_dtype=wl.Q4_0)
+BF16_OPERAND_TOL = 2e-2
+
+
+def _max_rel(got, ref):
+    return float(np.max(np.abs(np.asarray(got, np.float64) - ref)) / max(np.max(np.abs(ref)), 1e-30))
+
+
+def _routing(kind, T, thr):
+    rng = np.random.default_rng(T)
+    rw = rng.uniform(0.1, 1.0, size=(T, 2))
+    rw /= rw.sum(1, keepdims=True)
+    if kind == "collide":  # every token on experts 0 and 1
+        return np.tile(np.array([[0, 1]], np.int32), (T, 1)), rw
+    ids = np.tile(np.array([[4, 5]], np.int32), (T, 1))  # edge: thr on {0, 1}, thr - 1 on {2, 3}
+    ids[:thr] = [0, 1]
+    ids[thr:2 * thr - 1] = [2, 3]
+    return ids, rw
+
+
+@pytest.mark.parametrize("T,kind", [(16, "collide"), (31, "edge"), (45, "collide"), (100, "collide")])
+def test_q4_0_mfma_expert_fwd(T, kind):
+    note("q4_0 mfma expert_fwd T=%d %s" % (T, kind))
+    w, layer, olayer = make_device_layer(MIXED_Q4)
+    x = wl.make_x(T, MIXED_Q4.H, draw=T)
+    thr = moe.moe_mfma_min_routes(layer.struct, T, 0)
+    assert thr > 0
+    ids, rw = _routing(kind, T, thr)
+    big = np.bincount(ids.ravel(), minlength=MIXED_Q4.E) >= thr
+    ref = oracle.expert_fwd(olayer, x, ids, rw)
+    got = gpu_expert_fwd(layer, x, ids, rw)
+    gemv = gpu_expert_fwd(layer, x, ids, rw, flags=moe.MOE_NO_MFMA)
+    note("  max rel err %.3g (GEMV path %.3g)" % (_max_rel(got, ref), _max_rel(gemv, ref)))
+    assert _max_rel(got, ref) <= BF16_OPERAND_TOL
+    assert _max_rel(gemv, ref) <= 1e-4
+    assert not np.array_equal(got, gemv), "no segment took the MFMA path"
+    small_only = ~big[ids].any(axis=1)
+    assert np.array_equal(got[small_only], gemv[small_only])
+    p1 = gpu_expert_fwd(layer, x, ids, rw, flags=moe.MOE_WALK_DEDUP_PASS1)
+    assert _max_rel(p1, ref) <= BF16_OPERAND_TOL
+    assert np.array_equal(gpu_expert_fwd(layer, x, ids, rw, flags=moe.MOE_WALK_PER_ROUTE), gemv)
+    assert np.array_equal(gpu_expert_fwd(layer, x, ids, rw), got)
+
+
+def test_q4_0_from_128_tokens_stays_on_gemv():
+    """The wide tiles take no q4_0: from 128 tokens every segment is a GEMV one."""
+    note("q4_0 at 128 tokens")
+    w, layer, olayer = make_device_layer(MIXED_Q4)
+    T = 128
+    x = wl.make_x(T, MIXED_Q4.H, draw=7)
+    ids, rw = _routing("collide", T, 0)
+    assert moe.moe_mfma_min_routes(layer.struct, T, 0) == 0
+    got = gpu_expert_fwd(layer, x, ids, rw)
+    assert np.array_equal(got, gpu_expert_fwd(layer, x, ids, rw, flags=moe.MOE_NO_MFMA))
+    assert _max_rel(got, oracle.expert_fwd(olayer, x, ids, rw)) <= 1e-4
+
+
+@pytest.mark.parametrize("T", [16, 45, 100])
+def test_q4_0_mfma_narrow_long_k(T):
+    """Pass 1 over 20 stages of 128 (the ring's steady state), pass 2 over 5;
+    one to four token blocks; bitwise unchanged under token permutation."""
+    note("q4_0 mfma long K T=%d" % T)
+    w, layer, olayer = make_device_layer(LONG_K_Q4)
+    x = wl.make_x(T, LONG_K_Q4.H, draw=40 + T)
+    ids, rw = _routing("collide", T, 0)
+    ref = oracle.expert_fwd(olayer, x, ids, rw)
+    got = gpu_expert_fwd(layer, x, ids, rw)
+    note("  max rel err %.3g" % _max_rel(got, ref))
+    assert _max_rel(got, ref) <= BF16_OPERAND_TOL
+    perm = np.random.default_rng(T).permutation(T)
+    c = gpu_expert_fwd(layer, x[perm], ids[perm], rw[perm])
+    assert np.array_equal(c[np.argsort(perm)], got)
+
+
+def _q4_codes_layer_128():
+    """One q4_0 expert, H = I = 128 (4 blocks per row).  Gate row i, column p
+    holds code (i + p) % 16 with scale 2^((i + p // 32) % 5 - 2); up rows hold
+    the value 1 (code 9, scale 1); down is the identity (code 9 on the
+    diagonal, 8 elsewhere) with scale 2^((3 h + h // 32) % 4 - 1) on row h."""
+    H = I = 128
+    gate = np.array([[(i + p) % 16 for p in range(H)] for i in range(I)])
+    up = np.full((I, H), 9)
+    gu = _pack(np.concatenate([gate, up]))[None]
+    s_gu = _f16(np.ones((1, 2 * I, H // 32)))
+    for i in range(I):
+        s_gu[0, i, :] = _f16([2.0 ** ((i + b) % 5 - 2) for b in range(H // 32)])
+    dn = _pack(np.where(np.eye(H, I, dtype=bool), 9, 8))[None]
+    s_dn = _f16(np.ones((1, H, I // 32)))
+    for h in range(H):
+        s_dn[0, h, :] = _f16(2.0 ** ((3 * h + h // 32) % 4 - 1))
+    spec = wl.LayerSpec(E=1, top_k=1, H=H, I=I, expert_dtype=wl.Q4_0, router_dtype=wl.BF16)
+    return dict(spec=spec, w_router=np.zeros((1, H), np.uint16), w_gate_up=gu, w_down=dn, s_gate_up=s_gu,
+                s_down=s_dn)
+
+
+def test_q4_0_mfma_every_code_every_position():
+    """Every q4_0 code at every column of a gate row, a scale per (row,
+    block), through the MFMA path (127 tokens, narrow tiles): (code - 8) *
+    scale is exact, so the only rounding is the activation's to bf16 before
+    the down projection (at most 2^-8 relative).  A swapped nibble half,
+    word or block, or a wrong row's scale, fails it."""
+    note("q4_0 mfma all codes")
+    w = _q4_codes_layer_128()
+    layer = moe.DeviceLayer(w, device=dev())
+    olayer = oracle.Layer(w)
+    T = 127
+    x = np.eye(T, 128, dtype=np.float32)
+    ids = np.zeros((T, 1), np.int32)
+    got = gpu_expert_fwd(layer, x, ids, np.ones((T, 1)))
+    ref = oracle.expert_fwd(olayer, x, ids, np.ones((T, 1)))
+    assert np.allclose(got, ref, rtol=2.0 ** -8 * 1.01, atol=1e-30)
+    gemv = gpu_expert_fwd(layer, x, ids, np.ones((T, 1)), flags=moe.MOE_NO_MFMA)
+    assert not np.array_equal(got, gemv)
+    assert np.allclose(gemv, ref, rtol=4e-7, atol=1e-30)
+
+
+def test_q4_0_scales_off_4_byte_alignment_stay_on_gemv():
+    """q4_0 scale arrays 2-byte but not 4-byte aligned are accepted, and every
+    segment stays on the GEMV kernels (the MFMA kernels copy scale words)."""
+    import torch
+
+    note("q4_0 2-byte aligned scales")
+    w, layer, olayer = make_device_layer(MIXED_Q4)
+    T = 64
+    x = wl.make_x(T, MIXED_Q4.H, draw=11)
+    ids, rw = _routing("collide", T, 0)
+    shifted = layer.with_bias(None)
+    for n in ("s_gate_up", "s_down"):
+        src = layer.tensors[n].reshape(-1).view(torch.uint8)
+        buf = torch.zeros(src.numel() + 16, dtype=torch.uint8, device=src.device)
+        buf[2:2 + src.numel()] = src
+        shifted.tensors[n + "_buf"] = buf
+    t = shifted.tensors
+    s = MIXED_Q4
+    shifted.struct = moe.moe_layer_t(s.E, s.top_k, s.H, s.I, s.router_dtype, s.expert_dtype,
+                                     t["w_router"].data_ptr(), t["w_gate_up"].data_ptr(), t["w_down"].data_ptr(),
+                                     t["s_gate_up_buf"].data_ptr() + 2, t["s_down_buf"].data_ptr() + 2, None)
+    got = gpu_expert_fwd(shifted, x, ids, rw)
+    gemv = gpu_expert_fwd(layer, x, ids, rw, flags=moe.MOE_NO_MFMA)
+    assert np.array_equal(got, gemv)
+    assert not np.array_equal(gpu_expert_fwd(layer, x, ids, rw), gemv), "the aligned layer takes the MFMA path"
