@@ -87,8 +87,7 @@ def parse():
                          "stack: 30-layer stack, one HIP graph vs a host-sync arm; "
                          "large: E=256 H=4096 I=1536 Zipf layer at bs 128/256/512 with MFMA segments")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp8", "mxfp4", "q4_0"],
-                    help="expert weights: bf16 or mxfp4 (every workload but stack), fp8 (large workload), "
-                         "q4_0 (sweep and skewed workloads, GEMV kernels)")
+                    help="expert weights: bf16, mxfp4 or q4_0 (every workload but stack), fp8 (large workload)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a device-to-device copy of this many MiB, 3 times (reference for HBM counters)")
     return ap.parse_args()
@@ -508,7 +507,8 @@ def stack_rows(torch, moe, wl, reps):
 # ---- the large-batch layer ----------------------------------------------------------
 
 def spec_name(dtype):
-    return {"fp8": "fp8 e4m3 (128x128 block scales)", "mxfp4": "MXFP4 (E2M1, E8M0 scale per 32)"}.get(dtype, "bf16")
+    return {"fp8": "fp8 e4m3 (128x128 block scales)", "mxfp4": "MXFP4 (E2M1, E8M0 scale per 32)",
+            "q4_0": "q4_0 (4-bit codes, binary16 scale per 32)"}.get(dtype, "bf16")
 
 
 def large_rows(torch, moe, wl, dtype, sizes, steps, warmup, draws):
@@ -517,10 +517,10 @@ def large_rows(torch, moe, wl, dtype, sizes, steps, warmup, draws):
     unique-expert bytes, MFMA TFLOP/s on the MFMA stages, and the roofline of
     the stage that dominates."""
     dev = torch.device("cuda:0")
-    spec = {"fp8": wl.LARGE_FP8, "mxfp4": wl.LARGE_MXFP4}.get(dtype, wl.LARGE)
+    spec = {"fp8": wl.LARGE_FP8, "mxfp4": wl.LARGE_MXFP4, "q4_0": wl.LARGE_Q4_0}.get(dtype, wl.LARGE)
     # bytes per weight, scales included: fp8 1 (+ 4 per 128x128 block), MXFP4
-    # half a byte plus one scale byte per 32
-    bpw = {wl.FP8: 1 + 4 / (128 * 128), wl.MXFP4: 17 / 32}.get(spec.expert_dtype, 2)
+    # half a byte plus one scale byte per 32, q4_0 two scale bytes per 32
+    bpw = {wl.FP8: 1 + 4 / (128 * 128), wl.MXFP4: 17 / 32, wl.Q4_0: 18 / 32}.get(spec.expert_dtype, 2)
     H, I = spec.H, spec.I
     expert_bytes = 3 * H * I * bpw
     bias = wl.zipf_bias(spec.E)
@@ -696,7 +696,8 @@ def main():
             "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None,
             "dtype": {"fp8": "fp8_e4m3 weights, bf16 MFMA operands",
-                      "mxfp4": "mxfp4 weights, bf16 MFMA operands"}.get(args.dtype, "bf16"),
+                      "mxfp4": "mxfp4 weights, bf16 MFMA operands",
+                      "q4_0": "q4_0 weights, bf16 MFMA operands"}.get(args.dtype, "bf16"),
             "data": "synthetic (seeded)",
             "config": {"workload": "large-batch single MoE layer, Zipf(1.1) routing, E=256 top_k=8 H=4096 I=1536 "
                                    "%s experts, MFMA for experts with >= 4 routes (moe_mfma_min_routes at 128+ tokens)" % spec_name(args.dtype),

@@ -124,6 +124,23 @@ __device__ __forceinline__ void q4x8_decode(uint32_t v, float *f) {
     }
 }
 
+// 8 q4_0 codes of a word (bytes b0..b3 of a block's word g) as 8 bf16 values
+// (code - 8) * scale: the low nibbles (block elements 4g .. 4g + 3), then the
+// high nibbles (16 + 4g .. 16 + 4g + 3).  Exact for scale 1 (and any power
+// of two); otherwise each product is rounded to bf16 once.  A nibble with
+// its top bit flipped, read as a signed 4-bit field, is code - 8.
+__device__ __forceinline__ u32x4 q4x8_to_bf16(unsigned w, float scale = 1.f) {
+    const int s = (int)(w ^ 0x88888888u);
+    float v[8];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        v[b] = (float)((s << (28 - 8 * b)) >> 28) * scale;
+        v[4 + b] = (float)((s << (24 - 8 * b)) >> 28) * scale;
+    }
+    return u32x4{bf16_pair_rne(v[0], v[1]), bf16_pair_rne(v[2], v[3]), bf16_pair_rne(v[4], v[5]),
+                 bf16_pair_rne(v[6], v[7])};
+}
+
 // IEEE binary16 bit pattern to fp32 (exact).
 __device__ __forceinline__ float f16_value(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (unsigned short)h);

@@ -158,12 +158,11 @@ static bool mfma_eligible(const moe_layer_t &L, int T, uint32_t flags) {
     // the wide ones mark unused rows with offsets from 2 GiB up
     const bool offsets32 = (unsigned long long)T * L.H * 2 < (1ull << 31) &&
                            (unsigned long long)T * L.top_k * L.I * 4 < (1ull << 31);
-    // MXFP4 and q4_0 scale words are copied 4 bytes at a time; q4_0 runs on
-    // the narrow tiles only (below kMfmaWideTokens tokens)
+    // MXFP4 and q4_0 scale words are copied 4 bytes at a time
     const bool s4 = (reinterpret_cast<uintptr_t>(L.s_gate_up) & 3) == 0 &&
                     (reinterpret_cast<uintptr_t>(L.s_down) & 3) == 0;
     const bool fp4_ok = L.expert_dtype == MOE_MXFP4 && s4;
-    const bool q4_ok = L.expert_dtype == MOE_Q4_0 && s4 && T < kMfmaWideTokens;
+    const bool q4_ok = L.expert_dtype == MOE_Q4_0 && s4;
     return (L.expert_dtype == MOE_BF16 || L.expert_dtype == MOE_FP8_E4M3 || fp4_ok || q4_ok) && L.H % 128 == 0 &&
            L.I % 128 == 0 &&
            !(flags & MOE_NO_MFMA) && T >= kMfmaMinTokens && (int)(flags & MOE_WALK_MASK) != MOE_WALK_PER_ROUTE &&
@@ -211,6 +210,7 @@ static hipError_t launch_mfma_pass(const moe_layer_t &L, int pass, int T, const 
     if (wide) switch (L.expert_dtype) {
             case MOE_BF16: return launch_mfma_wide<MOE_BF16>(pass, grid, st, a);
             case MOE_FP8_E4M3: return launch_mfma_wide<MOE_FP8_E4M3>(pass, grid, st, a);
+            case MOE_Q4_0: return launch_mfma_wide<MOE_Q4_0>(pass, grid, st, a);
             default: return launch_mfma_wide<MOE_MXFP4>(pass, grid, st, a);
         }
     switch (L.expert_dtype) {

@@ -961,6 +961,7 @@ hipError_t launch_mfma_wide(int pass, int grid, hipStream_t st, const MfmaArgs &
 extern template hipError_t launch_mfma_wide<MOE_BF16>(int, int, hipStream_t, const MfmaArgs &);
 extern template hipError_t launch_mfma_wide<MOE_FP8_E4M3>(int, int, hipStream_t, const MfmaArgs &);
 extern template hipError_t launch_mfma_wide<MOE_MXFP4>(int, int, hipStream_t, const MfmaArgs &);
+extern template hipError_t launch_mfma_wide<MOE_Q4_0>(int, int, hipStream_t, const MfmaArgs &);
 
 // Defined in experts_<dtype>.hip.
 extern template hipError_t launch_pass1<MOE_F32>(int, int, hipStream_t, const Pass1Args &);

@@ -123,22 +123,6 @@ __device__ __forceinline__ u32x4 e2m1x8_to_bf16(unsigned w, float s) {
                  __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3))};
 }
 
-// 8 q4_0 codes of a word (bytes b0..b3 of a block's word g) as 8 bf16 values
-// code - 8 (exact): the low nibbles (block elements 4g .. 4g + 3), then the
-// high nibbles (16 + 4g .. 16 + 4g + 3).  A nibble with its top bit flipped,
-// read as a signed 4-bit field, is code - 8.
-__device__ __forceinline__ u32x4 q4x8_to_bf16(unsigned w) {
-    const int s = (int)(w ^ 0x88888888u);
-    float v[8];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        v[b] = (float)((s << (28 - 8 * b)) >> 28);
-        v[4 + b] = (float)((s << (24 - 8 * b)) >> 28);
-    }
-    return u32x4{bf16_pair_rne(v[0], v[1]), bf16_pair_rne(v[2], v[3]), bf16_pair_rne(v[4], v[5]),
-                 bf16_pair_rne(v[6], v[7])};
-}
-
 // A wave-uniform pointer (kept in scalar registers).
 template <typename P>
 __device__ __forceinline__ P *uniform_ptr(P *p) {

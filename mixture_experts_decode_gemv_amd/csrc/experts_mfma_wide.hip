@@ -156,14 +156,15 @@ __device__ int build_item_table(const MfmaArgs &a, int nu, int n_rb, int *pre, i
 
 template <int WDT, int PASS>
 __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
-    constexpr bool kFp8 = WDT == MOE_FP8_E4M3, kFp4 = WDT == MOE_MXFP4;
-    constexpr int NWL = kFp4 ? 1 : kFp8 ? 2 : 4;  // 16-byte weight loads per tile per stage
+    constexpr bool kFp8 = WDT == MOE_FP8_E4M3, kFp4 = WDT == MOE_MXFP4, kQ4 = WDT == MOE_Q4_0;
+    constexpr int NWL = kFp4 || kQ4 ? 1 : kFp8 ? 2 : 4;  // 16-byte weight loads per tile per stage
     // stages in the register ring (kD - 1 in flight); deeper rings for the
     // narrower fp8 and MXFP4 stages measured slower (4 and 5 stages)
     constexpr int kD = 3;
-    constexpr int kStageB = kFp4 ? kKS / 2 : kKS * WT<WDT>::kBytes;  // bytes of a row per stage
+    constexpr int kStageB = kFp4 || kQ4 ? kKS / 2 : kKS * WT<WDT>::kBytes;  // bytes of a row per stage
     // per tile and stage: fp8 its block scale; MXFP4 the lane's row's 4 scale bytes
-    using ScaleT = std::conditional_t<kFp4, unsigned, float>;
+    // q4_0: the lane's row's 4 binary16 scales of the stage
+    using ScaleT = std::conditional_t<kFp4, unsigned, std::conditional_t<kQ4, uint2, float>>;
     __shared__ __align__(16) unsigned char xs[2 * kBufLds];
     __shared__ __align__(16) unsigned char wls[kBlock / kWave][kWTile];
     __shared__ int pre[kMaxE + 1];
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
     const int nst = K / kKS;
     const int n_rb = PASS == 1 ? a.I / 64 : a.H / 128;
     const int w_rows = PASS == 1 ? 2 * a.I : a.H;
-    const size_t row_bytes = kFp4 ? (size_t)K / 2 : (size_t)K * WT<WDT>::kBytes;  // MXFP4: 2 codes a byte
+    const size_t row_bytes = kFp4 || kQ4 ? (size_t)K / 2 : (size_t)K * WT<WDT>::kBytes;  // 4-bit: 2 codes a byte
     // bf16 activation rows: pass 1 reads xb [T, H]; pass 2 reads a[r] from the
     // first half of the fp32 activation row r (4I bytes apart)
     const size_t src_stride = PASS == 1 ? (size_t)a.H * 2 : (size_t)a.I * 4;
@@ -245,6 +246,15 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
             sp0 = reinterpret_cast<const unsigned *>(sb + (size_t)(r0 + (lane & 15)) * sk);
             sp1 = reinterpret_cast<const unsigned *>(sb + (size_t)(r1 + (lane & 15)) * sk);
         }
+        // q4_0: the scale words of rows r0 + lane % 16 and r1 + lane % 16 (two
+        // words, four binary16 scales, a row and stage; arrays 4-byte aligned)
+        const unsigned *sq0 = nullptr, *sq1 = nullptr;
+        if constexpr (kQ4) {
+            const size_t sk = (size_t)K / 16;  // bytes of scales per row
+            const unsigned char *sb = static_cast<const unsigned char *>(a.scales) + (size_t)e * w_rows * sk;
+            sq0 = reinterpret_cast<const unsigned *>(sb + (size_t)(r0 + (lane & 15)) * sk);
+            sq1 = reinterpret_cast<const unsigned *>(sb + (size_t)(r1 + (lane & 15)) * sk);
+        }
         // activation rows this thread stages: chunk tid % 16 of tokens
         // tid / 16 + 16 j (16 lanes fill one 256-byte row segment: contiguous
         // global reads and conflict-free LDS writes).  They are buffer loads:
@@ -280,9 +290,13 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
             const size_t off = (size_t)ks * kStageB;  // kKS elements
 #pragma unroll
             for (int c = 0; c < 2 * NWL; ++c) W[c] = *reinterpret_cast<const u32x4 *>(wsrc[c] + off);
-            if (kFp8 || kFp4) {
+            if constexpr (kFp8 || kFp4) {
                 S[0] = sp0[ks];
                 S[1] = sp1[ks];
+            }
+            if constexpr (kQ4) {
+                S[0] = make_uint2(sq0[2 * ks], sq0[2 * ks + 1]);
+                S[1] = make_uint2(sq1[2 * ks], sq1[2 * ks + 1]);
             }
         };
 
@@ -312,7 +326,13 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
                 for (int s = 0; s < 4; ++s) {
                     const int koff = 32 * s + 8 * g;  // k of this lane's 8 elements within the stage
                     u32x4 a0, a1;
-                    if constexpr (kFp4) {
+                    if constexpr (kQ4) {  // (code - 8) * the row's scale of block s, rounded to bf16
+                        const unsigned c0 = *reinterpret_cast<const unsigned *>(wa0 + koff / 2);
+                        const unsigned c1 = *reinterpret_cast<const unsigned *>(wa1 + koff / 2);
+                        const unsigned h0 = s < 2 ? S[0].x : S[0].y, h1 = s < 2 ? S[1].x : S[1].y;
+                        a0 = q4x8_to_bf16(c0, f16_value((h0 >> (16 * (s & 1))) & 0xffffu));
+                        a1 = q4x8_to_bf16(c1, f16_value((h1 >> (16 * (s & 1))) & 0xffffu));
+                    } else if constexpr (kFp4) {
                         const unsigned c0 = *reinterpret_cast<const unsigned *>(wa0 + koff / 2);
                         const unsigned c1 = *reinterpret_cast<const unsigned *>(wa1 + koff / 2);
                         a0 = e2m1x8_to_bf16(c0, e8m0_value((S[0] >> (8 * s)) & 0xffu));
@@ -328,7 +348,15 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
                     }
 #pragma unroll
                     for (int tt = 0; tt < NT; ++tt) {
-                        const u32x4 b = *reinterpret_cast<const u32x4 *>(xb + tt * 16 * kRowLds + koff * 2);
+                        u32x4 b;
+                        if constexpr (kQ4) {  // elements 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3 of block s
+                            const uint2 u0 = *reinterpret_cast<const uint2 *>(xb + tt * 16 * kRowLds + 64 * s + 8 * g);
+                            const uint2 u1 =
+                                *reinterpret_cast<const uint2 *>(xb + tt * 16 * kRowLds + 64 * s + 32 + 8 * g);
+                            b = u32x4{u0.x, u0.y, u1.x, u1.y};
+                        } else {
+                            b = *reinterpret_cast<const u32x4 *>(xb + tt * 16 * kRowLds + koff * 2);
+                        }
                         if constexpr (kFp8) {
                             p0[tt] = mfma16(a0, b, s == 0 ? zero : p0[tt]);
                             p1[tt] = mfma16(a1, b, s == 0 ? zero : p1[tt]);
@@ -354,7 +382,10 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
             u32x4 W[kD][2 * NWL], X[kD][kXChunks];
             ScaleT S[kD][2];
 #pragma unroll
-            for (int d = 0; d < kD; ++d) S[d][0] = S[d][1] = 1;
+            for (int d = 0; d < kD; ++d) {
+                if constexpr (kQ4) S[d][0] = S[d][1] = make_uint2(0u, 0u);
+                else S[d][0] = S[d][1] = 1;
+            }
             // Every stage issues the same loads (stage indices past the end are
             // clamped to the last stage) and the loop runs a multiple of kD
             // stages, so the compiler's wait counts see the same load sequence on
@@ -410,7 +441,7 @@ __global__ __launch_bounds__(kBlock, 2) void mfma_wide_kernel(MfmaArgs a) {
         };
         // (bf16: one body for all counts; four took more than 256 VGPRs)
         static_assert(kTT == 4, "token tiles 1 to 4");
-        if constexpr (kFp8 || kFp4) {
+        if constexpr (kFp8 || kFp4 || kQ4) {
             switch (ntt) {
                 case 1: run(std::integral_constant<int, 1>{}); break;
                 case 2: run(std::integral_constant<int, 2>{}); break;
@@ -434,5 +465,6 @@ hipError_t launch_mfma_wide(int pass, int grid, hipStream_t st, const MfmaArgs &
 template hipError_t launch_mfma_wide<MOE_BF16>(int, int, hipStream_t, const MfmaArgs &);
 template hipError_t launch_mfma_wide<MOE_FP8_E4M3>(int, int, hipStream_t, const MfmaArgs &);
 template hipError_t launch_mfma_wide<MOE_MXFP4>(int, int, hipStream_t, const MfmaArgs &);
+template hipError_t launch_mfma_wide<MOE_Q4_0>(int, int, hipStream_t, const MfmaArgs &);
 
 }  // namespace moe

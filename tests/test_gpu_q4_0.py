@@ -8,8 +8,9 @@ products in fp32 and applies the chunk's scale to the sum; every weight is
 exact in fp32, so the outputs follow the oracle to fp32 rounding (bar 1e-4,
 as for the other GEMV paths).  The per-code test places every code at every
 element position of a block, so a swapped nibble half or code offset fails
-it.  Below 128 tokens, segments at the matrix-core threshold run on the narrow
-MFMA kernels (tested against the oracle at the bf16-operand bar, 2e-2).
+it.  Segments at the matrix-core threshold run on the MFMA kernels (narrow
+tiles below 128 tokens, wide from 128), tested against the oracle at the
+bf16-operand bar, 2e-2.
 
 Also here: down rows whose chunks would exceed a lane's largest instance at
 32 or 16 lanes per row (bf16 I = 2304, MXFP4 I = 7680), which take 64 lanes."""
@@ -87,7 +88,7 @@ def test_q4_0_layer_against_oracle(shape, T):
     outs = [gpu_layer_fwd(layer, x, f | moe.MOE_NO_MFMA) for f in (moe.MOE_WALK_DEDUP, moe.MOE_WALK_PER_ROUTE,
                                                                     moe.MOE_WALK_DEDUP_PASS1)]
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
-    assert (moe.moe_mfma_min_routes(layer.struct, T, 0) > 0) == (16 <= T < 128)
+    assert (moe.moe_mfma_min_routes(layer.struct, T, 0) > 0) == (T >= 16)
 
 
 @pytest.mark.parametrize("dtype,I", [(wl.BF16, 2304), (wl.MXFP4, 7680)], ids=["bf16-I2304", "mxfp4-I7680"])
@@ -105,9 +106,10 @@ def test_down_rows_beyond_eight_chunks_at_fewer_lanes(dtype, I, T):
 
 
 # ---------------------------------------------------------------------------
-# q4_0 segments on the matrix cores (narrow tiles, below 128 tokens): codes
-# minus 8 as exact bf16 operands, each k-step (one block per row) summed
-# fresh and scaled by the rows' binary16 scales.
+# q4_0 segments on the matrix cores.  Narrow tiles (below 128 tokens): codes
+# minus 8 as exact bf16 operands, each k-step (one block per row) summed fresh
+# and scaled by the rows' binary16 scales.  Wide tiles: (code - 8) * scale
+# rounded to bf16 once.
 
 MIXED_Q4 = wl.LayerSpec(E=8, top_k=2, H=384, I=256, expert_dtype=wl.Q4_0)
 LONG_K_Q4 = wl.LayerSpec(E=8, top_k=2, H=2560, I=640, expert_dtype=wl.Q4_0)
@@ -154,17 +156,30 @@ def test_q4_0_mfma_expert_fwd(T, kind):
     assert np.array_equal(gpu_expert_fwd(layer, x, ids, rw), got)
 
 
-def test_q4_0_from_128_tokens_stays_on_gemv():
-    """The wide tiles take no q4_0: from 128 tokens every segment is a GEMV one."""
-    note("q4_0 at 128 tokens")
+@pytest.mark.parametrize("T", [128, 300])
+def test_q4_0_wide_tiles(T):
+    """From 128 tokens q4_0 segments run on the wide tiles, whose operands are
+    (code - 8) * scale rounded to bf16 once: within the bf16-operand bar,
+    deterministic, stable under token permutation, GEMV-only rows unchanged."""
+    note("q4_0 wide tiles T=%d" % T)
     w, layer, olayer = make_device_layer(MIXED_Q4)
-    T = 128
     x = wl.make_x(T, MIXED_Q4.H, draw=7)
-    ids, rw = _routing("collide", T, 0)
-    assert moe.moe_mfma_min_routes(layer.struct, T, 0) == 0
+    thr = moe.moe_mfma_min_routes(layer.struct, T, 0)
+    assert thr > 0
+    ids, rw = _routing("edge", T, thr)
+    big = np.bincount(ids.ravel(), minlength=MIXED_Q4.E) >= thr
+    ref = oracle.expert_fwd(olayer, x, ids, rw)
     got = gpu_expert_fwd(layer, x, ids, rw)
-    assert np.array_equal(got, gpu_expert_fwd(layer, x, ids, rw, flags=moe.MOE_NO_MFMA))
-    assert _max_rel(got, oracle.expert_fwd(olayer, x, ids, rw)) <= 1e-4
+    gemv = gpu_expert_fwd(layer, x, ids, rw, flags=moe.MOE_NO_MFMA)
+    note("  max rel err %.3g" % _max_rel(got, ref))
+    assert _max_rel(got, ref) <= BF16_OPERAND_TOL
+    assert not np.array_equal(got, gemv)
+    small_only = ~big[ids].any(axis=1)
+    assert np.array_equal(got[small_only], gemv[small_only])
+    assert np.array_equal(gpu_expert_fwd(layer, x, ids, rw), got)
+    perm = np.random.default_rng(T).permutation(T)
+    c = gpu_expert_fwd(layer, x[perm], ids[perm], rw[perm])
+    assert np.array_equal(c[np.argsort(perm)], got)
 
 
 @pytest.mark.parametrize("T", [16, 45, 100])
@@ -205,17 +220,17 @@ def _q4_codes_layer_128():
                 s_down=s_dn)
 
 
-def test_q4_0_mfma_every_code_every_position():
-    """Every q4_0 code at every column of a gate row, a scale per (row,
-    block), through the MFMA path (127 tokens, narrow tiles): (code - 8) *
+@pytest.mark.parametrize("T", [127, 128], ids=["narrow", "wide"])
+def test_q4_0_mfma_every_code_every_position(T):
+    """Every q4_0 code at every column of a gate row, a power-of-two scale per
+    (row, block), through the MFMA path (narrow and wide tiles): (code - 8) *
     scale is exact, so the only rounding is the activation's to bf16 before
     the down projection (at most 2^-8 relative).  A swapped nibble half,
     word or block, or a wrong row's scale, fails it."""
-    note("q4_0 mfma all codes")
+    note("q4_0 mfma all codes T=%d" % T)
     w = _q4_codes_layer_128()
     layer = moe.DeviceLayer(w, device=dev())
     olayer = oracle.Layer(w)
-    T = 127
     x = np.eye(T, 128, dtype=np.float32)
     ids = np.zeros((T, 1), np.int32)
     got = gpu_expert_fwd(layer, x, ids, np.ones((T, 1)))

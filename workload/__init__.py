@@ -247,6 +247,7 @@ STACK = LayerSpec(E=128, top_k=2, H=2048, I=1024)
 LARGE = LayerSpec(E=256, top_k=8, H=4096, I=1536)
 LARGE_FP8 = LayerSpec(E=256, top_k=8, H=4096, I=1536, expert_dtype=FP8)
 LARGE_MXFP4 = LayerSpec(E=256, top_k=8, H=4096, I=1536, expert_dtype=MXFP4)
+LARGE_Q4_0 = LayerSpec(E=256, top_k=8, H=4096, I=1536, expert_dtype=Q4_0)
 SWEEP_MXFP4 = LayerSpec(E=256, top_k=8, H=2048, I=768, expert_dtype=MXFP4)
 SWEEP_Q4_0 = LayerSpec(E=256, top_k=8, H=2048, I=768, expert_dtype=Q4_0)
 
