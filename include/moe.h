@@ -105,9 +105,10 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3, MOE_Q
  * block is 16 code bytes, element j < 16 in the low nibble of byte j and
  * element j + 16 in its high nibble (a row of K elements is K/2 bytes); the
  * scales sit in their own arrays, binary16 bit patterns, 2-byte aligned:
- * s_gate_up uint16 [E, 2I, H/32], s_down uint16 [E, H, I/32].  q4_0 experts
- * reach the matrix cores below 128 tokens only (narrow tiles; their scale
- * arrays 4-byte aligned), else they run on the GEMV kernels.
+ * s_gate_up uint16 [E, 2I, H/32], s_down uint16 [E, H, I/32].  On the
+ * matrix cores (scale arrays 4-byte aligned) the codes minus 8 are exact bf16
+ * operands below 128 tokens, each k-step's sums scaled by the rows' scales;
+ * from 128 tokens each operand is (code - 8) * scale rounded to bf16 once.
  *
  * Matrix cores: in a call of 16 or more tokens, an expert that holds
  * moe_mfma_min_routes() routes or more (5 below 128 tokens, 4 from 128) runs,
