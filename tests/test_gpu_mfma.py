@@ -436,3 +436,31 @@ def test_layer_mfma_only_with_a_hot_expert(largest):
         assert np.array_equal(got[~mf], gemv[~mf])
         assert not np.array_equal(got[mf], gemv[mf])
         assert max_rel(got, ref) <= BF16_OPERAND_TOL
+
+
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.FP8, wl.MXFP4, wl.Q4_0], ids=["bf16", "fp8", "mxfp4", "q4_0"])
+def test_mfma_narrow_many_items_per_workgroup(dtype):
+    """Eight hot experts of 100 routes each on the narrow tiles (H = 2048,
+    I = 768): 1536 pass-1 and 2048 pass-2 items, 3 and 4 per workgroup of the
+    512-workgroup grid, so each workgroup takes its next item's route ids,
+    scales and first stages while it finishes the current one.  Against the
+    oracle at the bf16-operand bar, deterministic, and bitwise stable under
+    token permutation."""
+    note("mfma narrow many items per workgroup %s" % wl.DTYPE_NAMES[dtype])
+    spec = wl.LayerSpec(E=16, top_k=8, H=2048, I=768, expert_dtype=dtype, router_dtype=wl.BF16)
+    w, layer, olayer = make_device_layer(spec)
+    T = 100
+    x = wl.make_x(T, spec.H, draw=90)
+    ids = np.tile(np.arange(8, dtype=np.int32), (T, 1))
+    rw = np.random.default_rng(90).uniform(0.1, 1.0, size=(T, 8))
+    rw /= rw.sum(1, keepdims=True)
+    assert _min_routes(layer, T) > 0
+    ref = oracle.expert_fwd(olayer, x, ids, rw)
+    got = gpu_expert_fwd(layer, x, ids, rw)
+    note("  max rel err %.3g" % max_rel(got, ref))
+    assert max_rel(got, ref) <= BF16_OPERAND_TOL
+    assert not np.array_equal(got, gpu_expert_fwd(layer, x, ids, rw, flags=moe.MOE_NO_MFMA))
+    assert np.array_equal(gpu_expert_fwd(layer, x, ids, rw), got)
+    perm = np.random.default_rng(91).permutation(T)
+    c = gpu_expert_fwd(layer, x[perm], ids[perm], rw[perm])
+    assert np.array_equal(c[np.argsort(perm)], got)
