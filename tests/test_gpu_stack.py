@@ -121,11 +121,13 @@ def test_stack_fused_equals_layer_calls(T, flags):
     assert np.array_equal(_fused(layers, x0, T, flags), ref)
 
 
-@pytest.mark.parametrize("dtype", [wl.FP8, wl.MXFP4], ids=["fp8", "mxfp4"])
-@pytest.mark.parametrize("T", [3, 40])
+@pytest.mark.parametrize("dtype", [wl.FP8, wl.MXFP4, wl.Q4_0], ids=["fp8", "mxfp4", "q4_0"])
+@pytest.mark.parametrize("T", [3, 40, 130])
 def test_stack_fused_equals_layer_calls_quantised(dtype, T):
-    """fp8 (128x128 block scales) and MXFP4 experts, below and above the
-    MFMA threshold."""
+    """fp8 (128x128 block scales), MXFP4 and q4_0 experts, below and above
+    the MFMA threshold, on narrow and wide tiles; MXFP4 and q4_0 down rows of
+    8 chunks (I = 256) take pass 2 without the combine at any batch, so the
+    next layer's routing launch forms the combine."""
     spec = wl.LayerSpec(E=16, top_k=5, H=512, I=256, expert_dtype=dtype, router_dtype=wl.BF16)
     note("fused stack, %s, T=%d" % (wl.DTYPE_NAMES[dtype], T))
     bias = np.zeros(spec.E, np.float32)
