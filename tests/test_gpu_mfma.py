@@ -297,7 +297,7 @@ def test_mxfp4_unaligned_scales_stay_on_gemv():
 
 # ---------------------------------------------------------------------------
 # The large-batch regime at its full size: E=256, top_k=8, H=4096, I=1536,
-# Zipf(1.1)-skewed routing, bf16, fp8 e4m3 with 128x128 block scales, MXFP4.
+# Zipf(1.1)-skewed routing, bf16, fp8 e4m3 with 128x128 block scales, MXFP4, q4_0.
 # Every token's routing is checked; outputs on sampled tokens.
 
 def _sample(g, T, thr, n_random=6):
@@ -368,6 +368,21 @@ def large_mxfp4():
 def test_large_mxfp4_sampled(large_mxfp4, T):
     note("large mxfp4 T=%d" % T)
     _run_large(large_mxfp4, T)
+
+
+@pytest.fixture(scope="module")
+def large_q4_0():
+    note("generating the E=256 H=4096 I=1536 q4_0 layer")
+    yield _large(wl.LARGE_Q4_0)
+
+
+@pytest.mark.parametrize("T", [64, 128])
+def test_large_q4_0_sampled(large_q4_0, T):
+    """q4_0 at the large layer's size: narrow tiles (exact operands, sums
+    scaled per k-step) at 64 tokens, wide tiles ((code - 8) * scale rounded
+    to bf16) at 128."""
+    note("large q4_0 T=%d" % T)
+    _run_large(large_q4_0, T)
 
 
 def test_mfma_narrow_many_experts():
