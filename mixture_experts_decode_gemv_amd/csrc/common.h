@@ -111,17 +111,23 @@ __device__ __forceinline__ void e2m1x8_decode(uint32_t v, float *f) {
 }
 
 // 8 q4_0 codes of a 32-bit word (bytes b0..b3 of a block's word v) as the
-// exact fp32 values code - 8: f[0..3] the low nibbles (elements 4v .. 4v + 3
-// of the block), f[4..7] the high nibbles (elements 16 + 4v .. 16 + 4v + 3).
-// With every nibble's top bit flipped, a nibble read as a signed 4-bit field
-// is code - 8: one signed bitfield extract and one conversion per element.
-__device__ __forceinline__ void q4x8_decode(uint32_t v, float *f) {
-    const int s = (int)(v ^ 0x88888888u);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        f[b] = (float)((s << (28 - 8 * b)) >> 28);
-        f[4 + b] = (float)((s << (24 - 8 * b)) >> 28);
-    }
+// exact fp32 values (code - 8) / 16: f[0..3] the low nibbles (elements
+// 4v .. 4v + 3 of the block), f[4..7] the high nibbles (elements 16 + 4v ..
+// 16 + 4v + 3); callers fold the 16 into the block's scale, which leaves every
+// sum the one of code - 8 times x, scaled by a power of two.  With every
+// nibble's top bit flipped, a nibble read as a signed 4-bit field is
+// code - 8, which v_cvt_off_f32_i4 converts (divided by 16) from the low 4
+// bits of the byte its SDWA operand selects: one instruction per element.
+__device__ __forceinline__ void q4x8_decode16(uint32_t v, float *f) {
+    const uint32_t lo = v ^ 0x88888888u, hi = lo >> 4;
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(f[0]) : "v"(lo));
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(f[1]) : "v"(lo));
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(f[2]) : "v"(lo));
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(f[3]) : "v"(lo));
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(f[4]) : "v"(hi));
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(f[5]) : "v"(hi));
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(f[6]) : "v"(hi));
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(f[7]) : "v"(hi));
 }
 
 // 8 q4_0 codes of a word (bytes b0..b3 of a block's word g) as 8 bf16 values

@@ -234,9 +234,10 @@ __device__ __forceinline__ void dot_rows(u32x4 (&w)[NS][NC], const float (&sc)[N
         // scaled by the chunk's scale (E8M0, or q4_0's binary16).  MXFP4
         // word v holds elements 8v .. 8v + 7; q4_0 word v elements
         // 4v .. 4v + 3 (low nibbles) and 16 + 4v .. 16 + 4v + 3 (high).
-        // Each element's value is exact in fp32 (a q4_0 code minus 8: taking
-        // the offset out of the sums instead, as sum q x - 8 sum x, loses
-        // the low bits of a small sum to cancellation).
+        // Each element's value is exact in fp32 (q4_0: (code - 8) / 16, the
+        // 16 folded into the scale; taking the offset out of the sums instead,
+        // as sum q x - 8 sum x, loses the low bits of a small sum to
+        // cancellation).
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const int q = sub + G * c;
@@ -260,7 +261,7 @@ __device__ __forceinline__ void dot_rows(u32x4 (&w)[NS][NC], const float (&sc)[N
                     for (int s = 0; s < NS; ++s) {
                         const uint32_t word = v == 0 ? w[s][c].x : v == 1 ? w[s][c].y : v == 2 ? w[s][c].z : w[s][c].w;
                         float wf[8];
-                        if constexpr (WDT == MOE_Q4_0) q4x8_decode(word, wf);
+                        if constexpr (WDT == MOE_Q4_0) q4x8_decode16(word, wf);
                         else e2m1x8_decode(word, wf);
 #pragma unroll
                         for (int r = 0; r < RB; ++r)
@@ -389,8 +390,8 @@ __global__ __launch_bounds__(kGemvBlock) void pass1_kernel(Pass1Args a) {
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
                     const int q = min(lane + G * c, nq - 1);
-                    sc[2 * p][c] = f16_value(sg[((size_t)e * 2 * I + i) * nq + q]);
-                    sc[2 * p + 1][c] = f16_value(sg[((size_t)e * 2 * I + I + i) * nq + q]);
+                    sc[2 * p][c] = 16.f * f16_value(sg[((size_t)e * 2 * I + i) * nq + q]);  // decode's 1/16
+                    sc[2 * p + 1][c] = 16.f * f16_value(sg[((size_t)e * 2 * I + I + i) * nq + q]);
                 }
             }
         }
@@ -501,7 +502,7 @@ __device__ __forceinline__ void down_rows(const void *down, const void *s_down, 
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 const int q = min((lane & (G - 1)) + G * c, nq - 1);
-                sc[j][c] = f16_value(sd[((size_t)e * H + h) * nq + q]);
+                sc[j][c] = 16.f * f16_value(sd[((size_t)e * H + h) * nq + q]);  // decode's 1/16
             }
         }
     }
