@@ -55,13 +55,17 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
         objs.append(obj)
         cmds.append([HIPCC, *compile_flags, "-c", src, "-o", obj])
     jobs = jobs or max(1, min(len(cmds), os.cpu_count() or 1, 16))
-    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB + ".tmp%d" % os.getpid()
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    for o in objs:
-        os.remove(o)
+    try:
+        with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+            list(ex.map(lambda c: _run(c, verbose), cmds))
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+        os.replace(tmp, LIB)
+    finally:
+        # Objects are per build process; a failed build leaves none behind.
+        for o in objs + [tmp]:
+            if os.path.exists(o):
+                os.remove(o)
     ptmp = PROBE_LIB + ".tmp%d" % os.getpid()
     _run([HIPCC, *FLAGS, PROBE_SRC, "-o", ptmp], verbose)
     os.replace(ptmp, PROBE_LIB)
