@@ -61,3 +61,19 @@ def test_static_scratch_refuses_a_batch_it_cannot_hold():
     with pytest.raises(moe.MoeError) as e:
         moe.moe_layer_fwd_static(big, x, T, x, 0, stream())
     assert e.value.status == 4
+
+
+@pytest.mark.parametrize("dtype", [wl.FP8, wl.MXFP4, wl.Q4_0], ids=["fp8", "mxfp4", "q4_0"])
+def test_static_scratch_weight_formats(dtype):
+    """The skewed layer shape with fp8, MXFP4 and q4_0 experts: 150 tokens
+    (wide tiles), 64 (narrow MFMA items: some expert holds 8 or more routes)
+    and 8 (GEMV kernels only), in that order on the one array."""
+    spec = wl.LayerSpec(E=256, top_k=6, H=2048, I=768, expert_dtype=dtype)
+    w, layer, _ = make_device_layer(spec, wl.zipf_bias(spec.E))
+    for T in (150, 64, 8):
+        note("static scratch, skewed shape, expert dtype %d, T=%d" % (dtype, T))
+        assert moe.moe_workspace_bytes(layer.struct, T) <= moe.MOE_STATIC_SCRATCH_BYTES
+        x = wl.make_x(T, spec.H, draw=1300 + T)
+        got = _static(layer, x)
+        assert np.isfinite(got).all()
+        assert np.array_equal(got, gpu_layer_fwd(layer, x))
