@@ -116,8 +116,9 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3, MOE_Q
  * moe_mfma_hot_routes() routes or more (8 below 128 tokens), both passes as
  * bf16 MFMA products with fp32 accumulation (the activations
  * and the decoded weights rounded to bf16; decoded MXFP4 weights are exact in
- * bf16) when the experts are bf16, fp8 or MXFP4 with H and I multiples of
- * 128 (MXFP4 also needs 4-byte aligned scale arrays), unless the flags ask
+ * bf16) when the experts are bf16, fp8, MXFP4 or q4_0 with H and I multiples
+ * of 128 (MXFP4 and q4_0 also need 4-byte aligned scale arrays; q4_0 operands
+ * as described above), unless the flags ask
  * for MOE_NO_MFMA or the per-route walk.  Every other segment runs on the
  * GEMV kernels (fp32 accumulation of exactly decoded weights). */
 typedef struct {

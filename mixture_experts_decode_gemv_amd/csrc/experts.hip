@@ -149,7 +149,7 @@ static int persistent_grid(long long max_items) {
 }
 
 // Segments with at least mfma_min_routes routes go to the MFMA kernels when
-// the weights are bf16, fp8 or MXFP4 with H and I multiples of 128, unless the
+// the weights are bf16, fp8, MXFP4 or q4_0 with H and I multiples of 128, unless the
 // caller asked for the GEMV path only, and from kMfmaMinTokens tokens on
 // (below that the MFMA launches would mostly be idle, and batches up to
 // kPass2cMaxT tokens run pass 2 with the combine, on GEMV segments only).
