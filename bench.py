@@ -46,7 +46,7 @@ MFMA_PEAK_TFS = 2500.0  # dense bf16
 # (uniform routing, bs=64), from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
 # scaled by a 1 GiB copy calibration: profiles/pass_kernels_uniform_bs64_hbm_counters.md.
 # Reported only while the kernel source is the one that was measured.
-PASS1_TRAFFIC_BS64 = {"read_bytes": 1.38556e+09, "write_bytes": 1.53467e+06, "source": "4fa9e85aeb7731fa"}
+PASS1_TRAFFIC_BS64 = {"read_bytes": 1.38555e+09, "write_bytes": 1.53456e+06, "source": "b5d718c057119eb6"}
 
 
 def pass1_source_fingerprint():

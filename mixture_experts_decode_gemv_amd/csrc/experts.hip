@@ -138,12 +138,12 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const float *__restrict
 }
 
 // ---- launchers -------------------------------------------------------------------
-// GEMV grids: up to 16 workgroups of 256 threads per CU (4096 threads), of
-// which a quarter are resident at a time;
-// the later ones start as the first finish, which evens out the tail (1 %
-// faster than 8 per CU at bs = 64, 2 % at bs = 8).
+// GEMV grids: up to 32 workgroups of 256 threads per CU (8192 threads), of
+// which an eighth are resident at a time; the later ones start as the first
+// finish, which evens out the tail (16 per CU: 1 % slower at bs = 64 in bf16,
+// MXFP4 and q4_0; 8 per CU slower again, 48 per CU slower on skewed routing).
 static int persistent_grid(long long max_items) {
-    const long long cap = (long long)num_cus() * (16 * 256 / kGemvBlock);
+    const long long cap = (long long)num_cus() * (32 * 256 / kGemvBlock);
     long long g = max_items < cap ? max_items : cap;
     return (int)(g < 1 ? 1 : g);
 }
